@@ -1,0 +1,182 @@
+"""ctypes front end of the fp64 CPU oracle (``oracle/sfi_oracle.c``).
+
+TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
+CPU-baseline leg import this package.  It builds ``liboracle.so`` with gcc (no fast-math)
+and wraps the four reference functions.  Inputs are torch tensors (any device: they are
+copied to host memory) holding exactly the bytes the GPU reads; results are float64
+numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sfi_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle (plain gcc, -O2, OpenMP, IEEE double semantics)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("is_bf16", ctypes.c_int32),
+                ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("n_cap", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("block_size", ctypes.c_int32),
+                ("max_blocks", ctypes.c_int32), ("len", ctypes.c_void_p)]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        L.orc_dense.argtypes = [ctypes.POINTER(_Cache), P, P, P, P, ctypes.c_int64]
+        L.orc_select.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                                 ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 P, ctypes.c_int32, P, P]
+        L.orc_sparse.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int32, P,
+                                 ctypes.c_int32, P, P, P]
+        L.orc_sink_mask.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_double, P]
+        for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _host_bytes(t: torch.Tensor) -> np.ndarray:
+    """Host copy of a tensor's raw bytes (bf16 kept as uint16 bits)."""
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.int32:
+        return t.numpy()
+    if t.dtype == torch.uint8:
+        return t.numpy()
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Cache:
+    """Host copy of a KV cache in the library's layout (contiguous or paged)."""
+
+    def __init__(self, k, v, lens, Hq, block_table=None, block_size=0, max_blocks=0):
+        self.k = _host_bytes(k)
+        self.v = _host_bytes(v)
+        self.is_bf16 = int(k.dtype == torch.bfloat16)
+        self.lens = np.ascontiguousarray(np.asarray(
+            lens.cpu() if torch.is_tensor(lens) else lens, dtype=np.int32))
+        self.B = int(self.lens.shape[0])
+        self.Hq = int(Hq)
+        if block_table is None:
+            assert k.dim() == 4
+            self.Hkv, self.n_cap, self.d = int(k.shape[1]), int(k.shape[2]), int(k.shape[3])
+            self.bt = None
+            self.block_size = 0
+            self.max_blocks = 0
+        else:
+            self.Hkv, self.d = int(k.shape[1]), int(k.shape[3])
+            self.n_cap = 0
+            self.bt = _host_bytes(block_table.to(torch.int32))
+            self.block_size = int(block_size)
+            self.max_blocks = int(max_blocks)
+
+    def with_lens(self, lens):
+        c = object.__new__(Cache)
+        c.__dict__.update(self.__dict__)
+        c.lens = np.ascontiguousarray(np.asarray(
+            lens.cpu() if torch.is_tensor(lens) else lens, dtype=np.int32))
+        return c
+
+    def _struct(self):
+        return _Cache(self.B, self.Hq, self.Hkv, self.d, self.is_bf16,
+                      self.k.ctypes.data, self.v.ctypes.data, self.n_cap,
+                      self.bt.ctypes.data if self.bt is not None else None,
+                      self.block_size, self.max_blocks, self.lens.ctypes.data)
+
+
+def dense(cache: Cache, q, logit_stride: int | None = None, want_logits: bool = True):
+    """Returns (out [B][Hq][d], lse [B][Hq], logits [B][Hq][stride] or None), float64."""
+    qh = _host_bytes(q)
+    stride = int(logit_stride or max(int(cache.lens.max()), 1))
+    out = np.zeros((cache.B, cache.Hq, cache.d), np.float64)
+    lse = np.zeros((cache.B, cache.Hq), np.float64)
+    logits = np.full((cache.B, cache.Hq, stride), np.nan, np.float64) if want_logits else None
+    s = cache._struct()
+    rc = lib().orc_dense(ctypes.byref(s), _ptr(qh), _ptr(out), _ptr(lse),
+                         _ptr(logits) if logits is not None else None, stride)
+    assert rc == 0
+    return out, lse, logits
+
+
+def select(lens, Hq: int, Hkv: int, logits, n_sink: int, n_recent: int, k_sel: int,
+           idx_stride: int | None = None, want_f: bool = False):
+    """logits: array-like [B][Hq][stride] (fp32 values are widened exactly).
+    Returns (idx int32 [B][Hkv][idx_stride], n_idx int32 [B][Hkv], f or None)."""
+    z = np.ascontiguousarray(np.asarray(logits.cpu() if torch.is_tensor(logits) else logits,
+                                        dtype=np.float64))
+    B, _, stride = z.shape
+    lens = np.ascontiguousarray(np.asarray(lens.cpu() if torch.is_tensor(lens) else lens,
+                                           dtype=np.int32))
+    idx_stride = int(idx_stride or (n_sink + k_sel))
+    idx = np.zeros((B, Hkv, idx_stride), np.int32)
+    n_idx = np.zeros((B, Hkv), np.int32)
+    f = np.zeros((B, Hkv, stride), np.float64) if want_f else None
+    rc = lib().orc_select(B, Hq, Hkv, _ptr(lens), _ptr(z), stride, n_sink, n_recent, k_sel,
+                          _ptr(idx), idx_stride, _ptr(n_idx), _ptr(f) if f is not None else None)
+    if rc != 0:
+        raise ValueError("idx_stride too small for sink + selected")
+    return idx, n_idx, f
+
+
+def sparse(cache: Cache, q, idx, n_idx, n_recent: int, head_mask=None):
+    """Returns (out [B][Hq][d], lse [B][Hq]) over sink+selected+recent, float64."""
+    qh = _host_bytes(q)
+    idx = np.ascontiguousarray(np.asarray(idx.cpu() if torch.is_tensor(idx) else idx,
+                                          dtype=np.int32))
+    n_idx = np.ascontiguousarray(np.asarray(n_idx.cpu() if torch.is_tensor(n_idx) else n_idx,
+                                            dtype=np.int32))
+    hm = None
+    if head_mask is not None:
+        hm = np.ascontiguousarray(np.asarray(
+            head_mask.cpu() if torch.is_tensor(head_mask) else head_mask, dtype=np.uint8))
+    out = np.zeros((cache.B, cache.Hq, cache.d), np.float64)
+    lse = np.zeros((cache.B, cache.Hq), np.float64)
+    s = cache._struct()
+    rc = lib().orc_sparse(ctypes.byref(s), _ptr(qh), _ptr(idx), idx.shape[-1], _ptr(n_idx),
+                          n_recent, _ptr(hm) if hm is not None else None, _ptr(out), _ptr(lse))
+    assert rc == 0
+    return out, lse
+
+
+def sink_mask(z0, lse, frac: float):
+    """z0, lse: [B][Hq].  Returns uint8 mask [B][Hq]."""
+    z0 = np.ascontiguousarray(np.asarray(z0.cpu() if torch.is_tensor(z0) else z0, np.float64))
+    lse = np.ascontiguousarray(np.asarray(lse.cpu() if torch.is_tensor(lse) else lse,
+                                          np.float64))
+    B, Hq = z0.shape
+    m = np.zeros((B, Hq), np.uint8)
+    rc = lib().orc_sink_mask(B, Hq, _ptr(z0), _ptr(lse), float(frac), _ptr(m))
+    if rc != 0:
+        raise ValueError("frac outside [0, 1]")
+    return m

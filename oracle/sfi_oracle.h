@@ -1,0 +1,80 @@
+/*
+ * sfi_oracle.h -- plain fp64 CPU reference for Slow-Fast decode attention.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  The HIP library never calls it and
+ * shares no code, header or table with it.
+ *
+ * Every floating-point step is done in double precision with the C library's exp
+ * and log; bf16 inputs are widened exactly (bf16 bits << 16 -> fp32 -> double).
+ *
+ * Cache addressing (the same bytes the GPU reads):
+ *   contiguous: element (b, h, pos, c) at ((b*Hkv + h)*n_cap + pos)*d + c
+ *   paged:      element (b, h, pos, c) at ((bt[b*max_blocks + pos/bs]*Hkv + h)*bs + pos%bs)*d + c
+ * Query head i reads KV head i / G with G = Hq / Hkv (grouped-query attention as in
+ * the SkipKV token-importance equation, Sec. 4.1).
+ */
+#ifndef SFI_ORACLE_H
+#define SFI_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct orc_cache {
+    int32_t B, Hq, Hkv, d;
+    int32_t is_bf16;               /* 1: K, V, q hold bf16 bits (uint16); 0: fp32 */
+    const void* k;
+    const void* v;
+    int64_t n_cap;                 /* rows per (b, h) when contiguous */
+    const int32_t* block_table;    /* NULL when contiguous; [B][max_blocks] when paged */
+    int32_t block_size, max_blocks;
+    const int32_t* len;            /* [B] current lengths (including the current token) */
+} orc_cache;
+
+/* Dense decode (Slow-Fast Inference, Sec. 1 and Sec. 3: a slow step runs full attention
+ * over the accessible history and exposes its logits).  For every batch b and query
+ * head i:  z_j = (q . k_j)/sqrt(d) for j < len[b];  logits[(b*Hq+i)*logit_stride + j] = z_j;
+ * lse = log sum_j exp(z_j);  out = sum_j exp(z_j - lse) v_j.
+ * out [B][Hq][d], lse [B][Hq]; logits may be NULL.  len[b] == 0 gives out = 0, lse = -inf. */
+int orc_dense(const orc_cache* c, const void* q, double* out, double* lse,
+              double* logits, int64_t logit_stride);
+
+/* Selector at decode (Slow-Fast Inference, Sec. 3.2 evidence with a window of one query,
+ * Sec. 3.3 Top-K discretization; prior and refinements off).  Per (b, h) with N = len[b]:
+ *   S = [0, min(n_sink, N)),  J = [n_sink, N - n_recent)  (empty when N - n_recent <= n_sink)
+ *   LSE_i = log sum_{j in J} exp(z_ij)                    for the G query heads i of group h
+ *   f(j)  = (1/G) sum_i exp(z_ij - LSE_i)                 for j in J
+ *   taken = the min(k_sel, |J|) positions of J with the largest f, ties to the lower j
+ *   idx[(b*Hkv+h)*idx_stride ...] = ascending(S u taken), n_idx[b*Hkv+h] = its size.
+ * logits are [B][Hq][logit_stride] doubles.  f_out (optional) receives f(j) at
+ * f_out[(b*Hkv+h)*logit_stride + j] for j in J and 0 elsewhere.
+ * Returns 0, or -1 when idx_stride < min(n_sink,N) + min(k_sel,|J|) for some (b, h). */
+int orc_select(int32_t B, int32_t Hq, int32_t Hkv, const int32_t* len,
+               const double* logits, int64_t logit_stride,
+               int32_t n_sink, int32_t n_recent, int32_t k_sel,
+               int32_t* idx, int32_t idx_stride, int32_t* n_idx, double* f_out);
+
+/* Sparse decode (Slow-Fast Inference, Sec. 1: a fast step attends only to sink + selected
+ * + recent tokens, the recent window moving with every step).  Per (b, i), h = i / G,
+ * N = len[b], r0 = max(0, N - n_recent):
+ *   I = { p in idx[(b*Hkv+h)*idx_stride + s], s < n_idx[b*Hkv+h] : p < r0 }  u  [r0, N)
+ * (a set: repeated entries count once), and out = softmax over I of z, applied to V.
+ * A query head with head_mask[b*Hq+i] != 0 outputs exact zeros (SinkRouter, Sec. 4.2
+ * "Execution policy": a bypassed unit writes a zero surrogate) and lse = -inf.
+ * head_mask may be NULL. */
+int orc_sparse(const orc_cache* c, const void* q, const int32_t* idx, int32_t idx_stride,
+               const int32_t* n_idx, int32_t n_recent, const uint8_t* head_mask,
+               double* out, double* lse);
+
+/* Sink-bypass mask (SinkRouter, Sec. 4.2 "Target regime": heads whose token-0 attention
+ * mass is large are treated as idle).  p0[b,i] = exp(z0[b*Hq+i] - lse[b*Hq+i]); per b the
+ * floor(frac*Hq) heads with the largest p0 are masked, ties to the lower head index. */
+int orc_sink_mask(int32_t B, int32_t Hq, const double* z0, const double* lse, double frac,
+                  uint8_t* head_mask);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,354 @@
+"""Pins for the fp64 CPU oracle, checked against things other than the oracle itself.
+
+* dense attention against torch's scaled_dot_product_attention in float64 (a library
+  routine) and closed forms (one token, identical keys, zero query, zero-norm sink,
+  weights summing to one, permutation invariance, exact integer logits, a hand-derived
+  golden case);
+* the selector against planted rankings known by construction, the identity when the
+  budget covers J, a library sort when the group has one head, brute-force rank
+  counting with ties, and a hand-derived case for the per-head normalisation over J;
+* the sparse step against the library attention with a boolean mask, the dense result
+  when the set is everything, and the zero surrogate;
+* the sink-bypass mask against a library sort.
+No test here needs a GPU.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_attention_dense_amd import synth
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _cache(orc, K, V, lens, Hq, **kw):
+    return orc.Cache(K, V, torch.tensor(lens, dtype=torch.int32), Hq, **kw)
+
+
+def _sdpa_ref(q, Kl, Vl, mask=None):
+    """Library attention (float64) for one sequence: q [Hq][d], K/V [Hkv][n][d]."""
+    Hq, Hkv = q.shape[0], Kl.shape[0]
+    G = Hq // Hkv
+    k = Kl.double().repeat_interleave(G, dim=0)
+    v = Vl.double().repeat_interleave(G, dim=0)
+    qq = q.double()[:, None, :]
+    am = None if mask is None else mask.repeat_interleave(G, dim=0)[:, None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(qq, k, v, attn_mask=am)[:, 0]
+    z = (qq @ k.transpose(1, 2))[:, 0] / math.sqrt(q.shape[-1])
+    if mask is not None:
+        z = z.masked_fill(~mask.repeat_interleave(G, dim=0), -math.inf)
+    return out, torch.logsumexp(z, dim=-1), (qq @ k.transpose(1, 2))[:, 0] / math.sqrt(q.shape[-1])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("Hq,Hkv,d", [(4, 1, 16), (4, 2, 8), (8, 4, 32), (6, 3, 64)])
+def test_dense_matches_library_attention(orc, dtype, Hq, Hkv, d):
+    g = torch.Generator().manual_seed(Hq * 100 + d)
+    B, cap = 3, 70
+    lens = [1, 37, 70]
+    K = torch.randn((B, Hkv, cap, d), generator=g).to(dtype)
+    V = torch.randn((B, Hkv, cap, d), generator=g).to(dtype)
+    q = torch.randn((B, Hq, d), generator=g).to(dtype)
+    out, lse, logits = orc.dense(_cache(orc, K, V, lens, Hq), q, logit_stride=cap)
+    for b in range(B):
+        n = lens[b]
+        ro, rl, rz = _sdpa_ref(q[b], K[b, :, :n], V[b, :, :n])
+        np.testing.assert_allclose(out[b], ro.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl.numpy(), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(logits[b, :, :n], rz.numpy(), rtol=0, atol=1e-12)
+
+
+def test_dense_paged_matches_contiguous_library(orc):
+    """Paged cache read through a shuffled block table equals the logical sequence."""
+    wl = synth.Workload("paged_tiny", 77, 3, 8, 2, 32, "bf16", 90, 4, 8, 16, 3, paged=True,
+                        block_size=16, len_lo=20)
+    lay = synth.make_layer(wl, 0)
+    q = synth.make_query(wl, 0, 0)
+    c = orc.Cache(lay.k, lay.v, lay.len0, wl.Hq, block_table=lay.block_table,
+                  block_size=wl.block_size, max_blocks=lay.max_blocks)
+    out, lse, logits = orc.dense(c, q, logit_stride=lay.cap)
+    for b in range(wl.B):
+        n = lay.len0_host[b]
+        Ks, Vs = zip(*[synth.logical_kv(lay, b, h, n) for h in range(wl.Hkv)])
+        ro, rl, rz = _sdpa_ref(q[b].float(), torch.stack(Ks), torch.stack(Vs))
+        np.testing.assert_allclose(out[b], ro.numpy(), atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl.numpy(), atol=1e-12)
+        np.testing.assert_allclose(logits[b, :, :n], rz.numpy(), atol=1e-12)
+
+
+def test_dense_golden_two_token(orc):
+    gd = json.load(open(os.path.join(HERE, "golden", "dense_two_token.json")))
+    K = torch.tensor(gd["k"], dtype=torch.float32)[None, None]
+    V = torch.tensor(gd["v"], dtype=torch.float32)[None, None]
+    q = torch.tensor(gd["q"], dtype=torch.float32)[None, None]
+    out, lse, logits = orc.dense(_cache(orc, K, V, [2], 1), q)
+    tol = gd["tolerance"]
+    np.testing.assert_allclose(logits[0, 0, :2], gd["expected_logits"], atol=tol)
+    assert abs(lse[0, 0] - gd["expected_lse"]) < tol
+    np.testing.assert_allclose(out[0, 0], gd["expected_out"], atol=tol)
+
+
+def test_dense_closed_forms(orc):
+    g = torch.Generator().manual_seed(5)
+    d, n = 16, 50
+    K = torch.randn((1, 1, n, d), generator=g)
+    V = torch.randn((1, 1, n, d), generator=g)
+    q = torch.randn((1, 2, d), generator=g)
+    # one token: out = v0, lse = z0
+    out, lse, z = orc.dense(_cache(orc, K, V, [1], 2), q)
+    np.testing.assert_allclose(out[0, 0], V[0, 0, 0].double().numpy(), atol=1e-14)
+    assert abs(lse[0, 1] - z[0, 1, 0]) < 1e-14
+    # identical keys: uniform weights -> mean of V, lse = z + ln n
+    Ks = K[:, :, :1].expand(1, 1, n, d).contiguous()
+    out, lse, z = orc.dense(_cache(orc, Ks, V, [n], 2), q)
+    np.testing.assert_allclose(out[0, 0], V[0, 0].double().mean(0).numpy(), atol=1e-12)
+    assert abs(lse[0, 0] - (z[0, 0, 0] + math.log(n))) < 1e-12
+    # zero query: lse = ln n, out = mean of V
+    out, lse, _ = orc.dense(_cache(orc, K, V, [n], 2), torch.zeros((1, 2, d)))
+    assert abs(lse[0, 0] - math.log(n)) < 1e-13
+    np.testing.assert_allclose(out[0, 1], V[0, 0].double().mean(0).numpy(), atol=1e-12)
+    # weights sum to one: sum_j exp(z_j - lse) = 1
+    out, lse, z = orc.dense(_cache(orc, K, V, [n], 2), q)
+    assert abs(np.exp(z[0, 0, :n] - lse[0, 0]).sum() - 1.0) < 1e-12
+
+
+def test_dense_zero_norm_sink(orc):
+    """v0 = 0: out = (1 - p0) * (attention over positions >= 1)."""
+    g = torch.Generator().manual_seed(6)
+    d, n = 32, 40
+    K = torch.randn((1, 1, n, d), generator=g)
+    V = torch.randn((1, 1, n, d), generator=g)
+    V[0, 0, 0] = 0
+    q = torch.randn((1, 1, d), generator=g)
+    out, lse, z = orc.dense(_cache(orc, K, V, [n], 1), q)
+    p0 = math.exp(z[0, 0, 0] - lse[0, 0])
+    out_rest, _, _ = orc.dense(_cache(orc, K[:, :, 1:].contiguous(), V[:, :, 1:].contiguous(),
+                                      [n - 1], 1), q)
+    np.testing.assert_allclose(out[0, 0], (1 - p0) * out_rest[0, 0], atol=1e-13)
+
+
+def test_dense_permutation_invariance(orc):
+    g = torch.Generator().manual_seed(7)
+    d, n = 16, 33
+    K = torch.randn((1, 2, n, d), generator=g)
+    V = torch.randn((1, 2, n, d), generator=g)
+    q = torch.randn((1, 4, d), generator=g)
+    perm = torch.randperm(n, generator=g)
+    o1, l1, z1 = orc.dense(_cache(orc, K, V, [n], 4), q)
+    o2, l2, z2 = orc.dense(_cache(orc, K[:, :, perm].contiguous(), V[:, :, perm].contiguous(),
+                                  [n], 4), q)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    np.testing.assert_allclose(z1[:, :, perm.numpy()], z2, atol=0)
+
+
+def test_dense_exact_integer_logits_and_group_map(orc):
+    """Small-integer q and k make every logit exact: z = (q.k)/8 at d = 64.  Query head i
+    must read KV head i // G (here G = 2, KV heads 0..2 hold different keys)."""
+    g = torch.Generator().manual_seed(8)
+    d, n, Hkv, G = 64, 9, 3, 2
+    K = torch.randint(-3, 4, (1, Hkv, n, d), generator=g).float()
+    V = torch.randn((1, Hkv, n, d), generator=g)
+    q = torch.randint(-3, 4, (1, Hkv * G, d), generator=g).float()
+    _, _, z = orc.dense(_cache(orc, K, V, [n], Hkv * G), q)
+    for i in range(Hkv * G):
+        for j in range(n):
+            exact = sum(int(a) * int(b) for a, b in zip(q[0, i], K[0, i // G, j])) / 8.0
+            assert z[0, i, j] == exact
+
+
+# ---------------------------------------------------------------------------- selector
+
+def _expected_from_ranks(ranks, lens, n_sink, n_recent, k_sel, Hkv):
+    exp = []
+    for b, rb in enumerate(ranks):
+        N = int(lens[b])
+        ns = min(n_sink, N)
+        row = []
+        for h in range(Hkv):
+            pi = rb[h]
+            J_lo = n_sink
+            keep = sorted((torch.nonzero(pi < k_sel).flatten() + J_lo).tolist())
+            row.append(list(range(ns)) + keep)
+        exp.append(row)
+    return exp
+
+
+@pytest.mark.parametrize("G,lens,k_sel", [(4, [300, 257, 1000], 64), (1, [500], 37),
+                                          (8, [2000, 2000], 511)])
+def test_select_planted_ranks(orc, G, lens, k_sel):
+    Hkv, n_sink, n_recent = 2, 4, 16
+    Hq = Hkv * G
+    stride = max(lens)
+    z, ranks = synth.planted_logits(len(lens), Hq, Hkv, lens, n_sink, n_recent, stride,
+                                    seed=11 + G, noise_sink=40.0)
+    idx, n_idx, f = orc.select(lens, Hq, Hkv, z, n_sink, n_recent, k_sel, want_f=True)
+    exp = _expected_from_ranks(ranks, lens, n_sink, n_recent, k_sel, Hkv)
+    for b in range(len(lens)):
+        for h in range(Hkv):
+            got = idx[b, h, :n_idx[b, h]].tolist()
+            assert got == exp[b][h]
+            N = lens[b]
+            assert abs(f[b, h, n_sink:N - n_recent].sum() - 1.0) < 1e-12
+            assert (f[b, h, :n_sink] == 0).all() and (f[b, h, N - n_recent:] == 0).all()
+
+
+def test_select_budget_covers_J_is_identity(orc):
+    lens = [100, 40, 3]
+    Hq, Hkv, n_sink, n_recent = 4, 2, 4, 16
+    z = torch.randn((3, Hq, 100), generator=torch.Generator().manual_seed(3))
+    idx, n_idx, _ = orc.select(lens, Hq, Hkv, z, n_sink, n_recent, k_sel=200,
+                               idx_stride=300)
+    for b, N in enumerate(lens):
+        J = list(range(n_sink, max(n_sink, N - n_recent)))
+        for h in range(Hkv):
+            assert idx[b, h, :n_idx[b, h]].tolist() == list(range(min(n_sink, N))) + J
+
+
+def test_select_single_head_is_library_topk(orc):
+    """G = 1: f is the softmax over J, monotone in z, so the choice is a plain sort of z
+    (numpy lexsort: z descending, position ascending)."""
+    g = torch.Generator().manual_seed(4)
+    N, n_sink, n_recent, k_sel = 700, 4, 32, 50
+    z = torch.randint(-20, 20, (1, 3, N), generator=g).float() / 4   # many exact ties
+    idx, n_idx, _ = orc.select([N], 3, 3, z, n_sink, n_recent, k_sel)
+    for h in range(3):
+        zJ = z[0, h, n_sink:N - n_recent].double().numpy()
+        pos = np.arange(n_sink, N - n_recent)
+        order = np.lexsort((pos, -zJ))[:k_sel]
+        exp = list(range(n_sink)) + sorted(pos[order].tolist())
+        assert idx[0, h, :n_idx[0, h]].tolist() == exp
+
+
+def test_select_brute_force_rank_counting(orc):
+    """O(n^2) rank counting on tiny inputs with ties: j is kept iff fewer than k_sel
+    positions beat it ((f larger) or (f equal and position lower))."""
+    g = torch.Generator().manual_seed(9)
+    N, n_sink, n_recent, k_sel, Hq, Hkv = 60, 3, 5, 17, 4, 2
+    z = torch.randint(-3, 3, (2, Hq, N), generator=g).double()
+    idx, n_idx, f = orc.select([N, N - 7], Hq, Hkv, z, n_sink, n_recent, k_sel, want_f=True)
+    for b, Nb in enumerate([N, N - 7]):
+        for h in range(Hkv):
+            J = range(n_sink, Nb - n_recent)
+            fb = f[b, h]
+            keep = [j for j in J
+                    if sum(1 for j2 in J if fb[j2] > fb[j] or (fb[j2] == fb[j] and j2 < j))
+                    < k_sel]
+            assert idx[b, h, :n_idx[b, h]].tolist() == list(range(n_sink)) + keep
+
+
+def test_select_ignores_sink_and_recent_logits(orc):
+    lens = [400]
+    Hq, Hkv, n_sink, n_recent, k_sel = 4, 1, 4, 64, 30
+    z = torch.randn((1, Hq, 400), generator=torch.Generator().manual_seed(12))
+    a, _, _ = orc.select(lens, Hq, Hkv, z, n_sink, n_recent, k_sel)
+    z2 = z.clone()
+    z2[:, :, :n_sink] = 1e4
+    z2[:, :, 400 - n_recent:] = -1e4
+    z2[:, 1, 400 - n_recent:] = 1e4
+    b, _, _ = orc.select(lens, Hq, Hkv, z2, n_sink, n_recent, k_sel)
+    assert (a == b).all()
+
+
+def test_select_golden_normalisation_over_J(orc):
+    gd = json.load(open(os.path.join(HERE, "golden", "select_lse_j.json")))
+    N = gd["N"]
+    z = torch.tensor([[gd["z_head0"], gd["z_head1"]]], dtype=torch.float64)
+    idx, n_idx, f = orc.select([N], 2, 1, z, gd["n_sink"], gd["n_recent"], gd["k_sel"],
+                               want_f=True)
+    assert idx[0, 0, :n_idx[0, 0]].tolist() == gd["expected_idx"]
+    for j, v in gd["expected_f_at"].items():
+        assert abs(f[0, 0, int(j)] - v) < gd["tolerance"]
+
+
+def test_select_short_contexts(orc):
+    """N - n_recent <= n_sink: J is empty and only the sinks come back; N < n_sink: [0, N)."""
+    z = torch.randn((3, 2, 30), generator=torch.Generator().manual_seed(2))
+    idx, n_idx, _ = orc.select([30, 12, 2], 2, 1, z, n_sink=4, n_recent=26, k_sel=8)
+    assert idx[0, 0, :n_idx[0, 0]].tolist() == [0, 1, 2, 3]
+    assert idx[1, 0, :n_idx[1, 0]].tolist() == [0, 1, 2, 3]
+    assert idx[2, 0, :n_idx[2, 0]].tolist() == [0, 1]
+
+
+# ------------------------------------------------------------------------------ sparse
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_matches_library_masked_attention(orc, paged):
+    wl = synth.Workload("sp_tiny", 91, 2, 8, 2, 32, "bf16", 300, 4, 20, 40, 3, paged=paged,
+                        block_size=16, len_lo=150 if paged else 0)
+    lay = synth.make_layer(wl, 0)
+    q = synth.make_query(wl, 0, 1)
+    lens = [n + 1 for n in lay.len0_host]          # one fast step after the slow step
+    idx, n_idx = synth.synthetic_index_set(lay, "spans", seed=5)
+    kw = dict(block_table=lay.block_table, block_size=wl.block_size,
+              max_blocks=lay.max_blocks) if paged else {}
+    c = orc.Cache(lay.k, lay.v, torch.tensor(lens, dtype=torch.int32), wl.Hq, **kw)
+    out, lse = orc.sparse(c, q, idx, n_idx, wl.n_recent)
+    for b in range(wl.B):
+        N = lens[b]
+        Ks, Vs = zip(*[synth.logical_kv(lay, b, h, N) for h in range(wl.Hkv)])
+        mask = torch.zeros((wl.Hkv, N), dtype=torch.bool)
+        for h in range(wl.Hkv):
+            sel = idx[b, h, :n_idx[b, h]].long()
+            mask[h, sel[sel < N - wl.n_recent]] = True
+            mask[h, max(0, N - wl.n_recent):] = True
+        ro, rl, _ = _sdpa_ref(q[b].float(), torch.stack(Ks), torch.stack(Vs), mask)
+        np.testing.assert_allclose(out[b], ro.numpy(), atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl.numpy(), atol=1e-12)
+
+
+def test_sparse_full_set_equals_dense_and_mask_zero(orc):
+    g = torch.Generator().manual_seed(13)
+    d, n, Hq, Hkv, n_recent = 16, 80, 4, 2, 10
+    K = torch.randn((1, Hkv, n, d), generator=g)
+    V = torch.randn((1, Hkv, n, d), generator=g)
+    q = torch.randn((1, Hq, d), generator=g)
+    c = _cache(orc, K, V, [n], Hq)
+    od, ld, _ = orc.dense(c, q)
+    full = torch.arange(n - n_recent, dtype=torch.int32).repeat(1, Hkv, 1)
+    os_, ls, = orc.sparse(c, q, full, torch.full((1, Hkv), n - n_recent, dtype=torch.int32),
+                          n_recent)
+    np.testing.assert_allclose(os_, od, atol=1e-13)
+    np.testing.assert_allclose(ls, ld, atol=1e-13)
+    # entries in the recent window or beyond the length are ignored; repeats count once
+    noisy = torch.cat([full, full[:, :, :5], torch.full((1, Hkv, 4), n + 3, dtype=torch.int32)],
+                      dim=2)
+    on, _ = orc.sparse(c, q, noisy, torch.full((1, Hkv), noisy.shape[-1], dtype=torch.int32),
+                       n_recent)
+    np.testing.assert_allclose(on, od, atol=1e-13)
+    # empty selection: window attention over the last n_recent positions
+    ow, lw = orc.sparse(c, q, full, torch.zeros((1, Hkv), dtype=torch.int32), n_recent)
+    cw = _cache(orc, K[:, :, n - n_recent:].contiguous(), V[:, :, n - n_recent:].contiguous(),
+                [n_recent], Hq)
+    ow2, lw2, _ = orc.dense(cw, q)
+    np.testing.assert_allclose(ow, ow2, atol=1e-13)
+    # a masked head outputs exact zeros
+    hm = torch.tensor([[0, 1, 0, 1]], dtype=torch.uint8)
+    om, lm = orc.sparse(c, q, full, torch.full((1, Hkv), n - n_recent, dtype=torch.int32),
+                        n_recent, head_mask=hm)
+    assert (om[0, 1] == 0).all() and (om[0, 3] == 0).all() and np.isneginf(lm[0, 1])
+    np.testing.assert_allclose(om[0, 0], od[0, 0], atol=1e-13)
+
+
+# -------------------------------------------------------------------------------- mask
+
+def test_sink_mask_library_sort(orc):
+    g = torch.Generator().manual_seed(14)
+    B, Hq = 3, 64
+    z0 = torch.randn((B, Hq), generator=g).double()
+    lse = z0 + torch.rand((B, Hq), generator=g).double() * 3
+    lse[1, 10] = lse[1, 20] = z0[1, 10] = z0[1, 20] = 0.0     # an exact tie
+    for frac in (0.0, 0.25, 0.5, 1.0):
+        m = orc.sink_mask(z0, lse, frac)
+        for b in range(B):
+            p0 = np.exp((z0[b] - lse[b]).numpy())
+            order = np.lexsort((np.arange(Hq), -p0))[:int(math.floor(frac * Hq))]
+            exp = np.zeros(Hq, np.uint8)
+            exp[order] = 1
+            assert (m[b] == exp).all()
+    with pytest.raises(ValueError):
+        orc.sink_mask(z0, lse, 1.5)
