@@ -341,8 +341,10 @@ def test_sink_mask_library_sort(orc):
     B, Hq = 3, 64
     z0 = torch.randn((B, Hq), generator=g).double()
     lse = z0 + torch.rand((B, Hq), generator=g).double() * 3
-    lse[1, 10] = lse[1, 20] = z0[1, 10] = z0[1, 20] = 0.0     # an exact tie
-    for frac in (0.0, 0.25, 0.5, 1.0):
+    # batch 2: only four distinct p0 values, so the cut falls inside a group of ties
+    z0[2] = 0.0
+    lse[2] = torch.randint(1, 5, (Hq,), generator=g).double() / 2
+    for frac in (0.0, 0.25, 0.3, 0.5, 1.0):
         m = orc.sink_mask(z0, lse, frac)
         for b in range(B):
             p0 = np.exp((z0[b] - lse[b]).numpy())
