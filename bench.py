@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of one Slow-Fast decode-attention layer on one MI355X.
+
+A step is one slow-fast cycle of the workload: the dense slow step with fp32 logit write
+(sfi_dense_decode), the Selector (sfi_select), the sink-bypass mask when the workload has
+one (sfi_sink_bypass_mask), then cycle-1 fast steps (sfi_sparse_decode) whose recent
+window moves by one token per step.  Steps rotate over --layers distinct layer buffers
+(own K/V, logits, indices) so repeated reads are not served from the 256 MB Infinity Cache.
+Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  value = microseconds per decode step, amortised over the cycle
+(slow + (cycle-1) fast) / cycle.  roofline = the dense slow-step kernel's algorithmic HBM
+bytes per launch / its mean launch time, measured with HIP events on the launch stream.
+cpu_baseline = the fp64 CPU oracle timed on the host on one whole cycle of one layer.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fast/slow decode-attn µs/step + achieved HBM GB/s (% of peak) at 32K–512K ctx"
+PEAK_HBM_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "dense_sink_128k_b4_counters.json")
+ATTN_SRC = os.path.join(ROOT, "sparse_kv_attention_dense_amd", "csrc", "sfi_attention.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="sink_128k_b4")
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kv_bytes_per_row(wl):
+    return 2 * wl.d * wl.elem_bytes             # one K row and one V row
+
+
+def dense_bytes(wl, lens):
+    n = sum(lens)
+    return (n * wl.Hkv * kv_bytes_per_row(wl) + n * wl.Hq * 4 +
+            wl.B * wl.Hq * wl.d * (wl.elem_bytes + 4) + wl.B * wl.Hq * 4)
+
+
+def select_bytes(wl, lens):
+    nJ = sum(max(0, n - wl.n_recent - wl.n_sink) for n in lens)
+    # logits over J read twice (log-sum-exp pass, evidence pass); one key written per
+    # (KV head, position) and read back by two histogram passes, the count and the emit
+    return 2 * wl.Hq * nJ * 4 + 5 * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
+                                                         for _ in lens)
+
+
+def fast_bytes(wl, lens_t, n_idx_host, mask_host):
+    tot = 0
+    for b, N in enumerate(lens_t):
+        rec = min(wl.n_recent, N)
+        for h in range(wl.Hkv):
+            if mask_host is not None and all(mask_host[b][h * wl.G:(h + 1) * wl.G]):
+                continue
+            rows = int(n_idx_host[b][h]) + rec
+            tot += rows * kv_bytes_per_row(wl) + int(n_idx_host[b][h]) * 4
+    return tot + wl.B * wl.Hq * wl.d * (wl.elem_bytes + 4) + wl.B * wl.Hq * 4
+
+
+def counter_traffic():
+    """HBM bytes per dense launch from the committed rocprofv3 counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    try:
+        with open(COUNTERS) as fh:
+            c = json.load(fh)
+        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if c.get("source_sha256") != sha:
+            return None
+        return int(c["fetch_bytes_per_launch"]) + int(c["write_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, layer, queries, lay0_host_lens):
+    import oracle
+    import numpy as np
+    t_start = time.perf_counter()
+    kw = {}
+    if wl.paged:
+        kw = dict(block_table=layer.block_table, block_size=wl.block_size,
+                  max_blocks=layer.max_blocks)
+    cache = oracle.Cache(layer.k, layer.v, layer.len0, wl.Hq, **kw)
+    copy_s = time.perf_counter() - t_start
+    t0 = time.perf_counter()
+    eo, el, ez = oracle.dense(cache, queries[0])
+    t1 = time.perf_counter()
+    eidx, en, _ = oracle.select(lay0_host_lens, wl.Hq, wl.Hkv, ez, wl.n_sink, wl.n_recent, wl.k_sel)
+    t2 = time.perf_counter()
+    hm = oracle.sink_mask(ez[:, :, 0], el, wl.mask_frac) if wl.mask_frac > 0 else None
+    t3 = time.perf_counter()
+    for t in range(1, wl.cycle):
+        oracle.sparse(cache.with_lens(np.asarray(lay0_host_lens) + t), queries[t], eidx, en,
+                      wl.n_recent, hm)
+    t4 = time.perf_counter()
+    cycle_s = t4 - t0
+    return {
+        "value": cycle_s * 1e6 / wl.cycle,
+        "unit": "us/step",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": (f"one whole cycle of one layer of {wl.name} (full batch {wl.B}): dense "
+                   f"{t1 - t0:.2f} s, select {t2 - t1:.2f} s, mask {t3 - t2:.3f} s, "
+                   f"{wl.cycle - 1} fast steps {t4 - t3:.2f} s; host copy {copy_s:.1f} s "
+                   f"not timed"),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the decode-attention path runs on a single MI355X "
+              f"and has no multi-GPU mode (asked for --gpus {args.gpus}, WORLD_SIZE {world}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_kv_attention_dense_amd import binding as B
+    from sparse_kv_attention_dense_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = "cuda"
+    wl = synth.WORKLOADS[args.workload]
+    L = max(1, args.layers)
+    print(f"# building {L} layers of {wl.name}", file=sys.stderr, flush=True)
+
+    layers, descs, queries, logits, idxs, nidxs, masks, outs, lses = [], [], [], [], [], [], [], [], []
+    lens_t = None
+    for li in range(L):
+        lay = synth.make_layer(wl, li, device=dev)
+        layers.append(lay)
+        if lens_t is None:
+            lens_t = [lay.len_at(t).to(dev) for t in range(wl.cycle)]
+            max_t = [lay.max_len_at(t) for t in range(wl.cycle)]
+        kw = dict(block_table=lay.block_table, block_size=wl.block_size) if wl.paged else {}
+        descs.append([B.KVDesc(lay.k, lay.v, lens_t[t], max_t[t], wl.Hq, **kw)
+                      for t in range(wl.cycle)])
+        queries.append([synth.make_query(wl, li, t, device=dev, u=lay.u) for t in range(wl.cycle)])
+        stride = (max_t[0] + 3) // 4 * 4
+        logits.append(torch.empty((wl.B, wl.Hq, stride), device=dev))
+        idxs.append(torch.empty((wl.B, wl.Hkv, wl.n_sink + wl.k_sel), dtype=torch.int32, device=dev))
+        nidxs.append(torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev))
+        masks.append(torch.zeros((wl.B, wl.Hq), dtype=torch.uint8, device=dev)
+                     if wl.mask_frac > 0 else None)
+        print(f"#   layer {li} ready", file=sys.stderr, flush=True)
+    stride = logits[0].shape[-1]
+    out = torch.empty((wl.B, wl.Hq, wl.d), device=dev)
+    lse = torch.empty((wl.B, wl.Hq), device=dev)
+    idx_stride = wl.n_sink + wl.k_sel
+    ws = B.workspace(descs[0][wl.cycle - 1], idx_stride=idx_stride, n_recent=wl.n_recent, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def cycle(li, rec):
+        d0 = descs[li]
+        e = [ev() for _ in range(4 + wl.cycle - 1)] if rec else None
+        if rec:
+            e[0].record(stream)
+        B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
+        if rec:
+            e[1].record(stream)
+        B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
+                     idx_stride, nidxs[li], ws)
+        if rec:
+            e[2].record(stream)
+        if masks[li] is not None:
+            B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
+        if rec:
+            e[3].record(stream)
+        for t in range(1, wl.cycle):
+            B.sfi_sparse_decode(d0[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
+                                wl.n_recent, masks[li], out, lse, ws)
+            if rec:
+                e[3 + t].record(stream)
+        return e
+
+    print("# warmup", file=sys.stderr, flush=True)
+    for s in range(args.warmup):
+        cycle(s % L, False)
+    torch.cuda.synchronize()
+    print("# timed region", file=sys.stderr, flush=True)
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        evs.append(cycle(s % L, True))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    dense_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    select_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    mask_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    fast_ms = [e[2 + t].elapsed_time(e[3 + t]) for e in evs for t in range(1, wl.cycle)]
+    mean = lambda x: sum(x) / len(x)
+    dense_us, select_us, mask_us, fast_us = (1e3 * mean(dense_ms), 1e3 * mean(select_ms),
+                                             1e3 * mean(mask_ms), 1e3 * mean(fast_ms))
+
+    lens0 = layers[0].len0_host
+    n_idx_host = nidxs[0].cpu().tolist()
+    mask_host = masks[0].cpu().tolist() if masks[0] is not None else None
+    d_bytes = dense_bytes(wl, lens0)
+    s_bytes = select_bytes(wl, lens0)
+    f_bytes = mean([fast_bytes(wl, [n + t for n in lens0], n_idx_host, mask_host)
+                    for t in range(1, wl.cycle)])
+    dense_gbps = d_bytes / (dense_us * 1e-6) / 1e9
+    fast_gbps = f_bytes / (fast_us * 1e-6) / 1e9
+    select_gbps = s_bytes / (select_us * 1e-6) / 1e9
+    value = ms_per_step * 1e3 / wl.cycle
+    traffic = counter_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "q_heads": wl.Hq, "kv_heads": wl.Hkv,
+                   "head_dim": wl.d, "context": wl.n0, "n_sink": wl.n_sink,
+                   "n_recent": wl.n_recent, "k_sel": wl.k_sel, "cycle": wl.cycle,
+                   "mask_frac": wl.mask_frac, "layers_rotated": L,
+                   "step": f"1 slow (dense+select{'+mask' if wl.mask_frac else ''}) + "
+                           f"{wl.cycle - 1} fast"},
+        "slow_us": round(dense_us + select_us + mask_us, 2),
+        "fast_us": round(fast_us, 2),
+        "dense_us": round(dense_us, 2),
+        "select_us": round(select_us, 2),
+        "mask_us": round(mask_us, 2),
+        "dense_gbps": round(dense_gbps, 1),
+        "fast_gbps": round(fast_gbps, 1),
+        "select_gbps": round(select_gbps, 1),
+        "fast_pct_peak": round(100 * fast_gbps / PEAK_HBM_GBS, 1),
+        "tokens_per_s": round(wl.B * 1e6 / value, 1),
+        "roofline": {"bound": "hbm", "achieved": round(dense_gbps, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(dense_gbps / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel": "sfi_dense_decode (attention_kernel)",
+                     "algorithmic_bytes": d_bytes},
+        "fast_roofline": {"bound": "hbm", "achieved": round(fast_gbps, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(fast_gbps / PEAK_HBM_GBS, 4),
+                          "algorithmic_bytes": int(f_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        host_q = [q.cpu() for q in queries[0]]
+        result["cpu_baseline"] = cpu_baseline(wl, layers[0], host_q, lens0)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * sfi.h -- C ABI of libsfi.so: Slow-Fast decode attention on AMD Instinct MI355X (gfx950).
+ *
+ * One decode step of grouped-query attention over a long KV cache, in the slow/fast form
+ * of "Slow-Fast Inference" (SFI):
+ *   - a slow step runs dense attention over the whole history and exposes the attention
+ *     logits (SFI Sec. 1; Sec. 4.2, kernels that expose logits)          -> sfi_dense_decode
+ *   - the Selector turns those logits into a per-KV-head Top-K index set
+ *     (SFI Sec. 3.2 evidence from slow-step logits, Sec. 3.3 Top-K)      -> sfi_select
+ *   - a sink-bypass mask marks query heads whose token-0 attention mass is largest
+ *     (SinkRouter Sec. 4.2, target regime and execution policy)          -> sfi_sink_bypass_mask
+ *   - a fast step attends only to sink + selected + recent positions
+ *     (SFI Sec. 1, the compact cache of fast steps)                       -> sfi_sparse_decode
+ *
+ * Conventions shared by every call
+ *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
+ *     never allocates, keeps no pointer after a call returns, and holds no global state
+ *     except a per-device cache of the compute-unit count.
+ *   - Calls are asynchronous on `stream` (0 = the null stream) and never synchronise the
+ *     host.  A returned SFI_OK means the arguments passed host-side validation and the
+ *     launches were queued; device data (lengths, block tables, indices) is trusted.
+ *   - Scores use scale 1/sqrt(head_dim) and query head i reads KV head i / G with
+ *     G = num_q_heads / num_kv_heads (the grouped-query map of SkipKV Sec. 4.1, token
+ *     importance score).  Accumulation is fp32; outputs, logits and lse are fp32.
+ *   - Workspace: `ws` must be 256-byte aligned, at least sfi_workspace_bytes() long, and
+ *     zero-filled before its first use.  Every call that completes leaves the counters it
+ *     uses at zero again, so one zero fill is enough.  Calls that share a workspace must be
+ *     ordered (same stream); concurrent calls need separate workspaces.
+ *   - The functions are thread-safe.
+ */
+#ifndef SFI_H
+#define SFI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sfi_status {
+    SFI_OK = 0,
+    SFI_E_INVALID = -1,      /* null pointer, inconsistent sizes, bad alignment */
+    SFI_E_UNSUPPORTED = -2,  /* well-formed but not built: head_dim, dtype, group size */
+    SFI_E_WORKSPACE = -3,    /* ws is NULL, misaligned or smaller than sfi_workspace_bytes() */
+    SFI_E_HIP = -4           /* the HIP runtime reported an error while launching */
+} sfi_status;
+
+typedef enum sfi_dtype { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
+
+typedef enum sfi_op { SFI_OP_DENSE = 0, SFI_OP_SELECT = 1, SFI_OP_SPARSE = 2 } sfi_op;
+
+/* The per-step cache descriptor (SFI Sec. 4.2: one packed description of cache bounds,
+ * block tables and layout, read by every kernel of the step).
+ *
+ *   batch, num_q_heads, num_kv_heads : B, Hq, Hkv; Hq % Hkv == 0 and G = Hq / Hkv <= 16
+ *   head_dim                          : d, 64 or 128
+ *   dtype                             : element type of k, v and q (SFI_F32 or SFI_BF16)
+ *   k, v      (device) contiguous: [B][Hkv][n_cap][d]; paged: [num_blocks][Hkv][block_size][d];
+ *                      16-byte aligned
+ *   n_cap               rows per (b, h) when contiguous (>= max_len); ignored when paged
+ *   block_table (device) NULL for contiguous; else int32 [B][max_blocks] of physical block
+ *                      numbers, logical position p of sequence b living in block
+ *                      block_table[b*max_blocks + p/block_size], row p % block_size
+ *   block_size          power of two in [1, 1024] when paged
+ *   len         (device) int32 [B]: current length of each sequence, the current token
+ *                      included; 0 <= len[b] <= max_len
+ *   max_len             host-side bound of len[] used to size grids (no device read)
+ */
+typedef struct sfi_kv_desc {
+    int32_t batch;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t dtype;
+    const void* k;
+    const void* v;
+    int64_t n_cap;
+    const int32_t* block_table;
+    int32_t block_size;
+    int32_t max_blocks;
+    const int32_t* len;
+    int32_t max_len;
+} sfi_kv_desc;
+
+/* Dense decode step (slow step).  SFI Sec. 1 and Sec. 3: dense full attention over the
+ * accessible history, exposing the attention logits the Selector needs (Sec. 4.2).
+ * For each b and query head i (h = i / G) over positions j < len[b]:
+ *   z_j = (q_i . k_{h,j}) / sqrt(d)
+ *   out_i = sum_j softmax(z)_j v_{h,j}             out    (device) fp32 [B][Hq][d]
+ *   lse_i = log sum_j exp(z_j)                      lse    (device) fp32 [B][Hq], may be NULL
+ *   logits[(b*Hq + i)*logit_stride + j] = z_j       logits (device) fp32, may be NULL; when
+ *       given, logit_stride >= max_len, logit_stride % 4 == 0 and logits 16-byte aligned.
+ *       Entries j >= len[b] are not written.
+ * q (device) [B][Hq][d] in kv->dtype, 16-byte aligned.  len[b] == 0 gives out = 0, lse = -inf.
+ * One kernel launch: split-K over the sequence with an in-kernel combine. */
+sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
+                            float* logits, int64_t logit_stride,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Selector (decode window of one query, prior and refinements off).  SFI Sec. 3.2: the
+ * slow-step logits over the allowed set J become a per-head distribution; Sec. 3.3: Top-K
+ * per KV head.  Per (b, h) with N = len[b]:
+ *   S = [0, min(n_sink, N)),  J = [n_sink, N - n_recent)   (empty if N - n_recent <= n_sink)
+ *   f(j) = (1/G) sum_{i in group h} exp(z_ij - log sum_{j' in J} exp(z_ij'))
+ *   taken = the min(k_sel, |J|) positions of J with the largest f; equal f -> lower j first
+ *   idx[(b*Hkv + h)*idx_stride + s], s < n_idx[b*Hkv + h]: ascending positions of S u taken
+ * logits (device) fp32 [B][Hq][logit_stride] as written by sfi_dense_decode.
+ * idx (device) int32 [B][Hkv][idx_stride], idx_stride >= n_sink + k_sel.
+ * n_idx (device) int32 [B][Hkv] = min(n_sink, N) + min(k_sel, |J|).
+ * n_sink, n_recent >= 0, k_sel >= 0.  kv->k and kv->v are not read. */
+sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                      int32_t n_sink, int32_t n_recent, int32_t k_sel,
+                      int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sink-bypass mask.  SinkRouter Sec. 4.2: heads whose attention mass on token 0 is large
+ * are in a low-impact regime and are bypassed with a zero surrogate.  Per b:
+ *   p0_i = exp(logits[(b*Hq + i)*logit_stride + 0] - lse[b*Hq + i])
+ *   head_mask[b*Hq + i] = 1 for the floor(frac * Hq) heads with the largest p0 (equal p0 ->
+ *   lower head index first), 0 otherwise.
+ * logits, lse (device) fp32 from sfi_dense_decode; head_mask (device) uint8 [B][Hq];
+ * 0 <= frac <= 1; every len[b] >= 1.  No workspace. */
+sfi_status sfi_sink_bypass_mask(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                                const float* lse, float frac, uint8_t* head_mask,
+                                hipStream_t stream);
+
+/* Sparse decode step (fast step).  SFI Sec. 1: attend only to sink + selected + recent, the
+ * recent window moving with every step; SinkRouter Sec. 4.2 execution policy: a bypassed
+ * head writes the zero surrogate.  Per b and query head i (h = i / G), N = len[b],
+ * r0 = max(0, N - n_recent):
+ *   I = { idx[(b*Hkv + h)*idx_stride + s] : s < n_idx[b*Hkv + h], the entry < r0 } u [r0, N)
+ *   out_i = sum_{j in I} softmax_I(z)_j v_{h,j},  lse_i = log sum_{j in I} exp(z_j)
+ *   head_mask[b*Hq + i] != 0  ->  out_i = 0 exactly, lse_i = -inf.
+ * idx (device) int32 [B][Hkv][idx_stride]: strictly ascending within each row (as written by
+ * sfi_select); entries >= r0 or < 0 are skipped, so the recent run is never counted twice.
+ * n_idx (device) int32 [B][Hkv], clamped to idx_stride.  head_mask (device) uint8 [B][Hq] or
+ * NULL.  out (device) fp32 [B][Hq][d]; lse (device) fp32 [B][Hq] or NULL.
+ * One kernel launch: split over the index set with an in-kernel combine. */
+sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
+                             const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+                             int32_t n_recent, const uint8_t* head_mask,
+                             float* out, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes needed by one call of `op` on this descriptor.  idx_stride and n_recent
+ * (index capacity and recent window) are used by SFI_OP_SPARSE only; SFI_OP_DENSE and
+ * SFI_OP_SELECT size from the descriptor (max_len) alone.  Returns 0 when the descriptor
+ * or op is invalid. */
+size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,
+                           int32_t n_recent);
+
+/* Static description of a status code. */
+const char* sfi_status_string(sfi_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SFI_H */

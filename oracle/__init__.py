@@ -53,7 +53,8 @@ def lib():
         L.orc_sparse.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int32, P,
                                  ctypes.c_int32, P, P, P]
         L.orc_sink_mask.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_double, P]
-        for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask):
+        L.orc_threads.argtypes = []
+        for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask, L.orc_threads):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -180,3 +181,8 @@ def sink_mask(z0, lse, frac: float):
     if rc != 0:
         raise ValueError("frac outside [0, 1]")
     return m
+
+
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(lib().orc_threads())

@@ -19,6 +19,7 @@
 #include "sfi_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -239,3 +240,7 @@ int orc_sink_mask(int32_t B, int32_t Hq, const double* z0, const double* lse, do
     free(p0);
     return 0;
 }
+
+/* ---- threads ---------------------------------------------------------------------------- */
+
+int orc_threads(void) { return omp_get_max_threads(); }

@@ -74,6 +74,9 @@ int orc_sparse(const orc_cache* c, const void* q, const int32_t* idx, int32_t id
 int orc_sink_mask(int32_t B, int32_t Hq, const double* z0, const double* lse, double frac,
                   uint8_t* head_mask);
 
+/* OpenMP threads the functions above use. */
+int orc_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,182 @@
+"""Thin ctypes binding of libsfi.so (include/sfi.h), with the same names as the C ABI.
+
+Argument marshalling only: tensors are passed as device pointers, the stream is torch's
+current HIP stream unless one is given, and a non-zero status raises ``SfiError``.  Every
+computation happens in the library's HIP kernels; there is no fallback of any kind, and
+importing this module fails loudly when libsfi.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfi.so")
+
+SFI_OK, SFI_E_INVALID, SFI_E_UNSUPPORTED, SFI_E_WORKSPACE, SFI_E_HIP = 0, -1, -2, -3, -4
+SFI_F32, SFI_BF16 = 0, 1
+SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE = 0, 1, 2
+
+EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
+            "sfi_workspace_bytes", "sfi_status_string")
+
+
+class SfiError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sfi_status_string(status)}")
+
+
+class sfi_kv_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("n_cap", ctypes.c_int64), ("block_table", ctypes.c_void_p),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing; build it with "
+                              "`python -m sparse_kv_attention_dense_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        D = ctypes.POINTER(sfi_kv_desc)
+        L.sfi_dense_decode.argtypes = [D, P, P, P, P, i64, P, ctypes.c_size_t, P]
+        L.sfi_select.argtypes = [D, P, i64, i32, i32, i32, P, i32, P, P, ctypes.c_size_t, P]
+        L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
+        L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
+        L.sfi_workspace_bytes.restype = ctypes.c_size_t
+        L.sfi_status_string.argtypes = [ctypes.c_int]
+        L.sfi_status_string.restype = ctypes.c_char_p
+        for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    if torch.cuda.is_available():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return None
+
+
+def _check(status: int, where: str):
+    if status != SFI_OK:
+        raise SfiError(status, where)
+
+
+class KVDesc:
+    """Builds an ``sfi_kv_desc`` from tensors and keeps them alive while it is in use.
+
+    k, v: contiguous [B][Hkv][n_cap][d] or paged [num_blocks][Hkv][block_size][d], fp32 or
+    bf16.  lens: int32 [B] on the device.  max_len: host bound of lens.  block_table: int32
+    [B][max_blocks] on the device for the paged layout.
+    """
+
+    def __init__(self, k, v, lens, max_len: int, num_q_heads: int, block_table=None,
+                 block_size: int = 0, batch: Optional[int] = None):
+        self._keep = (k, v, lens, block_table)
+        if k is not None:
+            dtype = {torch.float32: SFI_F32, torch.bfloat16: SFI_BF16}.get(k.dtype, 99)
+            hkv, d = int(k.shape[1]), int(k.shape[-1])
+        else:
+            dtype, hkv, d = SFI_F32, 0, 0
+        self.c = sfi_kv_desc()
+        self.c.batch = int(batch if batch is not None else lens.shape[0])
+        self.c.num_q_heads = int(num_q_heads)
+        self.c.num_kv_heads = hkv
+        self.c.head_dim = d
+        self.c.dtype = dtype
+        self.c.k = k.data_ptr() if k is not None else None
+        self.c.v = v.data_ptr() if v is not None else None
+        self.c.n_cap = int(k.shape[2]) if (k is not None and block_table is None) else 0
+        self.c.block_table = block_table.data_ptr() if block_table is not None else None
+        self.c.block_size = int(block_size)
+        self.c.max_blocks = int(block_table.shape[1]) if block_table is not None else 0
+        self.c.len = lens.data_ptr() if lens is not None else None
+        self.c.max_len = int(max_len)
+
+    @classmethod
+    def for_logits(cls, lens, max_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int = 128):
+        """Descriptor for calls that read no cache (sfi_select, sfi_sink_bypass_mask)."""
+        d = cls(None, None, lens, max_len, num_q_heads)
+        d.c.num_kv_heads = int(num_kv_heads)
+        d.c.head_dim = int(head_dim)
+        d.c.dtype = SFI_BF16
+        return d
+
+    def with_lens(self, lens, max_len: int) -> "KVDesc":
+        """Same cache, other lengths (a later decode step)."""
+        d = object.__new__(KVDesc)
+        d._keep = self._keep + (lens,)
+        d.c = sfi_kv_desc.from_buffer_copy(self.c)
+        d.c.len = lens.data_ptr()
+        d.c.max_len = int(max_len)
+        return d
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def sfi_status_string(status: int) -> str:
+    return lib().sfi_status_string(int(status)).decode()
+
+
+def sfi_workspace_bytes(desc: KVDesc, op: int, idx_stride: int = 0, n_recent: int = 0) -> int:
+    return int(lib().sfi_workspace_bytes(desc.ref, int(op), int(idx_stride), int(n_recent)))
+
+
+def sfi_dense_decode(desc: KVDesc, q, out, lse, logits, logit_stride: int, ws, stream=None):
+    _check(lib().sfi_dense_decode(desc.ref, _ptr(q), _ptr(out), _ptr(lse), _ptr(logits),
+                                  int(logit_stride), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "sfi_dense_decode")
+
+
+def sfi_select(desc: KVDesc, logits, logit_stride: int, n_sink: int, n_recent: int, k_sel: int,
+               idx, idx_stride: int, n_idx, ws, stream=None):
+    _check(lib().sfi_select(desc.ref, _ptr(logits), int(logit_stride), int(n_sink),
+                            int(n_recent), int(k_sel), _ptr(idx), int(idx_stride), _ptr(n_idx),
+                            _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "sfi_select")
+
+
+def sfi_sink_bypass_mask(desc: KVDesc, logits, logit_stride: int, lse, frac: float, head_mask,
+                         stream=None):
+    _check(lib().sfi_sink_bypass_mask(desc.ref, _ptr(logits), int(logit_stride), _ptr(lse),
+                                      float(frac), _ptr(head_mask), _stream(stream)),
+           "sfi_sink_bypass_mask")
+
+
+def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int, head_mask,
+                      out, lse, ws, stream=None):
+    _check(lib().sfi_sparse_decode(desc.ref, _ptr(q), _ptr(idx), int(idx_stride), _ptr(n_idx),
+                                   int(n_recent), _ptr(head_mask), _ptr(out), _ptr(lse),
+                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "sfi_sparse_decode")
+
+
+def workspace(desc: KVDesc, idx_stride: int = 1, n_recent: int = 0, device="cuda"):
+    """A zero-filled workspace large enough for every op on this descriptor (plumbing:
+    torch allocates it once; the library itself never allocates)."""
+    n = max(sfi_workspace_bytes(desc, op, idx_stride, n_recent)
+            for op in (SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE))
+    if n == 0:
+        raise SfiError(SFI_E_INVALID, "workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)

@@ -1,0 +1,283 @@
+// sfi_api.cpp -- host side of the libsfi.so C ABI (include/sfi.h): argument validation,
+// workspace layout and kernel launches.  No allocation, no synchronisation, no device
+// queries: the split plan depends only on the descriptor.
+#include <math.h>
+#include <string.h>
+
+#include "sfi.h"
+#include "sfi_internal.h"
+
+#define SFI_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace sfi;
+
+// Workgroups a launch aims for: four per compute unit of a 256-CU MI355X, enough to fill
+// the chip with two resident workgroups per CU and leave a short tail.
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+// Ticket counters sit at the start of every op's workspace so that one buffer, sized for
+// the largest op, can serve all calls: only the attention kernels touch this region and
+// they leave it zeroed.
+size_t ticket_bytes(const sfi_kv_desc& kv) {
+    return align_up((size_t)kv.batch * kv.num_kv_heads * (kGroupSplits + 1) * sizeof(uint32_t));
+}
+
+sfi_status check_desc(const sfi_kv_desc* kv, bool need_cache) {
+    if (!kv) return SFI_E_INVALID;
+    if (kv->batch < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1) return SFI_E_INVALID;
+    if (kv->num_q_heads % kv->num_kv_heads != 0) return SFI_E_INVALID;
+    if (kv->num_q_heads / kv->num_kv_heads > kMaxG) return SFI_E_UNSUPPORTED;
+    if (kv->batch > 65535 || kv->num_kv_heads > 65535 || kv->num_q_heads > 65535) return SFI_E_UNSUPPORTED;
+    if (kv->head_dim != 64 && kv->head_dim != 128) return SFI_E_UNSUPPORTED;
+    if (kv->dtype != SFI_F32 && kv->dtype != SFI_BF16) return SFI_E_UNSUPPORTED;
+    if (!kv->len || kv->max_len < 0) return SFI_E_INVALID;
+    if (!need_cache) return SFI_OK;
+    if (!kv->k || !kv->v || !aligned(kv->k, 16) || !aligned(kv->v, 16)) return SFI_E_INVALID;
+    if (kv->block_table) {
+        const int bs = kv->block_size;
+        if (bs < 1 || bs > 1024 || (bs & (bs - 1)) != 0) return SFI_E_INVALID;
+        if (kv->max_blocks < 1 || (int64_t)kv->max_blocks * bs < kv->max_len) return SFI_E_INVALID;
+    } else {
+        if (kv->n_cap < kv->max_len || kv->n_cap < 0) return SFI_E_INVALID;
+        // row numbers are kept in 32 bits
+        if ((int64_t)kv->batch * kv->num_kv_heads * kv->n_cap >= (int64_t(1) << 32)) return SFI_E_UNSUPPORTED;
+    }
+    return SFI_OK;
+}
+
+struct AttnPlan {
+    int split_len = 0, nsplit = 0, ngroups = 0, rec = 0;
+    size_t off_part = 0, off_part1 = 0, bytes = 0;
+};
+
+sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride, int64_t n_recent,
+                          AttnPlan* p) {
+    const bool tab = sparse || kv.block_table != nullptr;
+    const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
+    const int64_t G = kv.num_q_heads / kv.num_kv_heads;
+    int64_t slots = sparse ? idx_stride + n_recent : (int64_t)kv.max_len;
+    if (slots < 1) slots = 1;
+    const int64_t per_unit = ceil_div(kTargetWorkgroups, units);
+    int64_t split = ceil_div(ceil_div(slots, per_unit), kSplitQuantum) * kSplitQuantum;
+    if (tab && split > kTabMax) split = kTabMax;
+    int64_t nsplit = ceil_div(slots, split);
+    if (nsplit > kMaxSplits) {
+        if (tab) return SFI_E_UNSUPPORTED;        // more than kMaxSplits * kTabMax slots
+        split = ceil_div(ceil_div(slots, kMaxSplits), kSplitQuantum) * kSplitQuantum;
+        nsplit = ceil_div(slots, split);
+    }
+    p->split_len = (int)split;
+    p->nsplit = (int)nsplit;
+    p->ngroups = (int)ceil_div(nsplit, kGroupSplits);
+    p->rec = (int)(ceil_div(G * (kv.head_dim + 2), 4) * 4);
+    size_t off = ticket_bytes(kv);
+    p->off_part = off;
+    off += align_up((size_t)units * nsplit * p->rec * sizeof(float));
+    p->off_part1 = off;
+    if (p->ngroups > 1) off += align_up((size_t)units * p->ngroups * p->rec * sizeof(float));
+    p->bytes = off;
+    return SFI_OK;
+}
+
+struct SelPlan {
+    int nchunk = 0;
+    size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0, bytes = 0;
+};
+
+void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
+    const size_t B = kv.batch, Hq = kv.num_q_heads, Hkv = kv.num_kv_heads;
+    p->nchunk = (int)(kv.max_len > 0 ? ceil_div(kv.max_len, kSelChunk) : 1);
+    const size_t nc = p->nchunk;
+    size_t off = ticket_bytes(kv);
+    p->off_lse = off;    off += align_up(B * Hq * nc * sizeof(float2));
+    p->off_keys = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
+    p->off_hist = off;   off += align_up(B * Hkv * 3 * kRadixBins * sizeof(uint32_t));
+    p->off_state = off;  off += align_up(B * Hkv * 4 * sizeof(int32_t));
+    p->off_counts = off; off += align_up(B * Hkv * nc * 2 * sizeof(uint32_t));
+    p->bytes = off;
+}
+
+sfi_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+    if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return SFI_E_WORKSPACE;
+    return SFI_OK;
+}
+
+void fill_cache_args(const sfi_kv_desc& kv, AttnArgs* a) {
+    memset(a, 0, sizeof *a);
+    a->k = kv.k;
+    a->v = kv.v;
+    a->len = kv.len;
+    a->block_table = kv.block_table;
+    a->n_cap = kv.n_cap;
+    a->block_shift = 0;
+    if (kv.block_table)
+        while ((1 << a->block_shift) < kv.block_size) ++a->block_shift;
+    a->max_blocks = kv.max_blocks;
+    a->Hq = kv.num_q_heads;
+    a->Hkv = kv.num_kv_heads;
+    a->G = kv.num_q_heads / kv.num_kv_heads;
+    a->scale = (float)(1.0 / sqrt((double)kv.head_dim));
+    a->scale_log2 = (float)(1.4426950408889634 / sqrt((double)kv.head_dim));
+}
+
+void fill_plan_args(const AttnPlan& p, const sfi_kv_desc& kv, void* ws, AttnArgs* a) {
+    unsigned char* base = (unsigned char*)ws;
+    a->split_len = p.split_len;
+    a->nsplit = p.nsplit;
+    a->ngroups = p.ngroups;
+    a->rec_floats = p.rec;
+    a->tick1 = (uint32_t*)base;
+    a->tick2 = a->tick1 + (size_t)kv.batch * kv.num_kv_heads * kGroupSplits;
+    a->part = (float*)(base + p.off_part);
+    a->part1 = (float*)(base + p.off_part1);
+}
+
+}  // namespace
+
+SFI_EXPORT sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
+                                       float* logits, int64_t logit_stride,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+    sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return SFI_E_INVALID;
+    if (logits && (logit_stride < kv->max_len || logit_stride % 4 != 0 || !aligned(logits, 16)))
+        return SFI_E_INVALID;
+    AttnPlan plan;
+    st = plan_attention(*kv, false, 0, 0, &plan);
+    if (st != SFI_OK) return st;
+    st = check_ws(ws, ws_bytes, plan.bytes);
+    if (st != SFI_OK) return st;
+    AttnArgs a;
+    fill_cache_args(*kv, &a);
+    fill_plan_args(plan, *kv, ws, &a);
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.logits = logits;
+    a.logit_stride = logit_stride;
+    const hipError_t e = launch_attention(a, kv->batch, kv->head_dim, kv->dtype == SFI_BF16,
+                                          kv->block_table != nullptr, false, stream);
+    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
+                                        const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+                                        int32_t n_recent, const uint8_t* head_mask,
+                                        float* out, float* lse,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+    sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    if (!q || !out || !idx || !n_idx || !aligned(q, 16) || !aligned(out, 16)) return SFI_E_INVALID;
+    if (idx_stride < 1 || n_recent < 0) return SFI_E_INVALID;
+    AttnPlan plan;
+    st = plan_attention(*kv, true, idx_stride, n_recent, &plan);
+    if (st != SFI_OK) return st;
+    st = check_ws(ws, ws_bytes, plan.bytes);
+    if (st != SFI_OK) return st;
+    AttnArgs a;
+    fill_cache_args(*kv, &a);
+    fill_plan_args(plan, *kv, ws, &a);
+    a.q = q;
+    a.out = out;
+    a.lse = lse;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.n_idx = n_idx;
+    a.n_recent = n_recent;
+    a.head_mask = head_mask;
+    const hipError_t e = launch_attention(a, kv->batch, kv->head_dim, kv->dtype == SFI_BF16,
+                                          kv->block_table != nullptr, true, stream);
+    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                                 int32_t n_sink, int32_t n_recent, int32_t k_sel,
+                                 int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                                 void* ws, size_t ws_bytes, hipStream_t stream) {
+    sfi_status st = check_desc(kv, false);
+    if (st != SFI_OK) return st;
+    if (!logits || !idx || !n_idx || logit_stride < kv->max_len || logit_stride < 1) return SFI_E_INVALID;
+    if (n_sink < 0 || n_recent < 0 || k_sel < 0) return SFI_E_INVALID;
+    if ((int64_t)idx_stride < (int64_t)n_sink + k_sel || idx_stride < 1) return SFI_E_INVALID;
+    SelPlan plan;
+    plan_select(*kv, &plan);
+    st = check_ws(ws, ws_bytes, plan.bytes);
+    if (st != SFI_OK) return st;
+    unsigned char* base = (unsigned char*)ws;
+    SelArgs a;
+    a.logits = logits;
+    a.logit_stride = logit_stride;
+    a.len = kv->len;
+    a.B = kv->batch;
+    a.Hq = kv->num_q_heads;
+    a.Hkv = kv->num_kv_heads;
+    a.G = kv->num_q_heads / kv->num_kv_heads;
+    a.n_sink = n_sink;
+    a.n_recent = n_recent;
+    a.k_sel = k_sel;
+    a.nchunk = plan.nchunk;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.n_idx = n_idx;
+    a.lse_part = (float2*)(base + plan.off_lse);
+    a.keys = (uint32_t*)(base + plan.off_keys);
+    a.hist = (uint32_t*)(base + plan.off_hist);
+    a.state = (int32_t*)(base + plan.off_state);
+    a.counts = (uint32_t*)(base + plan.off_counts);
+    const hipError_t e = launch_select(a, stream);
+    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+SFI_EXPORT sfi_status sfi_sink_bypass_mask(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                                           const float* lse, float frac, uint8_t* head_mask,
+                                           hipStream_t stream) {
+    sfi_status st = check_desc(kv, false);
+    if (st != SFI_OK) return st;
+    if (!logits || !lse || !head_mask || logit_stride < 1) return SFI_E_INVALID;
+    if (!(frac >= 0.f && frac <= 1.f)) return SFI_E_INVALID;
+    if (kv->num_q_heads > 1024) return SFI_E_UNSUPPORTED;
+    MaskArgs a;
+    a.logits = logits;
+    a.logit_stride = logit_stride;
+    a.lse = lse;
+    a.B = kv->batch;
+    a.Hq = kv->num_q_heads;
+    a.n_mask = (int32_t)floor((double)frac * kv->num_q_heads);
+    a.head_mask = head_mask;
+    const hipError_t e = launch_sink_mask(a, stream);
+    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+SFI_EXPORT size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,
+                                      int32_t n_recent) {
+    if (op == SFI_OP_SELECT) {
+        if (check_desc(kv, false) != SFI_OK) return 0;
+        SelPlan p;
+        plan_select(*kv, &p);
+        return p.bytes;
+    }
+    if (op != SFI_OP_DENSE && op != SFI_OP_SPARSE) return 0;
+    if (check_desc(kv, true) != SFI_OK) return 0;
+    if (op == SFI_OP_SPARSE && (idx_stride < 1 || n_recent < 0)) return 0;
+    AttnPlan p;
+    if (plan_attention(*kv, op == SFI_OP_SPARSE, idx_stride, n_recent, &p) != SFI_OK) return 0;
+    return p.bytes;
+}
+
+SFI_EXPORT const char* sfi_status_string(sfi_status s) {
+    switch (s) {
+        case SFI_OK: return "SFI_OK: success";
+        case SFI_E_INVALID: return "SFI_E_INVALID: invalid pointer, size or alignment";
+        case SFI_E_UNSUPPORTED: return "SFI_E_UNSUPPORTED: head_dim, dtype, group size or length not supported";
+        case SFI_E_WORKSPACE: return "SFI_E_WORKSPACE: workspace missing, misaligned or too small";
+        case SFI_E_HIP: return "SFI_E_HIP: HIP runtime error at launch";
+    }
+    return "unknown sfi_status";
+}

@@ -1,0 +1,515 @@
+// sfi_attention.hip -- split-K GQA decode attention for gfx950 (dense slow step and sparse
+// fast step of Slow-Fast Inference).
+//
+// One workgroup (4 wavefronts) owns one (batch b, KV head h, split s): a contiguous range of
+// "slots".  A slot is a key position: in the dense step slot == position; in the sparse step
+// slot k < n_idx is idx[k] and the remaining slots walk the recent window [r0, len).  Each
+// wavefront takes 32-slot tiles round-robin and keeps an online softmax (m, l, acc) for the
+// G query heads of the group:
+//   - S^T = K_tile * Q^T on MFMA (v_mfma_f32_16x16x32_bf16, or 16x16x4 f32): the 16 rows of
+//     the A operand are 16 key rows, read straight from HBM as 16-byte pieces, and the 16
+//     columns are the (zero-padded) query heads, so each K row is read once for the group
+//     (grouped-query attention without repeating K/V, SinkRouter Sec. 4.3).
+//   - the fp32 logits z = S * 1/sqrt(d) go to HBM as float4 stores (dense step only; SFI
+//     Sec. 4.2 needs the logits exposed for the Selector).
+//   - O^T += V_tile^T * P^T on MFMA; bf16 V rows are staged through LDS and read back
+//     transposed, and P is split into a bf16 high part and a bf16 residual so the product
+//     keeps about 16 bits of the fp32 weight.
+// The (m, l, acc) partials of the splits are merged inside the same launch: the last
+// workgroup to finish a group of 16 splits merges them (an atomic ticket per group), and
+// the last group merger merges the groups.  Merging uses the log-sum-exp rule
+//   M = max_s m_s,  out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s
+// with m kept in log2 units.
+#include <type_traits>
+
+#include "sfi_internal.h"
+
+namespace sfi {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.693147180559945309417f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Orders this wavefront's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <bool BF, int D, bool PAGED, bool SPARSE>
+struct Cfg {
+    static constexpr int kVRow = D * 2 + 16;                       // staged bf16 row, bytes
+    static constexpr int kVStage = BF ? kWaves * kTile * kVRow : 0;
+    static constexpr int kRed = kWaves * kMaxG * (D + 2) * 4;      // cross-wave merge
+    static constexpr int kMerge = (2 * kGroupSplits * kMaxG + 2 * kMaxG) * 4;
+    static constexpr int kRaw0 = kVStage > kRed ? kVStage : kRed;
+    static constexpr int kRaw = kRaw0 > kMerge ? kRaw0 : kMerge;
+    static constexpr bool kTab = PAGED || SPARSE;
+    static constexpr int kNQ = BF ? D / 32 : D / 16;               // Q / K fragments per row
+    static constexpr int kNV = BF ? D / 16 : 2 * 4 * (D / 16);     // V registers per tile
+    static constexpr int kRPI = 1024 / (2 * D);                    // bf16 V rows per wave load
+    static constexpr int kLPR = 64 / kRPI;                         // lanes per bf16 V row
+    using QF = typename std::conditional<BF, u32x4, f32x4>::type;
+    using VR = typename std::conditional<BF, u32x4, float>::type;
+};
+
+template <bool BF, int D, bool PAGED, bool SPARSE>
+struct TileRegs {
+    using C = Cfg<BF, D, PAGED, SPARSE>;
+    typename C::QF k[2][C::kNQ];
+    typename C::VR v[C::kNV];
+};
+
+// Merges `count` partial records (stride a.rec_floats) for the G heads of (b, h).
+// dst != nullptr: writes one merged record (acc unnormalised, with its m and l).
+// dst == nullptr: writes out = acc / l and lse, zero surrogate for bypassed heads.
+template <int D, bool SPARSE>
+__device__ void merge_records(const AttnArgs& a, const float* src, int count, float* dst,
+                              int b, int h, float* scratch) {
+    const int tid = threadIdx.x;
+    const int G = a.G;
+    const int rec = a.rec_floats;
+    float* lm = scratch;                              // [count][G]
+    float* lw = lm + kGroupSplits * kMaxG;            // [count][G]
+    float* sM = lw + kGroupSplits * kMaxG;            // [G]
+    float* sL = sM + kMaxG;                           // [G]
+    for (int e = tid; e < count * G; e += kThreads) {
+        const int s = e / G, g = e - s * G;
+        lm[e] = src[(int64_t)s * rec + G * D + 2 * g];
+        lw[e] = src[(int64_t)s * rec + G * D + 2 * g + 1];
+    }
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+        for (int s = 0; s < count; ++s) M = fmaxf(M, lm[s * G + tid]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f;
+        for (int s = 0; s < count; ++s) L += exp2_fast(lm[s * G + tid] - Mu) * lw[s * G + tid];
+        sM[tid] = M;
+        sL[tid] = L;
+    }
+    __syncthreads();
+    for (int e = tid; e < count * G; e += kThreads) {
+        const int g = e % G;
+        const float Mu = (sM[g] == -INFINITY) ? 0.f : sM[g];
+        lw[e] = exp2_fast(lm[e] - Mu);
+    }
+    __syncthreads();
+    constexpr int Q4 = D / 4;
+    for (int o = tid; o < G * Q4; o += kThreads) {
+        const int g = o / Q4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 16
+        for (int s = 0; s < count; ++s) {
+            const f32x4 v = *(const f32x4*)(src + (int64_t)s * rec + 4 * o);
+            acc += lw[s * G + g] * v;
+        }
+        if (dst) {
+            *(f32x4*)(dst + 4 * o) = acc;
+        } else {
+            const float L = sL[g];
+            bool zero = !(L > 0.f);
+            if constexpr (SPARSE) {
+                if (a.head_mask) zero |= a.head_mask[b * a.Hq + h * G + g] != 0;
+            }
+            const f32x4 r = zero ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / L);
+            *(f32x4*)(a.out + ((int64_t)b * a.Hq + h * G + g) * D + 4 * (o - g * Q4)) = r;
+        }
+    }
+    if (tid < G) {
+        if (dst) {
+            dst[G * D + 2 * tid] = sM[tid];
+            dst[G * D + 2 * tid + 1] = sL[tid];
+        } else if (a.lse) {
+            const float L = sL[tid];
+            bool zero = !(L > 0.f);
+            if constexpr (SPARSE) {
+                if (a.head_mask) zero |= a.head_mask[b * a.Hq + h * G + tid] != 0;
+            }
+            a.lse[b * a.Hq + h * G + tid] = zero ? -INFINITY : (sM[tid] + log2f(L)) * kLn2;
+        }
+    }
+}
+
+template <bool BF, int D, bool PAGED, bool SPARSE>
+__global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_kernel(AttnArgs a) {
+    using C = Cfg<BF, D, PAGED, SPARSE>;
+    using Regs = TileRegs<BF, D, PAGED, SPARSE>;
+    __shared__ __attribute__((aligned(16))) unsigned char raw[C::kRaw];
+    __shared__ uint32_t tab_row[C::kTab ? kTabMax : 1];
+    __shared__ uint8_t tab_ok[SPARSE ? kTabMax : 1];
+    __shared__ int s_flag;
+
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int q4 = lane >> 4, n16 = lane & 15;
+    const int G = a.G;
+    const int hq0 = h * G;
+    const int unit = b * a.Hkv + h;
+    const int len_b = a.len[b];
+
+    // ---- slot range of this workgroup -------------------------------------------------
+    int n_sel = 0, r0 = 0, n_tot = len_b;
+    bool all_masked = false;
+    if constexpr (SPARSE) {
+        n_sel = min(max(a.n_idx[unit], 0), a.idx_stride);
+        r0 = max(0, len_b - a.n_recent);
+        n_tot = len_b > 0 ? n_sel + (len_b - r0) : 0;
+        if (a.head_mask) {
+            all_masked = true;
+            for (int g = 0; g < G; ++g) all_masked &= a.head_mask[b * a.Hq + hq0 + g] != 0;
+        }
+    }
+    const int s0 = split * a.split_len;
+    int s1 = min(n_tot, s0 + a.split_len);
+    if (all_masked || len_b <= 0) s1 = s0;
+    const int nslots = max(0, s1 - s0);
+
+    const uint32_t base_row = PAGED ? 0u : (uint32_t)((int64_t)unit * a.n_cap);
+
+    if constexpr (C::kTab) {
+        const int bmask = (1 << a.block_shift) - 1;
+        for (int t = tid; t < nslots; t += kThreads) {
+            const int slot = s0 + t;
+            int pos = slot;
+            if constexpr (SPARSE) {
+                bool ok = true;
+                if (slot < n_sel) {
+                    pos = a.idx[(int64_t)unit * a.idx_stride + slot];
+                    ok = pos >= 0 && pos < r0;
+                    if (!ok) pos = len_b - 1;
+                } else {
+                    pos = r0 + (slot - n_sel);
+                }
+                tab_ok[t] = ok;
+            }
+            uint32_t row;
+            if constexpr (PAGED) {
+                const int blk = a.block_table[(int64_t)b * a.max_blocks + (pos >> a.block_shift)];
+                row = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
+                      (uint32_t)(pos & bmask);
+            } else {
+                row = base_row + (uint32_t)pos;
+            }
+            tab_row[t] = row;
+        }
+        __syncthreads();
+    }
+
+    auto slot_row = [&](int slot) -> uint32_t {     // slot in [s0, s1)
+        if constexpr (C::kTab) return tab_row[slot - s0];
+        else return base_row + (uint32_t)slot;
+    };
+    auto slot_ok = [&](int slot) -> bool {
+        if (slot >= s1) return false;
+        if constexpr (SPARSE) return tab_ok[slot - s0] != 0;
+        else return true;
+    };
+
+    // ---- query fragments (B operand of S^T = K Q^T); heads >= G are zero columns ---------
+    typename C::QF qf[C::kNQ];
+    {
+        const bool has = n16 < G;
+        const int64_t qoff = ((int64_t)b * a.Hq + hq0 + (has ? n16 : 0)) * D;
+#pragma unroll
+        for (int c = 0; c < C::kNQ; ++c) {
+            if constexpr (BF) {
+                const uint16_t* qp = (const uint16_t*)a.q + qoff;
+                qf[c] = has ? *(const u32x4*)(qp + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+            } else {
+                const float* qp = (const float*)a.q + qoff;
+                qf[c] = has ? *(const f32x4*)(qp + 16 * c + 4 * q4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    unsigned char* vstage = raw + w * kTile * C::kVRow;
+    float* logit_row = nullptr;
+    if constexpr (!SPARSE) {
+        if (a.logits && n16 < G) logit_row = a.logits + ((int64_t)b * a.Hq + hq0 + n16) * a.logit_stride;
+    }
+
+    // ---- tile loads (issued one tile ahead of the math) ------------------------------------
+    auto issue = [&](Regs& r, int tile) {
+        const int sb = s0 + tile * kTile;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            const uint32_t row = slot_row(min(sb + 16 * st + n16, s1 - 1));
+#pragma unroll
+            for (int c = 0; c < C::kNQ; ++c) {
+                if constexpr (BF) {
+                    const uint16_t* kp = (const uint16_t*)a.k + (uint64_t)row * D;
+                    r.k[st][c] = *(const u32x4*)(kp + 32 * c + 8 * q4);
+                } else {
+                    const float* kp = (const float*)a.k + (uint64_t)row * D;
+                    r.k[st][c] = *(const f32x4*)(kp + 16 * c + 4 * q4);
+                }
+            }
+        }
+        if constexpr (BF) {
+#pragma unroll
+            for (int j = 0; j < C::kNV; ++j) {
+                const int rr = j * C::kRPI + lane / C::kLPR;
+                const uint32_t row = slot_row(min(sb + rr, s1 - 1));
+                r.v[j] = *(const u32x4*)((const uint16_t*)a.v + (uint64_t)row * D + (lane % C::kLPR) * 8);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t row = slot_row(min(sb + 16 * st + 4 * q4 + i, s1 - 1));
+                    const float* vp = (const float*)a.v + (uint64_t)row * D;
+#pragma unroll
+                    for (int mb = 0; mb < D / 16; ++mb) r.v[(st * 4 + i) * (D / 16) + mb] = vp[16 * mb + n16];
+                }
+        }
+    };
+
+    // ---- tile math ----------------------------------------------------------------------
+    auto compute = [&](Regs& r, int tile) {
+        const int sb = s0 + tile * kTile;
+        if constexpr (BF) {
+#pragma unroll
+            for (int j = 0; j < C::kNV; ++j) {
+                const int rr = j * C::kRPI + lane / C::kLPR;
+                *(u32x4*)(vstage + rr * C::kVRow + (lane % C::kLPR) * 16) = r.v[j];
+            }
+        }
+        f32x4 S[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            S[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < C::kNQ; ++c) {
+                if constexpr (BF) {
+                    S[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, r.k[st][c]), __builtin_bit_cast(bf16x8, qf[c]),
+                        S[st], 0, 0, 0);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        S[st] = __builtin_amdgcn_mfma_f32_16x16x4f32(r.k[st][c][e], qf[c][e], S[st], 0, 0, 0);
+                }
+            }
+        }
+        // scores of this lane: head n16, slots sb + 16*st + 4*q4 + i
+        float sv[2][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = slot_ok(sb + 16 * st + 4 * q4 + i);
+                sv[st][i] = ok ? S[st][i] * a.scale_log2 : -INFINITY;
+                tmax = fmaxf(tmax, sv[st][i]);
+            }
+        if constexpr (!SPARSE) {
+            if (logit_row) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const int p0 = sb + 16 * st + 4 * q4;
+                    const f32x4 z = S[st] * a.scale;
+                    if (p0 + 3 < s1) {
+                        *(f32x4*)(logit_row + p0) = z;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (p0 + i < s1) logit_row[p0 + i] = z[i];
+                    }
+                }
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run - m_use);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb) acc[mb] *= alpha;
+        float p[2][4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[st][i] = exp2_fast(sv[st][i] - m_use);
+                l_run += p[st][i];
+            }
+        if constexpr (BF) {
+            // P^T as the B operand: virtual k = 8*q4 + e maps to slot 4*q4 + e of block 0
+            // (e < 4) or of block 1 (e >= 4); the V^T A operand uses the same map.
+            bf16x8 ph, pl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pv = e < 4 ? p[0][e] : p[1][e - 4];
+                const __bf16 hi = (__bf16)pv;
+                ph[e] = hi;
+                pl[e] = (__bf16)(pv - (float)hi);
+            }
+            wave_lds_sync();
+            const uint16_t* vb16 = (const uint16_t*)vstage;
+#pragma unroll
+            for (int mb = 0; mb < D / 16; ++mb) {
+                u16x8 va;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tok = e < 4 ? 4 * q4 + e : 16 + 4 * q4 + (e - 4);
+                    va[e] = vb16[tok * (C::kVRow / 2) + 16 * mb + n16];
+                }
+                const bf16x8 vab = __builtin_bit_cast(bf16x8, va);
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vab, ph, acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vab, pl, acc[mb], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int mb = 0; mb < D / 16; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            r.v[(st * 4 + i) * (D / 16) + mb], p[st][i], acc[mb], 0, 0, 0);
+        }
+    };
+
+    // ---- main loop: wavefront w takes tiles w, w+4, ...; loads run one tile ahead ----------
+    const int ntiles = (nslots + kTile - 1) / kTile;
+    {
+        Regs ra, rb;
+        int t = w;
+        if (t < ntiles) issue(ra, t);
+        while (t < ntiles) {
+            int tn = t + kWaves;
+            if (tn < ntiles) issue(rb, tn);
+            compute(ra, t);
+            t = tn;
+            if (t >= ntiles) break;
+            tn = t + kWaves;
+            if (tn < ntiles) issue(ra, tn);
+            compute(rb, t);
+            t = tn;
+        }
+    }
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+
+    // ---- merge the four wavefronts, write this split's partial -----------------------------
+    __syncthreads();
+    float* red = (float*)raw;                         // [kWaves][kMaxG][D+2]
+    if (n16 < G) {
+        float* rp = red + (w * kMaxG + n16) * (D + 2);
+#pragma unroll
+        for (int mb = 0; mb < D / 16; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rp[16 * mb + 4 * q4 + i] = acc[mb][i];
+        if (q4 == 0) {
+            rp[D] = m_run;
+            rp[D + 1] = l_run;
+        }
+    }
+    __syncthreads();
+    {
+        float* part = a.part + ((int64_t)unit * a.nsplit + split) * a.rec_floats;
+        for (int e = tid; e < G * D; e += kThreads) {
+            const int g = e / D, dim = e - g * D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
+            const float Mu = (M == -INFINITY) ? 0.f : M;
+            float s = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww)
+                s += exp2_fast(red[(ww * kMaxG + g) * (D + 2) + D] - Mu) * red[(ww * kMaxG + g) * (D + 2) + dim];
+            part[e] = s;
+        }
+        if (tid < G) {
+            const int g = tid;
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
+            const float Mu = (M == -INFINITY) ? 0.f : M;
+            float L = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww)
+                L += exp2_fast(red[(ww * kMaxG + g) * (D + 2) + D] - Mu) * red[(ww * kMaxG + g) * (D + 2) + D + 1];
+            part[G * D + 2 * g] = M;
+            part[G * D + 2 * g + 1] = L;
+        }
+    }
+
+    // ---- in-launch combine: last of each group of 16 splits, then last group -------------
+    __threadfence();
+    __syncthreads();
+    const int grp = split / kGroupSplits;
+    const int gcount = min(kGroupSplits, a.nsplit - grp * kGroupSplits);
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(&a.tick1[unit * kGroupSplits + grp], 1u);
+        s_flag = old == (uint32_t)(gcount - 1);
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    if (tid == 0) atomicExch(&a.tick1[unit * kGroupSplits + grp], 0u);
+    __threadfence();
+    float* scratch = (float*)raw;
+    const float* gsrc = a.part + ((int64_t)unit * a.nsplit + grp * kGroupSplits) * a.rec_floats;
+    if (a.ngroups == 1) {
+        merge_records<D, SPARSE>(a, gsrc, gcount, nullptr, b, h, scratch);
+        return;
+    }
+    float* gdst = a.part1 + ((int64_t)unit * a.ngroups + grp) * a.rec_floats;
+    merge_records<D, SPARSE>(a, gsrc, gcount, gdst, b, h, scratch);
+    __threadfence();
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = atomicAdd(&a.tick2[unit], 1u);
+        s_flag = old == (uint32_t)(a.ngroups - 1);
+    }
+    __syncthreads();
+    if (!s_flag) return;
+    if (tid == 0) atomicExch(&a.tick2[unit], 0u);
+    __threadfence();
+    merge_records<D, SPARSE>(a, a.part1 + (int64_t)unit * a.ngroups * a.rec_floats, a.ngroups,
+                             nullptr, b, h, scratch);
+}
+
+template <bool BF, int D, bool PAGED, bool SPARSE>
+hipError_t launch_one(const AttnArgs& a, int B, hipStream_t stream) {
+    dim3 grid(a.nsplit, a.Hkv, B);
+    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <bool BF, int D>
+hipError_t launch_layout(const AttnArgs& a, int B, bool paged, bool sparse, hipStream_t s) {
+    if (paged) return sparse ? launch_one<BF, D, true, true>(a, B, s) : launch_one<BF, D, true, false>(a, B, s);
+    return sparse ? launch_one<BF, D, false, true>(a, B, s) : launch_one<BF, D, false, false>(a, B, s);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool paged, bool sparse,
+                            hipStream_t stream) {
+    if (bf16) {
+        if (d == 128) return launch_layout<true, 128>(a, B, paged, sparse, stream);
+        if (d == 64) return launch_layout<true, 64>(a, B, paged, sparse, stream);
+    } else {
+        if (d == 128) return launch_layout<false, 128>(a, B, paged, sparse, stream);
+        if (d == 64) return launch_layout<false, 64>(a, B, paged, sparse, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sfi

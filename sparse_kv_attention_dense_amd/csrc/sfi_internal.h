@@ -1,0 +1,91 @@
+// sfi_internal.h -- launch arguments and plans shared by the HIP sources of libsfi.so.
+// Not part of the public ABI (include/sfi.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sfi {
+
+// ---- attention kernels (dense slow step and sparse fast step share one kernel) ----------
+
+constexpr int kThreads = 256;        // 4 wavefronts of 64
+constexpr int kWaves = 4;
+constexpr int kTile = 32;            // slots per wavefront iteration (two 16-row MFMA blocks)
+constexpr int kSplitQuantum = kTile * kWaves;
+constexpr int kTabMax = 4096;        // slots per workgroup when rows come from a table
+constexpr int kGroupSplits = 16;     // partials merged by one combine step
+constexpr int kMaxSplits = kGroupSplits * kGroupSplits;
+constexpr int kMaxG = 16;            // query heads per KV head (MFMA N dimension)
+
+struct AttnArgs {
+    const void* k;
+    const void* v;
+    const void* q;
+    const int32_t* len;
+    const int32_t* block_table;      // paged only
+    int64_t n_cap;                   // contiguous only
+    int32_t block_shift;             // log2(block_size), paged only
+    int32_t max_blocks;
+    int32_t Hq, Hkv, G;
+    float scale;                     // 1/sqrt(d)
+    float scale_log2;                // scale * log2(e)
+    float* logits;                   // dense only, may be null
+    int64_t logit_stride;
+    int32_t split_len;               // slots per workgroup, multiple of kSplitQuantum
+    int32_t nsplit;                  // workgroups per (b, h)
+    int32_t ngroups;                 // ceil(nsplit / kGroupSplits)
+    int32_t rec_floats;              // floats per partial record (G*(d+2) rounded to 4)
+    const int32_t* idx;              // sparse only
+    int32_t idx_stride;
+    const int32_t* n_idx;
+    int32_t n_recent;
+    const uint8_t* head_mask;        // sparse only, may be null
+    float* out;
+    float* lse;                      // may be null
+    float* part;                     // [units][nsplit][rec]
+    float* part1;                    // [units][ngroups][rec]
+    uint32_t* tick1;                 // [units][kGroupSplits]
+    uint32_t* tick2;                 // [units]
+};
+
+hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool paged, bool sparse,
+                            hipStream_t stream);
+
+// ---- selector -------------------------------------------------------------------------
+
+constexpr int kSelChunk = 4096;      // positions of J per workgroup
+constexpr int kRadixBins = 2048;
+
+struct SelArgs {
+    const float* logits;
+    int64_t logit_stride;
+    const int32_t* len;
+    int32_t B, Hq, Hkv, G;
+    int32_t n_sink, n_recent, k_sel;
+    int32_t nchunk;
+    int32_t* idx;
+    int32_t idx_stride;
+    int32_t* n_idx;
+    float2* lse_part;                // [B][Hq][nchunk]
+    uint32_t* keys;                  // [B][Hkv][nchunk*kSelChunk]
+    uint32_t* hist;                  // [B][Hkv][3][kRadixBins]
+    int32_t* state;                  // [B][Hkv][4]: prefix, k_rem, nJ, take_all
+    uint32_t* counts;                // [B][Hkv][nchunk][2]
+};
+
+hipError_t launch_select(const SelArgs& a, hipStream_t stream);
+
+struct MaskArgs {
+    const float* logits;
+    int64_t logit_stride;
+    const float* lse;
+    int32_t B, Hq;
+    int32_t n_mask;
+    uint8_t* head_mask;
+};
+
+hipError_t launch_sink_mask(const MaskArgs& a, hipStream_t stream);
+
+}  // namespace sfi

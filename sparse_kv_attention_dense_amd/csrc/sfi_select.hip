@@ -1,0 +1,381 @@
+// sfi_select.hip -- the Selector of Slow-Fast Inference at decode, and the sink-bypass mask.
+//
+// Selector (SFI Sec. 3.2, evidence from the slow-step logits over the allowed set J with a
+// window of one query; Sec. 3.3, Top-K per KV head; prior and refinements off):
+//   1. lse_kernel       partial log-sum-exp of each query head's logits over a 4096-wide
+//                        chunk of J (also clears the radix histograms of the group)
+//   2. evidence_kernel  f(j) = sum_{i in group} exp(z_ij - LSE_J,i) for the chunk, stored as
+//                        uint32 keys (the bit pattern of a non-negative float orders like
+//                        the float), plus a histogram of the top 11 key bits
+//   3. radix_step / radix_hist, three digit passes (11, 11, 10 bits): find the key T of the
+//      k-th largest evidence and how many keys equal to T are kept
+//   4. count_kernel + emit_kernel: ordered compaction.  Position j of J is kept when
+//      key > T, or key == T and fewer than k_rem earlier positions have key == T (ties go
+//      to the lower position); kept positions are written in ascending order after the
+//      sink positions [0, min(n_sink, N)).
+// f is computed without the 1/G factor: a positive common scale does not change the order.
+//
+// Sink-bypass mask (SinkRouter Sec. 4.2): rank the query heads of each sequence by their
+// token-0 log-mass z_i0 - lse_i (the log of p0, same order as p0) and flag the first n_mask.
+#include "sfi_internal.h"
+
+namespace sfi {
+namespace {
+
+constexpr int kPerThread = kSelChunk / kThreads;     // 16 positions per thread
+constexpr int kShift[3] = {21, 10, 0};
+constexpr uint32_t kDigitMask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
+
+__device__ __forceinline__ float wave_max(float x) {
+    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+__device__ __forceinline__ uint32_t wave_sum_u(uint32_t x) {
+    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Block-wide reductions over the 256 threads (4 wavefronts).
+__device__ float block_max(float x, float* sh) {
+    x = wave_max(x);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+    __syncthreads();
+    return x;
+}
+__device__ float block_sum(float x, float* sh) {
+    x = wave_sum(x);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+    __syncthreads();
+    return x;
+}
+__device__ uint32_t block_sum_u(uint32_t x, uint32_t* sh) {
+    x = wave_sum_u(x);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = sh[0] + sh[1] + sh[2] + sh[3];
+    __syncthreads();
+    return x;
+}
+
+// Exclusive prefix sum over the 256 threads in thread order.
+__device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t inc = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) sh[w] = inc;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int ww = 0; ww < w; ++ww) before += sh[ww];
+    __syncthreads();
+    return before + inc - x;
+}
+
+struct Range {
+    int N, j0, j1, nJ;
+};
+__device__ __forceinline__ Range j_range(const SelArgs& a, int b) {
+    Range r;
+    r.N = a.len[b];
+    r.j0 = a.n_sink;
+    r.j1 = r.N - a.n_recent;
+    r.nJ = max(0, r.j1 - r.j0);
+    return r;
+}
+
+__global__ void __launch_bounds__(kThreads) lse_kernel(SelArgs a) {
+    __shared__ float sh[4];
+    const int c = blockIdx.x, i = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int h = i / a.G;
+    const int unit = b * a.Hkv + h;
+    if (c == 0 && i % a.G == 0) {
+        uint32_t* hh = a.hist + (int64_t)unit * 3 * kRadixBins;
+        for (int t = tid; t < 3 * kRadixBins; t += kThreads) hh[t] = 0u;
+    }
+    const Range r = j_range(a, b);
+    const int lo = r.j0 + c * kSelChunk;
+    const int hi = min(r.j1, lo + kSelChunk);
+    const float* z = a.logits + ((int64_t)b * a.Hq + i) * a.logit_stride;
+    float v[kPerThread];
+    float m = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = lo + k * kThreads + tid;
+        v[k] = j < hi ? z[j] : -INFINITY;
+        m = fmaxf(m, v[k]);
+    }
+    m = block_max(m, sh);
+    float s = 0.f;
+    if (m != -INFINITY) {
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) s += expf(v[k] - m);
+    }
+    s = block_sum(s, sh);
+    if (tid == 0) a.lse_part[((int64_t)b * a.Hq + i) * a.nchunk + c] = make_float2(m, s);
+}
+
+__global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
+    __shared__ float s_lse[kMaxG];
+    __shared__ uint32_t lh[kRadixBins];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int G = a.G;
+    const int unit = b * a.Hkv + h;
+    const Range r = j_range(a, b);
+    const int lo = r.j0 + c * kSelChunk;
+    const int hi = min(r.j1, lo + kSelChunk);
+    if (lo >= hi) return;
+    for (int t = tid; t < kRadixBins; t += kThreads) lh[t] = 0u;
+    for (int g = w; g < G; g += kWaves) {
+        const float2* lp = a.lse_part + ((int64_t)b * a.Hq + h * G + g) * a.nchunk;
+        float M = -INFINITY;
+        for (int k = lane; k < a.nchunk; k += 64) M = fmaxf(M, lp[k].x);
+        M = wave_max(M);
+        float S = 0.f;
+        for (int k = lane; k < a.nchunk; k += 64) {
+            const float2 e = lp[k];
+            if (e.x != -INFINITY) S += expf(e.x - M) * e.y;
+        }
+        S = wave_sum(S);
+        if (lane == 0) s_lse[g] = M + logf(S);
+    }
+    __syncthreads();
+    uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
+    const float* zb = a.logits + ((int64_t)b * a.Hq + h * G) * a.logit_stride;
+#pragma unroll 4
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = lo + k * kThreads + tid;
+        if (j < hi) {
+            float f = 0.f;
+            for (int g = 0; g < G; ++g) f += expf(zb[(int64_t)g * a.logit_stride + j] - s_lse[g]);
+            const uint32_t key = __float_as_uint(f);
+            keys[j - lo] = key;
+            atomicAdd(&lh[key >> kShift[0]], 1u);
+        }
+    }
+    __syncthreads();
+    uint32_t* hg = a.hist + (int64_t)unit * 3 * kRadixBins;
+    for (int t = tid; t < kRadixBins; t += kThreads)
+        if (lh[t]) atomicAdd(&hg[t], lh[t]);
+}
+
+// state: [0] prefix (bits of T decided so far), [1] k_rem, [2] nJ, [3] take_all
+__global__ void __launch_bounds__(kThreads) radix_step_kernel(SelArgs a, int pass) {
+    __shared__ uint32_t sh[4];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    int32_t* st = a.state + unit * 4;
+    uint32_t prefix;
+    int32_t k_rem, nJ, take_all;
+    if (pass == 0) {
+        nJ = j_range(a, b).nJ;
+        take_all = a.k_sel >= nJ ? 1 : 0;
+        k_rem = take_all ? nJ : a.k_sel;
+        prefix = 0u;
+        if (!take_all && k_rem == 0) prefix = 0xffffffffu;   // keep nothing from J
+    } else {
+        prefix = (uint32_t)st[0];
+        k_rem = st[1];
+        nJ = st[2];
+        take_all = st[3];
+    }
+    const bool active = !take_all && k_rem > 0 && prefix != 0xffffffffu;
+    const uint32_t* hg = a.hist + ((int64_t)unit * 3 + pass) * kRadixBins;
+    uint32_t cnt[8];
+    uint32_t mine = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        cnt[k] = active ? hg[8 * tid + k] : 0u;
+        mine += cnt[k];
+    }
+    // number of keys in bins above this thread's bins (threads hold ascending bins)
+    const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
+    const uint32_t total = block_sum_u(mine, sh);
+    const uint32_t above = total - below_incl;
+    __syncthreads();
+    if (active && above < (uint32_t)k_rem && (uint32_t)k_rem <= above + mine) {
+        uint32_t cum = above;
+        for (int k = 7; k >= 0; --k) {
+            if (cum + cnt[k] >= (uint32_t)k_rem) {
+                st[0] = (int32_t)(prefix | ((uint32_t)(8 * tid + k) << kShift[pass]));
+                st[1] = k_rem - (int32_t)cum;
+                st[2] = nJ;
+                st[3] = take_all;
+                break;
+            }
+            cum += cnt[k];
+        }
+    }
+    if (!active && tid == 0) {
+        st[0] = (int32_t)prefix;
+        st[1] = k_rem;
+        st[2] = nJ;
+        st[3] = take_all;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) radix_hist_kernel(SelArgs a, int pass) {
+    __shared__ uint32_t lh[kRadixBins];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    const int32_t* st = a.state + unit * 4;
+    const uint32_t prefix = (uint32_t)st[0];
+    const int32_t k_rem = st[1], nJ = st[2], take_all = st[3];
+    if (take_all || k_rem <= 0 || prefix == 0xffffffffu) return;
+    const int lo = c * kSelChunk;
+    const int cnt = min(kSelChunk, nJ - lo);
+    if (cnt <= 0) return;
+    for (int t = tid; t < kRadixBins; t += kThreads) lh[t] = 0u;
+    __syncthreads();
+    const int hs = kShift[pass - 1];
+    const uint32_t want = prefix >> hs;
+    const uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
+    for (int k = tid; k < cnt; k += kThreads) {
+        const uint32_t key = keys[k];
+        if ((key >> hs) == want) atomicAdd(&lh[(key >> kShift[pass]) & kDigitMask[pass]], 1u);
+    }
+    __syncthreads();
+    uint32_t* hg = a.hist + ((int64_t)unit * 3 + pass) * kRadixBins;
+    for (int t = tid; t <= (int)kDigitMask[pass]; t += kThreads)
+        if (lh[t]) atomicAdd(&hg[t], lh[t]);
+}
+
+__global__ void __launch_bounds__(kThreads) count_kernel(SelArgs a) {
+    __shared__ uint32_t sh[4];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    const int32_t* st = a.state + unit * 4;
+    const uint32_t T = (uint32_t)st[0];
+    const int32_t nJ = st[2], take_all = st[3];
+    const int lo = c * kSelChunk;
+    const int cnt = max(0, min(kSelChunk, nJ - lo));
+    const uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
+    uint32_t gt = 0, eq = 0;
+    for (int k = tid; k < cnt; k += kThreads) {
+        const uint32_t key = keys[k];
+        gt += (take_all || key > T) ? 1u : 0u;
+        eq += (!take_all && key == T) ? 1u : 0u;
+    }
+    gt = block_sum_u(gt, sh);
+    eq = block_sum_u(eq, sh);
+    if (tid == 0) {
+        a.counts[((int64_t)unit * a.nchunk + c) * 2] = gt;
+        a.counts[((int64_t)unit * a.nchunk + c) * 2 + 1] = eq;
+    }
+}
+
+__global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
+    __shared__ uint32_t sh[4];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    const int32_t* st = a.state + unit * 4;
+    const uint32_t T = (uint32_t)st[0];
+    const int32_t k_rem = st[1], nJ = st[2], take_all = st[3];
+    const int N = a.len[b];
+    const int ns = max(0, min(a.n_sink, N));
+    int32_t* row = a.idx + (int64_t)unit * a.idx_stride;
+    if (c == 0) {
+        for (int t = tid; t < ns; t += kThreads) row[t] = t;
+        if (tid == 0) a.n_idx[unit] = ns + (take_all ? nJ : min(a.k_sel, nJ));
+    }
+    const int lo = c * kSelChunk;
+    const int cnt = min(kSelChunk, nJ - lo);
+    if (cnt <= 0) return;
+    // kept positions in earlier chunks
+    uint32_t gtb = 0, eqb = 0;
+    for (int k = tid; k < c; k += kThreads) {
+        gtb += a.counts[((int64_t)unit * a.nchunk + k) * 2];
+        eqb += a.counts[((int64_t)unit * a.nchunk + k) * 2 + 1];
+    }
+    gtb = block_sum_u(gtb, sh);
+    eqb = block_sum_u(eqb, sh);
+    const uint32_t kr = take_all ? 0u : (uint32_t)k_rem;
+    const uint32_t base = (uint32_t)ns + gtb + min(eqb, kr);
+    // this thread's 16 consecutive positions
+    const uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
+    uint32_t kv[kPerThread];
+    uint32_t my_eq = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int t = tid * kPerThread + k;
+        kv[k] = t < cnt ? keys[t] : 0u;
+        my_eq += (t < cnt && !take_all && kv[k] == T) ? 1u : 0u;
+    }
+    uint32_t eq_rank = eqb + block_exclusive_scan(my_eq, sh);
+    uint32_t keep_mask = 0, my_keep = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const int t = tid * kPerThread + k;
+        bool keep = false;
+        if (t < cnt) {
+            if (take_all || kv[k] > T) {
+                keep = true;
+            } else if (kv[k] == T) {
+                keep = eq_rank < kr;
+                ++eq_rank;
+            }
+        }
+        keep_mask |= keep ? (1u << k) : 0u;
+        my_keep += keep ? 1u : 0u;
+    }
+    uint32_t out = base + block_exclusive_scan(my_keep, sh);
+    const int jbase = a.n_sink + lo + tid * kPerThread;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (keep_mask & (1u << k)) row[out++] = jbase + k;
+}
+
+__global__ void __launch_bounds__(kThreads) sink_mask_kernel(MaskArgs a) {
+    __shared__ float s_log_p0[1024];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    for (int i = tid; i < a.Hq; i += kThreads) {
+        const int64_t u = (int64_t)b * a.Hq + i;
+        s_log_p0[i] = a.logits[u * a.logit_stride] - a.lse[u];
+    }
+    __syncthreads();
+    for (int i = tid; i < a.Hq; i += kThreads) {
+        const float x = s_log_p0[i];
+        int rank = 0;
+        for (int j = 0; j < a.Hq; ++j) {
+            const float y = s_log_p0[j];
+            rank += (y > x || (y == x && j < i)) ? 1 : 0;
+        }
+        a.head_mask[(int64_t)b * a.Hq + i] = rank < a.n_mask ? 1 : 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_select(const SelArgs& a, hipStream_t s) {
+    const dim3 blk(kThreads);
+    const dim3 g_head(a.nchunk, a.Hq, a.B);
+    const dim3 g_group(a.nchunk, a.Hkv, a.B);
+    const dim3 g_unit(a.Hkv, a.B);
+    hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
+    hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
+    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a, 0);
+    hipLaunchKernelGGL(radix_hist_kernel, g_group, blk, 0, s, a, 1);
+    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a, 1);
+    hipLaunchKernelGGL(radix_hist_kernel, g_group, blk, 0, s, a, 2);
+    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a, 2);
+    hipLaunchKernelGGL(count_kernel, g_group, blk, 0, s, a);
+    hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_sink_mask(const MaskArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(sink_mask_kernel, dim3(a.B), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace sfi

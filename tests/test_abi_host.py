@@ -1,0 +1,138 @@
+"""Host-only checks of libsfi.so: it loads, exports every function include/sfi.h declares,
+and rejects bad arguments with the documented status before any GPU work is queued.
+No test here needs a GPU (no call below passes validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_kv_attention_dense_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # an aligned address that host code never dereferences
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B._LIB_PATH):
+        from sparse_kv_attention_dense_amd import build
+        build.build()
+    return B.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "sfi.h")).read()
+    return sorted(set(re.findall(r"\b(sfi_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = _declared()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _desc(**kw):
+    d = B.sfi_kv_desc()
+    d.batch, d.num_q_heads, d.num_kv_heads, d.head_dim = 2, 32, 8, 128
+    d.dtype = B.SFI_BF16
+    d.k = d.v = FAKE
+    d.n_cap = 4096
+    d.block_table = None
+    d.block_size = 0
+    d.max_blocks = 0
+    d.len = FAKE
+    d.max_len = 4000
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def _dense(L, d, ws_bytes=0, q=FAKE, out=FAKE, logits=FAKE, stride=4000):
+    return L.sfi_dense_decode(ctypes.byref(d) if d is not None else None, q, out, FAKE, logits,
+                              stride, FAKE if ws_bytes else None, ws_bytes, None)
+
+
+def test_descriptor_validation(L):
+    big = 1 << 40
+    assert _dense(L, None, big) == B.SFI_E_INVALID
+    assert _dense(L, _desc(num_q_heads=30), big) == B.SFI_E_INVALID          # G not an integer
+    assert _dense(L, _desc(num_q_heads=8 * 17), big) == B.SFI_E_UNSUPPORTED  # G = 17
+    assert _dense(L, _desc(head_dim=96), big) == B.SFI_E_UNSUPPORTED
+    assert _dense(L, _desc(dtype=7), big) == B.SFI_E_UNSUPPORTED
+    assert _dense(L, _desc(k=None), big) == B.SFI_E_INVALID
+    assert _dense(L, _desc(k=FAKE + 4), big) == B.SFI_E_INVALID               # misaligned
+    assert _dense(L, _desc(len=None), big) == B.SFI_E_INVALID
+    assert _dense(L, _desc(n_cap=100), big) == B.SFI_E_INVALID                # max_len > n_cap
+    assert _dense(L, _desc(block_table=FAKE, block_size=12, max_blocks=400), big) == B.SFI_E_INVALID
+    assert _dense(L, _desc(block_table=FAKE, block_size=16, max_blocks=10), big) == B.SFI_E_INVALID
+    assert _dense(L, _desc(), big, q=None) == B.SFI_E_INVALID
+    assert _dense(L, _desc(), big, stride=3999) == B.SFI_E_INVALID            # stride < max_len
+    assert _dense(L, _desc(), big, stride=4002) == B.SFI_E_INVALID            # stride % 4
+    assert _dense(L, _desc(), 0) == B.SFI_E_WORKSPACE
+
+
+def test_workspace_size_is_checked(L):
+    d = _desc()
+    need = L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_DENSE, 0, 0)
+    assert need > 0
+    assert _dense(L, d, need - 1) == B.SFI_E_WORKSPACE
+    # misaligned workspace
+    rc = L.sfi_dense_decode(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, 4000, FAKE + 64, need, None)
+    assert rc == B.SFI_E_WORKSPACE
+    sp = L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 4 + 2048, 256)
+    assert sp > 0
+    rc = L.sfi_sparse_decode(ctypes.byref(d), FAKE, FAKE, 2052, FAKE, 256, None, FAKE, FAKE,
+                             FAKE, sp - 256, None)
+    assert rc == B.SFI_E_WORKSPACE
+    assert L.sfi_workspace_bytes(ctypes.byref(d), 9, 0, 0) == 0
+    assert L.sfi_workspace_bytes(None, B.SFI_OP_DENSE, 0, 0) == 0
+
+
+def test_select_and_mask_validation(L):
+    d = _desc(k=None, v=None)
+    ws = L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SELECT, 0, 0)
+    assert ws > 0
+    sel = lambda **k: L.sfi_select(ctypes.byref(d), k.get("logits", FAKE), k.get("stride", 4000),
+                                   k.get("ns", 4), k.get("nr", 256), k.get("ks", 2048),
+                                   FAKE, k.get("istride", 2052), FAKE,
+                                   FAKE, k.get("ws", ws - 1), None)
+    assert sel() == B.SFI_E_WORKSPACE
+    assert sel(istride=2051, ws=ws) == B.SFI_E_INVALID       # idx_stride < n_sink + k_sel
+    assert sel(ks=-1, ws=ws) == B.SFI_E_INVALID
+    assert sel(logits=None, ws=ws) == B.SFI_E_INVALID
+    assert sel(stride=10, ws=ws) == B.SFI_E_INVALID
+    mask = lambda frac, dd=d: L.sfi_sink_bypass_mask(ctypes.byref(dd), FAKE, 4000, FAKE,
+                                                     ctypes.c_float(frac), None, None)
+    assert mask(0.25) == B.SFI_E_INVALID                      # head_mask NULL
+    ok_ptr = lambda frac: L.sfi_sink_bypass_mask(ctypes.byref(d), FAKE, 4000, FAKE,
+                                                 ctypes.c_float(frac), FAKE + 1, None)
+    assert ok_ptr(1.5) == B.SFI_E_INVALID
+    assert ok_ptr(float("nan")) == B.SFI_E_INVALID
+    assert ok_ptr(-0.1) == B.SFI_E_INVALID
+
+
+def test_sparse_validation(L):
+    d = _desc()
+    ws = L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 2052, 256)
+    sp = lambda **k: L.sfi_sparse_decode(ctypes.byref(d), FAKE, k.get("idx", FAKE),
+                                         k.get("istride", 2052), FAKE, k.get("nr", 256), None,
+                                         FAKE, None, FAKE, ws, None)
+    assert sp(idx=None) == B.SFI_E_INVALID
+    assert sp(istride=0) == B.SFI_E_INVALID
+    assert sp(nr=-1) == B.SFI_E_INVALID
+    # far more slots than one launch plans for
+    assert L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 1 << 30, 0) == 0
+
+
+def test_status_strings(L):
+    for s in (B.SFI_OK, B.SFI_E_INVALID, B.SFI_E_UNSUPPORTED, B.SFI_E_WORKSPACE, B.SFI_E_HIP):
+        assert B.sfi_status_string(s).startswith("SFI_")
+    assert "unknown" in B.sfi_status_string(42)
+
+
+def test_workspace_grows_with_context(L):
+    small = L.sfi_workspace_bytes(ctypes.byref(_desc(max_len=1000, n_cap=1000)), B.SFI_OP_SELECT, 0, 0)
+    large = L.sfi_workspace_bytes(ctypes.byref(_desc(max_len=100000, n_cap=100000)), B.SFI_OP_SELECT, 0, 0)
+    assert large > small > 0

@@ -1,0 +1,117 @@
+"""Dense slow step on the GPU against the fp64 oracle (out, lse, fp32 logits)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_attention_dense_amd import synth
+from sparse_kv_attention_dense_amd import binding as B
+
+from gpu_util import (DEV, assert_close_out, assert_close_rel, assert_logits, gpu_dense,
+                      oracle_cache, say, tolerances, desc_for, workspace_for, round4)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+# Reduced contexts that keep each workload's structure, span several tiles and splits,
+# and end in a ragged tail; the oracle finishes each in about a second.
+SMALL = {
+    "tiny_2k_f32": W["tiny_2k_f32"],
+    "gqa4_32k": W["gqa4_32k"].scaled(5003),
+    "sink_128k_b4": W["sink_128k_b4"].scaled(9001, B=2),
+    "ragged_paged_b16": W["ragged_paged_b16"].scaled(6000, B=4, len_lo=2500),
+    "gqa8_512k": W["gqa8_512k"].scaled(12007),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_dense_matches_oracle(orc, name):
+    wl = SMALL[name]
+    say(f"[dense] {wl.name} B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} d={wl.d} {wl.dtype} n0={wl.n0}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    q = synth.make_query(wl, 0, 0, device=DEV, u=lay.u)
+    out, lse, logits, _ = gpu_dense(lay, q)
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lay.len0_host), q)
+    tol = tolerances(wl)
+    assert_close_out(out.cpu().numpy(), eo, tol["out"])
+    assert_close_rel(lse.cpu().numpy(), el, tol["rel"], "lse")
+    assert_logits(logits, ez, lay.len0_host, tol["rel"])
+    if wl.sink:
+        p0 = np.exp(ez[:, :, 0] - el)
+        say(f"    realised token-0 mass: mean {p0.mean():.3f}, range {p0.min():.3f}-{p0.max():.3f}")
+
+
+@pytest.mark.parametrize("dtype,d,G", [("bf16", 64, 1), ("bf16", 128, 16), ("f32", 128, 2),
+                                       ("bf16", 128, 3)])
+def test_dense_head_shapes(orc, dtype, d, G):
+    wl = synth.Workload(f"shape_{dtype}_{d}_{G}", 7100 + d + G, 2, 2 * G, 2, d, dtype, 1500,
+                        4, 64, 128, 2)
+    say(f"[dense] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[1500, 777])
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    out, lse, logits, _ = gpu_dense(lay, q)
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lay.len0_host), q)
+    tol = tolerances(wl)
+    assert_close_out(out.cpu().numpy(), eo, tol["out"])
+    assert_close_rel(lse.cpu().numpy(), el, tol["rel"], "lse")
+    assert_logits(logits, ez, lay.len0_host, tol["rel"])
+
+
+def test_dense_edge_lengths(orc):
+    """Lengths 0, 1, a tile minus one, a split plus one; logits past len stay untouched."""
+    wl = synth.Workload("edges", 7300, 5, 8, 2, 128, "bf16", 4200, 4, 16, 32, 1)
+    lens = [0, 1, 31, 129, 4200]
+    lay = synth.make_layer(wl, 0, device=DEV, lens=lens)
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    out, lse, logits, stride = gpu_dense(lay, q)
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lens), q)
+    assert (out[0] == 0).all() and torch.isneginf(lse[0]).all()
+    assert_close_out(out.cpu().numpy(), eo, 1e-2)
+    assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
+    assert_logits(logits, ez, lens, 1e-3)
+    lg = logits.cpu()
+    for b, n in enumerate(lens):
+        assert torch.isnan(lg[b, :, n:]).all(), "logits written past len"
+
+
+def test_dense_without_logits_matches(orc):
+    wl = SMALL["gqa4_32k"]
+    lay = synth.make_layer(wl, 1, device=DEV)
+    q = synth.make_query(wl, 1, 0, device=DEV)
+    o1, l1, _, _ = gpu_dense(lay, q, logits=True)
+    o2, l2, _, _ = gpu_dense(lay, q, logits=False)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_dense_deterministic():
+    wl = SMALL["sink_128k_b4"]
+    lay = synth.make_layer(wl, 2, device=DEV)
+    q = synth.make_query(wl, 2, 0, device=DEV, u=lay.u)
+    a = gpu_dense(lay, q)
+    b = gpu_dense(lay, q)
+    for x, y in zip(a[:3], b[:3]):
+        assert torch.equal(x.nan_to_num(7.0), y.nan_to_num(7.0))
+
+
+@pytest.mark.parametrize("name,samples", [("sink_128k_b4", [(0, 0), (3, 31), (1, 13)]),
+                                          ("gqa8_512k", [(0, 0), (0, 63), (0, 22)])])
+def test_dense_full_size_sampled(orc, name, samples):
+    """Full-size workloads in the benchmark's launch configuration; the oracle recomputes
+    sampled (batch, query head) rows one by one."""
+    wl = W[name]
+    say(f"[dense full] {wl.name} B={wl.B} n0={wl.n0}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    q = synth.make_query(wl, 0, 0, device=DEV, u=lay.u)
+    out, lse, logits, _ = gpu_dense(lay, q)
+    for b, i in samples:
+        h = i // wl.G
+        N = lay.len0_host[b]
+        K1 = lay.k[b:b + 1, h:h + 1, :N].contiguous()
+        V1 = lay.v[b:b + 1, h:h + 1, :N].contiguous()
+        c = orc.Cache(K1, V1, torch.tensor([N], dtype=torch.int32), 1)
+        eo, el, ez = orc.dense(c, q[b:b + 1, i:i + 1].contiguous())
+        say(f"  sample b={b} i={i}")
+        assert_close_out(out[b, i].cpu().numpy()[None, None], eo, 1e-2)
+        assert_close_rel(lse[b, i:i + 1].cpu().numpy()[None], el, 1e-3, "lse")
+        assert_logits(logits[b:b + 1, i:i + 1], ez, [N], 1e-3)
+    del lay, out, logits
+    torch.cuda.empty_cache()

@@ -1,0 +1,105 @@
+"""Selector on the GPU against the fp64 oracle, fed the same fp32 logits buffer."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_attention_dense_amd import synth
+
+from gpu_util import DEV, compare_index_sets, gpu_select, round4, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(orc, wl, lens, z, exact, n_sink=None, n_recent=None, k_sel=None, idx_stride=None):
+    n_sink = wl.n_sink if n_sink is None else n_sink
+    n_recent = wl.n_recent if n_recent is None else n_recent
+    k_sel = wl.k_sel if k_sel is None else k_sel
+    idx_stride = idx_stride or (n_sink + k_sel)
+    stride = z.shape[-1]
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    zd = z.to(DEV)
+    idx, n_idx = gpu_select(lens_dev, max(lens), wl, zd, stride, n_sink, n_recent, k_sel, idx_stride)
+    eidx, en, f = orc.select(lens, wl.Hq, wl.Hkv, z, n_sink, n_recent, k_sel, idx_stride,
+                             want_f=True)
+    swaps = compare_index_sets(idx, n_idx, eidx, en, f, lens, n_sink, n_recent, k_sel, exact)
+    return idx, n_idx, swaps
+
+
+def _planted(wl, lens, seed, noise=40.0, n_sink=None, n_recent=None):
+    n_sink = wl.n_sink if n_sink is None else n_sink
+    n_recent = wl.n_recent if n_recent is None else n_recent
+    z, ranks = synth.planted_logits(len(lens), wl.Hq, wl.Hkv, lens, n_sink, n_recent,
+                                    round4(max(lens)), seed, noise_sink=noise)
+    return z, ranks
+
+
+W = synth.WORKLOADS
+
+
+@pytest.mark.parametrize("name,lens", [("gqa4_32k", [5003]), ("sink_128k_b4", [9001, 12345]),
+                                       ("ragged_paged_b16", [2500, 3333, 4097, 8200]),
+                                       ("gqa8_512k", [40000]), ("tiny_2k_f32", [2048])])
+def test_select_planted_is_exact(orc, name, lens):
+    wl = W[name]
+    say(f"[select planted] {name} lens={lens}")
+    z, ranks = _planted(wl, lens, seed=sum(map(ord, name)))
+    idx, n_idx, _ = _run(orc, wl, lens, z, exact=True)
+    # and the planted expectation itself
+    ig = idx.cpu().numpy()
+    for b, N in enumerate(lens):
+        for h in range(wl.Hkv):
+            keep = sorted((torch.nonzero(ranks[b][h] < wl.k_sel).flatten() + wl.n_sink).tolist())
+            assert ig[b, h, :n_idx[b, h]].tolist() == list(range(min(wl.n_sink, N))) + keep
+
+
+@pytest.mark.parametrize("name", ["sink_128k_b4", "gqa8_512k"])
+def test_select_planted_full_size(orc, name):
+    wl = W[name]
+    lens = [wl.n0] * wl.B
+    say(f"[select planted full] {name} B={wl.B} N={wl.n0} k={wl.k_sel}")
+    z, _ = _planted(wl, lens, seed=17)
+    _run(orc, wl, lens, z, exact=True)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_select_random_logits_band(orc, seed):
+    wl = W["ragged_paged_b16"]
+    lens = [8192, 9000, 20000, 32768]
+    g = torch.Generator().manual_seed(seed)
+    z = (torch.randn((4, wl.Hq, 32768), generator=g) * 2.0)
+    _, _, swaps = _run(orc, wl, lens, z, exact=False)
+    say(f"    tie-band swaps: {swaps}")
+
+
+def test_select_edges(orc):
+    wl = synth.Workload("sel_edges", 1, 6, 8, 2, 128, "bf16", 5000, 4, 64, 100, 1)
+    g = torch.Generator().manual_seed(3)
+    # |J| = 0 (N - n_r <= n_s), N < n_s, |J| < k_sel (take all), |J| = k_sel, chunk edges
+    lens = [60, 2, 150, 168, 4096 + 68, 8192 + 69]
+    z = torch.randn((6, 8, round4(max(lens))), generator=g)
+    _run(orc, wl, lens, z, exact=True)
+    # k_sel = 0 keeps only sinks; n_sink = 0 keeps no sinks
+    _run(orc, wl, lens, z, exact=True, k_sel=0, idx_stride=8)
+    _run(orc, wl, lens, z, exact=True, n_sink=0, k_sel=37)
+    # many exact ties: quantised logits, lowest positions win
+    zq = torch.randint(-2, 2, z.shape, generator=g).float()
+    _run(orc, wl, lens, zq, exact=True)
+
+
+@pytest.mark.parametrize("G", [1, 16])
+def test_select_group_sizes(orc, G):
+    wl = synth.Workload(f"sel_G{G}", 1, 2, 2 * G, 2, 128, "bf16", 20000, 4, 256, 700, 1)
+    lens = [20000, 15000]
+    z, _ = _planted(wl, lens, seed=G)
+    _run(orc, wl, lens, z, exact=True)
+
+
+def test_select_deterministic():
+    wl = W["sink_128k_b4"]
+    lens = [30000, 20000]
+    g = torch.Generator().manual_seed(9)
+    z = torch.randn((2, wl.Hq, 30000), generator=g).to(DEV)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    a = gpu_select(lens_dev, 30000, wl, z, 30000)
+    b = gpu_select(lens_dev, 30000, wl, z, 30000)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
