@@ -14,18 +14,17 @@
  *
  * Conventions shared by every call
  *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
- *     never allocates, keeps no pointer after a call returns, and holds no global state
- *     except a per-device cache of the compute-unit count.
+ *     never allocates, keeps no pointer after a call returns, and holds no global state.
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never synchronise the
  *     host.  A returned SFI_OK means the arguments passed host-side validation and the
  *     launches were queued; device data (lengths, block tables, indices) is trusted.
  *   - Scores use scale 1/sqrt(head_dim) and query head i reads KV head i / G with
  *     G = num_q_heads / num_kv_heads (the grouped-query map of SkipKV Sec. 4.1, token
  *     importance score).  Accumulation is fp32; outputs, logits and lse are fp32.
- *   - Workspace: `ws` must be 256-byte aligned, at least sfi_workspace_bytes() long, and
- *     zero-filled before its first use.  Every call that completes leaves the counters it
- *     uses at zero again, so one zero fill is enough.  Calls that share a workspace must be
- *     ordered (same stream); concurrent calls need separate workspaces.
+ *   - Workspace: `ws` (device) must be 256-byte aligned and at least sfi_workspace_bytes()
+ *     long; its contents need no initialisation and are scratch between calls.  One buffer
+ *     sized for the largest op can serve every call on a descriptor.  Calls that share a
+ *     workspace must be ordered (same stream); concurrent calls need separate workspaces.
  *   - The functions are thread-safe.
  */
 #ifndef SFI_H
@@ -94,7 +93,7 @@ typedef struct sfi_kv_desc {
  *       given, logit_stride >= max_len, logit_stride % 4 == 0 and logits 16-byte aligned.
  *       Entries j >= len[b] are not written.
  * q (device) [B][Hq][d] in kv->dtype, 16-byte aligned.  len[b] == 0 gives out = 0, lse = -inf.
- * One kernel launch: split-K over the sequence with an in-kernel combine. */
+ * Two kernel launches: split-K partials over the sequence, then their log-sum-exp merge. */
 sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
                             float* logits, int64_t logit_stride,
                             void* ws, size_t ws_bytes, hipStream_t stream);
@@ -137,7 +136,7 @@ sfi_status sfi_sink_bypass_mask(const sfi_kv_desc* kv, const float* logits, int6
  * sfi_select); entries >= r0 or < 0 are skipped, so the recent run is never counted twice.
  * n_idx (device) int32 [B][Hkv], clamped to idx_stride.  head_mask (device) uint8 [B][Hq] or
  * NULL.  out (device) fp32 [B][Hq][d]; lse (device) fp32 [B][Hq] or NULL.
- * One kernel launch: split over the index set with an in-kernel combine. */
+ * Two kernel launches: partials over splits of the index set, then their merge. */
 sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
                              const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
                              int32_t n_recent, const uint8_t* head_mask,

@@ -173,7 +173,7 @@ def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: in
 
 
 def workspace(desc: KVDesc, idx_stride: int = 1, n_recent: int = 0, device="cuda"):
-    """A zero-filled workspace large enough for every op on this descriptor (plumbing:
+    """A workspace large enough for every op on this descriptor (plumbing:
     torch allocates it once; the library itself never allocates)."""
     n = max(sfi_workspace_bytes(desc, op, idx_stride, n_recent)
             for op in (SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE))

@@ -14,20 +14,14 @@ namespace {
 using namespace sfi;
 
 // Workgroups a launch aims for: four per compute unit of a 256-CU MI355X, enough to fill
-// the chip with two resident workgroups per CU and leave a short tail.
+// the chip with two resident workgroups per CU and leave a short tail.  The plan depends
+// only on the descriptor, so workspace sizes are the same on every device.
 constexpr int64_t kTargetWorkgroups = 1024;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
-
-// Ticket counters sit at the start of every op's workspace so that one buffer, sized for
-// the largest op, can serve all calls: only the attention kernels touch this region and
-// they leave it zeroed.
-size_t ticket_bytes(const sfi_kv_desc& kv) {
-    return align_up((size_t)kv.batch * kv.num_kv_heads * (kGroupSplits + 1) * sizeof(uint32_t));
-}
 
 sfi_status check_desc(const sfi_kv_desc* kv, bool need_cache) {
     if (!kv) return SFI_E_INVALID;
@@ -53,8 +47,8 @@ sfi_status check_desc(const sfi_kv_desc* kv, bool need_cache) {
 }
 
 struct AttnPlan {
-    int split_len = 0, nsplit = 0, ngroups = 0, rec = 0;
-    size_t off_part = 0, off_part1 = 0, bytes = 0;
+    int split_len = 0, nsplit = 0, rec = 0;
+    size_t bytes = 0;
 };
 
 sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride, int64_t n_recent,
@@ -75,14 +69,8 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
     }
     p->split_len = (int)split;
     p->nsplit = (int)nsplit;
-    p->ngroups = (int)ceil_div(nsplit, kGroupSplits);
     p->rec = (int)(ceil_div(G * (kv.head_dim + 2), 4) * 4);
-    size_t off = ticket_bytes(kv);
-    p->off_part = off;
-    off += align_up((size_t)units * nsplit * p->rec * sizeof(float));
-    p->off_part1 = off;
-    if (p->ngroups > 1) off += align_up((size_t)units * p->ngroups * p->rec * sizeof(float));
-    p->bytes = off;
+    p->bytes = align_up((size_t)units * nsplit * p->rec * sizeof(float));
     return SFI_OK;
 }
 
@@ -95,7 +83,7 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     const size_t B = kv.batch, Hq = kv.num_q_heads, Hkv = kv.num_kv_heads;
     p->nchunk = (int)(kv.max_len > 0 ? ceil_div(kv.max_len, kSelChunk) : 1);
     const size_t nc = p->nchunk;
-    size_t off = ticket_bytes(kv);
+    size_t off = 0;
     p->off_lse = off;    off += align_up(B * Hq * nc * sizeof(float2));
     p->off_keys = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
     p->off_hist = off;   off += align_up(B * Hkv * 3 * kRadixBins * sizeof(uint32_t));
@@ -127,16 +115,11 @@ void fill_cache_args(const sfi_kv_desc& kv, AttnArgs* a) {
     a->scale_log2 = (float)(1.4426950408889634 / sqrt((double)kv.head_dim));
 }
 
-void fill_plan_args(const AttnPlan& p, const sfi_kv_desc& kv, void* ws, AttnArgs* a) {
-    unsigned char* base = (unsigned char*)ws;
+void fill_plan_args(const AttnPlan& p, void* ws, AttnArgs* a) {
     a->split_len = p.split_len;
     a->nsplit = p.nsplit;
-    a->ngroups = p.ngroups;
     a->rec_floats = p.rec;
-    a->tick1 = (uint32_t*)base;
-    a->tick2 = a->tick1 + (size_t)kv.batch * kv.num_kv_heads * kGroupSplits;
-    a->part = (float*)(base + p.off_part);
-    a->part1 = (float*)(base + p.off_part1);
+    a->part = (float*)ws;
 }
 
 }  // namespace
@@ -156,7 +139,7 @@ SFI_EXPORT sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, flo
     if (st != SFI_OK) return st;
     AttnArgs a;
     fill_cache_args(*kv, &a);
-    fill_plan_args(plan, *kv, ws, &a);
+    fill_plan_args(plan, ws, &a);
     a.q = q;
     a.out = out;
     a.lse = lse;
@@ -183,7 +166,7 @@ SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
     if (st != SFI_OK) return st;
     AttnArgs a;
     fill_cache_args(*kv, &a);
-    fill_plan_args(plan, *kv, ws, &a);
+    fill_plan_args(plan, ws, &a);
     a.q = q;
     a.out = out;
     a.lse = lse;

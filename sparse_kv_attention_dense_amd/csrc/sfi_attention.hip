@@ -1,11 +1,11 @@
 // sfi_attention.hip -- split-K GQA decode attention for gfx950 (dense slow step and sparse
 // fast step of Slow-Fast Inference).
 //
-// One workgroup (4 wavefronts) owns one (batch b, KV head h, split s): a contiguous range of
-// "slots".  A slot is a key position: in the dense step slot == position; in the sparse step
-// slot k < n_idx is idx[k] and the remaining slots walk the recent window [r0, len).  Each
-// wavefront takes 32-slot tiles round-robin and keeps an online softmax (m, l, acc) for the
-// G query heads of the group:
+// attention_kernel: one workgroup (4 wavefronts) owns one (batch b, KV head h, split s): a
+// contiguous range of "slots".  A slot is a key position: in the dense step slot ==
+// position; in the sparse step slot k < n_idx is idx[k] and the remaining slots walk the
+// recent window [r0, len).  Each wavefront takes 32-slot tiles round-robin and keeps an
+// online softmax (m, l, acc) for the G query heads of the group:
 //   - S^T = K_tile * Q^T on MFMA (v_mfma_f32_16x16x32_bf16, or 16x16x4 f32): the 16 rows of
 //     the A operand are 16 key rows, read straight from HBM as 16-byte pieces, and the 16
 //     columns are the (zero-padded) query heads, so each K row is read once for the group
@@ -15,11 +15,14 @@
 //   - O^T += V_tile^T * P^T on MFMA; bf16 V rows are staged through LDS and read back
 //     transposed, and P is split into a bf16 high part and a bf16 residual so the product
 //     keeps about 16 bits of the fp32 weight.
-// The (m, l, acc) partials of the splits are merged inside the same launch: the last
-// workgroup to finish a group of 16 splits merges them (an atomic ticket per group), and
-// the last group merger merges the groups.  Merging uses the log-sum-exp rule
-//   M = max_s m_s,  out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s
-// with m kept in log2 units.
+// Each workgroup writes one partial record (acc, m, l) per query head of its group.
+//
+// combine_kernel: one workgroup per query head merges the records of all splits with the
+// log-sum-exp rule  M = max_s m_s,  out = sum_s 2^(m_s-M) acc_s / sum_s 2^(m_s-M) l_s
+// (m kept in log2 units) and writes out and lse; bypassed heads get the zero surrogate.
+// The merge is a second launch on the same stream rather than an in-kernel ticket: the
+// kernel boundary makes the partials visible across the chip's XCDs without per-workgroup
+// L2 write-back and invalidate fences.
 #include <type_traits>
 
 #include "sfi_internal.h"
@@ -47,9 +50,7 @@ struct Cfg {
     static constexpr int kVRow = D * 2 + 16;                       // staged bf16 row, bytes
     static constexpr int kVStage = BF ? kWaves * kTile * kVRow : 0;
     static constexpr int kRed = kWaves * kMaxG * (D + 2) * 4;      // cross-wave merge
-    static constexpr int kMerge = (2 * kGroupSplits * kMaxG + 2 * kMaxG) * 4;
-    static constexpr int kRaw0 = kVStage > kRed ? kVStage : kRed;
-    static constexpr int kRaw = kRaw0 > kMerge ? kRaw0 : kMerge;
+    static constexpr int kRaw = kVStage > kRed ? kVStage : kRed;
     static constexpr bool kTab = PAGED || SPARSE;
     static constexpr int kNQ = BF ? D / 32 : D / 16;               // Q / K fragments per row
     static constexpr int kNV = BF ? D / 16 : 2 * 4 * (D / 16);     // V registers per tile
@@ -66,77 +67,6 @@ struct TileRegs {
     typename C::VR v[C::kNV];
 };
 
-// Merges `count` partial records (stride a.rec_floats) for the G heads of (b, h).
-// dst != nullptr: writes one merged record (acc unnormalised, with its m and l).
-// dst == nullptr: writes out = acc / l and lse, zero surrogate for bypassed heads.
-template <int D, bool SPARSE>
-__device__ void merge_records(const AttnArgs& a, const float* src, int count, float* dst,
-                              int b, int h, float* scratch) {
-    const int tid = threadIdx.x;
-    const int G = a.G;
-    const int rec = a.rec_floats;
-    float* lm = scratch;                              // [count][G]
-    float* lw = lm + kGroupSplits * kMaxG;            // [count][G]
-    float* sM = lw + kGroupSplits * kMaxG;            // [G]
-    float* sL = sM + kMaxG;                           // [G]
-    for (int e = tid; e < count * G; e += kThreads) {
-        const int s = e / G, g = e - s * G;
-        lm[e] = src[(int64_t)s * rec + G * D + 2 * g];
-        lw[e] = src[(int64_t)s * rec + G * D + 2 * g + 1];
-    }
-    __syncthreads();
-    if (tid < G) {
-        float M = -INFINITY;
-        for (int s = 0; s < count; ++s) M = fmaxf(M, lm[s * G + tid]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float L = 0.f;
-        for (int s = 0; s < count; ++s) L += exp2_fast(lm[s * G + tid] - Mu) * lw[s * G + tid];
-        sM[tid] = M;
-        sL[tid] = L;
-    }
-    __syncthreads();
-    for (int e = tid; e < count * G; e += kThreads) {
-        const int g = e % G;
-        const float Mu = (sM[g] == -INFINITY) ? 0.f : sM[g];
-        lw[e] = exp2_fast(lm[e] - Mu);
-    }
-    __syncthreads();
-    constexpr int Q4 = D / 4;
-    for (int o = tid; o < G * Q4; o += kThreads) {
-        const int g = o / Q4;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 16
-        for (int s = 0; s < count; ++s) {
-            const f32x4 v = *(const f32x4*)(src + (int64_t)s * rec + 4 * o);
-            acc += lw[s * G + g] * v;
-        }
-        if (dst) {
-            *(f32x4*)(dst + 4 * o) = acc;
-        } else {
-            const float L = sL[g];
-            bool zero = !(L > 0.f);
-            if constexpr (SPARSE) {
-                if (a.head_mask) zero |= a.head_mask[b * a.Hq + h * G + g] != 0;
-            }
-            const f32x4 r = zero ? f32x4{0.f, 0.f, 0.f, 0.f} : acc * (1.f / L);
-            *(f32x4*)(a.out + ((int64_t)b * a.Hq + h * G + g) * D + 4 * (o - g * Q4)) = r;
-        }
-    }
-    if (tid < G) {
-        if (dst) {
-            dst[G * D + 2 * tid] = sM[tid];
-            dst[G * D + 2 * tid + 1] = sL[tid];
-        } else if (a.lse) {
-            const float L = sL[tid];
-            bool zero = !(L > 0.f);
-            if constexpr (SPARSE) {
-                if (a.head_mask) zero |= a.head_mask[b * a.Hq + h * G + tid] != 0;
-            }
-            a.lse[b * a.Hq + h * G + tid] = zero ? -INFINITY : (sM[tid] + log2f(L)) * kLn2;
-        }
-    }
-}
-
 template <bool BF, int D, bool PAGED, bool SPARSE>
 __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_kernel(AttnArgs a) {
     using C = Cfg<BF, D, PAGED, SPARSE>;
@@ -144,7 +74,6 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     __shared__ __attribute__((aligned(16))) unsigned char raw[C::kRaw];
     __shared__ uint32_t tab_row[C::kTab ? kTabMax : 1];
     __shared__ uint8_t tab_ok[SPARSE ? kTabMax : 1];
-    __shared__ int s_flag;
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -386,20 +315,25 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     };
 
     // ---- main loop: wavefront w takes tiles w, w+4, ...; loads run one tile ahead ----------
+    // The next tile's loads are issued unconditionally (past the end the wavefront re-reads
+    // its current tile, which hits in cache), so the number of loads younger than the
+    // current tile's is the same on every path and the wait before the math only covers
+    // the current tile.
     const int ntiles = (nslots + kTile - 1) / kTile;
-    {
+    if (w < ntiles) {
         Regs ra, rb;
         int t = w;
-        if (t < ntiles) issue(ra, t);
-        while (t < ntiles) {
+        issue(ra, t);
+        for (;;) {
             int tn = t + kWaves;
-            if (tn < ntiles) issue(rb, tn);
+            issue(rb, tn < ntiles ? tn : t);
             compute(ra, t);
+            if (tn >= ntiles) break;
             t = tn;
-            if (t >= ntiles) break;
             tn = t + kWaves;
-            if (tn < ntiles) issue(ra, tn);
+            issue(ra, tn < ntiles ? tn : t);
             compute(rb, t);
+            if (tn >= ntiles) break;
             t = tn;
         }
     }
@@ -450,45 +384,68 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         }
     }
 
-    // ---- in-launch combine: last of each group of 16 splits, then last group -------------
-    __threadfence();
+}
+
+// Merges the nsplit partial records of one query head (blockIdx.x) of batch blockIdx.y.
+template <int D, bool SPARSE>
+__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
+    __shared__ float s_w[kMaxSplits];
+    __shared__ float s_red[kThreads];
+    __shared__ float s_acc[kThreads];
+    const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int G = a.G, h = i / G, g = i - h * G;
+    const int S = a.nsplit, rec = a.rec_floats;
+    const float* base = a.part + (int64_t)(b * a.Hkv + h) * S * rec;
+    // global max of the split maxima
+    float M = -INFINITY;
+    for (int s = tid; s < S; s += kThreads) M = fmaxf(M, base[(int64_t)s * rec + G * D + 2 * g]);
+    s_red[tid] = M;
     __syncthreads();
-    const int grp = split / kGroupSplits;
-    const int gcount = min(kGroupSplits, a.nsplit - grp * kGroupSplits);
-    if (tid == 0) {
-        const uint32_t old = atomicAdd(&a.tick1[unit * kGroupSplits + grp], 1u);
-        s_flag = old == (uint32_t)(gcount - 1);
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
+        __syncthreads();
     }
+    M = s_red[0];
     __syncthreads();
-    if (!s_flag) return;
-    if (tid == 0) atomicExch(&a.tick1[unit * kGroupSplits + grp], 0u);
-    __threadfence();
-    float* scratch = (float*)raw;
-    const float* gsrc = a.part + ((int64_t)unit * a.nsplit + grp * kGroupSplits) * a.rec_floats;
-    if (a.ngroups == 1) {
-        merge_records<D, SPARSE>(a, gsrc, gcount, nullptr, b, h, scratch);
-        return;
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    // split weights 2^(m_s - M) and the merged normaliser
+    float L = 0.f;
+    for (int s = tid; s < S; s += kThreads) {
+        const float w = exp2_fast(base[(int64_t)s * rec + G * D + 2 * g] - Mu);
+        s_w[s] = w;
+        L += w * base[(int64_t)s * rec + G * D + 2 * g + 1];
     }
-    float* gdst = a.part1 + ((int64_t)unit * a.ngroups + grp) * a.rec_floats;
-    merge_records<D, SPARSE>(a, gsrc, gcount, gdst, b, h, scratch);
-    __threadfence();
+    s_red[tid] = L;
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = atomicAdd(&a.tick2[unit], 1u);
-        s_flag = old == (uint32_t)(a.ngroups - 1);
+    for (int o = kThreads / 2; o > 0; o >>= 1) {
+        if (tid < o) s_red[tid] += s_red[tid + o];
+        __syncthreads();
     }
+    L = s_red[0];
+    // weighted sum of the accumulators: thread -> (dim, phase); phases share the splits
+    constexpr int R = kThreads / D;
+    const int dim = tid % D, ph = tid / D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = ph; s < S; s += R) acc += s_w[s] * base[(int64_t)s * rec + g * D + dim];
+    s_acc[tid] = acc;
     __syncthreads();
-    if (!s_flag) return;
-    if (tid == 0) atomicExch(&a.tick2[unit], 0u);
-    __threadfence();
-    merge_records<D, SPARSE>(a, a.part1 + (int64_t)unit * a.ngroups * a.rec_floats, a.ngroups,
-                             nullptr, b, h, scratch);
+    if (tid < D) {
+        for (int r = 1; r < R; ++r) acc += s_acc[tid + r * D];
+        bool zero = !(L > 0.f);
+        if constexpr (SPARSE) {
+            if (a.head_mask) zero |= a.head_mask[b * a.Hq + i] != 0;
+        }
+        a.out[((int64_t)b * a.Hq + i) * D + tid] = zero ? 0.f : acc / L;
+        if (tid == 0 && a.lse) a.lse[b * a.Hq + i] = zero ? -INFINITY : (M + log2f(L)) * kLn2;
+    }
 }
 
 template <bool BF, int D, bool PAGED, bool SPARSE>
 hipError_t launch_one(const AttnArgs& a, int B, hipStream_t stream) {
-    dim3 grid(a.nsplit, a.Hkv, B);
-    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), dim3(a.nsplit, a.Hkv, B),
+                       dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((combine_kernel<D, SPARSE>), dim3(a.Hq, B), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -15,8 +15,7 @@ constexpr int kWaves = 4;
 constexpr int kTile = 32;            // slots per wavefront iteration (two 16-row MFMA blocks)
 constexpr int kSplitQuantum = kTile * kWaves;
 constexpr int kTabMax = 4096;        // slots per workgroup when rows come from a table
-constexpr int kGroupSplits = 16;     // partials merged by one combine step
-constexpr int kMaxSplits = kGroupSplits * kGroupSplits;
+constexpr int kMaxSplits = 1024;     // partial records per (b, h) that the combine merges
 constexpr int kMaxG = 16;            // query heads per KV head (MFMA N dimension)
 
 struct AttnArgs {
@@ -35,7 +34,6 @@ struct AttnArgs {
     int64_t logit_stride;
     int32_t split_len;               // slots per workgroup, multiple of kSplitQuantum
     int32_t nsplit;                  // workgroups per (b, h)
-    int32_t ngroups;                 // ceil(nsplit / kGroupSplits)
     int32_t rec_floats;              // floats per partial record (G*(d+2) rounded to 4)
     const int32_t* idx;              // sparse only
     int32_t idx_stride;
@@ -44,10 +42,7 @@ struct AttnArgs {
     const uint8_t* head_mask;        // sparse only, may be null
     float* out;
     float* lse;                      // may be null
-    float* part;                     // [units][nsplit][rec]
-    float* part1;                    // [units][ngroups][rec]
-    uint32_t* tick1;                 // [units][kGroupSplits]
-    uint32_t* tick2;                 // [units]
+    float* part;                     // [units][nsplit][rec]: acc [G][d], then (m, l) [G]
 };
 
 hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool paged, bool sparse,

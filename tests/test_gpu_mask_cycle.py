@@ -51,8 +51,8 @@ CYCLES = {
 @pytest.mark.parametrize("name", list(CYCLES))
 def test_cycle_matches_oracle_chain(orc, name):
     """One slow step and the following fast steps, the GPU feeding itself and the oracle
-    feeding itself; the selections must agree (up to near-ties at the Top-K boundary, which
-    these random inputs do not produce) and so must every output."""
+    feeding itself; the selections must agree up to near-ties at the Top-K boundary and
+    every output must agree to the output tolerance."""
     wl = CYCLES[name]
     say(f"[cycle] {wl.name} B={wl.B} cycle={wl.cycle}")
     lay = synth.make_layer(wl, 0, device=DEV)
@@ -69,8 +69,11 @@ def test_cycle_matches_oracle_chain(orc, name):
     idx, n_idx = gpu_select(lens0, lay.max_len_at(0), wl, logits, stride, ws=ws)
     eidx, en, f = orc.select(lay.len0_host, wl.Hq, wl.Hkv, ez, wl.n_sink, wl.n_recent, wl.k_sel,
                              want_f=True)
-    compare_index_sets(idx, n_idx, eidx, en, f, lay.len0_host, wl.n_sink, wl.n_recent,
-                       wl.k_sel, exact=True)
+    # GPU and oracle select from their own logits (fp32 vs fp64), so positions whose
+    # evidence ties the k-th largest to within 1e-5 may swap; nothing else may differ
+    swaps = compare_index_sets(idx, n_idx, eidx, en, f, lay.len0_host, wl.n_sink, wl.n_recent,
+                               wl.k_sel, exact=False)
+    say(f"    selection: {swaps} near-tie swaps at the Top-K boundary")
     hm, ehm = None, None
     if wl.mask_frac > 0:
         hm = _gpu_mask(lens0, lay.max_len_at(0), wl.Hq, wl.Hkv, logits, stride, lse, wl.mask_frac)
