@@ -28,7 +28,6 @@ if ROOT not in sys.path:
 
 METRIC = "fast/slow decode-attn µs/step + achieved HBM GB/s (% of peak) at 32K–512K ctx"
 PEAK_HBM_GBS = 8000.0
-COUNTERS = os.path.join(ROOT, "profiles", "dense_sink_128k_b4_counters.json")
 ATTN_SRC = os.path.join(ROOT, "sparse_kv_attention_dense_amd", "csrc", "sfi_attention.hip")
 
 
@@ -40,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="sink_128k_b4")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the timed region, copy MIB MiB on the device a few times (a "
+                         "known-size reference for rocprofv3 byte counters)")
     return ap.parse_args()
 
 
@@ -73,21 +75,27 @@ def fast_bytes(wl, lens_t, n_idx_host, mask_host):
     return tot + wl.B * wl.Hq * wl.d * (wl.elem_bytes + 4) + wl.B * wl.Hq * 4
 
 
-def counter_traffic():
-    """HBM bytes per dense launch from the committed rocprofv3 counter summary, or None when
+def counter_traffic(workload: str):
+    """HBM bytes per dense launch from the committed rocprofv3 counter summary of this workload
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a known-size copy), or None when there is none or
     the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_counters.md")
     try:
-        with open(COUNTERS) as fh:
-            c = json.load(fh)
+        text = open(path).read()
         sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if c.get("source_sha256") != sha:
-            return None
-        return int(c["fetch_bytes_per_launch"]) + int(c["write_bytes_per_launch"])
-    except (OSError, KeyError, ValueError):
+    except OSError:
         return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch="):
+            fields = dict(kv.split("=", 1) for kv in line.split())
+            if fields.get("source_sha256") == sha:
+                return int(fields["traffic_bytes_per_launch"])
+    return None
 
 
-def cpu_baseline(wl, layer, queries, lay0_host_lens):
+def cpu_baseline(wl, layer, queries, lay0_host_lens, min_seconds=10.0, max_cycles=64):
+    """The fp64 oracle on whole cycles of one layer (dense + select + mask + fast steps),
+    repeated until at least min_seconds of CPU work have run; returns µs per decode step."""
     import oracle
     import numpy as np
     t_start = time.perf_counter()
@@ -97,28 +105,51 @@ def cpu_baseline(wl, layer, queries, lay0_host_lens):
                   max_blocks=layer.max_blocks)
     cache = oracle.Cache(layer.k, layer.v, layer.len0, wl.Hq, **kw)
     copy_s = time.perf_counter() - t_start
-    t0 = time.perf_counter()
-    eo, el, ez = oracle.dense(cache, queries[0])
-    t1 = time.perf_counter()
-    eidx, en, _ = oracle.select(lay0_host_lens, wl.Hq, wl.Hkv, ez, wl.n_sink, wl.n_recent, wl.k_sel)
-    t2 = time.perf_counter()
-    hm = oracle.sink_mask(ez[:, :, 0], el, wl.mask_frac) if wl.mask_frac > 0 else None
-    t3 = time.perf_counter()
-    for t in range(1, wl.cycle):
-        oracle.sparse(cache.with_lens(np.asarray(lay0_host_lens) + t), queries[t], eidx, en,
-                      wl.n_recent, hm)
-    t4 = time.perf_counter()
-    cycle_s = t4 - t0
+    parts = {"dense": 0.0, "select": 0.0, "mask": 0.0, "fast": 0.0}
+    cycles = 0
+    t_all = time.perf_counter()
+    while cycles < max_cycles and (cycles == 0 or time.perf_counter() - t_all < min_seconds):
+        t0 = time.perf_counter()
+        eo, el, ez = oracle.dense(cache, queries[0])
+        t1 = time.perf_counter()
+        eidx, en, _ = oracle.select(lay0_host_lens, wl.Hq, wl.Hkv, ez, wl.n_sink, wl.n_recent,
+                                    wl.k_sel)
+        t2 = time.perf_counter()
+        hm = oracle.sink_mask(ez[:, :, 0], el, wl.mask_frac) if wl.mask_frac > 0 else None
+        t3 = time.perf_counter()
+        for t in range(1, wl.cycle):
+            oracle.sparse(cache.with_lens(np.asarray(lay0_host_lens) + t), queries[t], eidx, en,
+                          wl.n_recent, hm)
+        t4 = time.perf_counter()
+        for k, v in (("dense", t1 - t0), ("select", t2 - t1), ("mask", t3 - t2), ("fast", t4 - t3)):
+            parts[k] += v
+        cycles += 1
+    total = sum(parts.values())
     return {
-        "value": cycle_s * 1e6 / wl.cycle,
+        "value": round(total * 1e6 / (cycles * wl.cycle), 1),
         "unit": "us/step",
         "cores": oracle.threads(),
         "kind": "oracle",
-        "sample": (f"one whole cycle of one layer of {wl.name} (full batch {wl.B}): dense "
-                   f"{t1 - t0:.2f} s, select {t2 - t1:.2f} s, mask {t3 - t2:.3f} s, "
-                   f"{wl.cycle - 1} fast steps {t4 - t3:.2f} s; host copy {copy_s:.1f} s "
-                   f"not timed"),
+        "sample": (f"{cycles} whole cycles of one layer of {wl.name} (full batch {wl.B}, "
+                   f"1 slow + {wl.cycle - 1} fast steps each), {total:.1f} s of oracle time: "
+                   f"dense {parts['dense'] / cycles:.2f} s, select {parts['select'] / cycles:.3f} s, "
+                   f"mask {parts['mask'] / cycles:.4f} s, fast steps {parts['fast'] / cycles:.2f} s "
+                   f"per cycle; host copy of the cache ({copy_s:.1f} s) not timed"),
     }
+
+
+def copy_calibration(mib: int, reps: int = 3):
+    """A plain device copy of known size, for scaling the HBM byte counters (FETCH_SIZE,
+    WRITE_SIZE) that rocprofv3 reports per dispatch: each dispatch reads and writes exactly
+    mib MiB.  Runs after the timed region and is not part of any reported time."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# copy calibration: {reps} copies of {mib} MiB", file=sys.stderr, flush=True)
 
 
 def main():
@@ -225,7 +256,7 @@ def main():
     fast_gbps = f_bytes / (fast_us * 1e-6) / 1e9
     select_gbps = s_bytes / (select_us * 1e-6) / 1e9
     value = ms_per_step * 1e3 / wl.cycle
-    traffic = counter_traffic()
+    traffic = counter_traffic(wl.name)
 
     result = {
         "metric": METRIC,
@@ -264,6 +295,8 @@ def main():
                           "unit": "GB/s", "frac": round(fast_gbps / PEAK_HBM_GBS, 4),
                           "algorithmic_bytes": int(f_bytes)},
     }
+    if args.copy_calibration > 0:
+        copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:
         print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         host_q = [q.cpu() for q in queries[0]]

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "sfi.h"
 #include "sfi_internal.h"
 
@@ -13,10 +15,25 @@ namespace {
 
 using namespace sfi;
 
-// Workgroups a launch aims for: four per compute unit of a 256-CU MI355X, enough to fill
-// the chip with two resident workgroups per CU and leave a short tail.  The plan depends
-// only on the descriptor, so workspace sizes are the same on every device.
-constexpr int64_t kTargetWorkgroups = 1024;
+// Workgroups a launch aims for.  The attention kernel holds two tile buffers in registers
+// (about 240 VGPRs), so two 4-wavefront workgroups are resident per CU: 512 on a 256-CU
+// MI355X.  Dense steps use 1024 equal workgroups (two even rounds; 512 and 2048 measured
+// slower).  A fast step moves little data and is bound by latency, so it uses about 256
+// larger workgroups with 32-slot granularity (608 workgroups of 256 slots measured 27% slower
+// at 128K).  The plan depends only on the descriptor, so workspace sizes are the same on every
+// device.
+#ifndef SFI_TARGET_WG
+#define SFI_TARGET_WG 1024
+#endif
+#ifndef SFI_SPARSE_TARGET_WG
+#define SFI_SPARSE_TARGET_WG 256
+#endif
+#ifndef SFI_SPARSE_QUANTUM
+#define SFI_SPARSE_QUANTUM 32
+#endif
+constexpr int64_t kTargetWorkgroups = SFI_TARGET_WG;
+constexpr int64_t kSparseTargetWorkgroups = SFI_SPARSE_TARGET_WG;
+constexpr int64_t kSparseQuantum = SFI_SPARSE_QUANTUM;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -47,30 +64,49 @@ sfi_status check_desc(const sfi_kv_desc* kv, bool need_cache) {
 }
 
 struct AttnPlan {
-    int split_len = 0, nsplit = 0, rec = 0;
+    int split_len = 0, nsplit = 0, rec = 0, tab_bytes = 0;
     size_t bytes = 0;
 };
 
+// Split plan: per (b, KV head) unit, nsplit workgroups of split_len slots each, about
+// kTargetWorkgroups (dense) or kSparseTargetWorkgroups (sparse) per launch in total.
 sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride, int64_t n_recent,
                           AttnPlan* p) {
-    const bool tab = sparse || kv.block_table != nullptr;
+    const bool paged = kv.block_table != nullptr;
     const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
     const int64_t G = kv.num_q_heads / kv.num_kv_heads;
     int64_t slots = sparse ? idx_stride + n_recent : (int64_t)kv.max_len;
     if (slots < 1) slots = 1;
-    const int64_t per_unit = ceil_div(kTargetWorkgroups, units);
-    int64_t split = ceil_div(ceil_div(slots, per_unit), kSplitQuantum) * kSplitQuantum;
-    if (tab && split > kTabMax) split = kTabMax;
+    const int64_t quantum = sparse ? kSparseQuantum : kSplitQuantum;
+    const int64_t target = sparse ? kSparseTargetWorkgroups : kTargetWorkgroups;
+    const int64_t per_unit = ceil_div(target, units);
+    int64_t split = ceil_div(ceil_div(slots, per_unit), quantum) * quantum;
+    if ((sparse || paged) && split > kTabMax) split = kTabMax;
     int64_t nsplit = ceil_div(slots, split);
     if (nsplit > kMaxSplits) {
-        if (tab) return SFI_E_UNSUPPORTED;        // more than kMaxSplits * kTabMax slots
+        if (sparse || paged) return SFI_E_UNSUPPORTED;   // more than kMaxSplits * kTabMax slots
         split = ceil_div(ceil_div(slots, kMaxSplits), kSplitQuantum) * kSplitQuantum;
         nsplit = ceil_div(slots, split);
     }
     p->split_len = (int)split;
     p->nsplit = (int)nsplit;
     p->rec = (int)(ceil_div(G * (kv.head_dim + 2), 4) * 4);
-    p->bytes = align_up((size_t)units * nsplit * p->rec * sizeof(float));
+    int64_t tab = 0;
+    if (sparse) {
+        tab = split * 4 + split;                            // rows, then attend flags
+    } else if (paged) {
+        int shift = 0;
+        while ((1 << shift) < kv.block_size) ++shift;
+        tab = ((split >> shift) + 2) * 4;                   // one base row per block touched
+    }
+    p->tab_bytes = (int)(ceil_div(tab, 16) * 16);
+    // Partial records are sized for a bound on nsplit that never decreases as the length
+    // grows (the split itself is rounded, so nsplit alone can), so a workspace sized for the
+    // longest step of a cycle serves every shorter one.
+    int64_t bound = ceil_div(slots, quantum);
+    bound = std::min(bound, std::max(per_unit, (sparse || paged) ? ceil_div(slots, (int64_t)kTabMax) : 1));
+    bound = std::min(bound, (int64_t)kMaxSplits);
+    p->bytes = align_up((size_t)units * bound * p->rec * sizeof(float));
     return SFI_OK;
 }
 
@@ -118,6 +154,7 @@ void fill_cache_args(const sfi_kv_desc& kv, AttnArgs* a) {
 void fill_plan_args(const AttnPlan& p, void* ws, AttnArgs* a) {
     a->split_len = p.split_len;
     a->nsplit = p.nsplit;
+    a->tab_bytes = p.tab_bytes;
     a->rec_floats = p.rec;
     a->part = (float*)ws;
 }

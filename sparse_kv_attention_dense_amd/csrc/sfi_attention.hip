@@ -39,6 +39,57 @@ constexpr float kLn2 = 0.693147180559945309417f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Merges the nsplit partial records of query head i of batch b into out and lse.  Thread
+// (dim, phase) folds splits phase, phase + R, ... into a running (M, L, A) with the online
+// log-sum-exp rule; every load is independent of the running values, so the record set is
+// fetched in one round trip.  The R phases then merge through LDS (s_m, s_l, s_a: kThreads
+// floats each).
+template <int D, bool SPARSE>
+__device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s_l, float* s_a) {
+    constexpr int R = kThreads / D;
+    const int tid = threadIdx.x;
+    const int G = a.G, h = i / G, g = i - h * G;
+    const int S = a.nsplit, rec = a.rec_floats;
+    const float* base = a.part + (int64_t)(b * a.Hkv + h) * S * rec;
+    const int dim = tid % D, ph = tid / D;
+    float M = -INFINITY, L = 0.f, A = 0.f;
+#pragma unroll 8
+    for (int s = ph; s < S; s += R) {
+        const float* r = base + (int64_t)s * rec;
+        const float m = r[G * D + 2 * g], l = r[G * D + 2 * g + 1], x = r[g * D + dim];
+        const float Mn = fmaxf(M, m);
+        if (Mn == -INFINITY) continue;                 // nothing attended so far
+        const float c_old = exp2_fast(M - Mn), c_new = exp2_fast(m - Mn);
+        L = L * c_old + l * c_new;
+        A = A * c_old + x * c_new;
+        M = Mn;
+    }
+    s_m[tid] = M;
+    s_l[tid] = L;
+    s_a[tid] = A;
+    __syncthreads();
+    if (tid < D) {
+        float Mt = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < R; ++r) Mt = fmaxf(Mt, s_m[tid + r * D]);
+        const float Mu = (Mt == -INFINITY) ? 0.f : Mt;
+        float Lt = 0.f, At = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float c = exp2_fast(s_m[tid + r * D] - Mu);
+            Lt += c * s_l[tid + r * D];
+            At += c * s_a[tid + r * D];
+        }
+        bool zero = !(Lt > 0.f);
+        if constexpr (SPARSE) {
+            if (a.head_mask) zero |= a.head_mask[b * a.Hq + i] != 0;
+        }
+        a.out[((int64_t)b * a.Hq + i) * D + tid] = zero ? 0.f : At / Lt;
+        if (tid == 0 && a.lse) a.lse[b * a.Hq + i] = zero ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+    }
+    __syncthreads();
+}
+
 // Orders this wavefront's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -51,7 +102,6 @@ struct Cfg {
     static constexpr int kVStage = BF ? kWaves * kTile * kVRow : 0;
     static constexpr int kRed = kWaves * kMaxG * (D + 2) * 4;      // cross-wave merge
     static constexpr int kRaw = kVStage > kRed ? kVStage : kRed;
-    static constexpr bool kTab = PAGED || SPARSE;
     static constexpr int kNQ = BF ? D / 32 : D / 16;               // Q / K fragments per row
     static constexpr int kNV = BF ? D / 16 : 2 * 4 * (D / 16);     // V registers per tile
     static constexpr int kRPI = 1024 / (2 * D);                    // bf16 V rows per wave load
@@ -72,8 +122,10 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     using C = Cfg<BF, D, PAGED, SPARSE>;
     using Regs = TileRegs<BF, D, PAGED, SPARSE>;
     __shared__ __attribute__((aligned(16))) unsigned char raw[C::kRaw];
-    __shared__ uint32_t tab_row[C::kTab ? kTabMax : 1];
-    __shared__ uint8_t tab_ok[SPARSE ? kTabMax : 1];
+    // Row table in dynamic LDS, sized by the host for this launch's split length:
+    //   sparse: one row per slot, then one "attend" flag byte per slot;
+    //   dense paged: one base row per KV block the split touches.
+    extern __shared__ __attribute__((aligned(16))) uint32_t tab[];
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -81,6 +133,13 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     const int G = a.G;
     const int hq0 = h * G;
     const int unit = b * a.Hkv + h;
+    const int s0 = split * a.split_len;
+    // The first index entry of each thread depends only on the slot, so its load is issued
+    // before the lengths arrive and the two latencies overlap.
+    int idx_first = 0;
+    if constexpr (SPARSE) {
+        if (s0 + tid < a.idx_stride) idx_first = a.idx[(int64_t)unit * a.idx_stride + s0 + tid];
+    }
     const int len_b = a.len[b];
 
     // ---- slot range of this workgroup -------------------------------------------------
@@ -95,29 +154,28 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             for (int g = 0; g < G; ++g) all_masked &= a.head_mask[b * a.Hq + hq0 + g] != 0;
         }
     }
-    const int s0 = split * a.split_len;
     int s1 = min(n_tot, s0 + a.split_len);
     if (all_masked || len_b <= 0) s1 = s0;
     const int nslots = max(0, s1 - s0);
 
     const uint32_t base_row = PAGED ? 0u : (uint32_t)((int64_t)unit * a.n_cap);
 
-    if constexpr (C::kTab) {
-        const int bmask = (1 << a.block_shift) - 1;
+    const int bmask = (1 << a.block_shift) - 1;
+    uint8_t* tab_ok = (uint8_t*)(tab + a.split_len);
+    if constexpr (SPARSE) {
+        const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
         for (int t = tid; t < nslots; t += kThreads) {
             const int slot = s0 + t;
-            int pos = slot;
-            if constexpr (SPARSE) {
-                bool ok = true;
-                if (slot < n_sel) {
-                    pos = a.idx[(int64_t)unit * a.idx_stride + slot];
-                    ok = pos >= 0 && pos < r0;
-                    if (!ok) pos = len_b - 1;
-                } else {
-                    pos = r0 + (slot - n_sel);
-                }
-                tab_ok[t] = ok;
+            int pos;
+            bool ok = true;
+            if (slot < n_sel) {
+                pos = t == tid ? idx_first : irow[slot];
+                ok = pos >= 0 && pos < r0;
+                if (!ok) pos = len_b - 1;
+            } else {
+                pos = r0 + (slot - n_sel);
             }
+            tab_ok[t] = ok;
             uint32_t row;
             if constexpr (PAGED) {
                 const int blk = a.block_table[(int64_t)b * a.max_blocks + (pos >> a.block_shift)];
@@ -126,13 +184,24 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             } else {
                 row = base_row + (uint32_t)pos;
             }
-            tab_row[t] = row;
+            tab[t] = row;
+        }
+        __syncthreads();
+    } else if constexpr (PAGED) {
+        // blocks [s0 >> shift, (s1 - 1) >> shift] of sequence b
+        const int blk0 = s0 >> a.block_shift;
+        const int nblk = nslots > 0 ? ((s1 - 1) >> a.block_shift) - blk0 + 1 : 0;
+        for (int t = tid; t < nblk; t += kThreads) {
+            const int blk = a.block_table[(int64_t)b * a.max_blocks + blk0 + t];
+            tab[t] = ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift;
         }
         __syncthreads();
     }
 
     auto slot_row = [&](int slot) -> uint32_t {     // slot in [s0, s1)
-        if constexpr (C::kTab) return tab_row[slot - s0];
+        if constexpr (SPARSE) return tab[slot - s0];
+        else if constexpr (PAGED)
+            return tab[(slot >> a.block_shift) - (s0 >> a.block_shift)] | (uint32_t)(slot & bmask);
         else return base_row + (uint32_t)slot;
     };
     auto slot_ok = [&](int slot) -> bool {
@@ -383,68 +452,19 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             part[G * D + 2 * g + 1] = L;
         }
     }
-
 }
 
-// Merges the nsplit partial records of one query head (blockIdx.x) of batch blockIdx.y.
+// One workgroup per query head (blockIdx.x) of batch blockIdx.y merges the split records.
 template <int D, bool SPARSE>
 __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
-    __shared__ float s_w[kMaxSplits];
-    __shared__ float s_red[kThreads];
-    __shared__ float s_acc[kThreads];
-    const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int G = a.G, h = i / G, g = i - h * G;
-    const int S = a.nsplit, rec = a.rec_floats;
-    const float* base = a.part + (int64_t)(b * a.Hkv + h) * S * rec;
-    // global max of the split maxima
-    float M = -INFINITY;
-    for (int s = tid; s < S; s += kThreads) M = fmaxf(M, base[(int64_t)s * rec + G * D + 2 * g]);
-    s_red[tid] = M;
-    __syncthreads();
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-        if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
-        __syncthreads();
-    }
-    M = s_red[0];
-    __syncthreads();
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    // split weights 2^(m_s - M) and the merged normaliser
-    float L = 0.f;
-    for (int s = tid; s < S; s += kThreads) {
-        const float w = exp2_fast(base[(int64_t)s * rec + G * D + 2 * g] - Mu);
-        s_w[s] = w;
-        L += w * base[(int64_t)s * rec + G * D + 2 * g + 1];
-    }
-    s_red[tid] = L;
-    __syncthreads();
-    for (int o = kThreads / 2; o > 0; o >>= 1) {
-        if (tid < o) s_red[tid] += s_red[tid + o];
-        __syncthreads();
-    }
-    L = s_red[0];
-    // weighted sum of the accumulators: thread -> (dim, phase); phases share the splits
-    constexpr int R = kThreads / D;
-    const int dim = tid % D, ph = tid / D;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = ph; s < S; s += R) acc += s_w[s] * base[(int64_t)s * rec + g * D + dim];
-    s_acc[tid] = acc;
-    __syncthreads();
-    if (tid < D) {
-        for (int r = 1; r < R; ++r) acc += s_acc[tid + r * D];
-        bool zero = !(L > 0.f);
-        if constexpr (SPARSE) {
-            if (a.head_mask) zero |= a.head_mask[b * a.Hq + i] != 0;
-        }
-        a.out[((int64_t)b * a.Hq + i) * D + tid] = zero ? 0.f : acc / L;
-        if (tid == 0 && a.lse) a.lse[b * a.Hq + i] = zero ? -INFINITY : (M + log2f(L)) * kLn2;
-    }
+    __shared__ float s_m[kThreads], s_l[kThreads], s_a[kThreads];
+    merge_head<D, SPARSE>(a, blockIdx.y, blockIdx.x, s_m, s_l, s_a);
 }
 
 template <bool BF, int D, bool PAGED, bool SPARSE>
 hipError_t launch_one(const AttnArgs& a, int B, hipStream_t stream) {
     hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), dim3(a.nsplit, a.Hkv, B),
-                       dim3(kThreads), 0, stream, a);
+                       dim3(kThreads), (size_t)a.tab_bytes, stream, a);
     hipLaunchKernelGGL((combine_kernel<D, SPARSE>), dim3(a.Hq, B), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

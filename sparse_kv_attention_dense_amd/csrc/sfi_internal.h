@@ -14,7 +14,7 @@ constexpr int kThreads = 256;        // 4 wavefronts of 64
 constexpr int kWaves = 4;
 constexpr int kTile = 32;            // slots per wavefront iteration (two 16-row MFMA blocks)
 constexpr int kSplitQuantum = kTile * kWaves;
-constexpr int kTabMax = 4096;        // slots per workgroup when rows come from a table
+constexpr int kTabMax = 4096;        // row-table entries per workgroup (dynamic LDS)
 constexpr int kMaxSplits = 1024;     // partial records per (b, h) that the combine merges
 constexpr int kMaxG = 16;            // query heads per KV head (MFMA N dimension)
 
@@ -32,8 +32,9 @@ struct AttnArgs {
     float scale_log2;                // scale * log2(e)
     float* logits;                   // dense only, may be null
     int64_t logit_stride;
-    int32_t split_len;               // slots per workgroup, multiple of kSplitQuantum
+    int32_t split_len;               // slots per workgroup, a multiple of kTile
     int32_t nsplit;                  // workgroups per (b, h)
+    int32_t tab_bytes;               // dynamic LDS of the row table
     int32_t rec_floats;              // floats per partial record (G*(d+2) rounded to 4)
     const int32_t* idx;              // sparse only
     int32_t idx_stride;

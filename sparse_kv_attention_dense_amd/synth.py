@@ -155,7 +155,9 @@ def make_layer(wl: Workload, layer: int = 0, device="cpu", lens=None) -> Layer:
     if lens is not None:
         len_host = [int(x) for x in lens]
     elif wl.len_lo > 0:
-        gl = _gen("cpu", seed + 50)
+        # one set of sequence lengths per workload: every layer of a batch sees the same
+        # sequences, so the lengths do not depend on the layer
+        gl = _gen("cpu", wl.seed_base + 50)
         len_host = torch.randint(wl.len_lo, wl.n0 + 1, (wl.B,), generator=gl).tolist()
     else:
         len_host = [wl.n0] * wl.B

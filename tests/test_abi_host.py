@@ -136,3 +136,18 @@ def test_workspace_grows_with_context(L):
     small = L.sfi_workspace_bytes(ctypes.byref(_desc(max_len=1000, n_cap=1000)), B.SFI_OP_SELECT, 0, 0)
     large = L.sfi_workspace_bytes(ctypes.byref(_desc(max_len=100000, n_cap=100000)), B.SFI_OP_SELECT, 0, 0)
     assert large > small > 0
+
+
+def test_workspace_never_shrinks_as_length_grows(L):
+    """A workspace sized for the longest step of a cycle must serve every shorter step."""
+    for op, istride, nrec in ((B.SFI_OP_DENSE, 0, 0), (B.SFI_OP_SELECT, 0, 0),
+                              (B.SFI_OP_SPARSE, 2052, 256)):
+        for paged in (False, True):
+            prev = 0
+            for n in list(range(1, 600, 7)) + list(range(30000, 36000, 97)) + [131072, 524288 + 31]:
+                kw = dict(max_len=n, n_cap=n, batch=1, num_q_heads=32, num_kv_heads=8)
+                if paged:
+                    kw.update(block_table=FAKE, block_size=16, max_blocks=(n + 15) // 16)
+                need = L.sfi_workspace_bytes(ctypes.byref(_desc(**kw)), op, istride, nrec)
+                assert need >= prev > 0 or (prev == 0 and need > 0), (op, paged, n, need, prev)
+                prev = need
