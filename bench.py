@@ -201,49 +201,56 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def cycle(li, rec):
+        """One slow-fast cycle of layer li.  rec = "none": no events; "dense": events around
+        the dense call only (the timed region); "all": events around every call."""
         d0 = descs[li]
-        e = [ev() for _ in range(4 + wl.cycle - 1)] if rec else None
-        if rec:
+        e = [ev() for _ in range(4 + wl.cycle - 1)] if rec != "none" else None
+        if e:
             e[0].record(stream)
         B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
-        if rec:
+        if e:
             e[1].record(stream)
         B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
                      idx_stride, nidxs[li], ws)
-        if rec:
+        if rec == "all":
             e[2].record(stream)
         if masks[li] is not None:
             B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
-        if rec:
+        if rec == "all":
             e[3].record(stream)
         for t in range(1, wl.cycle):
             B.sfi_sparse_decode(d0[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
                                 wl.n_recent, masks[li], out, lse, ws)
-            if rec:
+            if rec == "all":
                 e[3 + t].record(stream)
         return e
 
     print("# warmup", file=sys.stderr, flush=True)
     for s in range(args.warmup):
-        cycle(s % L, False)
+        cycle(s % L, "none")
     torch.cuda.synchronize()
+    # Timed region: whole cycles back to back; the only events are the two around each dense
+    # call (the roofline kernel), so the wall clock is not inflated by event records.
     print("# timed region", file=sys.stderr, flush=True)
     evs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        evs.append(cycle(s % L, True))
+        evs.append(cycle(s % L, "dense"))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    dense_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    mean = lambda x: sum(x) / len(x)
+    dense_us = 1e3 * mean([e[0].elapsed_time(e[1]) for e in evs])
+    # Per-call breakdown: separate cycles with an event around every call (these events add
+    # small gaps, so the breakdown is not used for value).
+    print("# per-call breakdown", file=sys.stderr, flush=True)
+    evs = [cycle(s % L, "all") for s in range(max(1, min(args.steps, 2 * L)))]
+    torch.cuda.synchronize()
     select_ms = [e[1].elapsed_time(e[2]) for e in evs]
     mask_ms = [e[2].elapsed_time(e[3]) for e in evs]
     fast_ms = [e[2 + t].elapsed_time(e[3 + t]) for e in evs for t in range(1, wl.cycle)]
-    mean = lambda x: sum(x) / len(x)
-    dense_us, select_us, mask_us, fast_us = (1e3 * mean(dense_ms), 1e3 * mean(select_ms),
-                                             1e3 * mean(mask_ms), 1e3 * mean(fast_ms))
+    select_us, mask_us, fast_us = 1e3 * mean(select_ms), 1e3 * mean(mask_ms), 1e3 * mean(fast_ms)
 
     lens0 = layers[0].len0_host
     n_idx_host = nidxs[0].cpu().tolist()
