@@ -39,6 +39,51 @@ constexpr float kLn2 = 0.693147180559945309417f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Splits of sequence b that hold positions: ceil(len_b / split_len), at most nsplit.
+__device__ __forceinline__ int splits_of(const AttnArgs& a, int len_b) {
+    return len_b > 0 ? min((len_b + a.split_len - 1) / a.split_len, a.nsplit) : 0;
+}
+
+// Finds the (b, r, splits_of(b)) of dense workgroup wg, where r = h * splits_of(b) + split
+// counts the active workgroups of sequence b in order; workgroups are numbered sequence by
+// sequence.  Returns false when wg is past the last active workgroup.  sh: 8 ints of LDS.
+__device__ bool locate_split(const AttnArgs& a, int wg, int* sh, int* loc) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    if (tid == 0) sh[4] = -1;
+    int off = 0;
+    for (int base = 0; base < a.B; base += kThreads) {
+        const int bb = base + tid;
+        const int ns = bb < a.B ? splits_of(a, a.len[bb]) : 0;
+        const int cnt = ns * a.Hkv;
+        int inc = cnt;                                     // inclusive scan over the block
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
+        __syncthreads();
+        if (lane == 63) sh[w] = inc;
+        __syncthreads();
+        int before = off;
+        for (int ww = 0; ww < w; ++ww) before += sh[ww];
+        const int excl = before + inc - cnt;
+        if (cnt > 0 && wg >= excl && wg < excl + cnt) {
+            sh[4] = bb;
+            sh[5] = wg - excl;
+            sh[6] = ns;
+        }
+        off += sh[0] + sh[1] + sh[2] + sh[3];
+        __syncthreads();
+        if (sh[4] >= 0) break;
+    }
+    __syncthreads();
+    loc[0] = sh[4];
+    loc[1] = sh[5];
+    loc[2] = sh[6];
+    const bool found = loc[0] >= 0;
+    __syncthreads();                                       // sh is reused by the caller
+    return found;
+}
+
 // Merges the nsplit partial records of query head i of batch b into out and lse.  Thread
 // (dim, phase) folds splits phase, phase + R, ... into a running (M, L, A) with the online
 // log-sum-exp rule; every load is independent of the running values, so the record set is
@@ -49,8 +94,8 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
     constexpr int R = kThreads / D;
     const int tid = threadIdx.x;
     const int G = a.G, h = i / G, g = i - h * G;
-    const int S = a.nsplit, rec = a.rec_floats;
-    const float* base = a.part + (int64_t)(b * a.Hkv + h) * S * rec;
+    const int S = SPARSE ? a.nsplit : splits_of(a, a.len[b]), rec = a.rec_floats;
+    const float* base = a.part + (int64_t)(b * a.Hkv + h) * a.nsplit * rec;   // nsplit records per unit
     const int dim = tid % D, ph = tid / D;
     float M = -INFINITY, L = 0.f, A = 0.f;
 #pragma unroll 8
@@ -127,9 +172,22 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     //   dense paged: one base row per KV block the split touches.
     extern __shared__ __attribute__((aligned(16))) uint32_t tab[];
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int q4 = lane >> 4, n16 = lane & 15;
+    int split, h, b;
+    if constexpr (SPARSE) {
+        split = blockIdx.x;
+        h = blockIdx.y;
+        b = blockIdx.z;
+    } else {
+        // Dense: the 1-D grid enumerates only the splits that hold positions, sequence by
+        // sequence, so a ragged batch does not leave idle workgroups between busy ones.
+        int loc[3];
+        if (!locate_split(a, blockIdx.x, (int*)raw, loc)) return;
+        b = loc[0];
+        h = loc[1] / loc[2];
+        split = loc[1] - h * loc[2];
+    }
     const int G = a.G;
     const int hq0 = h * G;
     const int unit = b * a.Hkv + h;
@@ -463,8 +521,9 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
 
 template <bool BF, int D, bool PAGED, bool SPARSE>
 hipError_t launch_one(const AttnArgs& a, int B, hipStream_t stream) {
-    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), dim3(a.nsplit, a.Hkv, B),
-                       dim3(kThreads), (size_t)a.tab_bytes, stream, a);
+    const dim3 grid = SPARSE ? dim3(a.nsplit, a.Hkv, B) : dim3(a.nsplit * a.Hkv * B);
+    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), grid, dim3(kThreads),
+                       (size_t)a.tab_bytes, stream, a);
     hipLaunchKernelGGL((combine_kernel<D, SPARSE>), dim3(a.Hq, B), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -27,7 +27,7 @@ struct AttnArgs {
     int64_t n_cap;                   // contiguous only
     int32_t block_shift;             // log2(block_size), paged only
     int32_t max_blocks;
-    int32_t Hq, Hkv, G;
+    int32_t B, Hq, Hkv, G;
     float scale;                     // 1/sqrt(d)
     float scale_log2;                // scale * log2(e)
     float* logits;                   // dense only, may be null
