@@ -141,6 +141,8 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+constexpr int kFill = 8;             // sparse row-table slots per thread per batch
+
 template <bool BF, int D, bool PAGED, bool SPARSE>
 struct Cfg {
     static constexpr int kVRow = D * 2 + 16;                       // staged bf16 row, bytes
@@ -192,11 +194,20 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     const int hq0 = h * G;
     const int unit = b * a.Hkv + h;
     const int s0 = split * a.split_len;
-    // The first index entry of each thread depends only on the slot, so its load is issued
-    // before the lengths arrive and the two latencies overlap.
-    int idx_first = 0;
-    if constexpr (SPARSE) {
-        if (s0 + tid < a.idx_stride) idx_first = a.idx[(int64_t)unit * a.idx_stride + s0 + tid];
+    // The index entries of the first kFill * kThreads slots depend only on the slot, so their
+    // loads are issued before the lengths arrive and the latencies overlap.
+    int idx_pre[kFill];
+    // Table slots per thread in one batch: what the split needs, at most kFill (paged only).
+    const int nfill = min(kFill, (a.split_len + kThreads - 1) / kThreads);
+    if constexpr (SPARSE && !PAGED) {
+        idx_pre[0] = s0 + tid < a.idx_stride ? a.idx[(int64_t)unit * a.idx_stride + s0 + tid] : 0;
+    } else if constexpr (SPARSE) {
+        const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
+#pragma unroll
+        for (int u = 0; u < kFill; ++u) {
+            const int slot = s0 + u * kThreads + tid;
+            idx_pre[u] = (u < nfill && slot < a.idx_stride) ? irow[slot] : 0;
+        }
     }
     const int len_b = a.len[b];
 
@@ -222,27 +233,66 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     uint8_t* tab_ok = (uint8_t*)(tab + a.split_len);
     if constexpr (SPARSE) {
         const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
-        for (int t = tid; t < nslots; t += kThreads) {
-            const int slot = s0 + t;
-            int pos;
-            bool ok = true;
-            if (slot < n_sel) {
-                pos = t == tid ? idx_first : irow[slot];
-                ok = pos >= 0 && pos < r0;
-                if (!ok) pos = len_b - 1;
-            } else {
-                pos = r0 + (slot - n_sel);
+        if constexpr (!PAGED) {
+            for (int t = tid; t < nslots; t += kThreads) {
+                const int slot = s0 + t;
+                int pos;
+                bool ok = true;
+                if (slot < n_sel) {
+                    pos = t == tid ? idx_pre[0] : irow[slot];
+                    ok = pos >= 0 && pos < r0;
+                    if (!ok) pos = len_b - 1;
+                } else {
+                    pos = r0 + (slot - n_sel);
+                }
+                tab_ok[t] = ok;
+                tab[t] = base_row + (uint32_t)pos;
             }
-            tab_ok[t] = ok;
-            uint32_t row;
-            if constexpr (PAGED) {
-                const int blk = a.block_table[(int64_t)b * a.max_blocks + (pos >> a.block_shift)];
-                row = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
-                      (uint32_t)(pos & bmask);
-            } else {
-                row = base_row + (uint32_t)pos;
+        }
+        // Paged: slots are filled nfill per thread at a time; every index load of a batch is
+        // issued before any is used, then every block-table load, so a batch costs two memory
+        // round trips however many slots it holds (3% faster fast steps on a ragged batch;
+        // on a contiguous cache the plain loop above measured faster).
+        for (int t0 = 0; PAGED && t0 < nslots; t0 += nfill * kThreads) {
+            int pos[kFill];
+            bool ok[kFill];
+#pragma unroll
+            for (int u = 0; u < kFill; ++u) {
+                const int t = t0 + u * kThreads + tid;
+                const int slot = s0 + t;
+                ok[u] = true;
+                pos[u] = 0;
+                if (u < nfill && t < nslots) {
+                    if (slot < n_sel) {
+                        pos[u] = t0 == 0 ? idx_pre[u] : irow[slot];
+                        ok[u] = pos[u] >= 0 && pos[u] < r0;
+                        if (!ok[u]) pos[u] = len_b - 1;
+                    } else {
+                        pos[u] = r0 + (slot - n_sel);
+                    }
+                }
             }
-            tab[t] = row;
+            uint32_t row[kFill];
+#pragma unroll
+            for (int u = 0; u < kFill; ++u) {
+                if constexpr (PAGED) {
+                    const int t = t0 + u * kThreads + tid;
+                    const int blk = (u < nfill && t < nslots)
+                        ? a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)] : 0;
+                    row[u] = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
+                             (uint32_t)(pos[u] & bmask);
+                } else {
+                    row[u] = base_row + (uint32_t)pos[u];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kFill; ++u) {
+                const int t = t0 + u * kThreads + tid;
+                if (u < nfill && t < nslots) {
+                    tab_ok[t] = ok[u];
+                    tab[t] = row[u];
+                }
+            }
         }
         __syncthreads();
     } else if constexpr (PAGED) {
