@@ -105,7 +105,8 @@ sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, fl
  *   f(j) = (1/G) sum_{i in group h} exp(z_ij - log sum_{j' in J} exp(z_ij'))
  *   taken = the min(k_sel, |J|) positions of J with the largest f; equal f -> lower j first
  *   idx[(b*Hkv + h)*idx_stride + s], s < n_idx[b*Hkv + h]: ascending positions of S u taken
- * logits (device) fp32 [B][Hq][logit_stride] as written by sfi_dense_decode.
+ * logits (device) fp32 [B][Hq][logit_stride] as written by sfi_dense_decode: 16-byte aligned,
+ * logit_stride >= max_len and a multiple of 4.
  * idx (device) int32 [B][Hkv][idx_stride], idx_stride >= n_sink + k_sel.
  * n_idx (device) int32 [B][Hkv] = min(n_sink, N) + min(k_sel, |J|).
  * n_sink, n_recent >= 0, k_sel >= 0.  kv->k and kv->v are not read. */

@@ -42,6 +42,10 @@ constexpr int64_t kPagedTargetWorkgroups = SFI_PAGED_TARGET_WG;
 constexpr int64_t kSparseTargetWorkgroups = SFI_SPARSE_TARGET_WG;
 constexpr int64_t kSparseQuantum = SFI_SPARSE_QUANTUM;
 constexpr size_t kAlign = 256;
+constexpr double kUnitFixedUs = 12.0;           // Selector path estimates, see select_unit_path
+constexpr double kUnitUsPerMB = 60.0;
+constexpr double kChunkedFixedUs = 43.5;
+constexpr double kChunkedUsPerMB = 0.49;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -117,6 +121,25 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
     bound = std::min(bound, (int64_t)kMaxSplits);
     p->bytes = align_up((size_t)units * bound * p->rec * sizeof(float));
     return SFI_OK;
+}
+
+// Selector path.  One workgroup per (b, KV head) is bound by one compute unit's ALU rate on
+// that unit's logits; the chunked kernels spread the work over the chip but pay for nine
+// launches.  The plan takes whichever is estimated faster from the descriptor alone, with
+// linear fits to MI355X measurements of both paths: one workgroup per unit 17 us at 32 KB of
+// logits per unit, 41 us at 0.5 MB, 143 us at 2 MB; chunked 35 us at 32 KB of logits in all,
+// 46 us at 4 MB, 76 us at 67 MB, 96 us at 134 MB.
+#ifndef SFI_SELECT_PATH
+#define SFI_SELECT_PATH -1                      // -1: estimate; 0: chunked; 1: one per unit
+#endif
+bool select_unit_path(const sfi_kv_desc& kv) {
+    if (SFI_SELECT_PATH >= 0) return SFI_SELECT_PATH == 1;
+    const double G = (double)kv.num_q_heads / kv.num_kv_heads;
+    const double unit_mb = G * kv.max_len * 4.0 / 1e6;
+    const double all_mb = (double)kv.batch * kv.num_q_heads * kv.max_len * 4.0 / 1e6;
+    const double t_unit = kUnitFixedUs + kUnitUsPerMB * unit_mb;
+    const double t_chunked = kChunkedFixedUs + kChunkedUsPerMB * all_mb;
+    return t_unit < t_chunked;
 }
 
 struct SelPlan {
@@ -234,6 +257,7 @@ SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int
     sfi_status st = check_desc(kv, false);
     if (st != SFI_OK) return st;
     if (!logits || !idx || !n_idx || logit_stride < kv->max_len || logit_stride < 1) return SFI_E_INVALID;
+    if (logit_stride % 4 != 0 || !aligned(logits, 16)) return SFI_E_INVALID;
     if (n_sink < 0 || n_recent < 0 || k_sel < 0) return SFI_E_INVALID;
     if ((int64_t)idx_stride < (int64_t)n_sink + k_sel || idx_stride < 1) return SFI_E_INVALID;
     SelPlan plan;
@@ -261,6 +285,7 @@ SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int
     a.hist = (uint32_t*)(base + plan.off_hist);
     a.state = (int32_t*)(base + plan.off_state);
     a.counts = (uint32_t*)(base + plan.off_counts);
+    a.unit_path = select_unit_path(*kv) ? 1 : 0;
     const hipError_t e = launch_select(a, stream);
     return e == hipSuccess ? SFI_OK : SFI_E_HIP;
 }

@@ -69,6 +69,7 @@ struct SelArgs {
     uint32_t* hist;                  // [B][Hkv][3][kRadixBins]
     int32_t* state;                  // [B][Hkv][4]: prefix, k_rem, nJ, take_all
     uint32_t* counts;                // [B][Hkv][nchunk][2]
+    int32_t unit_path;               // 1: one workgroup per (b, KV head) does everything
 };
 
 hipError_t launch_select(const SelArgs& a, hipStream_t stream);

@@ -335,6 +335,314 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
         if (keep_mask & (1u << k)) row[out++] = jbase + k;
 }
 
+// ---- the whole Selector in one launch: one 1024-thread workgroup per (b, KV head) --------
+//
+// Used when each unit's logits are small enough that one compute unit walks them faster than
+// the chunked kernels above can be launched (the host decides from the descriptor).  Same
+// result: LSE over J per head, evidence keys, three radix digits of the k-th largest key in
+// LDS histograms, then an ordered emit in blocks of 4096 positions with one packed
+// (greater, equal) scan per block.  Keys are kept per position in the workspace (L2-resident
+// between the passes).
+
+// merge of two partial log-sum-exp pairs (max, sum of exp(x - max)); max = -inf is empty
+__device__ __forceinline__ float2 lse_merge(float2 p, float2 q) {
+    const float m = fmaxf(p.x, q.x);
+    if (m == -INFINITY) return make_float2(m, 0.f);
+    return make_float2(m, p.y * expf(p.x - m) + q.y * expf(q.x - m));
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// lse_merge in log2 units
+__device__ __forceinline__ float2 lse2_merge(float2 p, float2 q) {
+    const float m = fmaxf(p.x, q.x);
+    if (m == -INFINITY) return make_float2(m, 0.f);
+    return make_float2(m, p.y * exp2_hw(p.x - m) + q.y * exp2_hw(q.x - m));
+}
+
+constexpr int kUT = 1024;                              // threads per workgroup
+constexpr int kUW = kUT / 64;                          // wavefronts
+constexpr int kUQ = 4;                                 // position quads per thread per batch
+
+struct UnitShared {
+    uint32_t hist[kRadixBins];
+    uint32_t wtot[kUW];
+    float2 red[4 * kUW];
+    float lse[kMaxG];
+    uint32_t sel[2];
+};
+
+// exclusive scan over the 1024 threads (ascending thread order); total returned in *tot
+__device__ uint32_t unit_scan(uint32_t x, UnitShared& sm, uint32_t* tot) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    uint32_t inc = x;
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+    }
+    if (lane == 63) sm.wtot[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int ww = 0; ww < kUW; ++ww) {
+        const uint32_t t = sm.wtot[ww];
+        before += ww < w ? t : 0u;
+        all += t;
+    }
+    __syncthreads();
+    *tot = all;
+    return before + inc - x;
+}
+
+// Chooses the digit (bins of sm.hist, ascending) that holds the k_rem-th largest key; keeps
+// the digit in prefix at `shift` and subtracts the keys in higher bins from k_rem.
+__device__ void unit_resolve(UnitShared& sm, int shift, uint32_t& prefix, int32_t& k_rem) {
+    const int tid = threadIdx.x;
+    const uint32_t c0 = sm.hist[2 * tid], c1 = sm.hist[2 * tid + 1];
+    uint32_t total;
+    const uint32_t excl = unit_scan(c0 + c1, sm, &total);
+    const uint32_t above = total - excl - c0 - c1;      // keys in higher bins
+    const uint32_t k = (uint32_t)k_rem;
+    if (above < k && k <= above + c0 + c1) {
+        if (above + c1 >= k) {
+            sm.sel[0] = 2 * tid + 1;
+            sm.sel[1] = above;
+        } else {
+            sm.sel[0] = 2 * tid;
+            sm.sel[1] = above + c1;
+        }
+    }
+    __syncthreads();
+    prefix |= sm.sel[0] << shift;
+    k_rem -= (int32_t)sm.sel[1];
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kUT) select_unit_kernel(SelArgs a) {
+    __shared__ UnitShared sm;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int G = a.G;
+    const int unit = b * a.Hkv + h;
+    const Range r = j_range(a, b);
+    const int ns = max(0, min(a.n_sink, r.N));
+    const int nJ = r.nJ;
+    int32_t* row = a.idx + (int64_t)unit * a.idx_stride;
+    for (int t = tid; t < ns; t += kUT) row[t] = t;
+    const bool take_all = a.k_sel >= nJ;
+    if (tid == 0) a.n_idx[unit] = ns + (take_all ? nJ : a.k_sel);
+    if (take_all) {
+        for (int t = tid; t < nJ; t += kUT) row[ns + t] = r.j0 + t;
+        return;
+    }
+    if (a.k_sel == 0) return;
+
+    // Position quads [q0, q1) cover J; logit rows are 16-byte aligned with a stride that is a
+    // multiple of 4, so a quad is one float4 load.  Each pass keeps several loads per thread
+    // in flight: the passes are bound by memory latency, not bandwidth.
+    const int j0 = r.j0, j1 = r.j1;
+    const int q0 = j0 >> 2, q1 = (j1 + 3) >> 2;
+    const float* zg = a.logits + ((int64_t)b * a.Hq + (int64_t)h * G) * a.logit_stride;
+    auto in_j = [&](int qi, int e) { const int j = 4 * qi + e; return qi < q1 && j >= j0 && j < j1; };
+
+    // 1. log-sum-exp over J of each query head, four heads and kUQ quads per thread at a time
+    for (int g0 = 0; g0 < G; g0 += 4) {
+        float m[4], sum[4];
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            m[gg] = -INFINITY;
+            sum[gg] = 0.f;
+        }
+        for (int qb = q0 + tid; qb < q1; qb += kUQ * kUT) {
+            float4 v[4][kUQ];
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const float4* z4 = (const float4*)(zg + (int64_t)min(g0 + gg, G - 1) * a.logit_stride);
+#pragma unroll
+                for (int u = 0; u < kUQ; ++u) {
+                    const int qi = qb + u * kUT;
+                    v[gg][u] = qi < q1 ? z4[qi] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                // log2 units: x = z * log2(e), so each exponential is one v_exp_f32
+                float x[kUQ][4];
+                float mb = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < kUQ; ++u) {
+                    const float vv[4] = {v[gg][u].x, v[gg][u].y, v[gg][u].z, v[gg][u].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[u][e] = in_j(qb + u * kUT, e) ? vv[e] * kLog2e : -INFINITY;
+                        mb = fmaxf(mb, x[u][e]);
+                    }
+                }
+                if (mb == -INFINITY) continue;
+                const float mn = fmaxf(m[gg], mb);
+                float add = 0.f;
+#pragma unroll
+                for (int u = 0; u < kUQ; ++u)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) add += exp2_hw(x[u][e] - mn);
+                sum[gg] = (m[gg] == -INFINITY ? 0.f : sum[gg] * exp2_hw(m[gg] - mn)) + add;
+                m[gg] = mn;
+            }
+        }
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            float2 p = make_float2(m[gg], sum[gg]);
+            for (int o = 32; o >= 1; o >>= 1)
+                p = lse2_merge(p, make_float2(__shfl_xor(p.x, o), __shfl_xor(p.y, o)));
+            if (lane == 0) sm.red[gg * kUW + w] = p;
+        }
+        __syncthreads();
+        if (tid < 4 && g0 + tid < G) {
+            float2 q = sm.red[tid * kUW];
+            for (int ww = 1; ww < kUW; ++ww) q = lse2_merge(q, sm.red[tid * kUW + ww]);
+            sm.lse[g0 + tid] = q.x + log2f(q.y);                 // log2 of sum over J
+        }
+        __syncthreads();
+    }
+
+    // 2. evidence keys for every position of J, and the histogram of their top 11 bits
+    for (int t = tid; t < kRadixBins; t += kUT) sm.hist[t] = 0u;
+    __syncthreads();
+    uint4* keys4 = (uint4*)(a.keys + (int64_t)unit * a.nchunk * kSelChunk);
+    for (int qb = q0 + tid; qb < q1; qb += kUQ * kUT) {
+        float f[kUQ][4];
+#pragma unroll
+        for (int u = 0; u < kUQ; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[u][e] = 0.f;
+        for (int g0 = 0; g0 < G; g0 += 4) {
+            float4 v[4][kUQ];
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                const float4* z4 = (const float4*)(zg + (int64_t)min(g0 + gg, G - 1) * a.logit_stride);
+#pragma unroll
+                for (int u = 0; u < kUQ; ++u) {
+                    const int qi = qb + u * kUT;
+                    v[gg][u] = qi < q1 ? z4[qi] : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) {
+                if (g0 + gg < G) {
+                    const float l = sm.lse[g0 + gg];
+#pragma unroll
+                    for (int u = 0; u < kUQ; ++u) {
+                        f[u][0] += exp2_hw(fmaf(v[gg][u].x, kLog2e, -l));
+                        f[u][1] += exp2_hw(fmaf(v[gg][u].y, kLog2e, -l));
+                        f[u][2] += exp2_hw(fmaf(v[gg][u].z, kLog2e, -l));
+                        f[u][3] += exp2_hw(fmaf(v[gg][u].w, kLog2e, -l));
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUQ; ++u) {
+            const int qi = qb + u * kUT;
+            if (qi >= q1) continue;
+            uint4 k;
+            k.x = __float_as_uint(f[u][0]);
+            k.y = __float_as_uint(f[u][1]);
+            k.z = __float_as_uint(f[u][2]);
+            k.w = __float_as_uint(f[u][3]);
+            keys4[qi] = k;
+            const uint32_t kk[4] = {k.x, k.y, k.z, k.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (in_j(qi, e)) atomicAdd(&sm.hist[kk[e] >> kShift[0]], 1u);
+        }
+    }
+    __syncthreads();
+
+    // 3. the key T of the k_sel-th largest evidence, digit by digit
+    uint32_t prefix = 0u;
+    int32_t k_rem = a.k_sel;
+    unit_resolve(sm, kShift[0], prefix, k_rem);
+    for (int pass = 1; pass < 3; ++pass) {
+        for (int t = tid; t < kRadixBins; t += kUT) sm.hist[t] = 0u;
+        __syncthreads();
+        const int hs = kShift[pass - 1];
+        const uint32_t want = prefix >> hs;
+        for (int qb = q0 + tid; qb < q1; qb += 2 * kUQ * kUT) {
+            uint4 kq[2 * kUQ];
+#pragma unroll
+            for (int u = 0; u < 2 * kUQ; ++u) {
+                const int qi = qb + u * kUT;
+                kq[u] = qi < q1 ? keys4[qi] : make_uint4(0u, 0u, 0u, 0u);
+            }
+#pragma unroll
+            for (int u = 0; u < 2 * kUQ; ++u) {
+                const uint32_t kk[4] = {kq[u].x, kq[u].y, kq[u].z, kq[u].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (in_j(qb + u * kUT, e) && (kk[e] >> hs) == want)
+                        atomicAdd(&sm.hist[(kk[e] >> kShift[pass]) & kDigitMask[pass]], 1u);
+            }
+        }
+        __syncthreads();
+        unit_resolve(sm, kShift[pass], prefix, k_rem);
+    }
+    const uint32_t T = prefix;
+
+    // 4. ordered emit: position j of J is kept when key > T, or key == T and fewer than k_rem
+    //    earlier positions have key == T; its slot after the sinks is (kept before j) =
+    //    greater_before + min(equal_before, k_rem).  Thread t takes kUQ consecutive quads of
+    //    each block, so thread order is position order for the block scan.
+    uint32_t gt_run = 0, eq_run = 0;
+    uint4 next[kUQ];                                       // the next block's keys, in flight
+#pragma unroll
+    for (int u = 0; u < kUQ; ++u) {
+        const int qi = q0 + tid * kUQ + u;
+        next[u] = qi < q1 ? keys4[qi] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    for (int qb = q0; qb < q1; qb += kUQ * kUT) {
+        const int qt = qb + tid * kUQ;
+        uint32_t kk[kUQ][4];
+        uint32_t packed = 0;                               // greater | equal << 16
+#pragma unroll
+        for (int u = 0; u < kUQ; ++u) {
+            kk[u][0] = next[u].x; kk[u][1] = next[u].y; kk[u][2] = next[u].z; kk[u][3] = next[u].w;
+        }
+#pragma unroll
+        for (int u = 0; u < kUQ; ++u) {
+            const int qi = qt + kUQ * kUT + u;
+            next[u] = qi < q1 ? keys4[qi] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kUQ; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool in = in_j(qt + u, e);
+                packed += (in && kk[u][e] > T) ? 1u : 0u;
+                packed += (in && kk[u][e] == T) ? (1u << 16) : 0u;
+            }
+        uint32_t tot;
+        const uint32_t excl = unit_scan(packed, sm, &tot);
+        uint32_t gt = gt_run + (excl & 0xffffu), eq = eq_run + (excl >> 16);
+#pragma unroll
+        for (int u = 0; u < kUQ; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (!in_j(qt + u, e)) continue;
+                const int j = 4 * (qt + u) + e;
+                if (kk[u][e] > T) {
+                    row[ns + gt + min(eq, (uint32_t)k_rem)] = j;
+                    ++gt;
+                } else if (kk[u][e] == T) {
+                    if (eq < (uint32_t)k_rem) row[ns + gt + eq] = j;
+                    ++eq;
+                }
+            }
+        gt_run += tot & 0xffffu;
+        eq_run += tot >> 16;
+    }
+}
+
 __global__ void __launch_bounds__(kThreads) sink_mask_kernel(MaskArgs a) {
     __shared__ float s_log_p0[1024];
     const int b = blockIdx.x, tid = threadIdx.x;
@@ -357,6 +665,10 @@ __global__ void __launch_bounds__(kThreads) sink_mask_kernel(MaskArgs a) {
 }  // namespace
 
 hipError_t launch_select(const SelArgs& a, hipStream_t s) {
+    if (a.unit_path) {
+        hipLaunchKernelGGL(select_unit_kernel, dim3(a.Hkv, a.B), dim3(kUT), 0, s, a);
+        return hipGetLastError();
+    }
     const dim3 blk(kThreads);
     const dim3 g_head(a.nchunk, a.Hq, a.B);
     const dim3 g_group(a.nchunk, a.Hkv, a.B);

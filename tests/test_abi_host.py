@@ -103,6 +103,8 @@ def test_select_and_mask_validation(L):
     assert sel(ks=-1, ws=ws) == B.SFI_E_INVALID
     assert sel(logits=None, ws=ws) == B.SFI_E_INVALID
     assert sel(stride=10, ws=ws) == B.SFI_E_INVALID
+    assert sel(stride=4002, ws=ws) == B.SFI_E_INVALID          # stride not a multiple of 4
+    assert sel(logits=FAKE + 4, ws=ws) == B.SFI_E_INVALID      # logits not 16-byte aligned
     mask = lambda frac, dd=d: L.sfi_sink_bypass_mask(ctypes.byref(dd), FAKE, 4000, FAKE,
                                                      ctypes.c_float(frac), None, None)
     assert mask(0.25) == B.SFI_E_INVALID                      # head_mask NULL

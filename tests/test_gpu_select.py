@@ -10,15 +10,25 @@ from gpu_util import DEV, compare_index_sets, gpu_select, round4, say
 pytestmark = pytest.mark.gpu
 
 
-def _run(orc, wl, lens, z, exact, n_sink=None, n_recent=None, k_sel=None, idx_stride=None):
+# The library runs the Selector either as one workgroup per (b, KV head) or as chunked
+# kernels, choosing from the descriptor (unit logit bytes against all logit bytes).  A
+# declared max_len far above the real lengths makes it choose the chunked kernels, so both
+# paths run the same cases.
+CHUNKED_MAX_LEN = 300000
+
+
+def _run(orc, wl, lens, z, exact, n_sink=None, n_recent=None, k_sel=None, idx_stride=None,
+         max_len=None):
     n_sink = wl.n_sink if n_sink is None else n_sink
     n_recent = wl.n_recent if n_recent is None else n_recent
     k_sel = wl.k_sel if k_sel is None else k_sel
     idx_stride = idx_stride or (n_sink + k_sel)
-    stride = z.shape[-1]
+    max_len = max_len or max(lens)
+    stride = round4(max(max_len, z.shape[-1]))
     lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    zd = z.to(DEV)
-    idx, n_idx = gpu_select(lens_dev, max(lens), wl, zd, stride, n_sink, n_recent, k_sel, idx_stride)
+    zd = torch.zeros((z.shape[0], z.shape[1], stride), device=DEV)
+    zd[:, :, :z.shape[-1]] = z.to(DEV)
+    idx, n_idx = gpu_select(lens_dev, max_len, wl, zd, stride, n_sink, n_recent, k_sel, idx_stride)
     eidx, en, f = orc.select(lens, wl.Hq, wl.Hkv, z, n_sink, n_recent, k_sel, idx_stride,
                              want_f=True)
     swaps = compare_index_sets(idx, n_idx, eidx, en, f, lens, n_sink, n_recent, k_sel, exact)
@@ -61,37 +71,45 @@ def test_select_planted_full_size(orc, name):
     _run(orc, wl, lens, z, exact=True)
 
 
-@pytest.mark.parametrize("seed", [1, 2])
-def test_select_random_logits_band(orc, seed):
+@pytest.mark.parametrize("seed,path", [(1, "unit"), (2, "unit"), (3, "chunked")])
+def test_select_random_logits_band(orc, seed, path):
     wl = W["ragged_paged_b16"]
     lens = [8192, 9000, 20000, 32768]
     g = torch.Generator().manual_seed(seed)
     z = (torch.randn((4, wl.Hq, 32768), generator=g) * 2.0)
-    _, _, swaps = _run(orc, wl, lens, z, exact=False)
+    _, _, swaps = _run(orc, wl, lens, z, exact=False,
+                       max_len=CHUNKED_MAX_LEN if path == "chunked" else None)
     say(f"    tie-band swaps: {swaps}")
 
 
-def test_select_edges(orc):
+@pytest.mark.parametrize("path", ["unit", "chunked"])
+def test_select_edges(orc, path):
     wl = synth.Workload("sel_edges", 1, 6, 8, 2, 128, "bf16", 5000, 4, 64, 100, 1)
     g = torch.Generator().manual_seed(3)
+    ml = CHUNKED_MAX_LEN if path == "chunked" else None
+    say(f"[select edges] {path}")
     # |J| = 0 (N - n_r <= n_s), N < n_s, |J| < k_sel (take all), |J| = k_sel, chunk edges
     lens = [60, 2, 150, 168, 4096 + 68, 8192 + 69]
     z = torch.randn((6, 8, round4(max(lens))), generator=g)
-    _run(orc, wl, lens, z, exact=True)
-    # k_sel = 0 keeps only sinks; n_sink = 0 keeps no sinks
-    _run(orc, wl, lens, z, exact=True, k_sel=0, idx_stride=8)
-    _run(orc, wl, lens, z, exact=True, n_sink=0, k_sel=37)
+    _run(orc, wl, lens, z, exact=True, max_len=ml)
+    # k_sel = 0 keeps only sinks; n_sink = 0 keeps no sinks; an odd n_sink starts J mid-quad
+    _run(orc, wl, lens, z, exact=True, k_sel=0, idx_stride=8, max_len=ml)
+    _run(orc, wl, lens, z, exact=True, n_sink=0, k_sel=37, max_len=ml)
+    _run(orc, wl, lens, z, exact=True, n_sink=3, n_recent=5, k_sel=101, max_len=ml)
     # many exact ties: quantised logits, lowest positions win
     zq = torch.randint(-2, 2, z.shape, generator=g).float()
-    _run(orc, wl, lens, zq, exact=True)
+    _run(orc, wl, lens, zq, exact=True, max_len=ml)
+    _run(orc, wl, lens, zq, exact=True, k_sel=1, idx_stride=5, max_len=ml)
 
 
-@pytest.mark.parametrize("G", [1, 16])
-def test_select_group_sizes(orc, G):
+@pytest.mark.parametrize("G,path", [(1, "unit"), (16, "unit"), (1, "chunked"), (16, "chunked"),
+                                    (5, "unit")])
+def test_select_group_sizes(orc, G, path):
     wl = synth.Workload(f"sel_G{G}", 1, 2, 2 * G, 2, 128, "bf16", 20000, 4, 256, 700, 1)
-    lens = [20000, 15000]
+    # short enough that one workgroup per unit is the estimated-faster path at every G
+    lens = [3000, 2500] if path == "unit" else [20000, 15000]
     z, _ = _planted(wl, lens, seed=G)
-    _run(orc, wl, lens, z, exact=True)
+    _run(orc, wl, lens, z, exact=True, max_len=CHUNKED_MAX_LEN if path == "chunked" else None)
 
 
 def test_select_deterministic():
