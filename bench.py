@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="sink_128k_b4")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layered", action="store_true",
+                    help="skip the layer-wise slow-step measurement (sequential vs pipelined)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB on the device a few times (a "
                          "known-size reference for rocprofv3 byte counters)")
@@ -154,6 +156,57 @@ def copy_calibration(mib: int, reps: int = 3):
     print(f"# copy calibration: {reps} copies of {mib} MiB", file=sys.stderr, flush=True)
 
 
+def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
+                      idx_stride, slots: int = 4, reps: int = 5):
+    """The slow step over every rotated layer: the per-layer calls one after another, against
+    sfi_slow_step_layers (Selector and mask of each layer on a second stream, a ring of
+    `slots` logits buffers and Selector workspaces).  Host clock around whole slow steps."""
+    L = len(descs)
+    R = min(slots, L)
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    d0 = [descs[li][0] for li in range(L)]
+    outs = [torch.empty((wl.B, wl.Hq, wl.d), device=dev) for _ in range(L)]
+    lses = [torch.empty((wl.B, wl.Hq), device=dev) for _ in range(L)]
+    sel_ws = [ws] + [torch.empty_like(ws) for _ in range(R - 1)]
+    dense_ws = torch.empty_like(ws)
+    events = [torch.cuda.Event() for _ in range(R)]
+    attn_ev, done_ev = torch.cuda.Event(), torch.cuda.Event()
+    has_mask = masks[0] is not None
+
+    def sequential():
+        for l in range(L):
+            s = l % R
+            B.sfi_dense_decode(d0[l], queries[l][0], outs[l], lses[l], logits[s], stride, dense_ws)
+            B.sfi_select(d0[l], logits[s], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[l],
+                         idx_stride, nidxs[l], sel_ws[s])
+            if has_mask:
+                B.sfi_sink_bypass_mask(d0[l], logits[s], stride, lses[l], wl.mask_frac, masks[l])
+
+    def pipelined():
+        B.sfi_slow_step_layers(d0, [queries[l][0] for l in range(L)], outs, lses, logits[:R],
+                               stride, sel_ws, dense_ws, wl.n_sink, wl.n_recent, wl.k_sel, idxs,
+                               idx_stride, nidxs, wl.mask_frac, masks if has_mask else None,
+                               stream, side, events, attn_ev, done_ev)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / reps
+
+    print("# layered slow step", file=sys.stderr, flush=True)
+    t_seq = timed(sequential)
+    t_pipe = timed(pipelined)
+    return {"layers": L, "slots": R, "sequential_us": round(t_seq, 1),
+            "pipelined_us": round(t_pipe, 1), "per_layer_sequential_us": round(t_seq / L, 2),
+            "per_layer_pipelined_us": round(t_pipe / L, 2)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -254,6 +307,11 @@ def main():
     mask_us = 1e3 * mean([e[2].elapsed_time(e[3]) for e in evs]) if wl.mask_frac > 0 else 0.0
     fast_us = 1e3 * mean([e[3].elapsed_time(e[4]) / (wl.cycle - 1) for e in evs])
 
+    layered = None
+    if L >= 2 and not args.no_layered:
+        layered = layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
+                                    masks, ws, idx_stride)
+
     lens0 = layers[0].len0_host
     n_idx_host = nidxs[0].cpu().tolist()
     mask_host = masks[0].cpu().tolist() if masks[0] is not None else None
@@ -304,6 +362,8 @@ def main():
                           "unit": "GB/s", "frac": round(fast_gbps / PEAK_HBM_GBS, 4),
                           "algorithmic_bytes": int(f_bytes)},
     }
+    if layered is not None:
+        result["slow_step_layers"] = layered
     if args.copy_calibration > 0:
         copy_calibration(args.copy_calibration)
     if not args.no_cpu_baseline:

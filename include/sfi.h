@@ -144,6 +144,38 @@ sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
                              float* out, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Slow step over the layers of a model with the Selector off the critical path.  SFI Sec. 4.1,
+ * layer-wise asynchronous execution: the primary stream runs the dense step of layer after
+ * layer while the Selector (and the sink mask) of each layer runs on a second stream, with a
+ * ring of n_slots maintenance slots and one completion barrier at the end.  For l = 0 ..
+ * n_layers - 1, with slot s = l % n_slots:
+ *   on `stream`:      if l >= n_slots, wait until slot s is free (slot_events[s]); then
+ *                     sfi_dense_decode(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride)
+ *   on `side_stream`: wait for that dense step (attn_event); sfi_select(&kv[l], logits[s], ...)
+ *                     into idx[l], n_idx[l] with workspace sel_ws[s]; when head_mask is not NULL,
+ *                     sfi_sink_bypass_mask(&kv[l], logits[s], lse[l], mask_frac, head_mask[l]);
+ *                     then record slot_events[s] (slot s free again).
+ * Finally `stream` waits for everything queued on `side_stream` (done_event), so work queued on
+ * `stream` after this call sees every layer's indices and masks.  Every result equals that of
+ * the per-layer calls made one after another.
+ * Arguments: kv, q, out, lse, idx, n_idx (and head_mask, or NULL) are host arrays of n_layers
+ * entries; logits and sel_ws are host arrays of n_slots entries; all the pointers in them are
+ * device buffers laid out as for the single calls (lse is required here).  dense_ws (at least
+ * SFI_OP_DENSE bytes for every layer) serves the dense steps one after another; each sel_ws[s]
+ * needs at least SFI_OP_SELECT bytes.  slot_events (n_slots), attn_event and done_event are
+ * HIP events created by the caller; the library only records them and waits on them.
+ * stream and side_stream must differ; calls that share buffers or events must not overlap.
+ * Every layer is validated before anything is queued; on an error nothing has been queued
+ * (SFI_E_HIP aside, which may leave earlier layers queued). */
+sfi_status sfi_slow_step_layers(
+    int32_t n_layers, const sfi_kv_desc* kv, const void* const* q, float* const* out,
+    float* const* lse, int32_t n_slots, float* const* logits, int64_t logit_stride,
+    void* const* sel_ws, size_t sel_ws_bytes, void* dense_ws, size_t dense_ws_bytes,
+    int32_t n_sink, int32_t n_recent, int32_t k_sel, int32_t* const* idx, int32_t idx_stride,
+    int32_t* const* n_idx, float mask_frac, uint8_t* const* head_mask,
+    hipStream_t stream, hipStream_t side_stream, hipEvent_t* slot_events,
+    hipEvent_t attn_event, hipEvent_t done_event);
+
 /* Workspace bytes needed by one call of `op` on this descriptor.  idx_stride and n_recent
  * (index capacity and recent window) are used by SFI_OP_SPARSE only; SFI_OP_DENSE and
  * SFI_OP_SELECT size from the descriptor (max_len) alone.  Returns 0 when the descriptor

@@ -20,7 +20,7 @@ SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE = 0, 1, 2
 
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
-            "sfi_workspace_bytes", "sfi_status_string")
+            "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_status_string")
 
 
 class SfiError(RuntimeError):
@@ -54,11 +54,15 @@ def lib():
         L.sfi_select.argtypes = [D, P, i64, i32, i32, i32, P, i32, P, P, ctypes.c_size_t, P]
         L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
         L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.sfi_slow_step_layers.argtypes = [i32, D, P, P, P, i32, P, i64, P, ctypes.c_size_t, P,
+                                           ctypes.c_size_t, i32, i32, i32, P, i32, P,
+                                           ctypes.c_float, P, P, P, P, P, P]
         L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
         L.sfi_workspace_bytes.restype = ctypes.c_size_t
         L.sfi_status_string.argtypes = [ctypes.c_int]
         L.sfi_status_string.restype = ctypes.c_char_p
-        for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode"):
+        for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
+                  "sfi_slow_step_layers"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -170,6 +174,42 @@ def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: in
                                    int(n_recent), _ptr(head_mask), _ptr(out), _ptr(lse),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "sfi_sparse_decode")
+
+
+def _ptr_array(tensors):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = None if t is None else t.data_ptr()
+    return arr
+
+
+def _event_handle(ev, stream):
+    """Raw HIP event of a torch.cuda.Event (torch creates it on the first record)."""
+    if not ev.cuda_event:
+        ev.record(stream)
+    return ev.cuda_event
+
+
+def sfi_slow_step_layers(descs, qs, outs, lses, logits_slots, logit_stride: int, sel_ws_slots,
+                         dense_ws, n_sink: int, n_recent: int, k_sel: int, idxs, idx_stride: int,
+                         n_idxs, mask_frac: float, head_masks, stream, side_stream, slot_events,
+                         attn_event, done_event):
+    """Layer-wise slow step (see include/sfi.h).  descs, qs, outs, lses, idxs, n_idxs,
+    head_masks: one per layer (head_masks may be None); logits_slots, sel_ws_slots and
+    slot_events: one per ring slot; streams are torch.cuda.Stream, events torch.cuda.Event."""
+    n, r = len(descs), len(logits_slots)
+    darr = (sfi_kv_desc * n)(*[d.c for d in descs])
+    evs = (ctypes.c_void_p * r)(*[_event_handle(e, side_stream) for e in slot_events])
+    sel_bytes = min(w.numel() * w.element_size() for w in sel_ws_slots)
+    _check(lib().sfi_slow_step_layers(
+        n, darr, _ptr_array(qs), _ptr_array(outs), _ptr_array(lses), r, _ptr_array(logits_slots),
+        int(logit_stride), _ptr_array(sel_ws_slots), sel_bytes, _ptr(dense_ws),
+        dense_ws.numel() * dense_ws.element_size(), int(n_sink), int(n_recent), int(k_sel),
+        _ptr_array(idxs), int(idx_stride), _ptr_array(n_idxs), float(mask_frac),
+        None if head_masks is None else _ptr_array(head_masks),
+        ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(side_stream.cuda_stream), evs,
+        ctypes.c_void_p(_event_handle(attn_event, stream)),
+        ctypes.c_void_p(_event_handle(done_event, side_stream))), "sfi_slow_step_layers")
 
 
 def workspace(desc: KVDesc, idx_stride: int = 1, n_recent: int = 0, device="cuda"):

@@ -192,11 +192,10 @@ void fill_plan_args(const AttnPlan& p, void* ws, AttnArgs* a) {
     a->part = (float*)ws;
 }
 
-}  // namespace
+// ---- validation + argument packing, shared by the single calls and the layered slow step --
 
-SFI_EXPORT sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
-                                       float* logits, int64_t logit_stride,
-                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+sfi_status prep_dense(const sfi_kv_desc* kv, const void* q, float* out, float* lse, float* logits,
+                      int64_t logit_stride, void* ws, size_t ws_bytes, AttnArgs* a) {
     sfi_status st = check_desc(kv, true);
     if (st != SFI_OK) return st;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return SFI_E_INVALID;
@@ -207,17 +206,84 @@ SFI_EXPORT sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, flo
     if (st != SFI_OK) return st;
     st = check_ws(ws, ws_bytes, plan.bytes);
     if (st != SFI_OK) return st;
-    AttnArgs a;
-    fill_cache_args(*kv, &a);
-    fill_plan_args(plan, ws, &a);
-    a.q = q;
-    a.out = out;
-    a.lse = lse;
-    a.logits = logits;
-    a.logit_stride = logit_stride;
+    fill_cache_args(*kv, a);
+    fill_plan_args(plan, ws, a);
+    a->q = q;
+    a->out = out;
+    a->lse = lse;
+    a->logits = logits;
+    a->logit_stride = logit_stride;
+    return SFI_OK;
+}
+
+sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                       int32_t n_sink, int32_t n_recent, int32_t k_sel, int32_t* idx,
+                       int32_t idx_stride, int32_t* n_idx, void* ws, size_t ws_bytes, SelArgs* a) {
+    sfi_status st = check_desc(kv, false);
+    if (st != SFI_OK) return st;
+    if (!logits || !idx || !n_idx || logit_stride < kv->max_len || logit_stride < 1) return SFI_E_INVALID;
+    if (logit_stride % 4 != 0 || !aligned(logits, 16)) return SFI_E_INVALID;
+    if (n_sink < 0 || n_recent < 0 || k_sel < 0) return SFI_E_INVALID;
+    if ((int64_t)idx_stride < (int64_t)n_sink + k_sel || idx_stride < 1) return SFI_E_INVALID;
+    SelPlan plan;
+    plan_select(*kv, &plan);
+    st = check_ws(ws, ws_bytes, plan.bytes);
+    if (st != SFI_OK) return st;
+    unsigned char* base = (unsigned char*)ws;
+    a->logits = logits;
+    a->logit_stride = logit_stride;
+    a->len = kv->len;
+    a->B = kv->batch;
+    a->Hq = kv->num_q_heads;
+    a->Hkv = kv->num_kv_heads;
+    a->G = kv->num_q_heads / kv->num_kv_heads;
+    a->n_sink = n_sink;
+    a->n_recent = n_recent;
+    a->k_sel = k_sel;
+    a->nchunk = plan.nchunk;
+    a->idx = idx;
+    a->idx_stride = idx_stride;
+    a->n_idx = n_idx;
+    a->lse_part = (float2*)(base + plan.off_lse);
+    a->keys = (uint32_t*)(base + plan.off_keys);
+    a->hist = (uint32_t*)(base + plan.off_hist);
+    a->state = (int32_t*)(base + plan.off_state);
+    a->counts = (uint32_t*)(base + plan.off_counts);
+    a->unit_path = select_unit_path(*kv) ? 1 : 0;
+    return SFI_OK;
+}
+
+sfi_status prep_mask(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                     const float* lse, float frac, uint8_t* head_mask, MaskArgs* a) {
+    sfi_status st = check_desc(kv, false);
+    if (st != SFI_OK) return st;
+    if (!logits || !lse || !head_mask || logit_stride < 1) return SFI_E_INVALID;
+    if (!(frac >= 0.f && frac <= 1.f)) return SFI_E_INVALID;
+    if (kv->num_q_heads > 1024) return SFI_E_UNSUPPORTED;
+    a->logits = logits;
+    a->logit_stride = logit_stride;
+    a->lse = lse;
+    a->B = kv->batch;
+    a->Hq = kv->num_q_heads;
+    a->n_mask = (int32_t)floor((double)frac * kv->num_q_heads);
+    a->head_mask = head_mask;
+    return SFI_OK;
+}
+
+sfi_status launch_dense(const sfi_kv_desc* kv, const AttnArgs& a, hipStream_t stream) {
     const hipError_t e = launch_attention(a, kv->batch, kv->head_dim, kv->dtype == SFI_BF16,
                                           kv->block_table != nullptr, false, stream);
     return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+}  // namespace
+
+SFI_EXPORT sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
+                                       float* logits, int64_t logit_stride,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+    AttnArgs a;
+    const sfi_status st = prep_dense(kv, q, out, lse, logits, logit_stride, ws, ws_bytes, &a);
+    return st == SFI_OK ? launch_dense(kv, a, stream) : st;
 }
 
 SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
@@ -254,60 +320,76 @@ SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int
                                  int32_t n_sink, int32_t n_recent, int32_t k_sel,
                                  int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                                  void* ws, size_t ws_bytes, hipStream_t stream) {
-    sfi_status st = check_desc(kv, false);
-    if (st != SFI_OK) return st;
-    if (!logits || !idx || !n_idx || logit_stride < kv->max_len || logit_stride < 1) return SFI_E_INVALID;
-    if (logit_stride % 4 != 0 || !aligned(logits, 16)) return SFI_E_INVALID;
-    if (n_sink < 0 || n_recent < 0 || k_sel < 0) return SFI_E_INVALID;
-    if ((int64_t)idx_stride < (int64_t)n_sink + k_sel || idx_stride < 1) return SFI_E_INVALID;
-    SelPlan plan;
-    plan_select(*kv, &plan);
-    st = check_ws(ws, ws_bytes, plan.bytes);
-    if (st != SFI_OK) return st;
-    unsigned char* base = (unsigned char*)ws;
     SelArgs a;
-    a.logits = logits;
-    a.logit_stride = logit_stride;
-    a.len = kv->len;
-    a.B = kv->batch;
-    a.Hq = kv->num_q_heads;
-    a.Hkv = kv->num_kv_heads;
-    a.G = kv->num_q_heads / kv->num_kv_heads;
-    a.n_sink = n_sink;
-    a.n_recent = n_recent;
-    a.k_sel = k_sel;
-    a.nchunk = plan.nchunk;
-    a.idx = idx;
-    a.idx_stride = idx_stride;
-    a.n_idx = n_idx;
-    a.lse_part = (float2*)(base + plan.off_lse);
-    a.keys = (uint32_t*)(base + plan.off_keys);
-    a.hist = (uint32_t*)(base + plan.off_hist);
-    a.state = (int32_t*)(base + plan.off_state);
-    a.counts = (uint32_t*)(base + plan.off_counts);
-    a.unit_path = select_unit_path(*kv) ? 1 : 0;
-    const hipError_t e = launch_select(a, stream);
-    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+    const sfi_status st = prep_select(kv, logits, logit_stride, n_sink, n_recent, k_sel, idx,
+                                      idx_stride, n_idx, ws, ws_bytes, &a);
+    if (st != SFI_OK) return st;
+    return launch_select(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
 }
 
 SFI_EXPORT sfi_status sfi_sink_bypass_mask(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
                                            const float* lse, float frac, uint8_t* head_mask,
                                            hipStream_t stream) {
-    sfi_status st = check_desc(kv, false);
-    if (st != SFI_OK) return st;
-    if (!logits || !lse || !head_mask || logit_stride < 1) return SFI_E_INVALID;
-    if (!(frac >= 0.f && frac <= 1.f)) return SFI_E_INVALID;
-    if (kv->num_q_heads > 1024) return SFI_E_UNSUPPORTED;
     MaskArgs a;
-    a.logits = logits;
-    a.logit_stride = logit_stride;
-    a.lse = lse;
-    a.B = kv->batch;
-    a.Hq = kv->num_q_heads;
-    a.n_mask = (int32_t)floor((double)frac * kv->num_q_heads);
-    a.head_mask = head_mask;
-    const hipError_t e = launch_sink_mask(a, stream);
-    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+    const sfi_status st = prep_mask(kv, logits, logit_stride, lse, frac, head_mask, &a);
+    if (st != SFI_OK) return st;
+    return launch_sink_mask(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+SFI_EXPORT sfi_status sfi_slow_step_layers(
+        int32_t n_layers, const sfi_kv_desc* kv, const void* const* q, float* const* out,
+        float* const* lse, int32_t n_slots, float* const* logits, int64_t logit_stride,
+        void* const* sel_ws, size_t sel_ws_bytes, void* dense_ws, size_t dense_ws_bytes,
+        int32_t n_sink, int32_t n_recent, int32_t k_sel, int32_t* const* idx, int32_t idx_stride,
+        int32_t* const* n_idx, float mask_frac, uint8_t* const* head_mask,
+        hipStream_t stream, hipStream_t side_stream, hipEvent_t* slot_events,
+        hipEvent_t attn_event, hipEvent_t done_event) {
+    if (n_layers < 1 || n_slots < 1 || !kv || !q || !out || !lse || !logits || !sel_ws || !idx ||
+        !n_idx || !slot_events || !attn_event || !done_event || stream == side_stream)
+        return SFI_E_INVALID;
+    for (int s = 0; s < n_slots; ++s)
+        if (!slot_events[s]) return SFI_E_INVALID;
+    // Every layer's arguments pass validation before anything is queued.
+    for (int l = 0; l < n_layers; ++l) {
+        const int s = l % n_slots;
+        AttnArgs da;
+        SelArgs sa;
+        MaskArgs ma;
+        if (!lse[l]) return SFI_E_INVALID;
+        sfi_status st = prep_dense(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride,
+                                   dense_ws, dense_ws_bytes, &da);
+        if (st == SFI_OK && !logits[s]) st = SFI_E_INVALID;
+        if (st == SFI_OK)
+            st = prep_select(&kv[l], logits[s], logit_stride, n_sink, n_recent, k_sel, idx[l],
+                             idx_stride, n_idx[l], sel_ws[s], sel_ws_bytes, &sa);
+        if (st == SFI_OK && head_mask)
+            st = prep_mask(&kv[l], logits[s], logit_stride, lse[l], mask_frac, head_mask[l], &ma);
+        if (st != SFI_OK) return st;
+    }
+    for (int l = 0; l < n_layers; ++l) {
+        const int s = l % n_slots;
+        AttnArgs da;
+        SelArgs sa;
+        MaskArgs ma;
+        prep_dense(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride, dense_ws, dense_ws_bytes, &da);
+        prep_select(&kv[l], logits[s], logit_stride, n_sink, n_recent, k_sel, idx[l], idx_stride,
+                    n_idx[l], sel_ws[s], sel_ws_bytes, &sa);
+        // the slot's logits and Selector workspace are free once layer l - n_slots is selected
+        if (l >= n_slots && hipStreamWaitEvent(stream, slot_events[s], 0) != hipSuccess) return SFI_E_HIP;
+        if (launch_dense(&kv[l], da, stream) != SFI_OK) return SFI_E_HIP;
+        if (hipEventRecord(attn_event, stream) != hipSuccess) return SFI_E_HIP;
+        if (hipStreamWaitEvent(side_stream, attn_event, 0) != hipSuccess) return SFI_E_HIP;
+        if (launch_select(sa, side_stream) != hipSuccess) return SFI_E_HIP;
+        if (head_mask) {
+            prep_mask(&kv[l], logits[s], logit_stride, lse[l], mask_frac, head_mask[l], &ma);
+            if (launch_sink_mask(ma, side_stream) != hipSuccess) return SFI_E_HIP;
+        }
+        if (hipEventRecord(slot_events[s], side_stream) != hipSuccess) return SFI_E_HIP;
+    }
+    // one completion barrier: later work on `stream` sees every layer's indices and masks
+    if (hipEventRecord(done_event, side_stream) != hipSuccess) return SFI_E_HIP;
+    if (hipStreamWaitEvent(stream, done_event, 0) != hipSuccess) return SFI_E_HIP;
+    return SFI_OK;
 }
 
 SFI_EXPORT size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,

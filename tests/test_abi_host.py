@@ -153,3 +153,34 @@ def test_workspace_never_shrinks_as_length_grows(L):
                 need = L.sfi_workspace_bytes(ctypes.byref(_desc(**kw)), op, istride, nrec)
                 assert need >= prev > 0 or (prev == 0 and need > 0), (op, paged, n, need, prev)
                 prev = need
+
+
+def test_slow_step_layers_validation(L):
+    """Every layer is validated before anything is queued; the fake pointers below are never
+    dereferenced because each call fails validation."""
+    n = 3
+    descs = (B.sfi_kv_desc * n)(*[_desc() for _ in range(n)])
+    ptrs = lambda k, v=FAKE: (ctypes.c_void_p * k)(*([v] * k))
+    dws = L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_DENSE, 0, 0)
+    sws = L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_SELECT, 0, 0)
+
+    def call(n_layers=n, descs=descs, n_slots=2, stride=4000, dws_b=dws, sws_b=sws, side=FAKE + 16,
+             lse=None, ks=2048, events=None, head_mask=None, frac=0.25):
+        return L.sfi_slow_step_layers(
+            n_layers, descs, ptrs(n), ptrs(n), lse if lse is not None else ptrs(n), n_slots,
+            ptrs(2), stride, ptrs(2), sws_b, FAKE, dws_b, 4, 256, ks, ptrs(n), 2052, ptrs(n),
+            ctypes.c_float(frac), head_mask, FAKE, side, events if events is not None else ptrs(2),
+            FAKE, FAKE)
+
+    assert call(n_layers=0) == B.SFI_E_INVALID
+    assert call(n_slots=0) == B.SFI_E_INVALID
+    assert call(side=FAKE) == B.SFI_E_INVALID                 # the two streams must differ
+    assert call(events=(ctypes.c_void_p * 2)(FAKE, None)) == B.SFI_E_INVALID
+    assert call(lse=(ctypes.c_void_p * n)(FAKE, None, FAKE)) == B.SFI_E_INVALID
+    assert call(dws_b=dws - 1) == B.SFI_E_WORKSPACE
+    assert call(sws_b=sws - 1) == B.SFI_E_WORKSPACE
+    assert call(stride=4002) == B.SFI_E_INVALID               # logits stride not a multiple of 4
+    assert call(ks=5000) == B.SFI_E_INVALID                   # idx_stride < n_sink + k_sel
+    assert call(head_mask=ptrs(n), frac=1.5) == B.SFI_E_INVALID
+    bad = (B.sfi_kv_desc * n)(_desc(), _desc(), _desc(head_dim=96))
+    assert call(descs=bad) == B.SFI_E_UNSUPPORTED             # the last layer is checked too

@@ -1,0 +1,84 @@
+"""The layer-wise slow step (sfi_slow_step_layers) against the per-layer calls in sequence.
+
+Five layers share two ring slots, so every slot is reused; the Selector and the mask run on a
+second stream.  Every output must equal the sequential result bit for bit (the kernels are
+deterministic), and a fast step queued on the primary stream right after the call must see
+the last layer's indices (the completion barrier).
+"""
+import pytest
+import torch
+
+from sparse_kv_attention_dense_amd import binding as B
+from sparse_kv_attention_dense_amd import synth
+
+from gpu_util import DEV, desc_for, round4, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,n_slots", [("gqa8_512k", 2), ("ragged_paged_b16", 2),
+                                          ("gqa4_32k", 1)])
+def test_layered_slow_step_matches_sequential(name, n_slots):
+    base = synth.WORKLOADS[name]
+    wl = base.scaled(7001, B=min(base.B, 3), len_lo=3000 if base.len_lo else None)
+    n_layers = 5
+    say(f"[layers] {wl.name} layers={n_layers} slots={n_slots}")
+    lays = [synth.make_layer(wl, li, device=DEV) for li in range(n_layers)]
+    lens = lays[0].len_at(0).to(DEV)
+    max_len = lays[0].max_len_at(0)
+    descs = [desc_for(lay, lens, max_len) for lay in lays]
+    qs = [synth.make_query(wl, li, 0, device=DEV, u=lay.u) for li, lay in enumerate(lays)]
+    stride = round4(max_len)
+    istride = wl.n_sink + wl.k_sel
+    frac = 0.25
+    dense_ws = B.workspace(descs[0], idx_stride=istride, n_recent=wl.n_recent, device=DEV)
+
+    def bufs():
+        return dict(
+            out=[torch.full((wl.B, wl.Hq, wl.d), float("nan"), device=DEV) for _ in lays],
+            lse=[torch.full((wl.B, wl.Hq), float("nan"), device=DEV) for _ in lays],
+            idx=[torch.full((wl.B, wl.Hkv, istride), -3, dtype=torch.int32, device=DEV) for _ in lays],
+            n_idx=[torch.full((wl.B, wl.Hkv), -3, dtype=torch.int32, device=DEV) for _ in lays],
+            mask=[torch.full((wl.B, wl.Hq), 7, dtype=torch.uint8, device=DEV) for _ in lays],
+            logits=[torch.empty((wl.B, wl.Hq, stride), device=DEV) for _ in range(n_slots)],
+            sel_ws=[B.workspace(descs[0], idx_stride=istride, n_recent=wl.n_recent, device=DEV)
+                    for _ in range(n_slots)])
+
+    # sequential reference: the single calls, one layer after another
+    ref = bufs()
+    for l in range(n_layers):
+        s = l % n_slots
+        B.sfi_dense_decode(descs[l], qs[l], ref["out"][l], ref["lse"][l], ref["logits"][s], stride,
+                           dense_ws)
+        B.sfi_select(descs[l], ref["logits"][s], stride, wl.n_sink, wl.n_recent, wl.k_sel,
+                     ref["idx"][l], istride, ref["n_idx"][l], ref["sel_ws"][s])
+        B.sfi_sink_bypass_mask(descs[l], ref["logits"][s], stride, ref["lse"][l], frac,
+                               ref["mask"][l])
+    torch.cuda.synchronize()
+
+    got = bufs()
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    events = [torch.cuda.Event() for _ in range(n_slots)]
+    B.sfi_slow_step_layers(descs, qs, got["out"], got["lse"], got["logits"], stride,
+                           got["sel_ws"], dense_ws, wl.n_sink, wl.n_recent, wl.k_sel, got["idx"],
+                           istride, got["n_idx"], frac, got["mask"], stream, side, events,
+                           torch.cuda.Event(), torch.cuda.Event())
+    # queued on the primary stream right after: must see the last layer's indices and mask
+    lens1 = lays[0].len_at(1).to(DEV)
+    d1 = desc_for(lays[-1], lens1, lays[0].max_len_at(1))
+    q1 = synth.make_query(wl, n_layers - 1, 1, device=DEV, u=lays[-1].u)
+    fast_got = torch.empty((wl.B, wl.Hq, wl.d), device=DEV)
+    B.sfi_sparse_decode(d1, q1, got["idx"][-1], istride, got["n_idx"][-1], wl.n_recent,
+                        got["mask"][-1], fast_got, None, dense_ws)
+    torch.cuda.synchronize()
+    fast_ref = torch.empty_like(fast_got)
+    B.sfi_sparse_decode(d1, q1, ref["idx"][-1], istride, ref["n_idx"][-1], wl.n_recent,
+                        ref["mask"][-1], fast_ref, None, dense_ws)
+    torch.cuda.synchronize()
+
+    for key in ("out", "lse", "idx", "n_idx", "mask"):
+        for l in range(n_layers):
+            assert torch.equal(got[key][l], ref[key][l]), f"{key} differs at layer {l}"
+    assert torch.equal(fast_got, fast_ref)
+    say(f"    {n_layers} layers identical to the sequential calls; fast step after the call too")
