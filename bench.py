@@ -156,6 +156,40 @@ def copy_calibration(mib: int, reps: int = 3):
     print(f"# copy calibration: {reps} copies of {mib} MiB", file=sys.stderr, flush=True)
 
 
+def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
+                      idx_stride, L, gamma: float = 0.65):
+    """Fast steps with inline group routing (sfi_sparse_decode_routed), the slow step's lse as
+    the cached normaliser: per layer one slow step, then the cycle's fast steps timed as one
+    block.  Reports µs per fast step and the fraction of (sequence, KV head) groups bypassed."""
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    out = torch.empty((wl.B, wl.Hq, wl.d), device=dev)
+    lse_f = torch.empty((wl.B, wl.Hq), device=dev)
+    slow_lse = torch.empty((wl.B, wl.Hq), device=dev)
+    routed = torch.zeros((wl.B, wl.Hkv), dtype=torch.uint8, device=dev)
+    frac_sum, times = 0.0, []
+    print("# routed fast steps", file=sys.stderr, flush=True)
+    for li in list(range(L)) * 2:
+        d = descs[li]
+        B.sfi_dense_decode(d[0], queries[li][0], out, slow_lse, logits[li], stride, ws)
+        B.sfi_select(d[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
+                     idx_stride, nidxs[li], ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(1, wl.cycle):
+            B.sfi_sparse_decode_routed(d[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
+                                       wl.n_recent, masks[li], slow_lse, gamma, routed, out,
+                                       lse_f, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / (wl.cycle - 1))
+        frac_sum += float(routed.float().mean())
+    n = 2 * L
+    return {"gamma": gamma, "fast_us": round(sum(times) / n, 2),
+            "groups_routed_frac": round(frac_sum / n, 4),
+            "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
+
+
 def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
                       idx_stride, slots: int = 4, reps: int = 5):
     """The slow step over every rotated layer: the per-layer calls one after another, against
@@ -307,6 +341,11 @@ def main():
     mask_us = 1e3 * mean([e[2].elapsed_time(e[3]) for e in evs]) if wl.mask_frac > 0 else 0.0
     fast_us = 1e3 * mean([e[3].elapsed_time(e[4]) / (wl.cycle - 1) for e in evs])
 
+    routed = None
+    if wl.sink:
+        routed = routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
+                                   masks, ws, idx_stride, L)
+
     layered = None
     if L >= 2 and not args.no_layered:
         layered = layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
@@ -362,6 +401,8 @@ def main():
                           "unit": "GB/s", "frac": round(fast_gbps / PEAK_HBM_GBS, 4),
                           "algorithmic_bytes": int(f_bytes)},
     }
+    if routed is not None:
+        result["routed_fast"] = routed
     if layered is not None:
         result["slow_step_layers"] = layered
     if args.copy_calibration > 0:

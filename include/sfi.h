@@ -11,6 +11,10 @@
  *     (SinkRouter Sec. 4.2, target regime and execution policy)          -> sfi_sink_bypass_mask
  *   - a fast step attends only to sink + selected + recent positions
  *     (SFI Sec. 1, the compact cache of fast steps)                       -> sfi_sparse_decode
+ *   - the same with SinkRouter's inline group routing (SinkRouter Sec. 4.2-4.3)
+ *                                                                        -> sfi_sparse_decode_routed
+ *   - the slow step over a model's layers with the Selector on a second stream
+ *     (SFI Sec. 4.1, layer-wise asynchronous execution)                  -> sfi_slow_step_layers
  *
  * Conventions shared by every call
  *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
@@ -143,6 +147,27 @@ sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
                              int32_t n_recent, const uint8_t* head_mask,
                              float* out, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sparse decode step with inline group routing.  SinkRouter Sec. 4 (decide per KV group,
+ * before loading the group's history, whether it is in the sink-dominant regime, and if so
+ * write the zero surrogate instead of attending), Sec. 4.2 "Target regime" (token-0 mass at
+ * least gamma; the page uses 0.65) and Sec. 4.3 "Inline routing before historical KV loading".
+ * The page's routing score (its Eq. 11) is not in the text; this call reads it as the token-0
+ * logit of the current query against a normaliser cached from the last slow step:
+ *   z0_i = (q_i . k_{h,0}) / sqrt(d),   head i is sink-dominant  <=>  z0_i - route_lse_i >= log(gamma)
+ * (exp(z0_i - route_lse_i) estimates head i's token-0 attention mass without scanning the
+ * history), and KV group h of sequence b is bypassed when all its G heads are sink-dominant.
+ * A bypassed group reads no key or value row and its heads output exactly 0 (lse -inf).  Other
+ * groups run exactly as sfi_sparse_decode (head_mask still zeroes its heads).
+ * route_lse (device) fp32 [B][Hq], e.g. the lse output of sfi_dense_decode at the slow step;
+ * 0 < gamma <= 1; routed (device) uint8 [B][Hkv] or NULL receives 1 for bypassed groups (0 for
+ * len[b] == 0).  Every other argument as for sfi_sparse_decode, with the same workspace. */
+sfi_status sfi_sparse_decode_routed(const sfi_kv_desc* kv, const void* q,
+                                    const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+                                    int32_t n_recent, const uint8_t* head_mask,
+                                    const float* route_lse, float gamma, uint8_t* routed,
+                                    float* out, float* lse,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Slow step over the layers of a model with the Selector off the critical path.  SFI Sec. 4.1,
  * layer-wise asynchronous execution: the primary stream runs the dense step of layer after

@@ -53,8 +53,11 @@ def lib():
         L.orc_sparse.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int32, P,
                                  ctypes.c_int32, P, P, P]
         L.orc_sink_mask.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_double, P]
+        L.orc_sparse_routed.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int32, P,
+                                        ctypes.c_int32, P, P, ctypes.c_double, P, P, P, P]
         L.orc_threads.argtypes = []
-        for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask, L.orc_threads):
+        for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask, L.orc_threads,
+                  L.orc_sparse_routed):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -168,6 +171,35 @@ def sparse(cache: Cache, q, idx, n_idx, n_recent: int, head_mask=None):
                           n_recent, _ptr(hm) if hm is not None else None, _ptr(out), _ptr(lse))
     assert rc == 0
     return out, lse
+
+
+def sparse_routed(cache: Cache, q, idx, n_idx, n_recent: int, route_lse, gamma: float,
+                  head_mask=None):
+    """Fast step with group routing.  Returns (out [B][Hq][d], lse [B][Hq], routed uint8
+    [B][Hkv], margin [B][Hkv]) in float64; margin is the group's smallest
+    z0 - route_lse - log(gamma) (routed exactly when it is >= 0)."""
+    import math
+    qh = _host_bytes(q)
+    idx = np.ascontiguousarray(np.asarray(idx.cpu() if torch.is_tensor(idx) else idx,
+                                          dtype=np.int32))
+    n_idx = np.ascontiguousarray(np.asarray(n_idx.cpu() if torch.is_tensor(n_idx) else n_idx,
+                                            dtype=np.int32))
+    rl = np.ascontiguousarray(np.asarray(route_lse.cpu() if torch.is_tensor(route_lse)
+                                         else route_lse, dtype=np.float64))
+    hm = None
+    if head_mask is not None:
+        hm = np.ascontiguousarray(np.asarray(
+            head_mask.cpu() if torch.is_tensor(head_mask) else head_mask, dtype=np.uint8))
+    out = np.zeros((cache.B, cache.Hq, cache.d), np.float64)
+    lse = np.zeros((cache.B, cache.Hq), np.float64)
+    routed = np.zeros((cache.B, cache.Hkv), np.uint8)
+    margin = np.zeros((cache.B, cache.Hkv), np.float64)
+    s = cache._struct()
+    rc = lib().orc_sparse_routed(ctypes.byref(s), _ptr(qh), _ptr(idx), idx.shape[-1], _ptr(n_idx),
+                                 n_recent, _ptr(hm) if hm is not None else None, _ptr(rl),
+                                 math.log(gamma), _ptr(margin), _ptr(routed), _ptr(out), _ptr(lse))
+    assert rc == 0
+    return out, lse, routed, margin
 
 
 def sink_mask(z0, lse, frac: float):

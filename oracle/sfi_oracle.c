@@ -220,6 +220,44 @@ int orc_sparse(const orc_cache* c, const void* q, const int32_t* idx, int32_t id
     return 0;
 }
 
+/* ---- sparse fast step with group routing ------------------------------------------------ */
+
+int orc_sparse_routed(const orc_cache* c, const void* q, const int32_t* idx, int32_t idx_stride,
+                      const int32_t* n_idx, int32_t n_recent, const uint8_t* head_mask,
+                      const double* route_lse, double log_gamma, double* margin,
+                      uint8_t* routed, double* out, double* lse) {
+    const int G = c->Hq / c->Hkv;
+    const int units = c->B * c->Hkv;
+    uint8_t* mask = (uint8_t*)malloc((size_t)c->B * c->Hq);
+    double* qi = (double*)malloc(sizeof(double) * c->d);
+    for (int u = 0; u < units; ++u) {
+        int b = u / c->Hkv, h = u % c->Hkv;
+        int all = c->len[b] > 0;
+        double worst = INFINITY;
+        for (int g = 0; g < G; ++g) {
+            int i = h * G + g;
+            double m = -INFINITY;
+            if (c->len[b] > 0) {
+                load_query(c, q, b, i, qi);
+                m = logit_of(c, qi, b, h, 0) - route_lse[b * c->Hq + i] - log_gamma;
+            }
+            /* head i is sink-dominant when its estimated token-0 mass reaches gamma */
+            if (!(m >= 0.0)) all = 0;
+            worst = m < worst ? m : worst;
+        }
+        routed[u] = (uint8_t)all;
+        if (margin) margin[u] = worst;
+        for (int g = 0; g < G; ++g) {
+            int i = h * G + g;
+            mask[b * c->Hq + i] = (uint8_t)(all || (head_mask && head_mask[b * c->Hq + i]));
+        }
+    }
+    int rc = orc_sparse(c, q, idx, idx_stride, n_idx, n_recent, mask, out, lse);
+    free(qi);
+    free(mask);
+    return rc;
+}
+
 /* ---- sink-bypass mask ---------------------------------------------------------------- */
 
 int orc_sink_mask(int32_t B, int32_t Hq, const double* z0, const double* lse, double frac,

@@ -68,6 +68,19 @@ int orc_sparse(const orc_cache* c, const void* q, const int32_t* idx, int32_t id
                const int32_t* n_idx, int32_t n_recent, const uint8_t* head_mask,
                double* out, double* lse);
 
+/* Sparse decode with group routing (SinkRouter, Sec. 4.2-4.3: decide per KV group, before
+ * attending, whether the group is sink-dominant; a bypassed group outputs the zero surrogate).
+ * The page's routing score is not in the text; the reading implemented here: head i of group h
+ * is sink-dominant when z0_i - route_lse[b*Hq+i] >= log_gamma, with z0_i = (q_i . k_{h,0})/sqrt(d)
+ * (exp of the left side estimates the head's token-0 mass); the group is bypassed (routed[u] =
+ * 1, u = b*Hkv + h) when all its heads are.  margin[u] (optional) receives the smallest
+ * z0_i - route_lse_i - log_gamma of the group (-inf when len[b] == 0), so callers can tell
+ * decisions that rounding could flip.  Outputs as orc_sparse with bypassed heads masked. */
+int orc_sparse_routed(const orc_cache* c, const void* q, const int32_t* idx, int32_t idx_stride,
+                      const int32_t* n_idx, int32_t n_recent, const uint8_t* head_mask,
+                      const double* route_lse, double log_gamma, double* margin,
+                      uint8_t* routed, double* out, double* lse);
+
 /* Sink-bypass mask (SinkRouter, Sec. 4.2 "Target regime": heads whose token-0 attention
  * mass is large are treated as idle).  p0[b,i] = exp(z0[b*Hq+i] - lse[b*Hq+i]); per b the
  * floor(frac*Hq) heads with the largest p0 are masked, ties to the lower head index. */

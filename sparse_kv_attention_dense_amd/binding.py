@@ -20,7 +20,8 @@ SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE = 0, 1, 2
 
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
-            "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_status_string")
+            "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_workspace_bytes",
+            "sfi_status_string")
 
 
 class SfiError(RuntimeError):
@@ -54,6 +55,8 @@ def lib():
         L.sfi_select.argtypes = [D, P, i64, i32, i32, i32, P, i32, P, P, ctypes.c_size_t, P]
         L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
         L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.sfi_sparse_decode_routed.argtypes = [D, P, P, i32, P, i32, P, P, ctypes.c_float, P,
+                                               P, P, P, ctypes.c_size_t, P]
         L.sfi_slow_step_layers.argtypes = [i32, D, P, P, P, i32, P, i64, P, ctypes.c_size_t, P,
                                            ctypes.c_size_t, i32, i32, i32, P, i32, P,
                                            ctypes.c_float, P, P, P, P, P, P]
@@ -62,7 +65,7 @@ def lib():
         L.sfi_status_string.argtypes = [ctypes.c_int]
         L.sfi_status_string.restype = ctypes.c_char_p
         for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
-                  "sfi_slow_step_layers"):
+                  "sfi_sparse_decode_routed", "sfi_slow_step_layers"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -174,6 +177,17 @@ def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: in
                                    int(n_recent), _ptr(head_mask), _ptr(out), _ptr(lse),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "sfi_sparse_decode")
+
+
+def sfi_sparse_decode_routed(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int,
+                             head_mask, route_lse, gamma: float, routed, out, lse, ws,
+                             stream=None):
+    _check(lib().sfi_sparse_decode_routed(desc.ref, _ptr(q), _ptr(idx), int(idx_stride),
+                                          _ptr(n_idx), int(n_recent), _ptr(head_mask),
+                                          _ptr(route_lse), float(gamma), _ptr(routed), _ptr(out),
+                                          _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream)),
+           "sfi_sparse_decode_routed")
 
 
 def _ptr_array(tensors):

@@ -286,11 +286,13 @@ SFI_EXPORT sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, flo
     return st == SFI_OK ? launch_dense(kv, a, stream) : st;
 }
 
-SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
-                                        const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
-                                        int32_t n_recent, const uint8_t* head_mask,
-                                        float* out, float* lse,
-                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+sfi_status sparse_impl(const sfi_kv_desc* kv, const void* q, const int32_t* idx,
+                       int32_t idx_stride, const int32_t* n_idx, int32_t n_recent,
+                       const uint8_t* head_mask, const float* route_lse, float gamma,
+                       uint8_t* routed, float* out, float* lse, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
     sfi_status st = check_desc(kv, true);
     if (st != SFI_OK) return st;
     if (!q || !out || !idx || !n_idx || !aligned(q, 16) || !aligned(out, 16)) return SFI_E_INVALID;
@@ -311,9 +313,34 @@ SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
     a.n_idx = n_idx;
     a.n_recent = n_recent;
     a.head_mask = head_mask;
+    a.route_lse = route_lse;
+    a.route_log_gamma = route_lse ? (float)log((double)gamma) : 0.f;
+    a.routed = routed;
     const hipError_t e = launch_attention(a, kv->batch, kv->head_dim, kv->dtype == SFI_BF16,
                                           kv->block_table != nullptr, true, stream);
     return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+}  // namespace
+
+SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
+                                        const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+                                        int32_t n_recent, const uint8_t* head_mask,
+                                        float* out, float* lse,
+                                        void* ws, size_t ws_bytes, hipStream_t stream) {
+    return sparse_impl(kv, q, idx, idx_stride, n_idx, n_recent, head_mask, nullptr, 1.f, nullptr,
+                       out, lse, ws, ws_bytes, stream);
+}
+
+SFI_EXPORT sfi_status sfi_sparse_decode_routed(const sfi_kv_desc* kv, const void* q,
+                                               const int32_t* idx, int32_t idx_stride,
+                                               const int32_t* n_idx, int32_t n_recent,
+                                               const uint8_t* head_mask, const float* route_lse,
+                                               float gamma, uint8_t* routed, float* out, float* lse,
+                                               void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!route_lse || !(gamma > 0.f && gamma <= 1.f)) return SFI_E_INVALID;
+    return sparse_impl(kv, q, idx, idx_stride, n_idx, n_recent, head_mask, route_lse, gamma, routed,
+                       out, lse, ws, ws_bytes, stream);
 }
 
 SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,

@@ -143,6 +143,86 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 constexpr int kFill = 8;             // sparse row-table slots per thread per batch
 
+// Group routing of the fast step (SinkRouter Sec. 4.2-4.3): every query head g of KV group h
+// is scored against the group's token-0 key, z0_g = (q_g . k_{h,0}) / sqrt(d), and the group is
+// sink-dominant when every head satisfies z0_g - route_lse_g >= log(gamma), i.e. its token-0
+// attention mass estimated with the cached normaliser reaches gamma.  Thread (g, c) holds 8
+// elements of q_g and of k_{h,0}; route_load issues those loads at kernel entry so their latency
+// overlaps the other prologue loads, route_decide reduces the D/8 threads of each head by
+// shuffles and returns the same answer to every thread of the workgroup.
+template <bool BF, int D>
+struct RoutePre {
+    using V = typename std::conditional<BF, u32x4, f32x4>::type;
+    V q[BF ? 1 : 2], k[BF ? 1 : 2];
+    float lse;                                         // the head's cached normaliser
+};
+
+// Stage 0 (kernel entry): the query elements, and on a contiguous cache with rows the token-0
+// key elements.  Stage 1 (once len_b > 0 is known): on a paged cache the token-0 key through
+// the block table (its first entry is only defined for a non-empty sequence).
+template <bool BF, int D, bool PAGED>
+__device__ void route_load(const AttnArgs& a, int b, int h, int hq0, int unit, int stage,
+                           RoutePre<BF, D>& r) {
+    constexpr int kPer = 8, kLanes = D / kPer;
+    const int g = threadIdx.x / kLanes, c = threadIdx.x % kLanes;
+    if (g >= a.G) return;
+    const bool load_k = PAGED ? stage == 1 : (stage == 0 && a.n_cap > 0);
+    if (stage == 0) {
+        r.lse = a.route_lse[b * a.Hq + hq0 + g];
+        const int64_t qoff = ((int64_t)b * a.Hq + hq0 + g) * D + c * kPer;
+        if constexpr (BF) {
+            r.q[0] = *(const u32x4*)((const uint16_t*)a.q + qoff);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) r.q[e] = *(const f32x4*)((const float*)a.q + qoff + 4 * e);
+        }
+    }
+    if (!load_k) return;
+    uint32_t row;                                      // the row of position 0
+    if constexpr (PAGED)
+        row = ((uint32_t)a.block_table[(int64_t)b * a.max_blocks] * (uint32_t)a.Hkv + (uint32_t)h)
+              << a.block_shift;
+    else
+        row = (uint32_t)((int64_t)unit * a.n_cap);
+    if constexpr (BF) {
+        r.k[0] = *(const u32x4*)((const uint16_t*)a.k + (uint64_t)row * D + c * kPer);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            r.k[e] = *(const f32x4*)((const float*)a.k + (uint64_t)row * D + c * kPer + 4 * e);
+    }
+}
+
+template <bool BF, int D>
+__device__ bool route_decide(const AttnArgs& a, int b, int hq0, const RoutePre<BF, D>& r, float* sh) {
+    constexpr int kPer = 8, kLanes = D / kPer;
+    const int tid = threadIdx.x, G = a.G;
+    const int g = tid / kLanes, c = tid % kLanes;
+    float part = 0.f;
+    if (g < G) {
+        if constexpr (BF) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                part += __uint_as_float(r.q[0][e] << 16) * __uint_as_float(r.k[0][e] << 16);
+                part += __uint_as_float(r.q[0][e] & 0xffff0000u) * __uint_as_float(r.k[0][e] & 0xffff0000u);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part += r.q[e][i] * r.k[e][i];
+        }
+    }
+    for (int o = kLanes / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    if (g < G && c == 0)
+        sh[g] = (part * a.scale - r.lse >= a.route_log_gamma) ? 1.f : 0.f;
+    __syncthreads();
+    bool all = true;
+    for (int gg = 0; gg < G; ++gg) all &= sh[gg] != 0.f;
+    __syncthreads();
+    return all;
+}
+
 template <bool BF, int D, bool PAGED, bool SPARSE>
 struct Cfg {
     static constexpr int kVRow = D * 2 + 16;                       // staged bf16 row, bytes
@@ -209,6 +289,10 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             idx_pre[u] = (u < nfill && slot < a.idx_stride) ? irow[slot] : 0;
         }
     }
+    RoutePre<BF, D> route;
+    if constexpr (SPARSE) {
+        if (a.route_lse) route_load<BF, D, PAGED>(a, b, h, hq0, unit, 0, route);
+    }
     const int len_b = a.len[b];
 
     // ---- slot range of this workgroup -------------------------------------------------
@@ -221,6 +305,13 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         if (a.head_mask) {
             all_masked = true;
             for (int g = 0; g < G; ++g) all_masked &= a.head_mask[b * a.Hq + hq0 + g] != 0;
+        }
+        if (a.route_lse) {
+            // inline group routing before any key or value row of the group is read
+            if (PAGED && len_b > 0) route_load<BF, D, PAGED>(a, b, h, hq0, unit, 1, route);
+            const bool sink = len_b > 0 && route_decide<BF, D>(a, b, hq0, route, (float*)raw);
+            if (a.routed && split == 0 && tid == 0) a.routed[unit] = sink ? 1 : 0;
+            all_masked |= sink;
         }
     }
     int s1 = min(n_tot, s0 + a.split_len);

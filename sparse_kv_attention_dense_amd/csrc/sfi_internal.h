@@ -41,6 +41,9 @@ struct AttnArgs {
     const int32_t* n_idx;
     int32_t n_recent;
     const uint8_t* head_mask;        // sparse only, may be null
+    const float* route_lse;          // sparse only, may be null: per-head cached lse for routing
+    float route_log_gamma;           // log(gamma) of the routing threshold
+    uint8_t* routed;                 // may be null: [B][Hkv] routing decisions
     float* out;
     float* lse;                      // may be null
     float* part;                     // [units][nsplit][rec]: acc [G][d], then (m, l) [G]

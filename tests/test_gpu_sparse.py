@@ -3,9 +3,10 @@ import numpy as np
 import pytest
 import torch
 
+from sparse_kv_attention_dense_amd import binding as B
 from sparse_kv_attention_dense_amd import synth
 
-from gpu_util import (DEV, assert_close_out, assert_close_rel, gpu_dense, gpu_sparse,
+from gpu_util import (DEV, assert_close_out, assert_close_rel, desc_for, gpu_dense, gpu_sparse,
                       oracle_cache, say, tolerances)
 
 pytestmark = pytest.mark.gpu
@@ -140,3 +141,95 @@ def test_sparse_deterministic():
     a = gpu_sparse(lay, q, 2, idx.to(DEV), n_idx.to(DEV))
     b = gpu_sparse(lay, q, 2, idx.to(DEV), n_idx.to(DEV))
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def _routed_gpu(lay, q, t, idx, n_idx, route_lse, gamma, head_mask=None):
+    wl = lay.wl
+    lens = lay.len_at(t).to(DEV)
+    desc = desc_for(lay, lens, lay.max_len_at(t))
+    out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), device=DEV)
+    lse = torch.full((wl.B, wl.Hq), float("nan"), device=DEV)
+    routed = torch.full((wl.B, wl.Hkv), 9, dtype=torch.uint8, device=DEV)
+    ws = B.workspace(desc, idx_stride=idx.shape[-1], n_recent=wl.n_recent, device=DEV)
+    B.sfi_sparse_decode_routed(desc, q, idx.to(DEV), idx.shape[-1], n_idx.to(DEV), wl.n_recent,
+                               None if head_mask is None else head_mask.to(DEV),
+                               route_lse.to(DEV).float(), gamma, routed, out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse, routed
+
+
+@pytest.mark.parametrize("name", ["sink_128k_b4", "gqa8_512k", "ragged_paged_b16", "tiny_2k_f32"])
+def test_sparse_routed_planted_decisions(orc, name):
+    """Normalisers set head by head so the estimated token-0 mass is 0.9 or 0.3: every decision
+    is far from the threshold and must match the oracle; outputs within tolerance."""
+    base = W[name]
+    wl = base if name == "tiny_2k_f32" else base.scaled(9001, B=min(base.B, 2),
+                                                         len_lo=4000 if base.len_lo else None)
+    say(f"[sparse routed planted] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    t = 2
+    q = synth.make_query(wl, 0, t, device=DEV, u=lay.u)
+    idx, n_idx = synth.synthetic_index_set(lay, "spans", seed=31)
+    lens = [n + t for n in lay.len0_host]
+    c = oracle_cache(orc, lay, lens)
+    _, _, z = orc.dense(c, q)
+    g = torch.Generator().manual_seed(7)
+    # whole groups at 0.9 half of the time, otherwise a random mix of 0.9 and 0.3
+    grp = (torch.rand((wl.B, wl.Hkv), generator=g) < 0.5).repeat_interleave(wl.G, dim=1)
+    mix = torch.rand((wl.B, wl.Hq), generator=g) < 0.5
+    target = torch.where(grp | mix, 0.9, 0.3).double()
+    route_lse = torch.tensor(z[:, :, 0]) - torch.log(target)
+    out, lse, routed = _routed_gpu(lay, q, t, idx, n_idx, route_lse, 0.65)
+    eo, el, er, margin = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, route_lse, 0.65)
+    assert (np.abs(margin) > 0.3).all()
+    assert (routed.cpu().numpy() == er).all(), "routing decisions differ"
+    say(f"    groups routed: {int(er.sum())} of {er.size}")
+    tol = tolerances(wl)
+    assert_close_out(out.cpu().numpy(), eo, tol["out"])
+    assert_close_rel(lse.cpu().numpy(), el, tol["rel"], "lse")
+
+
+def test_sparse_routed_with_slow_step_lse(orc):
+    """The intended use: the slow step's lse as the cached normaliser and gamma = 0.65 on the
+    sink-dominated workload.  Decisions must agree wherever rounding cannot flip them; outputs
+    are checked against the oracle given the GPU's decisions."""
+    wl = W["sink_128k_b4"].scaled(12001, B=2)
+    lay = synth.make_layer(wl, 0, device=DEV)
+    q0 = synth.make_query(wl, 0, 0, device=DEV, u=lay.u)
+    _, lse0, _, _ = gpu_dense(lay, q0, 0, logits=False)
+    t = 3
+    q = synth.make_query(wl, 0, t, device=DEV, u=lay.u)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=32)
+    out, lse, routed = _routed_gpu(lay, q, t, idx, n_idx, lse0.cpu().double(), 0.65)
+    lens = [n + t for n in lay.len0_host]
+    c = oracle_cache(orc, lay, lens)
+    _, _, er, margin = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, lse0.cpu().double(), 0.65)
+    rg = routed.cpu().numpy()
+    clear = np.abs(margin) > 1e-3
+    assert (rg[clear] == er[clear]).all()
+    say(f"    groups routed: {int(rg.sum())} of {rg.size}; near-threshold: {int((~clear).sum())}")
+    hm = torch.tensor(rg).repeat_interleave(wl.G, dim=1).to(torch.uint8)
+    eo, el = orc.sparse(c, q, idx, n_idx, wl.n_recent, hm)
+    assert_close_out(out.cpu().numpy(), eo, 1e-2)
+    assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_sparse_routed_edges(paged):
+    """Lengths 0, 1 and 300: routing everything yields zeros (and no routing for the empty
+    sequence); routing nothing is bit-identical to sfi_sparse_decode."""
+    wl = synth.Workload("route_edges", 8300, 3, 16, 4, 128, "bf16", 300, 4, 32, 40, 2, sink=True,
+                        paged=paged, block_size=16)
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[0, 1, 300])
+    q = synth.make_query(wl, 0, 0, device=DEV, u=lay.u, n_for_sink=300)
+    idx, n_idx = synth.synthetic_index_set(lay, "spans", seed=33)
+    low = torch.full((wl.B, wl.Hq), -1e6, dtype=torch.float64)
+    high = torch.full((wl.B, wl.Hq), 1e6, dtype=torch.float64)
+    out, lse, routed = _routed_gpu(lay, q, 0, idx, n_idx, low, 0.65)
+    assert routed.cpu().tolist() == [[0] * 4, [1] * 4, [1] * 4]
+    assert (out == 0).all() and torch.isneginf(lse).all()
+    out, lse, routed = _routed_gpu(lay, q, 0, idx, n_idx, high, 0.65)
+    assert (routed == 0).all()
+    ref_o, ref_l = gpu_sparse(lay, q, 0, idx.to(DEV), n_idx.to(DEV))
+    assert torch.equal(out.nan_to_num(7.0), ref_o.nan_to_num(7.0))
+    assert torch.equal(lse, ref_l)

@@ -354,3 +354,62 @@ def test_sink_mask_library_sort(orc):
             assert (m[b] == exp).all()
     with pytest.raises(ValueError):
         orc.sink_mask(z0, lse, 1.5)
+
+
+# ------------------------------------------------------------------------- group routing
+
+def _routed_case(orc, seed=15):
+    wl = synth.Workload("route_tiny", 300 + seed, 3, 8, 2, 32, "bf16", 400, 4, 20, 60, 3,
+                        sink=True)
+    lay = synth.make_layer(wl, 0, lens=[400, 250, 0])
+    q = synth.make_query(wl, 0, 1, u=lay.u, n_for_sink=400)
+    lens = [401, 251, 0]
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=seed)
+    c = orc.Cache(lay.k, lay.v, torch.tensor(lens, dtype=torch.int32), wl.Hq)
+    return wl, lay, q, lens, idx, n_idx, c
+
+
+def test_routed_decision_matches_dense_position0_logit(orc):
+    """The routing decision equals the rule applied to the dense oracle's logit at position 0,
+    for a normaliser chosen head by head to land well clear of the threshold."""
+    wl, lay, q, lens, idx, n_idx, c = _routed_case(orc)
+    _, _, z = orc.dense(c, q)
+    g = torch.Generator().manual_seed(1)
+    gamma = 0.65
+    # each head's estimated token-0 mass is set to 0.9 (sink) or 0.3 (not) by its normaliser
+    target = torch.where(torch.rand((wl.B, wl.Hq), generator=g) < 0.7, 0.9, 0.3).double()
+    z0 = torch.tensor(np.nan_to_num(z[:, :, 0], nan=0.0))
+    route_lse = z0 - torch.log(target)
+    out, lse, routed, margin = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, route_lse, gamma)
+    G = wl.G
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            heads = target[b, h * G:(h + 1) * G]
+            expect = lens[b] > 0 and bool((heads >= gamma).all())
+            assert routed[b, h] == expect
+            if lens[b] > 0:
+                assert abs(margin[b, h] - float(torch.log(heads / gamma).min())) < 1e-9
+            if expect:
+                assert (out[b, h * G:(h + 1) * G] == 0).all()
+                assert np.isneginf(lse[b, h * G:(h + 1) * G]).all()
+
+
+def test_routed_reduces_to_sparse_and_to_zeros(orc):
+    wl, lay, q, lens, idx, n_idx, c = _routed_case(orc, seed=16)
+    base_o, base_l = orc.sparse(c, q, idx, n_idx, wl.n_recent)
+    # a normaliser far above every token-0 logit routes nothing: exactly the plain fast step
+    hi = torch.full((wl.B, wl.Hq), 1e6, dtype=torch.float64)
+    o, l, routed, _ = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, hi, 0.65)
+    assert routed.sum() == 0
+    assert np.array_equal(o, base_o) and np.array_equal(l, base_l)
+    # far below: every group with history is bypassed, all its heads output exact zeros
+    lo = torch.full((wl.B, wl.Hq), -1e6, dtype=torch.float64)
+    o, l, routed, _ = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, lo, 0.65)
+    assert routed.tolist() == [[1, 1], [1, 1], [0, 0]]           # len 0: nothing to route
+    assert (o == 0).all() and np.isneginf(l[:2]).all()
+    # a head mask still zeroes its heads in groups that are not routed
+    hm = torch.zeros((wl.B, wl.Hq), dtype=torch.uint8)
+    hm[0, 1] = 1
+    o, _, _, _ = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, hi, 0.65, head_mask=hm)
+    assert (o[0, 1] == 0).all()
+    assert np.array_equal(o[0, 0], base_o[0, 0])
