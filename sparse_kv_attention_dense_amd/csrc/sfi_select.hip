@@ -22,7 +22,12 @@
 namespace sfi {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kPerThread = kSelChunk / kThreads;     // 16 positions per thread
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 constexpr int kShift[3] = {21, 10, 0};
 constexpr uint32_t kDigitMask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
 
@@ -105,20 +110,34 @@ __global__ void __launch_bounds__(kThreads) lse_kernel(SelArgs a) {
     const Range r = j_range(a, b);
     const int lo = r.j0 + c * kSelChunk;
     const int hi = min(r.j1, lo + kSelChunk);
+    // 16-byte loads from the multiple of 4 at or below lo (rows are 16-byte aligned and their
+    // stride is a multiple of 4, so every load stays inside the row); positions outside
+    // [lo, hi) count as -inf.
     const float* z = a.logits + ((int64_t)b * a.Hq + i) * a.logit_stride;
-    float v[kPerThread];
+    const int base = lo & ~3;
+    const int n4 = hi > lo ? (hi - base + 3) >> 2 : 0;
+    constexpr int kV4 = kPerThread / 4 + 1;             // covers kSelChunk + 3 positions
+    f32x4 v[kV4];
     float m = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) {
-        const int j = lo + k * kThreads + tid;
-        v[k] = j < hi ? z[j] : -INFINITY;
-        m = fmaxf(m, v[k]);
+    for (int k = 0; k < kV4; ++k) {
+        const int f = k * kThreads + tid;
+        v[k] = f < n4 ? *(const f32x4*)(z + base + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = base + 4 * f + e;
+            if (f >= n4 || j < lo || j >= hi) v[k][e] = -INFINITY;
+            m = fmaxf(m, v[k][e]);
+        }
     }
     m = block_max(m, sh);
     float s = 0.f;
     if (m != -INFINITY) {
+        const float m2 = m * kLog2e;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) s += expf(v[k] - m);
+        for (int k = 0; k < kV4; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s += exp2_hw(fmaf(v[k][e], kLog2e, -m2));
     }
     s = block_sum(s, sh);
     if (tid == 0) a.lse_part[((int64_t)b * a.Hq + i) * a.nchunk + c] = make_float2(m, s);
@@ -144,10 +163,10 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
         float S = 0.f;
         for (int k = lane; k < a.nchunk; k += 64) {
             const float2 e = lp[k];
-            if (e.x != -INFINITY) S += expf(e.x - M) * e.y;
+            if (e.x != -INFINITY) S += exp2_hw((e.x - M) * kLog2e) * e.y;
         }
         S = wave_sum(S);
-        if (lane == 0) s_lse[g] = M + logf(S);
+        if (lane == 0) s_lse[g] = (M + logf(S)) * kLog2e;   // log2 units
     }
     __syncthreads();
     uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
@@ -157,7 +176,8 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
         const int j = lo + k * kThreads + tid;
         if (j < hi) {
             float f = 0.f;
-            for (int g = 0; g < G; ++g) f += expf(zb[(int64_t)g * a.logit_stride + j] - s_lse[g]);
+            for (int g = 0; g < G; ++g)
+                f += exp2_hw(fmaf(zb[(int64_t)g * a.logit_stride + j], kLog2e, -s_lse[g]));
             const uint32_t key = __float_as_uint(f);
             keys[j - lo] = key;
             atomicAdd(&lh[key >> kShift[0]], 1u);
@@ -302,13 +322,22 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
     const uint32_t kr = take_all ? 0u : (uint32_t)k_rem;
     const uint32_t base = (uint32_t)ns + gtb + min(eqb, kr);
     // this thread's 16 consecutive positions
-    const uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
+    // this thread's 16 consecutive keys as four 16-byte loads (a chunk holds kSelChunk keys
+    // in the workspace whatever cnt is, so the loads stay inside it)
+    const u32x4* keys4 =
+        (const u32x4*)(a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk) + tid * (kPerThread / 4);
     uint32_t kv[kPerThread];
+#pragma unroll
+    for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
+        const u32x4 x = tid * kPerThread < cnt ? keys4[k4] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[4 * k4 + e] = x[e];
+    }
     uint32_t my_eq = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int t = tid * kPerThread + k;
-        kv[k] = t < cnt ? keys[t] : 0u;
+        if (t >= cnt) kv[k] = 0u;
         my_eq += (t < cnt && !take_all && kv[k] == T) ? 1u : 0u;
     }
     uint32_t eq_rank = eqb + block_exclusive_scan(my_eq, sh);
@@ -350,9 +379,6 @@ __device__ __forceinline__ float2 lse_merge(float2 p, float2 q) {
     if (m == -INFINITY) return make_float2(m, 0.f);
     return make_float2(m, p.y * expf(p.x - m) + q.y * expf(q.x - m));
 }
-
-constexpr float kLog2e = 1.4426950408889634f;
-__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // lse_merge in log2 units
 __device__ __forceinline__ float2 lse2_merge(float2 p, float2 q) {
