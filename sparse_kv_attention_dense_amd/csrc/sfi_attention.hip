@@ -229,6 +229,9 @@ struct Cfg {
     static constexpr int kVStage = BF ? kWaves * kTile * kVRow : 0;
     static constexpr int kRed = kWaves * kMaxG * (D + 2) * 4;      // cross-wave merge
     static constexpr int kRaw = kVStage > kRed ? kVStage : kRed;
+    // dense: per-wavefront staging of fp32 logits, 64 (head, tile) rows of 32 positions
+    static constexpr int kZRows = 64;
+    static constexpr int kZWave = SPARSE ? 4 : kZRows * kTile;     // floats per wavefront
     static constexpr int kNQ = BF ? D / 32 : D / 16;               // Q / K fragments per row
     static constexpr int kNV = BF ? D / 16 : 2 * 4 * (D / 16);     // V registers per tile
     static constexpr int kRPI = 1024 / (2 * D);                    // bf16 V rows per wave load
@@ -249,6 +252,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     using C = Cfg<BF, D, PAGED, SPARSE>;
     using Regs = TileRegs<BF, D, PAGED, SPARSE>;
     __shared__ __attribute__((aligned(16))) unsigned char raw[C::kRaw];
+    __shared__ __attribute__((aligned(16))) float zstage[kWaves * C::kZWave];
     // Row table in dynamic LDS, sized by the host for this launch's split length:
     //   sparse: one row per slot, then one "attend" flag byte per slot;
     //   dense paged: one base row per KV block the split touches.
@@ -432,10 +436,49 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     unsigned char* vstage = raw + w * kTile * C::kVRow;
-    float* logit_row = nullptr;
+
+    // Tiles of this wavefront.  Logits in runs: with G <= 4 the wavefront takes a contiguous
+    // quarter of the split, stages its logits in LDS and writes kZRows / G tiles at a time,
+    // runs of at least 2 KB per head instead of 128 B per tile (HBM3E turns short writes
+    // mixed into the read stream into lost read bandwidth; on MI355X the dense step at 128K
+    // drops by about 11 us).  With larger groups the runs would be 1 KB or shorter, which
+    // measured slower than the per-tile writes, so those take tiles w, w + 4, ... and write
+    // each tile's logits directly, as does the sparse kernel (no logits).
+    // The tile order depends on G only, so out and lse do not depend on whether logits are
+    // requested.
+    const int zF = C::kZRows / G;                     // tiles per staged run
+    const bool quarters = !SPARSE && zF >= 16;
+    const bool staged = quarters && a.logits;
+    const int ntiles = (nslots + kTile - 1) / kTile;
+    const int tpw = (ntiles + kWaves - 1) / kWaves;
+    const int t_begin = quarters ? min(ntiles, w * tpw) : w;
+    const int t_end = quarters ? min(ntiles, t_begin + tpw) : ntiles;
+    const int t_step = quarters ? 1 : kWaves;
+    float* zst = staged ? zstage + w * C::kZWave : nullptr;
+    float* logit_row = nullptr;                       // unstaged logits of head n16
     if constexpr (!SPARSE) {
-        if (a.logits && n16 < G) logit_row = a.logits + ((int64_t)b * a.Hq + hq0 + n16) * a.logit_stride;
+        if (a.logits && !staged && n16 < G) logit_row = a.logits + ((int64_t)b * a.Hq + hq0 + n16) * a.logit_stride;
     }
+    // Writes the staged logits of tiles [t_first, t_first + nt) of this wavefront.
+    auto flush_logits = [&](int t_first, int nt) {
+        wave_lds_sync();
+        const int p_first = s0 + t_first * kTile;
+        const int n4 = nt * (kTile / 4);              // float4 per head
+        for (int e = lane; e < G * n4; e += 64) {
+            const int g = e / n4, o4 = e - g * n4;
+            const int p = p_first + 4 * o4;
+            const f32x4 z = *(const f32x4*)(zst + g * zF * kTile + 4 * o4);
+            float* dst = a.logits + ((int64_t)b * a.Hq + hq0 + g) * a.logit_stride + p;
+            if (p + 3 < s1) {
+                *(f32x4*)dst = z;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (p + i < s1) dst[i] = z[i];
+            }
+        }
+        wave_lds_sync();                              // the run is read before it is reused
+    };
 
     // ---- tile loads (issued one tile ahead of the math) ------------------------------------
     auto issue = [&](Regs& r, int tile) {
@@ -513,7 +556,15 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
                 tmax = fmaxf(tmax, sv[st][i]);
             }
         if constexpr (!SPARSE) {
-            if (logit_row) {
+            if (zst) {
+                const int slot = (tile - t_begin) % zF;
+                if (n16 < G) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st)
+                        *(f32x4*)(zst + n16 * zF * kTile + slot * kTile + 16 * st + 4 * q4) = S[st] * a.scale;
+                }
+                if (slot == zF - 1 || tile + 1 == t_end) flush_logits(tile - slot, slot + 1);
+            } else if (logit_row) {
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     const int p0 = sb + 16 * st + 4 * q4;
@@ -582,26 +633,25 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         }
     };
 
-    // ---- main loop: wavefront w takes tiles w, w+4, ...; loads run one tile ahead ----------
+    // ---- main loop over [t_begin, t_end) in steps of t_step; loads run one tile ahead --------
     // The next tile's loads are issued unconditionally (past the end the wavefront re-reads
     // its current tile, which hits in cache), so the number of loads younger than the
     // current tile's is the same on every path and the wait before the math only covers
     // the current tile.
-    const int ntiles = (nslots + kTile - 1) / kTile;
-    if (w < ntiles) {
+    if (t_begin < t_end) {
         Regs ra, rb;
-        int t = w;
+        int t = t_begin;
         issue(ra, t);
         for (;;) {
-            int tn = t + kWaves;
-            issue(rb, tn < ntiles ? tn : t);
+            int tn = t + t_step;
+            issue(rb, tn < t_end ? tn : t);
             compute(ra, t);
-            if (tn >= ntiles) break;
+            if (tn >= t_end) break;
             t = tn;
-            tn = t + kWaves;
-            issue(ra, tn < ntiles ? tn : t);
+            tn = t + t_step;
+            issue(ra, tn < t_end ? tn : t);
             compute(rb, t);
-            if (tn >= ntiles) break;
+            if (tn >= t_end) break;
             t = tn;
         }
     }
