@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layered", action="store_true",
                     help="skip the layer-wise slow-step measurement (sequential vs pipelined)")
+    ap.add_argument("--no-routed", action="store_true",
+                    help="skip the routed fast-step measurement on sink-dominated workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB on the device a few times (a "
                          "known-size reference for rocprofv3 byte counters)")
@@ -342,7 +344,7 @@ def main():
     fast_us = 1e3 * mean([e[3].elapsed_time(e[4]) / (wl.cycle - 1) for e in evs])
 
     routed = None
-    if wl.sink:
+    if wl.sink and not args.no_routed:
         routed = routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
                                    masks, ws, idx_stride, L)
 
