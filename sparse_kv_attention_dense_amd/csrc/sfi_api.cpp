@@ -144,7 +144,8 @@ bool select_unit_path(const sfi_kv_desc& kv) {
 
 struct SelPlan {
     int nchunk = 0;
-    size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0, bytes = 0;
+    size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0;
+    size_t off_cand = 0, off_cand_n = 0, bytes = 0;
 };
 
 void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
@@ -154,9 +155,11 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     size_t off = 0;
     p->off_lse = off;    off += align_up(B * Hq * nc * sizeof(float2));
     p->off_keys = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
-    p->off_hist = off;   off += align_up(B * Hkv * 3 * kRadixBins * sizeof(uint32_t));
+    p->off_hist = off;   off += align_up(B * Hkv * kSelHistBins * sizeof(uint32_t));
     p->off_state = off;  off += align_up(B * Hkv * 4 * sizeof(int32_t));
     p->off_counts = off; off += align_up(B * Hkv * nc * 2 * sizeof(uint32_t));
+    p->off_cand = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
+    p->off_cand_n = off; off += align_up(B * Hkv * nc * sizeof(uint32_t));
     p->bytes = off;
 }
 
@@ -249,6 +252,8 @@ sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit
     a->hist = (uint32_t*)(base + plan.off_hist);
     a->state = (int32_t*)(base + plan.off_state);
     a->counts = (uint32_t*)(base + plan.off_counts);
+    a->cand = (uint32_t*)(base + plan.off_cand);
+    a->cand_n = (uint32_t*)(base + plan.off_cand_n);
     a->unit_path = select_unit_path(*kv) ? 1 : 0;
     return SFI_OK;
 }

@@ -55,7 +55,8 @@ hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool pag
 // ---- selector -------------------------------------------------------------------------
 
 constexpr int kSelChunk = 4096;      // positions of J per workgroup
-constexpr int kRadixBins = 2048;
+constexpr int kRadixBins = 2048;     // LDS histogram bins of the one-launch path
+constexpr int kSelHistBins = 4096;   // digit-0 bins of the chunked path
 
 struct SelArgs {
     const float* logits;
@@ -69,9 +70,11 @@ struct SelArgs {
     int32_t* n_idx;
     float2* lse_part;                // [B][Hq][nchunk]
     uint32_t* keys;                  // [B][Hkv][nchunk*kSelChunk]
-    uint32_t* hist;                  // [B][Hkv][3][kRadixBins]
+    uint32_t* hist;                  // [B][Hkv][kSelHistBins]: digit 0 of the keys
     int32_t* state;                  // [B][Hkv][4]: prefix, k_rem, nJ, take_all
-    uint32_t* counts;                // [B][Hkv][nchunk][2]
+    uint32_t* counts;                // [B][Hkv][nchunk][2]: kept keys > T, == T per chunk
+    uint32_t* cand;                  // [B][Hkv][nchunk][kSelChunk]: keys of the digit-0 bin
+    uint32_t* cand_n;                // [B][Hkv][nchunk]: candidates per chunk
     int32_t unit_path;               // 1: one workgroup per (b, KV head) does everything
 };
 

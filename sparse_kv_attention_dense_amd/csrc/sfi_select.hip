@@ -1,18 +1,26 @@
 // sfi_select.hip -- the Selector of Slow-Fast Inference at decode, and the sink-bypass mask.
 //
 // Selector (SFI Sec. 3.2, evidence from the slow-step logits over the allowed set J with a
-// window of one query; Sec. 3.3, Top-K per KV head; prior and refinements off):
-//   1. lse_kernel       partial log-sum-exp of each query head's logits over a 4096-wide
-//                        chunk of J (also clears the radix histograms of the group)
-//   2. evidence_kernel  f(j) = sum_{i in group} exp(z_ij - LSE_J,i) for the chunk, stored as
-//                        uint32 keys (the bit pattern of a non-negative float orders like
-//                        the float), plus a histogram of the top 11 key bits
-//   3. radix_step / radix_hist, three digit passes (11, 11, 10 bits): find the key T of the
-//      k-th largest evidence and how many keys equal to T are kept
-//   4. count_kernel + emit_kernel: ordered compaction.  Position j of J is kept when
-//      key > T, or key == T and fewer than k_rem earlier positions have key == T (ties go
-//      to the lower position); kept positions are written in ascending order after the
-//      sink positions [0, min(n_sink, N)).
+// window of one query; Sec. 3.3, Top-K per KV head; prior and refinements off).  Chunked path
+// (long contexts):
+//   1. lse_kernel         partial log-sum-exp of each query head's logits over a 4096-wide
+//                          chunk of J (also clears the digit-0 histogram of the group)
+//   2. evidence_kernel    f(j) = sum_{i in group} exp(z_ij - LSE_J,i) for the chunk, stored as
+//                          uint32 keys (the bit pattern of a non-negative float orders like
+//                          the float), plus a histogram of digit 0 (key bits 30..19)
+//   3. radix_step_kernel  the digit-0 bin that holds the k-th largest key
+//   4. candidate_kernel   per chunk: the keys of that bin, compacted into the chunk's region,
+//                          and the number of keys in higher bins
+//   5. resolve_kernel     one workgroup per unit: digits 1 and 2 (bits 18..9, 8..0) over the
+//                          candidates give the key T of the k-th largest evidence and how many
+//                          keys equal to T are kept; then the per-chunk numbers of kept keys
+//                          above T and equal to T
+//   6. emit_kernel        ordered compaction.  Position j of J is kept when key > T, or
+//                          key == T and fewer than k_rem earlier positions have key == T (ties
+//                          go to the lower position); kept positions are written in ascending
+//                          order after the sink positions [0, min(n_sink, N)).
+// The one-launch path (select_unit_kernel, short contexts) does the same in one workgroup per
+// (b, KV head).
 // f is computed without the 1/G factor: a positive common scale does not change the order.
 //
 // Sink-bypass mask (SinkRouter Sec. 4.2): rank the query heads of each sequence by their
@@ -28,8 +36,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kPerThread = kSelChunk / kThreads;     // 16 positions per thread
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// One-launch path: key digits of 11, 11 and 10 bits (LDS histograms of kRadixBins).
 constexpr int kShift[3] = {21, 10, 0};
 constexpr uint32_t kDigitMask[3] = {0x7ffu, 0x7ffu, 0x3ffu};
+// Chunked path: keys are non-negative floats, so bit 31 is zero; digit 0 is bits 30..19
+// (exponent and 4 mantissa bits: bins of 1/16 octave, so the bin at the k-th largest key holds
+// few keys), then bits 18..9 and 8..0.
+constexpr int kCBins0 = kSelHistBins;
+constexpr int kCShift[3] = {19, 9, 0};
+constexpr uint32_t kCMask[3] = {0xfffu, 0x3ffu, 0x1ffu};
 
 __device__ __forceinline__ float wave_max(float x) {
     for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -104,8 +119,8 @@ __global__ void __launch_bounds__(kThreads) lse_kernel(SelArgs a) {
     const int h = i / a.G;
     const int unit = b * a.Hkv + h;
     if (c == 0 && i % a.G == 0) {
-        uint32_t* hh = a.hist + (int64_t)unit * 3 * kRadixBins;
-        for (int t = tid; t < 3 * kRadixBins; t += kThreads) hh[t] = 0u;
+        uint32_t* hh = a.hist + (int64_t)unit * kCBins0;
+        for (int t = tid; t < kCBins0; t += kThreads) hh[t] = 0u;
     }
     const Range r = j_range(a, b);
     const int lo = r.j0 + c * kSelChunk;
@@ -145,7 +160,7 @@ __global__ void __launch_bounds__(kThreads) lse_kernel(SelArgs a) {
 
 __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     __shared__ float s_lse[kMaxG];
-    __shared__ uint32_t lh[kRadixBins];
+    __shared__ uint32_t lh[kCBins0];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int G = a.G;
@@ -154,7 +169,7 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     const int lo = r.j0 + c * kSelChunk;
     const int hi = min(r.j1, lo + kSelChunk);
     if (lo >= hi) return;
-    for (int t = tid; t < kRadixBins; t += kThreads) lh[t] = 0u;
+    for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
     for (int g = w; g < G; g += kWaves) {
         const float2* lp = a.lse_part + ((int64_t)b * a.Hq + h * G + g) * a.nchunk;
         float M = -INFINITY;
@@ -180,54 +195,52 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
                 f += exp2_hw(fmaf(zb[(int64_t)g * a.logit_stride + j], kLog2e, -s_lse[g]));
             const uint32_t key = __float_as_uint(f);
             keys[j - lo] = key;
-            atomicAdd(&lh[key >> kShift[0]], 1u);
+            atomicAdd(&lh[key >> kCShift[0]], 1u);
         }
     }
     __syncthreads();
-    uint32_t* hg = a.hist + (int64_t)unit * 3 * kRadixBins;
-    for (int t = tid; t < kRadixBins; t += kThreads)
+    uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
+    for (int t = tid; t < kCBins0; t += kThreads)
         if (lh[t]) atomicAdd(&hg[t], lh[t]);
 }
 
 // state: [0] prefix (bits of T decided so far), [1] k_rem, [2] nJ, [3] take_all
-__global__ void __launch_bounds__(kThreads) radix_step_kernel(SelArgs a, int pass) {
+// A unit is active when some but not all of J is kept: !take_all, k_rem > 0 and a prefix
+// other than the keep-nothing mark 0xffffffff.
+__device__ __forceinline__ bool sel_active(uint32_t prefix, int32_t k_rem, int32_t take_all) {
+    return !take_all && k_rem > 0 && prefix != 0xffffffffu;
+}
+
+// Digit 0: the bin of the evidence histogram that holds the k_sel-th largest key; k_rem
+// becomes the rank inside that bin.
+__global__ void __launch_bounds__(kThreads) radix_step_kernel(SelArgs a) {
     __shared__ uint32_t sh[4];
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
     int32_t* st = a.state + unit * 4;
-    uint32_t prefix;
-    int32_t k_rem, nJ, take_all;
-    if (pass == 0) {
-        nJ = j_range(a, b).nJ;
-        take_all = a.k_sel >= nJ ? 1 : 0;
-        k_rem = take_all ? nJ : a.k_sel;
-        prefix = 0u;
-        if (!take_all && k_rem == 0) prefix = 0xffffffffu;   // keep nothing from J
-    } else {
-        prefix = (uint32_t)st[0];
-        k_rem = st[1];
-        nJ = st[2];
-        take_all = st[3];
-    }
-    const bool active = !take_all && k_rem > 0 && prefix != 0xffffffffu;
-    const uint32_t* hg = a.hist + ((int64_t)unit * 3 + pass) * kRadixBins;
-    uint32_t cnt[8];
+    const int32_t nJ = j_range(a, b).nJ;
+    const int32_t take_all = a.k_sel >= nJ ? 1 : 0;
+    const int32_t k_rem = take_all ? nJ : a.k_sel;
+    const uint32_t prefix = (!take_all && k_rem == 0) ? 0xffffffffu : 0u;   // keep nothing
+    const bool active = sel_active(prefix, k_rem, take_all);
+    constexpr int kPer = kCBins0 / kThreads;          // bins per thread, ascending
+    const uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
+    uint32_t cnt[kPer];
     uint32_t mine = 0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        cnt[k] = active ? hg[8 * tid + k] : 0u;
+    for (int k = 0; k < kPer; ++k) {
+        cnt[k] = active ? hg[kPer * tid + k] : 0u;
         mine += cnt[k];
     }
     // number of keys in bins above this thread's bins (threads hold ascending bins)
     const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
     const uint32_t total = block_sum_u(mine, sh);
     const uint32_t above = total - below_incl;
-    __syncthreads();
     if (active && above < (uint32_t)k_rem && (uint32_t)k_rem <= above + mine) {
         uint32_t cum = above;
-        for (int k = 7; k >= 0; --k) {
+        for (int k = kPer - 1; k >= 0; --k) {
             if (cum + cnt[k] >= (uint32_t)k_rem) {
-                st[0] = (int32_t)(prefix | ((uint32_t)(8 * tid + k) << kShift[pass]));
+                st[0] = (int32_t)((uint32_t)(kPer * tid + k) << kCShift[0]);
                 st[1] = k_rem - (int32_t)cum;
                 st[2] = nJ;
                 st[3] = take_all;
@@ -244,54 +257,70 @@ __global__ void __launch_bounds__(kThreads) radix_step_kernel(SelArgs a, int pas
     }
 }
 
-__global__ void __launch_bounds__(kThreads) radix_hist_kernel(SelArgs a, int pass) {
-    __shared__ uint32_t lh[kRadixBins];
+// Loads the 16 consecutive keys of thread tid in chunk c as four 16-byte loads (a chunk holds
+// kSelChunk keys in the workspace whatever its length, so the loads stay inside it); keys at
+// or past cnt read as 0.
+__device__ __forceinline__ void load_chunk_keys(const SelArgs& a, int unit, int c, int cnt,
+                                                uint32_t* kv) {
+    const int tid = threadIdx.x;
+    const u32x4* keys4 =
+        (const u32x4*)(a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk) + tid * (kPerThread / 4);
+#pragma unroll
+    for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
+        const u32x4 x = tid * kPerThread < cnt ? keys4[k4] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kv[4 * k4 + e] = x[e];
+    }
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (tid * kPerThread + k >= cnt) kv[k] = 0u;
+}
+
+// Per chunk: compacts the keys of the digit-0 bin into the chunk's own region of the candidate
+// buffer (no cross-workgroup atomics), writes their number to cand_n[chunk] and
+// counts[chunk] = (keys in higher digit-0 bins, 0); the resolve pass adds the candidates'
+// share.  Inactive units get their final counts here: everything (take_all) or nothing.
+__global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
+    __shared__ uint32_t sh[4];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
     const int32_t* st = a.state + unit * 4;
     const uint32_t prefix = (uint32_t)st[0];
     const int32_t k_rem = st[1], nJ = st[2], take_all = st[3];
-    if (take_all || k_rem <= 0 || prefix == 0xffffffffu) return;
-    const int lo = c * kSelChunk;
-    const int cnt = min(kSelChunk, nJ - lo);
-    if (cnt <= 0) return;
-    for (int t = tid; t < kRadixBins; t += kThreads) lh[t] = 0u;
-    __syncthreads();
-    const int hs = kShift[pass - 1];
-    const uint32_t want = prefix >> hs;
-    const uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
-    for (int k = tid; k < cnt; k += kThreads) {
-        const uint32_t key = keys[k];
-        if ((key >> hs) == want) atomicAdd(&lh[(key >> kShift[pass]) & kDigitMask[pass]], 1u);
+    const int cnt = max(0, min(kSelChunk, nJ - c * kSelChunk));
+    uint32_t* cn = a.counts + ((int64_t)unit * a.nchunk + c) * 2;
+    uint32_t* cand_n = a.cand_n + (int64_t)unit * a.nchunk + c;
+    if (!sel_active(prefix, k_rem, take_all) || cnt == 0) {
+        if (tid == 0) {
+            cn[0] = take_all ? (uint32_t)cnt : 0u;
+            cn[1] = 0u;
+            *cand_n = 0u;
+        }
+        return;
     }
-    __syncthreads();
-    uint32_t* hg = a.hist + ((int64_t)unit * 3 + pass) * kRadixBins;
-    for (int t = tid; t <= (int)kDigitMask[pass]; t += kThreads)
-        if (lh[t]) atomicAdd(&hg[t], lh[t]);
-}
-
-__global__ void __launch_bounds__(kThreads) count_kernel(SelArgs a) {
-    __shared__ uint32_t sh[4];
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int unit = b * a.Hkv + h;
-    const int32_t* st = a.state + unit * 4;
-    const uint32_t T = (uint32_t)st[0];
-    const int32_t nJ = st[2], take_all = st[3];
-    const int lo = c * kSelChunk;
-    const int cnt = max(0, min(kSelChunk, nJ - lo));
-    const uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
-    uint32_t gt = 0, eq = 0;
-    for (int k = tid; k < cnt; k += kThreads) {
-        const uint32_t key = keys[k];
-        gt += (take_all || key > T) ? 1u : 0u;
-        eq += (!take_all && key == T) ? 1u : 0u;
+    const uint32_t d0 = prefix >> kCShift[0];
+    uint32_t kv[kPerThread];
+    load_chunk_keys(a, unit, c, cnt, kv);
+    uint32_t gt = 0, nc = 0;
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+        const bool in = tid * kPerThread + k < cnt;
+        const uint32_t d = kv[k] >> kCShift[0];
+        gt += (in && d > d0) ? 1u : 0u;
+        nc += (in && d == d0) ? 1u : 0u;
     }
-    gt = block_sum_u(gt, sh);
-    eq = block_sum_u(eq, sh);
+    // counts packed as (greater << 16) | candidates: at most kSelChunk each
+    const uint32_t excl = block_exclusive_scan((gt << 16) | nc, sh);
+    const uint32_t tot = block_sum_u((gt << 16) | nc, sh);
     if (tid == 0) {
-        a.counts[((int64_t)unit * a.nchunk + c) * 2] = gt;
-        a.counts[((int64_t)unit * a.nchunk + c) * 2 + 1] = eq;
+        *cand_n = tot & 0xffffu;
+        cn[0] = tot >> 16;
+        cn[1] = 0u;
     }
+    uint32_t* out = a.cand + ((int64_t)unit * a.nchunk + c) * kSelChunk + (excl & 0xffffu);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (tid * kPerThread + k < cnt && (kv[k] >> kCShift[0]) == d0) *out++ = kv[k];
 }
 
 __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
@@ -322,22 +351,13 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
     const uint32_t kr = take_all ? 0u : (uint32_t)k_rem;
     const uint32_t base = (uint32_t)ns + gtb + min(eqb, kr);
     // this thread's 16 consecutive positions
-    // this thread's 16 consecutive keys as four 16-byte loads (a chunk holds kSelChunk keys
-    // in the workspace whatever cnt is, so the loads stay inside it)
-    const u32x4* keys4 =
-        (const u32x4*)(a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk) + tid * (kPerThread / 4);
+    // this thread's 16 consecutive keys
     uint32_t kv[kPerThread];
-#pragma unroll
-    for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
-        const u32x4 x = tid * kPerThread < cnt ? keys4[k4] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kv[4 * k4 + e] = x[e];
-    }
+    load_chunk_keys(a, unit, c, cnt, kv);
     uint32_t my_eq = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const int t = tid * kPerThread + k;
-        if (t >= cnt) kv[k] = 0u;
         my_eq += (t < cnt && !take_all && kv[k] == T) ? 1u : 0u;
     }
     uint32_t eq_rank = eqb + block_exclusive_scan(my_eq, sh);
@@ -443,6 +463,133 @@ __device__ void unit_resolve(UnitShared& sm, int shift, uint32_t& prefix, int32_
     prefix |= sm.sel[0] << shift;
     k_rem -= (int32_t)sm.sel[1];
     __syncthreads();
+}
+
+// Digits 1 and 2 over the unit's candidates (all in the digit-0 bin), then the per-chunk
+// numbers of candidates above T and equal to T added to the counts of the candidate pass.
+// One 1024-thread workgroup per (b, KV head).  Chunks are taken kCntGroup at a time: their
+// candidate numbers are scanned in LDS, and candidate i of the group is found in its chunk's
+// region by a binary search over the scan.  When a unit's candidates fit (the usual case: a
+// digit-0 bin is 1/16 octave of evidence) they are copied to LDS once and the three
+// passes run from there; otherwise each pass reads them again, kResolveBatch per thread at a
+// time so the loads overlap.
+constexpr int kCntGroup = kUT;
+constexpr int kCandLds = 16384;
+constexpr int kResolveBatch = 4;
+struct ResolveShared {
+    UnitShared u;
+    uint32_t off[kCntGroup + 1];      // exclusive scan of the group's candidate numbers
+    uint32_t gt[kCntGroup], eq[kCntGroup];
+    uint32_t key[kCandLds];
+};
+
+__global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
+    __shared__ ResolveShared rs;
+    UnitShared& sm = rs.u;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    int32_t* st = a.state + unit * 4;
+    uint32_t prefix = (uint32_t)st[0];
+    int32_t k_rem = st[1];
+    const int32_t nJ = st[2], take_all = st[3];
+    if (!sel_active(prefix, k_rem, take_all)) return;
+    const int nch = (nJ + kSelChunk - 1) / kSelChunk;
+    const uint32_t* cand = a.cand + (int64_t)unit * a.nchunk * kSelChunk;
+    const uint32_t* cand_n = a.cand_n + (int64_t)unit * a.nchunk;
+    // scans the candidate numbers of chunks [g0, g0 + kCntGroup); returns their total
+    auto load_group = [&](int g0) -> uint32_t {
+        const uint32_t n = g0 + tid < nch ? cand_n[g0 + tid] : 0u;
+        uint32_t tot;
+        const uint32_t ex = unit_scan(n, sm, &tot);
+        rs.off[tid] = ex;
+        if (tid == 0) rs.off[kCntGroup] = tot;
+        __syncthreads();
+        return tot;
+    };
+    // the chunk (within the group) of candidate i < total: the last c with off[c] <= i
+    auto chunk_of = [&](uint32_t i) -> int {
+        int lo = 0, hi = kCntGroup;                        // off[lo] <= i < off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (rs.off[mid] <= i) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
+    // calls fn(key, chunk in group) for every candidate of the group
+    auto for_each = [&](int g0, uint32_t total, bool in_lds, auto&& fn) {
+        if (in_lds) {
+            for (uint32_t i = tid; i < total; i += kUT) fn(rs.key[i], chunk_of(i));
+            return;
+        }
+        for (uint32_t i0 = tid; i0 < total; i0 += kResolveBatch * kUT) {
+            uint32_t kk[kResolveBatch];
+            int cc[kResolveBatch];
+#pragma unroll
+            for (int u = 0; u < kResolveBatch; ++u) {
+                const uint32_t i = i0 + u * kUT;
+                cc[u] = i < total ? chunk_of(i) : 0;
+                kk[u] = i < total ? cand[(int64_t)(g0 + cc[u]) * kSelChunk + (i - rs.off[cc[u]])] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < kResolveBatch; ++u)
+                if (i0 + u * kUT < total) fn(kk[u], cc[u]);
+        }
+    };
+    const bool one_group = nch <= kCntGroup;
+    uint32_t total = one_group ? load_group(0) : 0u;
+    const bool in_lds = one_group && total <= (uint32_t)kCandLds;
+    if (in_lds) {
+        for (uint32_t i0 = tid; i0 < total; i0 += kResolveBatch * kUT) {
+            uint32_t kk[kResolveBatch];
+#pragma unroll
+            for (int u = 0; u < kResolveBatch; ++u) {
+                const uint32_t i = i0 + u * kUT;
+                const int c = i < total ? chunk_of(i) : 0;
+                kk[u] = i < total ? cand[(int64_t)c * kSelChunk + (i - rs.off[c])] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < kResolveBatch; ++u)
+                if (i0 + u * kUT < total) rs.key[i0 + u * kUT] = kk[u];
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int pass = 1; pass < 3; ++pass) {
+        for (int t = tid; t < kRadixBins; t += kUT) sm.hist[t] = 0u;
+        __syncthreads();
+        const int hs = kCShift[pass - 1];
+        const uint32_t want = prefix >> hs;
+        for (int g0 = 0; g0 < nch; g0 += kCntGroup) {
+            if (!one_group) total = load_group(g0);
+            for_each(g0, total, in_lds, [&](uint32_t key, int) {
+                if ((key >> hs) == want) atomicAdd(&sm.hist[(key >> kCShift[pass]) & kCMask[pass]], 1u);
+            });
+            __syncthreads();
+        }
+        unit_resolve(sm, kCShift[pass], prefix, k_rem);
+    }
+    const uint32_t T = prefix;
+    for (int g0 = 0; g0 < nch; g0 += kCntGroup) {
+        if (!one_group) total = load_group(g0);
+        rs.gt[tid] = 0u;
+        rs.eq[tid] = 0u;
+        __syncthreads();
+        for_each(g0, total, in_lds, [&](uint32_t key, int c) {
+            if (key > T) atomicAdd(&rs.gt[c], 1u);
+            else if (key == T) atomicAdd(&rs.eq[c], 1u);
+        });
+        __syncthreads();
+        if (g0 + tid < nch) {
+            uint32_t* cn = a.counts + ((int64_t)unit * a.nchunk + g0 + tid) * 2;
+            cn[0] += rs.gt[tid];
+            cn[1] = rs.eq[tid];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        st[0] = (int32_t)T;
+        st[1] = k_rem;
+    }
 }
 
 __global__ void __launch_bounds__(kUT) select_unit_kernel(SelArgs a) {
@@ -701,12 +848,9 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     const dim3 g_unit(a.Hkv, a.B);
     hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
     hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
-    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a, 0);
-    hipLaunchKernelGGL(radix_hist_kernel, g_group, blk, 0, s, a, 1);
-    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a, 1);
-    hipLaunchKernelGGL(radix_hist_kernel, g_group, blk, 0, s, a, 2);
-    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a, 2);
-    hipLaunchKernelGGL(count_kernel, g_group, blk, 0, s, a);
+    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a);
+    hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
+    hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
     hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);
     return hipGetLastError();
 }

@@ -100,6 +100,8 @@ def test_select_edges(orc, path):
     zq = torch.randint(-2, 2, z.shape, generator=g).float()
     _run(orc, wl, lens, zq, exact=True, max_len=ml)
     _run(orc, wl, lens, zq, exact=True, k_sel=1, idx_stride=5, max_len=ml)
+    # every key equal: the first k_sel positions of J
+    _run(orc, wl, lens, torch.zeros_like(z), exact=True, max_len=ml)
 
 
 @pytest.mark.parametrize("G,path", [(1, "unit"), (16, "unit"), (1, "chunked"), (16, "chunked"),
@@ -110,6 +112,20 @@ def test_select_group_sizes(orc, G, path):
     lens = [3000, 2500] if path == "unit" else [20000, 15000]
     z, _ = _planted(wl, lens, seed=G)
     _run(orc, wl, lens, z, exact=True, max_len=CHUNKED_MAX_LEN if path == "chunked" else None)
+
+
+def test_select_beyond_one_chunk_group(orc):
+    """A context of more than 1024 Selector chunks (4M positions): the resolve pass then scans
+    the per-chunk candidate numbers group by group.  Random logits, then all keys equal (every
+    key is a candidate, more than fit in LDS)."""
+    wl = synth.Workload("sel_4m", 1, 1, 2, 1, 128, "bf16", 4096 * 1024 + 5000, 4, 64, 2048, 1)
+    lens = [4096 * 1024 + 5000]
+    g = torch.Generator().manual_seed(11)
+    z = torch.randn((1, 2, round4(lens[0])), generator=g)
+    say("[select] 4M positions, random logits")
+    _run(orc, wl, lens, z, exact=True, max_len=lens[0])
+    say("[select] 4M positions, all keys equal")
+    _run(orc, wl, lens, torch.zeros_like(z), exact=True, max_len=lens[0])
 
 
 def test_select_deterministic():
