@@ -42,10 +42,11 @@ constexpr int64_t kPagedTargetWorkgroups = SFI_PAGED_TARGET_WG;
 constexpr int64_t kSparseTargetWorkgroups = SFI_SPARSE_TARGET_WG;
 constexpr int64_t kSparseQuantum = SFI_SPARSE_QUANTUM;
 constexpr size_t kAlign = 256;
-constexpr double kUnitFixedUs = 12.0;           // Selector path estimates, see select_unit_path
-constexpr double kUnitUsPerMB = 60.0;
-constexpr double kChunkedFixedUs = 43.5;
-constexpr double kChunkedUsPerMB = 0.49;
+constexpr double kUnitFixedUs = 14.7;           // Selector path estimates, see select_unit_path
+constexpr double kUnitUsPerPos = 6.0e-4;
+constexpr double kUnitUsPerPosHead = 1.1e-4;
+constexpr double kChunkedFixedUs = 31.0;
+constexpr double kChunkedUsPerMB = 0.37;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -124,20 +125,20 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
 }
 
 // Selector path.  One workgroup per (b, KV head) is bound by one compute unit's ALU rate on
-// that unit's logits; the chunked kernels spread the work over the chip but pay for nine
+// that unit's positions; the chunked kernels spread the work over the chip but pay for six
 // launches.  The plan takes whichever is estimated faster from the descriptor alone, with
-// linear fits to MI355X measurements of both paths: one workgroup per unit 17 us at 32 KB of
-// logits per unit, 41 us at 0.5 MB, 143 us at 2 MB; chunked 35 us at 32 KB of logits in all,
-// 46 us at 4 MB, 76 us at 67 MB, 96 us at 134 MB.
+// linear fits to MI355X measurements of both paths on random logits: one workgroup per unit
+// 18 us at 2K positions (G = 4), 42 us at 32K, 126 us at 128K, 209 us at 128K with G = 8,
+// 66 us at 64K with G = 1; chunked 30 us at 32 KB of logits in all, 35 us at 4 MB, 37 us at
+// 17 MB, 57 us at 67 MB, 81 us at 134 MB.
 #ifndef SFI_SELECT_PATH
 #define SFI_SELECT_PATH -1                      // -1: estimate; 0: chunked; 1: one per unit
 #endif
 bool select_unit_path(const sfi_kv_desc& kv) {
     if (SFI_SELECT_PATH >= 0) return SFI_SELECT_PATH == 1;
     const double G = (double)kv.num_q_heads / kv.num_kv_heads;
-    const double unit_mb = G * kv.max_len * 4.0 / 1e6;
     const double all_mb = (double)kv.batch * kv.num_q_heads * kv.max_len * 4.0 / 1e6;
-    const double t_unit = kUnitFixedUs + kUnitUsPerMB * unit_mb;
+    const double t_unit = kUnitFixedUs + (kUnitUsPerPos + kUnitUsPerPosHead * G) * kv.max_len;
     const double t_chunked = kChunkedFixedUs + kChunkedUsPerMB * all_mb;
     return t_unit < t_chunked;
 }
