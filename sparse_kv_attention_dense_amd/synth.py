@@ -36,7 +36,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Optional
+from typing import List, Optional
 
 import torch
 
@@ -146,21 +146,22 @@ def _fill_seq(wl: Workload, Kb: torch.Tensor, Vb: torch.Tensor, u: Optional[torc
     Vb[:, 0, :] = v0 * (1e-3 / v0.norm(dim=-1, keepdim=True))
 
 
+def slow_step_lengths(wl: Workload) -> List[int]:
+    """Sequence lengths at the slow step: n0 for every sequence, or for a ragged workload one
+    draw per workload (every layer of a batch sees the same sequences)."""
+    if wl.len_lo > 0:
+        gl = _gen("cpu", wl.seed_base + 50)
+        return torch.randint(wl.len_lo, wl.n0 + 1, (wl.B,), generator=gl).tolist()
+    return [wl.n0] * wl.B
+
+
 def make_layer(wl: Workload, layer: int = 0, device="cpu", lens=None) -> Layer:
     """Draw one layer's cache.  Capacity covers the whole cycle (n0 + cycle - 1 rows)."""
     seed = wl.seed_base + layer
     g = _gen(device, seed)
     dt = wl.torch_dtype
     # lengths at the slow step
-    if lens is not None:
-        len_host = [int(x) for x in lens]
-    elif wl.len_lo > 0:
-        # one set of sequence lengths per workload: every layer of a batch sees the same
-        # sequences, so the lengths do not depend on the layer
-        gl = _gen("cpu", wl.seed_base + 50)
-        len_host = torch.randint(wl.len_lo, wl.n0 + 1, (wl.B,), generator=gl).tolist()
-    else:
-        len_host = [wl.n0] * wl.B
+    len_host = [int(x) for x in lens] if lens is not None else slow_step_lengths(wl)
     caps = [n + wl.cycle - 1 for n in len_host]
     cap = max(caps)
     u = _sink_dirs(wl, g, device) if wl.sink else None

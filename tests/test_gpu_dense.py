@@ -93,7 +93,9 @@ def test_dense_deterministic():
 
 
 @pytest.mark.parametrize("name,samples", [("sink_128k_b4", [(0, 0), (3, 31), (1, 13)]),
-                                          ("gqa8_512k", [(0, 0), (0, 63), (0, 22)])])
+                                          ("gqa8_512k", [(0, 0), (0, 63), (0, 22)]),
+                                          ("ragged_paged_b16", [(0, 0), (7, 17), (15, 31)]),
+                                          ("gqa4_32k", [(0, 5)])])
 def test_dense_full_size_sampled(orc, name, samples):
     """Full-size workloads in the benchmark's launch configuration; the oracle recomputes
     sampled (batch, query head) rows one by one."""
@@ -105,8 +107,9 @@ def test_dense_full_size_sampled(orc, name, samples):
     for b, i in samples:
         h = i // wl.G
         N = lay.len0_host[b]
-        K1 = lay.k[b:b + 1, h:h + 1, :N].contiguous()
-        V1 = lay.v[b:b + 1, h:h + 1, :N].contiguous()
+        Kf, Vf = synth.logical_kv(lay, b, h, N)        # gathers through the block table when paged
+        K1 = Kf.to(wl.torch_dtype)[None, None].contiguous()
+        V1 = Vf.to(wl.torch_dtype)[None, None].contiguous()
         c = orc.Cache(K1, V1, torch.tensor([N], dtype=torch.int32), 1)
         eo, el, ez = orc.dense(c, q[b:b + 1, i:i + 1].contiguous())
         say(f"  sample b={b} i={i}")

@@ -62,10 +62,10 @@ def test_select_planted_is_exact(orc, name, lens):
             assert ig[b, h, :n_idx[b, h]].tolist() == list(range(min(wl.n_sink, N))) + keep
 
 
-@pytest.mark.parametrize("name", ["sink_128k_b4", "gqa8_512k"])
+@pytest.mark.parametrize("name", ["sink_128k_b4", "gqa8_512k", "ragged_paged_b16", "gqa4_32k"])
 def test_select_planted_full_size(orc, name):
     wl = W[name]
-    lens = [wl.n0] * wl.B
+    lens = synth.slow_step_lengths(wl)
     say(f"[select planted full] {name} B={wl.B} N={wl.n0} k={wl.k_sel}")
     z, _ = _planted(wl, lens, seed=17)
     _run(orc, wl, lens, z, exact=True)

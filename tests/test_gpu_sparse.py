@@ -109,7 +109,9 @@ def test_sparse_all_heads_masked_and_group_skip(orc):
 
 
 @pytest.mark.parametrize("name,samples", [("sink_128k_b4", [(0, 0), (3, 30)]),
-                                          ("gqa8_512k", [(0, 5), (0, 60)])])
+                                          ("gqa8_512k", [(0, 5), (0, 60)]),
+                                          ("ragged_paged_b16", [(2, 3), (11, 28)]),
+                                          ("gqa4_32k", [(0, 30)])])
 def test_sparse_full_size_sampled(orc, name, samples):
     wl = W[name]
     say(f"[sparse full] {wl.name}")
@@ -121,8 +123,9 @@ def test_sparse_full_size_sampled(orc, name, samples):
     for b, i in samples:
         h = i // wl.G
         N = lay.len0_host[b] + t
-        K1 = lay.k[b:b + 1, h:h + 1, :N].contiguous()
-        V1 = lay.v[b:b + 1, h:h + 1, :N].contiguous()
+        Kf, Vf = synth.logical_kv(lay, b, h, N)        # gathers through the block table when paged
+        K1 = Kf.to(wl.torch_dtype)[None, None].contiguous()
+        V1 = Vf.to(wl.torch_dtype)[None, None].contiguous()
         c = orc.Cache(K1, V1, torch.tensor([N], dtype=torch.int32), 1)
         eo, el = orc.sparse(c, q[b:b + 1, i:i + 1].contiguous(), idx[b:b + 1, h:h + 1].contiguous(),
                             n_idx[b:b + 1, h:h + 1].contiguous(), wl.n_recent)
