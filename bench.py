@@ -12,7 +12,10 @@ Prints one JSON line.  value = microseconds per decode step, amortised over the 
 (slow + (cycle-1) fast) / cycle, from the host clock around whole cycles run back to back.
 roofline = the dense slow step's algorithmic HBM bytes per launch / its mean time, measured
 with HIP events on the launch stream inside the timed region (the only events there).
-The per-call breakdown (select, mask, fast) comes from separate instrumented cycles.
+The per-call breakdown (select, mask, fast) comes from separate instrumented cycles;
+spread_us gives p10/p50/p90 over single calls each bracketed by its own events (an event pair
+adds about 1.5 us to a call, so these sit above the block means), and dense_nolog_us the dense
+step without its logit write.
 cpu_baseline = the fp64 CPU oracle timed on the host on whole cycles of one layer.
 """
 from __future__ import annotations
@@ -64,8 +67,9 @@ def dense_bytes(wl, lens):
 def select_bytes(wl, lens):
     nJ = sum(max(0, n - wl.n_recent - wl.n_sink) for n in lens)
     # logits over J read twice (log-sum-exp pass, evidence pass); one key written per
-    # (KV head, position) and read back by two histogram passes, the count and the emit
-    return 2 * wl.Hq * nJ * 4 + 5 * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
+    # (KV head, position) and read back by the candidate pass and the emit (the candidates
+    # themselves, well under 1 % of J, are not counted)
+    return 2 * wl.Hq * nJ * 4 + 3 * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
                                                          for _ in lens)
 
 
@@ -343,6 +347,38 @@ def main():
     mask_us = 1e3 * mean([e[2].elapsed_time(e[3]) for e in evs]) if wl.mask_frac > 0 else 0.0
     fast_us = 1e3 * mean([e[3].elapsed_time(e[4]) / (wl.cycle - 1) for e in evs])
 
+    # Spread: one more pass with events around every single call (p10 / p50 / p90), and the
+    # dense step without its logit write as a reference for the cost of the logits.
+    print("# per-call spread", file=sys.stderr, flush=True)
+    dense_calls, nolog_calls, fast_calls = [], [], []
+    for li in range(L):
+        d0 = descs[li]
+        e = [ev() for _ in range(2 * wl.cycle + 2)]
+        e[0].record(stream)
+        B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
+        e[1].record(stream)
+        B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
+                     idx_stride, nidxs[li], ws)
+        if masks[li] is not None:
+            B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
+        for t in range(1, wl.cycle):
+            e[2 * t].record(stream)
+            B.sfi_sparse_decode(d0[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
+                                wl.n_recent, masks[li], out, lse, ws)
+            e[2 * t + 1].record(stream)
+        e[2 * wl.cycle].record(stream)
+        B.sfi_dense_decode(d0[0], queries[li][0], out, lse, None, stride, ws)
+        e[2 * wl.cycle + 1].record(stream)
+        torch.cuda.synchronize()
+        dense_calls.append(1e3 * e[0].elapsed_time(e[1]))
+        nolog_calls.append(1e3 * e[2 * wl.cycle].elapsed_time(e[2 * wl.cycle + 1]))
+        fast_calls += [1e3 * e[2 * t].elapsed_time(e[2 * t + 1]) for t in range(1, wl.cycle)]
+
+    def pct(xs):
+        xs = sorted(xs)
+        at = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+        return [round(at(0.1), 2), round(at(0.5), 2), round(at(0.9), 2)]
+
     routed = None
     if wl.sink and not args.no_routed:
         routed = routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
@@ -360,6 +396,8 @@ def main():
     s_bytes = select_bytes(wl, lens0)
     f_bytes = mean([fast_bytes(wl, [n + t for n in lens0], n_idx_host, mask_host)
                     for t in range(1, wl.cycle)])
+    f_bytes_unmasked = mean([fast_bytes(wl, [n + t for n in lens0], n_idx_host, None)
+                             for t in range(1, wl.cycle)])
     dense_gbps = d_bytes / (dense_us * 1e-6) / 1e9
     fast_gbps = f_bytes / (fast_us * 1e-6) / 1e9
     select_gbps = s_bytes / (select_us * 1e-6) / 1e9
@@ -394,6 +432,10 @@ def main():
         "fast_gbps": round(fast_gbps, 1),
         "select_gbps": round(select_gbps, 1),
         "fast_pct_peak": round(100 * fast_gbps / PEAK_HBM_GBS, 1),
+        "dense_nolog_us": round(mean(nolog_calls), 2),
+        "spread_us": {"p10_p50_p90": True, "dense": pct(dense_calls),
+                      "dense_nolog": pct(nolog_calls), "fast": pct(fast_calls),
+                      "calls": {"dense": len(dense_calls), "fast": len(fast_calls)}},
         "tokens_per_s": round(wl.B * 1e6 / value, 1),
         "roofline": {"bound": "hbm", "achieved": round(dense_gbps, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dense_gbps / PEAK_HBM_GBS, 4),
@@ -401,7 +443,8 @@ def main():
                      "algorithmic_bytes": d_bytes},
         "fast_roofline": {"bound": "hbm", "achieved": round(fast_gbps, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(fast_gbps / PEAK_HBM_GBS, 4),
-                          "algorithmic_bytes": int(f_bytes)},
+                          "algorithmic_bytes": int(f_bytes),
+                          "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
     if routed is not None:
         result["routed_fast"] = routed
