@@ -48,6 +48,9 @@ def parse():
                     help="skip the layer-wise slow-step measurement (sequential vs pipelined)")
     ap.add_argument("--no-routed", action="store_true",
                     help="skip the routed fast-step measurement on sink-dominated workloads")
+    ap.add_argument("--retention-sweep", action="store_true",
+                    help="add dense-vs-sparse timings over retention ratios on a layer shaped "
+                         "like the SFI page's retention table (KV 16K, batch 16, 32/8 heads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB on the device a few times (a "
                          "known-size reference for rocprofv3 byte counters)")
@@ -194,6 +197,70 @@ def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
     return {"gamma": gamma, "fast_us": round(sum(times) / n, 2),
             "groups_routed_frac": round(frac_sum / n, 4),
             "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
+
+
+def retention_sweep(B, torch, synth, ratios=(0.016, 0.031, 0.0625, 0.125, 0.25, 0.5, 1.0),
+                    n_sets=16, rounds=3):
+    """Dense against sparse attention on one layer shaped like the SFI page's retention table
+    (Sec. 5: KV 16K, batch 16; here 32/8 heads, d 128, bf16, sink 4 + recent 256), with the
+    selected positions drawn as sentence-like spans.  retention = |I| / N, the attended
+    positions over the context.  Each ratio rotates over n_sets different selections so the
+    rows a call reads were not left in the 256 MB Infinity Cache by the previous calls."""
+    import dataclasses
+    dev = "cuda"
+    wl = synth.Workload("retention_16k_b16", 6000, 16, 32, 8, 128, "bf16", 16384, 4, 256, 0, 2)
+    lay = synth.make_layer(wl, 0, device=dev)
+    N = wl.n0
+    lens = lay.len_at(0).to(dev)
+    desc = B.KVDesc(lay.k, lay.v, lens, N, wl.Hq)
+    q = synth.make_query(wl, 0, 0, device=dev)
+    stride = (N + 3) // 4 * 4
+    logits = torch.empty((wl.B, wl.Hq, stride), device=dev)
+    out = torch.empty((wl.B, wl.Hq, wl.d), device=dev)
+    lse = torch.empty((wl.B, wl.Hq), device=dev)
+    J_lo, J_hi = wl.n_sink, N - wl.n_recent
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / n
+
+    ws = B.workspace(desc, idx_stride=N, n_recent=wl.n_recent, device=dev)
+    dense_us = timed(lambda i: B.sfi_dense_decode(desc, q, out, lse, logits, stride, ws), 10)
+    nolog_us = timed(lambda i: B.sfi_dense_decode(desc, q, out, lse, None, stride, ws), 10)
+    rows = []
+    for r in ratios:
+        k = min(J_hi - J_lo, max(0, int(round(r * N)) - wl.n_sink - wl.n_recent))
+        stride_i = wl.n_sink + max(k, 1)
+        sets = []
+        for s in range(n_sets):
+            g = torch.Generator().manual_seed(7000 + s)
+            idx = torch.zeros((wl.B, wl.Hkv, stride_i), dtype=torch.int32)
+            for b in range(wl.B):
+                for h in range(wl.Hkv):
+                    sel = synth.span_selection(J_lo, J_hi, k, g) if k > 0 else torch.zeros(0, dtype=torch.int32)
+                    row = torch.cat([torch.arange(wl.n_sink, dtype=torch.int32), sel])
+                    idx[b, h, :row.numel()] = row
+            n_idx = torch.full((wl.B, wl.Hkv), wl.n_sink + k, dtype=torch.int32)
+            sets.append((idx.to(dev), n_idx.to(dev)))
+        wsr = B.workspace(desc, idx_stride=stride_i, n_recent=wl.n_recent, device=dev)
+        sparse_us = timed(lambda i: B.sfi_sparse_decode(desc, q, sets[i % n_sets][0], stride_i,
+                                                        sets[i % n_sets][1], wl.n_recent, None,
+                                                        out, lse, wsr), rounds * n_sets)
+        slots = wl.n_sink + k + wl.n_recent
+        rows.append({"retention": round(slots / N, 4), "k_sel": k, "sparse_us": round(sparse_us, 2),
+                     "dense_over_sparse": round(dense_us / sparse_us, 2),
+                     "dense_nolog_over_sparse": round(nolog_us / sparse_us, 2)})
+        del sets, wsr
+    return {"shape": "B 16, 32/8 heads, d 128, bf16, N 16384, sink 4, recent 256, spans",
+            "dense_us": round(dense_us, 2), "dense_nolog_us": round(nolog_us, 2), "rows": rows}
 
 
 def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
@@ -456,6 +523,11 @@ def main():
         print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         host_q = [q.cpu() for q in queries[0]]
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], host_q, lens0)
+    if args.retention_sweep:
+        print("# retention sweep", file=sys.stderr, flush=True)
+        del layers, descs, queries, logits, idxs, nidxs, masks
+        torch.cuda.empty_cache()
+        result["retention_sweep"] = retention_sweep(B, torch, synth)
     print(json.dumps(result), flush=True)
 
 
