@@ -66,7 +66,9 @@ typedef enum sfi_op { SFI_OP_DENSE = 0, SFI_OP_SELECT = 1, SFI_OP_SPARSE = 2 } s
  *   block_table (device) NULL for contiguous; else int32 [B][max_blocks] of physical block
  *                      numbers, logical position p of sequence b living in block
  *                      block_table[b*max_blocks + p/block_size], row p % block_size
- *   block_size          power of two in [1, 1024] when paged
+ *   block_size          power of two in [1, 1024] when paged; the paged cache holds fewer than
+ *                      2^32 rows (num_blocks * Hkv * block_size), as any cache that fits in
+ *                      one MI355X's memory does (a contiguous cache is checked: B*Hkv*n_cap)
  *   len         (device) int32 [B]: current length of each sequence, the current token
  *                      included; 0 <= len[b] <= max_len
  *   max_len             host-side bound of len[] used to size grids (no device read)
