@@ -481,11 +481,16 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     };
 
     // ---- tile loads (issued one tile ahead of the math) ------------------------------------
-    // The gather through a block table streams its rows with nontemporal loads: on MI355X that
-    // made the paged fast step about 5 % faster, while it slowed the contiguous fast step and
-    // the dense step with its logit writes.
-    auto load16 = [](const void* p) -> u32x4 {
-        if constexpr (SPARSE && PAGED) return __builtin_nontemporal_load((const u32x4*)p);
+    // Cache policy of the V loads, chosen by measurement on MI355X: nontemporal V loads make
+    // the dense step 3-4 % faster (128K: 416 -> 403 us; 512K: 466 -> 449) and the paged fast
+    // step 10 % faster (35.1 -> 31.6 us on the ragged batch); on the contiguous fast step they
+    // gain nothing.  Nontemporal K loads (the K rows are read in the MFMA operand layout, 64
+    // bytes from each of 16 rows per wavefront load) slowed every step, so K loads stay
+    // ordinary.
+    constexpr bool kNtV = !SPARSE || PAGED;
+    auto load_k = [](const void* p) -> u32x4 { return *(const u32x4*)p; };
+    auto load_v = [](const void* p) -> u32x4 {
+        if constexpr (kNtV) return __builtin_nontemporal_load((const u32x4*)p);
         else return *(const u32x4*)p;
     };
     auto issue = [&](Regs& r, int tile) {
@@ -497,7 +502,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             for (int c = 0; c < C::kNQ; ++c) {
                 if constexpr (BF) {
                     const uint16_t* kp = (const uint16_t*)a.k + (uint64_t)row * D;
-                    r.k[st][c] = load16(kp + 32 * c + 8 * q4);
+                    r.k[st][c] = load_k(kp + 32 * c + 8 * q4);
                 } else {
                     const float* kp = (const float*)a.k + (uint64_t)row * D;
                     r.k[st][c] = *(const f32x4*)(kp + 16 * c + 4 * q4);
@@ -509,7 +514,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             for (int j = 0; j < C::kNV; ++j) {
                 const int rr = j * C::kRPI + lane / C::kLPR;
                 const uint32_t row = slot_row(min(sb + rr, s1 - 1));
-                r.v[j] = load16((const uint16_t*)a.v + (uint64_t)row * D + (lane % C::kLPR) * 8);
+                r.v[j] = load_v((const uint16_t*)a.v + (uint64_t)row * D + (lane % C::kLPR) * 8);
             }
         } else {
 #pragma unroll
