@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-layered", action="store_true",
                     help="skip the layer-wise slow-step measurement (sequential vs pipelined)")
+    ap.add_argument("--no-spread", action="store_true",
+                    help="skip the per-call spread pass (it also runs the dense step without "
+                         "logits, which a kernel trace would mix into the dense kernel's stats)")
     ap.add_argument("--no-routed", action="store_true",
                     help="skip the routed fast-step measurement on sink-dominated workloads")
     ap.add_argument("--retention-sweep", action="store_true",
@@ -416,9 +419,10 @@ def main():
 
     # Spread: one more pass with events around every single call (p10 / p50 / p90), and the
     # dense step without its logit write as a reference for the cost of the logits.
-    print("# per-call spread", file=sys.stderr, flush=True)
     dense_calls, nolog_calls, fast_calls = [], [], []
-    for li in range(L):
+    if not args.no_spread:
+        print("# per-call spread", file=sys.stderr, flush=True)
+    for li in range(0 if args.no_spread else L):
         d0 = descs[li]
         e = [ev() for _ in range(2 * wl.cycle + 2)]
         e[0].record(stream)
@@ -442,6 +446,8 @@ def main():
         fast_calls += [1e3 * e[2 * t].elapsed_time(e[2 * t + 1]) for t in range(1, wl.cycle)]
 
     def pct(xs):
+        if not xs:
+            return None
         xs = sorted(xs)
         at = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
         return [round(at(0.1), 2), round(at(0.5), 2), round(at(0.9), 2)]
@@ -499,7 +505,7 @@ def main():
         "fast_gbps": round(fast_gbps, 1),
         "select_gbps": round(select_gbps, 1),
         "fast_pct_peak": round(100 * fast_gbps / PEAK_HBM_GBS, 1),
-        "dense_nolog_us": round(mean(nolog_calls), 2),
+        "dense_nolog_us": round(mean(nolog_calls), 2) if nolog_calls else None,
         "spread_us": {"p10_p50_p90": True, "dense": pct(dense_calls),
                       "dense_nolog": pct(nolog_calls), "fast": pct(fast_calls),
                       "calls": {"dense": len(dense_calls), "fast": len(fast_calls)}},
