@@ -158,7 +158,7 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     p->off_keys = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
     p->off_hist = off;   off += align_up(B * Hkv * kSelHistBins * sizeof(uint32_t));
     p->off_state = off;  off += align_up(B * Hkv * 4 * sizeof(int32_t));
-    p->off_counts = off; off += align_up(B * Hkv * nc * 2 * sizeof(uint32_t));
+    p->off_counts = off; off += align_up(B * Hkv * nc * 3 * sizeof(uint32_t));
     p->off_cand = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
     p->off_cand_n = off; off += align_up(B * Hkv * nc * sizeof(uint32_t));
     p->bytes = off;

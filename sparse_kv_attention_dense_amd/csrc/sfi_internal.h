@@ -72,7 +72,8 @@ struct SelArgs {
     uint32_t* keys;                  // [B][Hkv][nchunk*kSelChunk]
     uint32_t* hist;                  // [B][Hkv][kSelHistBins]: digit 0 of the keys
     int32_t* state;                  // [B][Hkv][4]: prefix, k_rem, nJ, take_all
-    uint32_t* counts;                // [B][Hkv][nchunk][2]: kept keys > T, == T per chunk
+    uint32_t* counts;                // [B][Hkv][nchunk][3]: keys of higher digit-0 bins,
+                                     // candidates > T, kept keys == T, per chunk
     uint32_t* cand;                  // [B][Hkv][nchunk][kSelChunk]: keys of the digit-0 bin
     uint32_t* cand_n;                // [B][Hkv][nchunk]: candidates per chunk
     int32_t unit_path;               // 1: one workgroup per (b, KV head) does everything

@@ -8,14 +8,15 @@
 //   2. evidence_kernel    f(j) = sum_{i in group} exp(z_ij - LSE_J,i) for the chunk, stored as
 //                          uint32 keys (the bit pattern of a non-negative float orders like
 //                          the float), plus a histogram of digit 0 (key bits 30..19)
-//   3. radix_step_kernel  the digit-0 bin that holds the k-th largest key
-//   4. candidate_kernel   per chunk: the keys of that bin, compacted into the chunk's region,
-//                          and the number of keys in higher bins
-//   5. resolve_kernel     one workgroup per unit: digits 1 and 2 (bits 18..9, 8..0) over the
+//   3. candidate_kernel   per chunk: the digit-0 bin that holds the k-th largest key (every
+//                          workgroup scans the unit's histogram), then the keys of that bin
+//                          compacted into the chunk's region, and the number of keys in
+//                          higher bins
+//   4. resolve_kernel     one workgroup per unit: digits 1 and 2 (bits 18..9, 8..0) over the
 //                          candidates give the key T of the k-th largest evidence and how many
 //                          keys equal to T are kept; then the per-chunk numbers of kept keys
 //                          above T and equal to T
-//   6. emit_kernel        ordered compaction.  Position j of J is kept when key > T, or
+//   5. emit_kernel        ordered compaction.  Position j of J is kept when key > T, or
 //                          key == T and fewer than k_rem earlier positions have key == T (ties
 //                          go to the lower position); kept positions are written in ascending
 //                          order after the sink positions [0, min(n_sink, N)).
@@ -211,96 +212,92 @@ __device__ __forceinline__ bool sel_active(uint32_t prefix, int32_t k_rem, int32
     return !take_all && k_rem > 0 && prefix != 0xffffffffu;
 }
 
-// Digit 0: the bin of the evidence histogram that holds the k_sel-th largest key; k_rem
-// becomes the rank inside that bin.
-__global__ void __launch_bounds__(kThreads) radix_step_kernel(SelArgs a) {
-    __shared__ uint32_t sh[4];
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-    const int unit = b * a.Hkv + h;
-    int32_t* st = a.state + unit * 4;
-    const int32_t nJ = j_range(a, b).nJ;
-    const int32_t take_all = a.k_sel >= nJ ? 1 : 0;
-    const int32_t k_rem = take_all ? nJ : a.k_sel;
-    const uint32_t prefix = (!take_all && k_rem == 0) ? 0xffffffffu : 0u;   // keep nothing
-    const bool active = sel_active(prefix, k_rem, take_all);
-    constexpr int kPer = kCBins0 / kThreads;          // bins per thread, ascending
-    const uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
-    uint32_t cnt[kPer];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        cnt[k] = active ? hg[kPer * tid + k] : 0u;
-        mine += cnt[k];
-    }
-    // number of keys in bins above this thread's bins (threads hold ascending bins)
-    const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
-    const uint32_t total = block_sum_u(mine, sh);
-    const uint32_t above = total - below_incl;
-    if (active && above < (uint32_t)k_rem && (uint32_t)k_rem <= above + mine) {
-        uint32_t cum = above;
-        for (int k = kPer - 1; k >= 0; --k) {
-            if (cum + cnt[k] >= (uint32_t)k_rem) {
-                st[0] = (int32_t)((uint32_t)(kPer * tid + k) << kCShift[0]);
-                st[1] = k_rem - (int32_t)cum;
-                st[2] = nJ;
-                st[3] = take_all;
-                break;
-            }
-            cum += cnt[k];
-        }
-    }
-    if (!active && tid == 0) {
-        st[0] = (int32_t)prefix;
-        st[1] = k_rem;
-        st[2] = nJ;
-        st[3] = take_all;
-    }
-}
+// counts: [unit][chunk][3] = (keys in higher digit-0 bins, candidates above T, kept keys
+// equal to T); the first is written by the candidate pass, the others by the resolve pass.
+constexpr int kCountSlots = 3;
 
-// Loads the 16 consecutive keys of thread tid in chunk c as four 16-byte loads (a chunk holds
-// kSelChunk keys in the workspace whatever its length, so the loads stay inside it); keys at
-// or past cnt read as 0.
-__device__ __forceinline__ void load_chunk_keys(const SelArgs& a, int unit, int c, int cnt,
-                                                uint32_t* kv) {
+// Loads the 16 consecutive keys of thread tid in chunk c as four 16-byte loads.  A chunk holds
+// kSelChunk keys in the workspace whatever its length, so the loads stay inside it and can be
+// issued before the chunk's length is known; the caller masks keys at or past the length.
+__device__ __forceinline__ void load_chunk_keys(const SelArgs& a, int unit, int c, uint32_t* kv) {
     const int tid = threadIdx.x;
     const u32x4* keys4 =
         (const u32x4*)(a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk) + tid * (kPerThread / 4);
 #pragma unroll
     for (int k4 = 0; k4 < kPerThread / 4; ++k4) {
-        const u32x4 x = tid * kPerThread < cnt ? keys4[k4] : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 x = keys4[k4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) kv[4 * k4 + e] = x[e];
     }
-#pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-        if (tid * kPerThread + k >= cnt) kv[k] = 0u;
 }
 
-// Per chunk: compacts the keys of the digit-0 bin into the chunk's own region of the candidate
-// buffer (no cross-workgroup atomics), writes their number to cand_n[chunk] and
-// counts[chunk] = (keys in higher digit-0 bins, 0); the resolve pass adds the candidates'
-// share.  Inactive units get their final counts here: everything (take_all) or nothing.
+// Per chunk, with digit 0 found by every workgroup of the unit from the evidence histogram
+// (an L2-resident 16 KB read, so no separate launch is needed; workgroup 0 stores the state):
+// compacts the keys of the digit-0 bin that holds the k-th largest key into the chunk's own
+// region of the candidate buffer (no cross-workgroup atomics), writes their number to
+// cand_n[chunk] and counts[chunk] = (keys in higher digit-0 bins, 0, 0); the resolve pass fills
+// in the candidates' share.  Inactive units get their final counts here: everything (take_all)
+// or nothing.  The histogram, the keys and the length are loaded together at entry.
 __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
     __shared__ uint32_t sh[4];
+    __shared__ uint32_t s_sel[2];
+    constexpr int kPer = kCBins0 / kThreads;          // histogram bins per thread, ascending
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
-    const int32_t* st = a.state + unit * 4;
-    const uint32_t prefix = (uint32_t)st[0];
-    const int32_t k_rem = st[1], nJ = st[2], take_all = st[3];
+    uint32_t kv[kPerThread];
+    load_chunk_keys(a, unit, c, kv);
+    const uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
+    uint32_t bins[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) bins[k] = hg[kPer * tid + k];
+    const int32_t nJ = j_range(a, b).nJ;
+    const int32_t take_all = a.k_sel >= nJ ? 1 : 0;
+    int32_t k_rem = take_all ? nJ : a.k_sel;
+    uint32_t prefix = (!take_all && k_rem == 0) ? 0xffffffffu : 0u;   // keep nothing
+    const bool active = sel_active(prefix, k_rem, take_all);
+    if (active) {
+        uint32_t mine = 0;
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) mine += bins[k];
+        // keys in bins above this thread's bins
+        const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
+        const uint32_t total = block_sum_u(mine, sh);
+        const uint32_t above = total - below_incl;
+        if (above < (uint32_t)k_rem && (uint32_t)k_rem <= above + mine) {
+            uint32_t cum = above;
+            for (int k = kPer - 1; k >= 0; --k) {
+                if (cum + bins[k] >= (uint32_t)k_rem) {
+                    s_sel[0] = (uint32_t)(kPer * tid + k);
+                    s_sel[1] = cum;
+                    break;
+                }
+                cum += bins[k];
+            }
+        }
+        __syncthreads();
+        prefix = s_sel[0] << kCShift[0];
+        k_rem -= (int32_t)s_sel[1];
+    }
+    if (c == 0 && tid == 0) {
+        int32_t* st = a.state + unit * 4;
+        st[0] = (int32_t)prefix;
+        st[1] = k_rem;
+        st[2] = nJ;
+        st[3] = take_all;
+    }
     const int cnt = max(0, min(kSelChunk, nJ - c * kSelChunk));
-    uint32_t* cn = a.counts + ((int64_t)unit * a.nchunk + c) * 2;
+    uint32_t* cn = a.counts + ((int64_t)unit * a.nchunk + c) * kCountSlots;
     uint32_t* cand_n = a.cand_n + (int64_t)unit * a.nchunk + c;
-    if (!sel_active(prefix, k_rem, take_all) || cnt == 0) {
+    if (!active || cnt == 0) {
         if (tid == 0) {
             cn[0] = take_all ? (uint32_t)cnt : 0u;
             cn[1] = 0u;
+            cn[2] = 0u;
             *cand_n = 0u;
         }
         return;
     }
     const uint32_t d0 = prefix >> kCShift[0];
-    uint32_t kv[kPerThread];
-    load_chunk_keys(a, unit, c, cnt, kv);
     uint32_t gt = 0, nc = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -316,6 +313,7 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
         *cand_n = tot & 0xffffu;
         cn[0] = tot >> 16;
         cn[1] = 0u;
+        cn[2] = 0u;
     }
     uint32_t* out = a.cand + ((int64_t)unit * a.nchunk + c) * kSelChunk + (excl & 0xffffu);
 #pragma unroll
@@ -327,6 +325,15 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
     __shared__ uint32_t sh[4];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
+    // keys, earlier chunks' counts and the state are independent loads: issue them together
+    uint32_t kv[kPerThread];
+    load_chunk_keys(a, unit, c, kv);
+    uint32_t gtb = 0, eqb = 0;                        // kept positions in earlier chunks
+    for (int k = tid; k < c; k += kThreads) {
+        const uint32_t* ck = a.counts + ((int64_t)unit * a.nchunk + k) * kCountSlots;
+        gtb += ck[0] + ck[1];
+        eqb += ck[2];
+    }
     const int32_t* st = a.state + unit * 4;
     const uint32_t T = (uint32_t)st[0];
     const int32_t k_rem = st[1], nJ = st[2], take_all = st[3];
@@ -340,20 +347,13 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
     const int lo = c * kSelChunk;
     const int cnt = min(kSelChunk, nJ - lo);
     if (cnt <= 0) return;
-    // kept positions in earlier chunks
-    uint32_t gtb = 0, eqb = 0;
-    for (int k = tid; k < c; k += kThreads) {
-        gtb += a.counts[((int64_t)unit * a.nchunk + k) * 2];
-        eqb += a.counts[((int64_t)unit * a.nchunk + k) * 2 + 1];
-    }
     gtb = block_sum_u(gtb, sh);
     eqb = block_sum_u(eqb, sh);
     const uint32_t kr = take_all ? 0u : (uint32_t)k_rem;
     const uint32_t base = (uint32_t)ns + gtb + min(eqb, kr);
-    // this thread's 16 consecutive positions
-    // this thread's 16 consecutive keys
-    uint32_t kv[kPerThread];
-    load_chunk_keys(a, unit, c, cnt, kv);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k)
+        if (tid * kPerThread + k >= cnt) kv[k] = 0u;
     uint32_t my_eq = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -488,17 +488,20 @@ __global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
     UnitShared& sm = rs.u;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
+    const uint32_t* cand = a.cand + (int64_t)unit * a.nchunk * kSelChunk;
+    const uint32_t* cand_n = a.cand_n + (int64_t)unit * a.nchunk;
+    // the candidate pass wrote cand_n for all nchunk chunks, so the first group's numbers can
+    // be loaded with the state
+    const uint32_t n_first = tid < a.nchunk ? cand_n[tid] : 0u;
     int32_t* st = a.state + unit * 4;
     uint32_t prefix = (uint32_t)st[0];
     int32_t k_rem = st[1];
     const int32_t nJ = st[2], take_all = st[3];
     if (!sel_active(prefix, k_rem, take_all)) return;
     const int nch = (nJ + kSelChunk - 1) / kSelChunk;
-    const uint32_t* cand = a.cand + (int64_t)unit * a.nchunk * kSelChunk;
-    const uint32_t* cand_n = a.cand_n + (int64_t)unit * a.nchunk;
     // scans the candidate numbers of chunks [g0, g0 + kCntGroup); returns their total
     auto load_group = [&](int g0) -> uint32_t {
-        const uint32_t n = g0 + tid < nch ? cand_n[g0 + tid] : 0u;
+        const uint32_t n = g0 == 0 ? (tid < nch ? n_first : 0u) : (g0 + tid < nch ? cand_n[g0 + tid] : 0u);
         uint32_t tot;
         const uint32_t ex = unit_scan(n, sm, &tot);
         rs.off[tid] = ex;
@@ -580,9 +583,9 @@ __global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
         });
         __syncthreads();
         if (g0 + tid < nch) {
-            uint32_t* cn = a.counts + ((int64_t)unit * a.nchunk + g0 + tid) * 2;
-            cn[0] += rs.gt[tid];
-            cn[1] = rs.eq[tid];
+            uint32_t* cn = a.counts + ((int64_t)unit * a.nchunk + g0 + tid) * kCountSlots;
+            cn[1] = rs.gt[tid];
+            cn[2] = rs.eq[tid];
         }
         __syncthreads();
     }
@@ -848,7 +851,6 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     const dim3 g_unit(a.Hkv, a.B);
     hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
     hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
-    hipLaunchKernelGGL(radix_step_kernel, g_unit, blk, 0, s, a);
     hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
     hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
     hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);
