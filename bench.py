@@ -266,6 +266,35 @@ def retention_sweep(B, torch, synth, ratios=(0.016, 0.031, 0.0625, 0.125, 0.25, 
             "dense_us": round(dense_us, 2), "dense_nolog_us": round(nolog_us, 2), "rows": rows}
 
 
+def synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out, lse, ws,
+                                   idx_stride, L):
+    """Fast steps on the workload's synthetic selections instead of the Selector's: sentence-
+    like spans of 10-40 positions, and uniformly scattered positions (the two variants the
+    ragged workload is stated with), each timed over whole cycles of every rotated layer."""
+    dev = "cuda"
+    res = {}
+    for kind in ("spans", "scattered"):
+        sets = []
+        for li in range(L):
+            i, n = synth.synthetic_index_set(layers[li], kind, seed=900 + li, idx_stride=idx_stride)
+            sets.append((i.to(dev), n.to(dev)))
+
+        def run():
+            for li in range(L):
+                for t in range(1, wl.cycle):
+                    B.sfi_sparse_decode(descs[li][t], queries[li][t], sets[li][0], idx_stride,
+                                        sets[li][1], wl.n_recent, None, out, lse, ws)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        res[kind + "_us"] = round(1e3 * e0.elapsed_time(e1) / (L * (wl.cycle - 1)), 2)
+    return res
+
+
 def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
                       idx_stride, slots: int = 4, reps: int = 5):
     """The slow step over every rotated layer: the per-layer calls one after another, against
@@ -452,6 +481,10 @@ def main():
         at = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
         return [round(at(0.1), 2), round(at(0.5), 2), round(at(0.9), 2)]
 
+    print("# fast steps on synthetic selections", file=sys.stderr, flush=True)
+    synth_fast = synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out,
+                                                lse, ws, idx_stride, L)
+
     routed = None
     if wl.sink and not args.no_routed:
         routed = routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
@@ -519,6 +552,7 @@ def main():
                           "algorithmic_bytes": int(f_bytes),
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
+    result["fast_synthetic_selections"] = synth_fast
     if routed is not None:
         result["routed_fast"] = routed
     if layered is not None:
