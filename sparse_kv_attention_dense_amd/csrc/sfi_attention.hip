@@ -482,12 +482,12 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 
     // ---- tile loads (issued one tile ahead of the math) ------------------------------------
     // Cache policy of the V loads, chosen by measurement on MI355X: nontemporal V loads make
-    // the dense step 3-4 % faster (128K: 416 -> 403 us; 512K: 466 -> 449) and the paged fast
-    // step 10 % faster with span selections (35.1 -> 31.6 us on the ragged batch; unchanged
-    // with the Selector's own selections); on the contiguous fast step they gain nothing.  Nontemporal K loads (the K rows are read in the MFMA operand layout, 64
-    // bytes from each of 16 rows per wavefront load) slowed every step, so K loads stay
-    // ordinary.
-    constexpr bool kNtV = !SPARSE || PAGED;
+    // the dense step 3-4 % faster (128K: 416 -> 403 us; 512K: 466 -> 449).  In the fast step
+    // they gain nothing in the benchmark's rotation of layers (contiguous 128K 20.8 us either
+    // way, ragged paged batch 31.0 vs 31.1 us), so it keeps ordinary loads.  Nontemporal K
+    // loads (the K rows are read in the MFMA operand layout, 64 bytes from each of 16 rows
+    // per wavefront load) slowed every step, so K loads stay ordinary.
+    constexpr bool kNtV = !SPARSE;
     auto load_k = [](const void* p) -> u32x4 { return *(const u32x4*)p; };
     auto load_v = [](const void* p) -> u32x4 {
         if constexpr (kNtV) return __builtin_nontemporal_load((const u32x4*)p);
