@@ -97,18 +97,44 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
     const int S = SPARSE ? a.nsplit : splits_of(a, a.len[b]), rec = a.rec_floats;
     const float* base = a.part + (int64_t)(b * a.Hkv + h) * a.nsplit * rec;   // nsplit records per unit
     const int dim = tid % D, ph = tid / D;
+    // Records are merged kMB per thread at a time, all loaded before any is used (one memory
+    // round trip per batch); records past S read record 0 and count as empty.  Few splits (a
+    // ragged batch has 2 per sequence) take small batches, so no loads are wasted.
     float M = -INFINITY, L = 0.f, A = 0.f;
-#pragma unroll 8
-    for (int s = ph; s < S; s += R) {
-        const float* r = base + (int64_t)s * rec;
-        const float m = r[G * D + 2 * g], l = r[G * D + 2 * g + 1], x = r[g * D + dim];
-        const float Mn = fmaxf(M, m);
-        if (Mn == -INFINITY) continue;                 // nothing attended so far
-        const float c_old = exp2_fast(M - Mn), c_new = exp2_fast(m - Mn);
-        L = L * c_old + l * c_new;
-        A = A * c_old + x * c_new;
-        M = Mn;
-    }
+    auto merge_batches = [&](auto kmb) {
+        constexpr int kMB = decltype(kmb)::value;
+        for (int s0 = ph; s0 < S; s0 += R * kMB) {
+            float m[kMB], l[kMB], x[kMB];
+#pragma unroll
+            for (int u = 0; u < kMB; ++u) {
+                const int s = s0 + u * R;
+                const float* r = base + (int64_t)(s < S ? s : 0) * rec;
+                m[u] = r[G * D + 2 * g];
+                l[u] = r[G * D + 2 * g + 1];
+                x[u] = r[g * D + dim];
+            }
+            float Mb = M;
+#pragma unroll
+            for (int u = 0; u < kMB; ++u) {
+                if (s0 + u * R >= S) m[u] = -INFINITY;
+                Mb = fmaxf(Mb, m[u]);
+            }
+            const float Mu = (Mb == -INFINITY) ? 0.f : Mb;   // nothing attended yet: weights 0
+            const float c = exp2_fast(M - Mu);
+            L *= c;
+            A *= c;
+#pragma unroll
+            for (int u = 0; u < kMB; ++u) {
+                const float w = exp2_fast(m[u] - Mu);
+                L += w * l[u];
+                A += w * x[u];
+            }
+            M = Mb;
+        }
+    };
+    if (S <= 2 * R) merge_batches(std::integral_constant<int, 2>{});
+    else if (S <= 8 * R) merge_batches(std::integral_constant<int, 8>{});
+    else merge_batches(std::integral_constant<int, 16>{});
     s_m[tid] = M;
     s_l[tid] = L;
     s_a[tid] = A;
