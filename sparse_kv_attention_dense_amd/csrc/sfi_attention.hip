@@ -4,14 +4,16 @@
 // attention_kernel: one workgroup (4 wavefronts) owns one (batch b, KV head h, split s): a
 // contiguous range of "slots".  A slot is a key position: in the dense step slot ==
 // position; in the sparse step slot k < n_idx is idx[k] and the remaining slots walk the
-// recent window [r0, len).  Each wavefront takes 32-slot tiles round-robin and keeps an
-// online softmax (m, l, acc) for the G query heads of the group:
+// recent window [r0, len).  Each wavefront takes 32-slot tiles (round-robin, or a contiguous
+// quarter of the split when the dense step stages its logits) and keeps an online softmax
+// (m, l, acc) for the G query heads of the group:
 //   - S^T = K_tile * Q^T on MFMA (v_mfma_f32_16x16x32_bf16, or 16x16x4 f32): the 16 rows of
 //     the A operand are 16 key rows, read straight from HBM as 16-byte pieces, and the 16
 //     columns are the (zero-padded) query heads, so each K row is read once for the group
 //     (grouped-query attention without repeating K/V, SinkRouter Sec. 4.3).
-//   - the fp32 logits z = S * 1/sqrt(d) go to HBM as float4 stores (dense step only; SFI
-//     Sec. 4.2 needs the logits exposed for the Selector).
+//   - the fp32 logits z = S * 1/sqrt(d) go to HBM (dense step only; SFI Sec. 4.2 needs the
+//     logits exposed for the Selector): staged per wavefront in LDS and written as runs of at
+//     least 2 KB per head when G <= 4, else as float4 stores per tile.
 //   - O^T += V_tile^T * P^T on MFMA; bf16 V rows are staged through LDS and read back
 //     transposed, and P is split into a bf16 high part and a bf16 residual so the product
 //     keeps about 16 bits of the fp32 weight.
@@ -85,10 +87,9 @@ __device__ bool locate_split(const AttnArgs& a, int wg, int* sh, int* loc) {
 }
 
 // Merges the nsplit partial records of query head i of batch b into out and lse.  Thread
-// (dim, phase) folds splits phase, phase + R, ... into a running (M, L, A) with the online
-// log-sum-exp rule; every load is independent of the running values, so the record set is
-// fetched in one round trip.  The R phases then merge through LDS (s_m, s_l, s_a: kThreads
-// floats each).
+// (dim, phase) folds splits phase, phase + R, ... into a running (M, L, A) with the
+// log-sum-exp rule, a batch of records at a time; the R phases then merge through LDS (s_m,
+// s_l, s_a: kThreads floats each).
 template <int D, bool SPARSE>
 __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s_l, float* s_a) {
     constexpr int R = kThreads / D;
