@@ -12,8 +12,8 @@
 //     columns are the (zero-padded) query heads, so each K row is read once for the group
 //     (grouped-query attention without repeating K/V, SinkRouter Sec. 4.3).
 //   - the fp32 logits z = S * 1/sqrt(d) go to HBM (dense step only; SFI Sec. 4.2 needs the
-//     logits exposed for the Selector): staged per wavefront in LDS and written as runs of at
-//     least 2 KB per head when G <= 4, else as float4 stores per tile.
+//     logits exposed for the Selector): staged per wavefront in LDS and written as runs of
+//     1-2 KB or more per head when G <= 8, else as float4 stores per tile, all nontemporal.
 //   - O^T += V_tile^T * P^T on MFMA; bf16 V rows are staged through LDS and read back
 //     transposed, and P is split into a bf16 high part and a bf16 residual so the product
 //     keeps about 16 bits of the fp32 weight.
@@ -464,17 +464,17 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 
     unsigned char* vstage = raw + w * kTile * C::kVRow;
 
-    // Tiles of this wavefront.  Logits in runs: with G <= 4 the wavefront takes a contiguous
+    // Tiles of this wavefront.  Logits in runs: with G <= 8 the wavefront takes a contiguous
     // quarter of the split, stages its logits in LDS and writes kZRows / G tiles at a time,
-    // runs of at least 2 KB per head instead of 128 B per tile (HBM3E turns short writes
-    // mixed into the read stream into lost read bandwidth; on MI355X the dense step at 128K
-    // drops by about 11 us).  With larger groups the runs would be 1 KB or shorter, which
-    // measured slower than the per-tile writes, so those take tiles w, w + 4, ... and write
-    // each tile's logits directly, as does the sparse kernel (no logits).
+    // runs of 1-2 KB or more per head instead of 128 B per tile, with nontemporal stores (HBM3E
+    // turns short writes mixed into the read stream into lost read bandwidth; on MI355X the
+    // runs and the store policy together take the dense step at 128K from 428 to 374 us).
+    // Larger groups would get runs under 1 KB; they take tiles w, w + 4, ... and write each
+    // tile's logits directly, as does the sparse kernel (no logits).
     // The tile order depends on G only, so out and lse do not depend on whether logits are
     // requested.
     const int zF = C::kZRows / G;                     // tiles per staged run
-    const bool quarters = !SPARSE && zF >= 16;
+    const bool quarters = !SPARSE && zF >= 8;
     const bool staged = quarters && a.logits;
     const int ntiles = (nslots + kTile - 1) / kTile;
     const int tpw = (ntiles + kWaves - 1) / kWaves;
@@ -497,7 +497,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             const f32x4 z = *(const f32x4*)(zst + g * zF * kTile + 4 * o4);
             float* dst = a.logits + ((int64_t)b * a.Hq + hq0 + g) * a.logit_stride + p;
             if (p + 3 < s1) {
-                *(f32x4*)dst = z;
+                __builtin_nontemporal_store(z, (f32x4*)dst);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -609,7 +609,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
                     const int p0 = sb + 16 * st + 4 * q4;
                     const f32x4 z = S[st] * a.scale;
                     if (p0 + 3 < s1) {
-                        *(f32x4*)(logit_row + p0) = z;
+                        __builtin_nontemporal_store(z, (f32x4*)(logit_row + p0));
                     } else {
 #pragma unroll
                         for (int i = 0; i < 4; ++i)

@@ -41,7 +41,7 @@ def test_dense_matches_oracle(orc, name):
 
 
 @pytest.mark.parametrize("dtype,d,G", [("bf16", 64, 1), ("bf16", 128, 16), ("f32", 128, 2),
-                                       ("bf16", 128, 3)])
+                                       ("bf16", 128, 3), ("bf16", 128, 5), ("bf16", 64, 7)])
 def test_dense_head_shapes(orc, dtype, d, G):
     wl = synth.Workload(f"shape_{dtype}_{d}_{G}", 7100 + d + G, 2, 2 * G, 2, d, dtype, 1500,
                         4, 64, 128, 2)
