@@ -36,6 +36,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.693147180559945309417f;
 
@@ -253,12 +254,22 @@ __device__ bool route_decide(const AttnArgs& a, int b, int hq0, const RoutePre<B
 template <bool BF, int D, bool PAGED, bool SPARSE>
 struct Cfg {
     static constexpr int kVRow = D * 2 + 16;                       // staged bf16 row, bytes
-    static constexpr int kVStage = BF ? kWaves * kTile * kVRow : 0;
+    // The dense step stages V half a tile at a time (16 slots, k = 16 MFMAs) so that its LDS
+    // holds longer logit runs; the fast step stages whole tiles (k = 32 MFMAs), which measured
+    // faster there (20.2 vs 21.0 us at 128K).
+    static constexpr bool kHalfV = BF && !SPARSE;
+    static constexpr int kVRows = kHalfV ? kTile / 2 : kTile;      // V rows staged at a time
+    static constexpr int kVStage = BF ? kWaves * kVRows * kVRow : 0;
     static constexpr int kRed = kWaves * kMaxG * (D + 2) * 4;      // cross-wave merge
-    static constexpr int kRaw = kVStage > kRed ? kVStage : kRed;
-    // dense: per-wavefront staging of fp32 logits, 64 (head, tile) rows of 32 positions
-    static constexpr int kZRows = 64;
+    // dense: per-wavefront staging of fp32 logits, kZRows (head, tile) rows of 32 positions;
+    // 120 rows (15 KB) for bf16 d = 128 keeps two workgroups per CU in 160 KB of LDS
+    static constexpr int kZRows = (BF && D == 128) ? 120 : 64;
     static constexpr int kZWave = SPARSE ? 4 : kZRows * kTile;     // floats per wavefront
+    // the cross-wave merge reuses the logit staging area when that is large enough (it runs
+    // after the last run has been written), else the V staging area
+    static constexpr bool kRedInZ = !SPARSE && kWaves * kZWave * 4 >= kRed;
+    static constexpr int kRaw0 = kRedInZ ? kVStage : (kVStage > kRed ? kVStage : kRed);
+    static constexpr int kRaw = kRaw0 > 64 ? kRaw0 : 64;
     static constexpr int kNQ = BF ? D / 32 : D / 16;               // Q / K fragments per row
     static constexpr int kNV = BF ? D / 16 : 2 * 4 * (D / 16);     // V registers per tile
     static constexpr int kRPI = 1024 / (2 * D);                    // bf16 V rows per wave load
@@ -462,7 +473,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    unsigned char* vstage = raw + w * kTile * C::kVRow;
+    unsigned char* vstage = raw + w * C::kVRows * C::kVRow;
 
     // Tiles of this wavefront.  Logits in runs: with G <= 8 the wavefront takes a contiguous
     // quarter of the split, stages its logits in LDS and writes kZRows / G tiles at a time,
@@ -561,7 +572,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         const int sb = s0 + tile * kTile;
         if constexpr (BF) {
 #pragma unroll
-            for (int j = 0; j < C::kNV; ++j) {
+            for (int j = 0; j < (C::kHalfV ? C::kNV / 2 : C::kNV); ++j) {   // rows staged first
                 const int rr = j * C::kRPI + lane / C::kLPR;
                 *(u32x4*)(vstage + rr * C::kVRow + (lane % C::kLPR) * 16) = r.v[j];
             }
@@ -635,7 +646,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
                 p[st][i] = exp2_fast(sv[st][i] - m_use);
                 l_run += p[st][i];
             }
-        if constexpr (BF) {
+        if constexpr (BF && !C::kHalfV) {
             // P^T as the B operand: virtual k = 8*q4 + e maps to slot 4*q4 + e of block 0
             // (e < 4) or of block 1 (e >= 4); the V^T A operand uses the same map.
             bf16x8 ph, pl;
@@ -659,6 +670,40 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
                 const bf16x8 vab = __builtin_bit_cast(bf16x8, va);
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vab, ph, acc[mb], 0, 0, 0);
                 acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vab, pl, acc[mb], 0, 0, 0);
+            }
+        } else if constexpr (BF) {
+            // V in two halves of 16 slots, each staged through LDS and read back transposed as
+            // the A operand of a k = 16 MFMA whose B operand is P^T for the same slots: lane
+            // (q4, n16) holds slots 16*st + 4*q4 + i of head n16.  P is split into a bf16 high
+            // part and a bf16 residual (two MFMAs) to keep about 16 bits of the weight.
+            const uint16_t* vb16 = (const uint16_t*)vstage;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                if (st == 1) {
+                    wave_lds_sync();                    // half 0 is read before it is replaced
+#pragma unroll
+                    for (int j = C::kNV / 2; j < C::kNV; ++j) {
+                        const int rr = j * C::kRPI + lane / C::kLPR - kTile / 2;
+                        *(u32x4*)(vstage + rr * C::kVRow + (lane % C::kLPR) * 16) = r.v[j];
+                    }
+                }
+                s16x4 ph, pl;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const __bf16 hi = (__bf16)p[st][i];
+                    ph[i] = __builtin_bit_cast(short, hi);
+                    pl[i] = __builtin_bit_cast(short, (__bf16)(p[st][i] - (float)hi));
+                }
+                wave_lds_sync();
+#pragma unroll
+                for (int mb = 0; mb < D / 16; ++mb) {
+                    s16x4 va;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        va[i] = (short)vb16[(4 * q4 + i) * (C::kVRow / 2) + 16 * mb + n16];
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, ph, acc[mb], 0, 0, 0);
+                    acc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pl, acc[mb], 0, 0, 0);
+                }
             }
         } else {
 #pragma unroll
@@ -699,7 +744,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 
     // ---- merge the four wavefronts, write this split's partial -----------------------------
     __syncthreads();
-    float* red = (float*)raw;                         // [kWaves][kMaxG][D+2]
+    float* red = C::kRedInZ ? zstage : (float*)raw;   // [kWaves][kMaxG][D+2]
     if (n16 < G) {
         float* rp = red + (w * kMaxG + n16) * (D + 2);
 #pragma unroll
