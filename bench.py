@@ -17,6 +17,8 @@ spread_us gives p10/p50/p90 over single calls each bracketed by its own events (
 adds about 1.5 us to a call, so these sit above the block means), and dense_nolog_us the dense
 step without its logit write.
 cpu_baseline = the fp64 CPU oracle timed on the host on whole cycles of one layer.
+read_yardstick = a plain sequential read of 4 GiB (sfi_stream_read) on the same box; the
+rooflines also give the dense and fast rates as a fraction of it, next to the 8 TB/s peak.
 """
 from __future__ import annotations
 
@@ -166,6 +168,32 @@ def copy_calibration(mib: int, reps: int = 3):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(f"# copy calibration: {reps} copies of {mib} MiB", file=sys.stderr, flush=True)
+
+
+def read_yardstick(B, torch, gib: int = 4, grids=(1024, 2048, 4096), reps: int = 10):
+    """Achievable HBM read bandwidth on this machine: sfi_stream_read over a zeroed buffer of
+    `gib` GiB (far beyond the 256 MB Infinity Cache), mean of `reps` event-timed launches for
+    each grid size; the best grid is reported."""
+    buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    per_grid = {}
+    for g in grids:
+        for _ in range(2):
+            B.sfi_stream_read(buf, g, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            B.sfi_stream_read(buf, g, sink)
+        e1.record(stream)
+        e1.synchronize()
+        per_grid[g] = buf.numel() / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    best = max(per_grid, key=per_grid.get)
+    return {"kernel": "sfi_stream_read (sequential 16-byte nontemporal loads)",
+            "bytes": gib << 30, "workgroups": best, "gbps": round(per_grid[best], 1),
+            "gbps_by_workgroups": {str(g): round(v, 1) for g, v in per_grid.items()}}
 
 
 def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
@@ -495,6 +523,9 @@ def main():
         layered = layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
                                     masks, ws, idx_stride)
 
+    print("# streaming-read yardstick", file=sys.stderr, flush=True)
+    yard = read_yardstick(B, torch)
+
     lens0 = layers[0].len0_host
     n_idx_host = nidxs[0].cpu().tolist()
     mask_host = masks[0].cpu().tolist() if masks[0] is not None else None
@@ -552,6 +583,9 @@ def main():
                           "algorithmic_bytes": int(f_bytes),
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
+    result["read_yardstick"] = yard
+    result["roofline"]["frac_of_measured_read"] = round(dense_gbps / yard["gbps"], 4)
+    result["fast_roofline"]["frac_of_measured_read"] = round(fast_gbps / yard["gbps"], 4)
     result["fast_synthetic_selections"] = synth_fast
     if routed is not None:
         result["routed_fast"] = routed

@@ -210,6 +210,19 @@ sfi_status sfi_slow_step_layers(
 size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,
                            int32_t n_recent);
 
+/* Measurement yardstick, not a step of the method: a plain sequential read of `bytes` bytes
+ * of device memory at `buf` by `n_workgroups` workgroups of 256 threads, each reading one
+ * contiguous chunk with 16-byte loads.  Timing it with events on `stream` gives the read
+ * bandwidth the memory system delivers on this device, against which the attention kernels'
+ * algorithmic rates are also reported (the datasheet peak is not reachable).
+ *   buf   (device) 16-byte aligned, bytes > 0 and a multiple of 16; only read
+ *   sink  (device) at least 64 uint32 words; written only if the XOR of all words read
+ *                  equals a fixed constant (practically never), so its contents are undefined
+ *   n_workgroups   1 ... 2^20
+ * SFI_E_INVALID for a null pointer, a bad size, alignment or count; asynchronous on stream. */
+sfi_status sfi_stream_read(const void* buf, uint64_t bytes, int32_t n_workgroups, uint32_t* sink,
+                           hipStream_t stream);
+
 /* Static description of a status code. */
 const char* sfi_status_string(sfi_status status);
 

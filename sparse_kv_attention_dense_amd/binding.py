@@ -21,7 +21,7 @@ SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE = 0, 1, 2
 
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
             "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_workspace_bytes",
-            "sfi_status_string")
+            "sfi_stream_read", "sfi_status_string")
 
 
 class SfiError(RuntimeError):
@@ -62,10 +62,11 @@ def lib():
                                            ctypes.c_float, P, P, P, P, P, P]
         L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
         L.sfi_workspace_bytes.restype = ctypes.c_size_t
+        L.sfi_stream_read.argtypes = [P, ctypes.c_uint64, i32, P, P]
         L.sfi_status_string.argtypes = [ctypes.c_int]
         L.sfi_status_string.restype = ctypes.c_char_p
         for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
-                  "sfi_sparse_decode_routed", "sfi_slow_step_layers"):
+                  "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_stream_read"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -148,6 +149,12 @@ def sfi_status_string(status: int) -> str:
 
 def sfi_workspace_bytes(desc: KVDesc, op: int, idx_stride: int = 0, n_recent: int = 0) -> int:
     return int(lib().sfi_workspace_bytes(desc.ref, int(op), int(idx_stride), int(n_recent)))
+
+
+def sfi_stream_read(buf, n_workgroups: int, sink, stream=None):
+    """Sequential read of the whole of `buf` (a measurement yardstick); sink: >= 64 int32."""
+    _check(lib().sfi_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(n_workgroups),
+                                 _ptr(sink), _stream(stream)), "sfi_stream_read")
 
 
 def sfi_dense_decode(desc: KVDesc, q, out, lse, logits, logit_stride: int, ws, stream=None):

@@ -441,6 +441,15 @@ SFI_EXPORT size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t
     return p.bytes;
 }
 
+SFI_EXPORT sfi_status sfi_stream_read(const void* buf, uint64_t bytes, int32_t n_workgroups,
+                                      uint32_t* sink, hipStream_t stream) {
+    if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || !aligned(buf, 16) ||
+        !aligned(sink, 4) || n_workgroups < 1 || n_workgroups > (1 << 20))
+        return SFI_E_INVALID;
+    return launch_stream_read(buf, bytes, n_workgroups, sink, stream) == hipSuccess ? SFI_OK
+                                                                                     : SFI_E_HIP;
+}
+
 SFI_EXPORT const char* sfi_status_string(sfi_status s) {
     switch (s) {
         case SFI_OK: return "SFI_OK: success";

@@ -13,7 +13,8 @@
 //     (grouped-query attention without repeating K/V, SinkRouter Sec. 4.3).
 //   - the fp32 logits z = S * 1/sqrt(d) go to HBM (dense step only; SFI Sec. 4.2 needs the
 //     logits exposed for the Selector): staged per wavefront in LDS and written as runs of
-//     1-2 KB or more per head when G <= 8, else as float4 stores per tile, all nontemporal.
+//     at least 1 KB per head (G <= 15 at bf16 d = 128, G <= 8 otherwise), else as float4
+//     stores per tile, all nontemporal.
 //   - O^T += V_tile^T * P^T on MFMA; bf16 V rows are staged through LDS and read back
 //     transposed, and P is split into a bf16 high part and a bf16 residual so the product
 //     keeps about 16 bits of the fp32 weight.
@@ -475,13 +476,15 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 
     unsigned char* vstage = raw + w * C::kVRows * C::kVRow;
 
-    // Tiles of this wavefront.  Logits in runs: with G <= 8 the wavefront takes a contiguous
+    // Tiles of this wavefront.  Logits in runs: when a run holds at least 8 tiles (kZRows / G
+    // >= 8: G <= 15 at bf16 d = 128, G <= 8 otherwise) the wavefront takes a contiguous
     // quarter of the split, stages its logits in LDS and writes kZRows / G tiles at a time,
-    // runs of 1-2 KB or more per head instead of 128 B per tile, with nontemporal stores (HBM3E
-    // turns short writes mixed into the read stream into lost read bandwidth; on MI355X the
-    // runs and the store policy together take the dense step at 128K from 428 to 374 us).
-    // Larger groups would get runs under 1 KB; they take tiles w, w + 4, ... and write each
-    // tile's logits directly, as does the sparse kernel (no logits).
+    // runs of 1 KB or more per head instead of 128 B per tile (3.75 KB at G = 4), with
+    // nontemporal stores (HBM3E turns short writes mixed into the read stream into lost read
+    // bandwidth; on MI355X the runs, the store policy and the half-tile V staging that makes
+    // room for them take the dense step at 128K from 428 to about 362 us).  Larger groups
+    // would get runs under 1 KB; they take tiles w, w + 4, ... and write each tile's logits
+    // directly, as does the sparse kernel (no logits).
     // The tile order depends on G only, so out and lse do not depend on whether logits are
     // requested.
     const int zF = C::kZRows / G;                     // tiles per staged run

@@ -92,4 +92,10 @@ struct MaskArgs {
 
 hipError_t launch_sink_mask(const MaskArgs& a, hipStream_t stream);
 
+// Streaming-read yardstick (sfi_stream.hip): n_wg workgroups each read a contiguous chunk of
+// buf (bytes a multiple of 16); sink is a device buffer of kStreamSinkWords words.
+constexpr int kStreamSinkWords = 64;
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, int n_wg, uint32_t* sink,
+                              hipStream_t stream);
+
 }  // namespace sfi

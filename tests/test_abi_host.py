@@ -184,3 +184,14 @@ def test_slow_step_layers_validation(L):
     assert call(head_mask=ptrs(n), frac=1.5) == B.SFI_E_INVALID
     bad = (B.sfi_kv_desc * n)(_desc(), _desc(), _desc(head_dim=96))
     assert call(descs=bad) == B.SFI_E_UNSUPPORTED             # the last layer is checked too
+
+
+def test_stream_read_validation(L):
+    assert L.sfi_stream_read(None, 1 << 20, 1024, FAKE, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE, 1 << 20, 1024, None, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE, 0, 1024, FAKE, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE, (1 << 20) + 8, 1024, FAKE, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE + 8, 1 << 20, 1024, FAKE, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE, 1 << 20, 1024, FAKE + 2, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE, 1 << 20, 0, FAKE, None) == B.SFI_E_INVALID
+    assert L.sfi_stream_read(FAKE, 1 << 20, (1 << 20) + 1, FAKE, None) == B.SFI_E_INVALID
