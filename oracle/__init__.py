@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE.  Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 CPU-baseline leg import this package.  It builds ``liboracle.so`` with gcc (no fast-math)
-and wraps the four reference functions.  Inputs are torch tensors (any device: they are
+and wraps the reference functions.  Inputs are torch tensors (any device: they are
 copied to host memory) holding exactly the bytes the GPU reads; results are float64
 numpy arrays.
 """
@@ -55,9 +55,12 @@ def lib():
         L.orc_sink_mask.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_double, P]
         L.orc_sparse_routed.argtypes = [ctypes.POINTER(_Cache), P, P, ctypes.c_int32, P,
                                         ctypes.c_int32, P, P, ctypes.c_double, P, P, P, P]
+        L.orc_reorg.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_int32, P, P, P, P]
+        L.orc_sparse_compact.argtypes = [ctypes.POINTER(_Cache), P, P, P, P, ctypes.c_int32, P,
+                                         ctypes.c_int32, P, P, P]
         L.orc_threads.argtypes = []
         for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask, L.orc_threads,
-                  L.orc_sparse_routed):
+                  L.orc_sparse_routed, L.orc_reorg, L.orc_sparse_compact):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -169,6 +172,49 @@ def sparse(cache: Cache, q, idx, n_idx, n_recent: int, head_mask=None):
     s = cache._struct()
     rc = lib().orc_sparse(ctypes.byref(s), _ptr(qh), _ptr(idx), idx.shape[-1], _ptr(n_idx),
                           n_recent, _ptr(hm) if hm is not None else None, _ptr(out), _ptr(lse))
+    assert rc == 0
+    return out, lse
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a.cpu() if torch.is_tensor(a) else a, dtype=np.int32))
+
+
+def reorg(cache: Cache, idx, n_idx):
+    """Compact segment of the two-segment layout.  Returns (ck, cv, cpos): ck, cv hold
+    [B][Hkv][idx_stride][d] rows in the cache's element format (uint16 bf16 bits or float32),
+    cpos int32 [B][Hkv][idx_stride]."""
+    idx = _i32(idx)
+    n_idx = _i32(n_idx)
+    B, Hkv, stride = idx.shape
+    ck = np.empty((B, Hkv, stride, cache.d), cache.k.dtype)
+    cv = np.empty_like(ck)
+    cpos = np.empty((B, Hkv, stride), np.int32)
+    s = cache._struct()
+    rc = lib().orc_reorg(ctypes.byref(s), _ptr(idx), stride, _ptr(n_idx), _ptr(ck), _ptr(cv),
+                         _ptr(cpos))
+    assert rc == 0
+    return ck, cv, cpos
+
+
+def sparse_compact(cache: Cache, q, ck, cv, cpos, n_idx, n_recent: int, head_mask=None):
+    """Fast step on the two-segment layout.  Returns (out [B][Hq][d], lse [B][Hq]), float64."""
+    qh = _host_bytes(q)
+    ck = np.ascontiguousarray(ck)
+    cv = np.ascontiguousarray(cv)
+    assert ck.dtype == cache.k.dtype and cv.dtype == cache.k.dtype
+    cpos = _i32(cpos)
+    n_idx = _i32(n_idx)
+    hm = None
+    if head_mask is not None:
+        hm = np.ascontiguousarray(np.asarray(
+            head_mask.cpu() if torch.is_tensor(head_mask) else head_mask, dtype=np.uint8))
+    out = np.zeros((cache.B, cache.Hq, cache.d), np.float64)
+    lse = np.zeros((cache.B, cache.Hq), np.float64)
+    s = cache._struct()
+    rc = lib().orc_sparse_compact(ctypes.byref(s), _ptr(qh), _ptr(ck), _ptr(cv), _ptr(cpos),
+                                  cpos.shape[-1], _ptr(n_idx), n_recent,
+                                  _ptr(hm) if hm is not None else None, _ptr(out), _ptr(lse))
     assert rc == 0
     return out, lse
 

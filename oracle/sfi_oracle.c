@@ -220,6 +220,102 @@ int orc_sparse(const orc_cache* c, const void* q, const int32_t* idx, int32_t id
     return 0;
 }
 
+/* ---- Reorg and the two-segment fast step ----------------------------------------------- */
+
+int orc_reorg(const orc_cache* c, const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+              void* ck, void* cv, int32_t* cpos) {
+    const size_t es = c->is_bf16 ? 2 : 4;
+    const size_t rb = es * (size_t)c->d;
+    for (int u = 0; u < c->B * c->Hkv; ++u) {
+        int b = u / c->Hkv, h = u % c->Hkv;
+        int64_t N = c->len[b];
+        int32_t n = n_idx[u] < 0 ? 0 : (n_idx[u] > idx_stride ? idx_stride : n_idx[u]);
+        for (int32_t s = 0; s < idx_stride; ++s) {
+            int64_t slot = (int64_t)u * idx_stride + s;
+            int64_t p = s < n ? idx[slot] : -1;
+            unsigned char* dk = (unsigned char*)ck + slot * rb;
+            unsigned char* dv = (unsigned char*)cv + slot * rb;
+            if (p >= 0 && p < N) {
+                int64_t r = row_start(c, b, h, p);
+                memcpy(dk, (const unsigned char*)c->k + r * es, rb);
+                memcpy(dv, (const unsigned char*)c->v + r * es, rb);
+                cpos[slot] = (int32_t)p;
+            } else {
+                memset(dk, 0, rb);
+                memset(dv, 0, rb);
+                cpos[slot] = -1;
+            }
+        }
+    }
+    return 0;
+}
+
+int orc_sparse_compact(const orc_cache* c, const void* q, const void* ck, const void* cv,
+                       const int32_t* cpos, int32_t idx_stride, const int32_t* n_idx,
+                       int32_t n_recent, const uint8_t* head_mask, double* out, double* lse) {
+    const int G = c->Hq / c->Hkv;
+    const int units = c->B * c->Hq;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < units; ++u) {
+        int b = u / c->Hq, i = u % c->Hq, h = i / G;
+        int64_t N = c->len[b];
+        int64_t r0 = N - n_recent > 0 ? N - n_recent : 0;
+        double* o = out + (int64_t)u * c->d;
+        for (int x = 0; x < c->d; ++x) o[x] = 0.0;
+        if (head_mask && head_mask[u]) {
+            lse[u] = -INFINITY;
+            continue;
+        }
+        /* where each attended position's rows live: segment slot (>= 0), the cache (-1),
+         * or not attended (-2); a position named by several slots counts once */
+        int64_t* src = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+        for (int64_t p = 0; p < N; ++p) src[p] = p >= r0 ? -1 : -2;
+        int64_t seg0 = ((int64_t)b * c->Hkv + h) * idx_stride;
+        int32_t n = n_idx[b * c->Hkv + h];
+        n = n < 0 ? 0 : (n > idx_stride ? idx_stride : n);
+        for (int32_t s = 0; s < n; ++s) {
+            int64_t p = cpos[seg0 + s];
+            if (p >= 0 && p < r0 && src[p] == -2) src[p] = seg0 + s;
+        }
+        double* qi = (double*)malloc(sizeof(double) * c->d);
+        load_query(c, q, b, i, qi);
+        /* logits in ascending position order, then the softmax-weighted sum of V */
+        double* z = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        int64_t n_att = 0;
+        double m = -INFINITY;
+        for (int64_t p = 0; p < N; ++p) {
+            if (src[p] == -2) continue;
+            const void* kb = src[p] >= 0 ? ck : c->k;
+            int64_t r = src[p] >= 0 ? src[p] * c->d : row_start(c, b, h, p);
+            double dot = 0.0;
+            for (int x = 0; x < c->d; ++x) dot += qi[x] * load_elem(kb, c->is_bf16, r + x);
+            z[n_att] = dot / sqrt((double)c->d);
+            m = z[n_att] > m ? z[n_att] : m;
+            ++n_att;
+        }
+        if (n_att == 0) {
+            lse[u] = -INFINITY;
+        } else {
+            double l = 0.0;
+            for (int64_t j = 0; j < n_att; ++j) l += exp(z[j] - m);
+            double L = m + log(l);
+            int64_t j = 0;
+            for (int64_t p = 0; p < N; ++p) {
+                if (src[p] == -2) continue;
+                const void* vb = src[p] >= 0 ? cv : c->v;
+                int64_t r = src[p] >= 0 ? src[p] * c->d : row_start(c, b, h, p);
+                double w = exp(z[j++] - L);
+                for (int x = 0; x < c->d; ++x) o[x] += w * load_elem(vb, c->is_bf16, r + x);
+            }
+            lse[u] = L;
+        }
+        free(src);
+        free(qi);
+        free(z);
+    }
+    return 0;
+}
+
 /* ---- sparse fast step with group routing ------------------------------------------------ */
 
 int orc_sparse_routed(const orc_cache* c, const void* q, const int32_t* idx, int32_t idx_stride,

@@ -81,6 +81,28 @@ int orc_sparse_routed(const orc_cache* c, const void* q, const int32_t* idx, int
                       const double* route_lse, double log_gamma, double* margin,
                       uint8_t* routed, double* out, double* lse);
 
+/* Reorg for the two-segment layout (Slow-Fast Inference, Sec. 4.1: after the Selector the
+ * sink and selected KV entries of each (b, h) are gathered into a contiguous compact buffer).
+ * Per unit u = b*Hkv + h, n = n_idx[u] clamped to [0, idx_stride], every slot s < idx_stride:
+ * if s < n and p = idx[u*idx_stride + s] lies in [0, len[b]), the key and value rows of p are
+ * copied byte for byte to slot u*idx_stride + s of ck and cv and cpos[...] = p; otherwise the
+ * slot's rows are zero bytes and cpos = -1.  ck, cv hold B*Hkv*idx_stride rows of d elements
+ * in the cache's element format. */
+int orc_reorg(const orc_cache* c, const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+              void* ck, void* cv, int32_t* cpos);
+
+/* Fast step on the two-segment layout (Slow-Fast Inference, Sec. 4.2: the long-range
+ * segment is read from the compact buffer, the recent tokens in place from the cache).  The
+ * attended set is that of orc_sparse with idx = cpos:
+ *   I = { cpos[u*idx_stride + s], s < n_idx[u] : 0 <= entry < r0 }  u  [r0, N),
+ * but a long-range position's key and value rows are read from its segment slot (the first
+ * slot naming it) of ck, cv, and recent positions from the cache.  Masked heads output zeros,
+ * lse -inf.  Logits and the weighted sum run over positions in ascending order, as in
+ * orc_sparse, so with segment rows equal to the cache rows the two agree exactly. */
+int orc_sparse_compact(const orc_cache* c, const void* q, const void* ck, const void* cv,
+                       const int32_t* cpos, int32_t idx_stride, const int32_t* n_idx,
+                       int32_t n_recent, const uint8_t* head_mask, double* out, double* lse);
+
 /* Sink-bypass mask (SinkRouter, Sec. 4.2 "Target regime": heads whose token-0 attention
  * mass is large are treated as idle).  p0[b,i] = exp(z0[b*Hq+i] - lse[b*Hq+i]); per b the
  * floor(frac*Hq) heads with the largest p0 are masked, ties to the lower head index. */

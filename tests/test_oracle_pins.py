@@ -9,6 +9,9 @@
   counting with ties, and a hand-derived case for the per-head normalisation over J;
 * the sparse step against the library attention with a boolean mask, the dense result
   when the set is everything, and the zero surrogate;
+* the Reorg and the two-segment step: segment rows against the cache rows read by tensor
+  indexing, exact agreement with the gather step on the same index set, snapshot semantics
+  against the library attention on the original rows;
 * the sink-bypass mask against a library sort.
 No test here needs a GPU.
 """
@@ -332,6 +335,123 @@ def test_sparse_full_set_equals_dense_and_mask_zero(orc):
                         n_recent, head_mask=hm)
     assert (om[0, 1] == 0).all() and (om[0, 3] == 0).all() and np.isneginf(lm[0, 1])
     np.testing.assert_allclose(om[0, 0], od[0, 0], atol=1e-13)
+
+
+# ------------------------------------------------------- reorg and the two-segment step
+
+def _as_f32(rows):
+    """Segment rows (bf16 bits as uint16, or float32) as float32 values."""
+    if rows.dtype == np.uint16:
+        return (rows.astype(np.uint32) << 16).view(np.float32)
+    return rows
+
+
+def _two_segment_case(paged, seed=21):
+    wl = synth.Workload("ts_tiny", 95, 2, 8, 2, 32, "bf16", 300, 4, 20, 40, 6, paged=paged,
+                        block_size=16, len_lo=150 if paged else 0)
+    lay = synth.make_layer(wl, 0)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=seed)
+    return wl, lay, idx, n_idx
+
+
+def _orc_cache(orc, wl, lay, lens):
+    kw = dict(block_table=lay.block_table, block_size=wl.block_size,
+              max_blocks=lay.max_blocks) if wl.paged else {}
+    return orc.Cache(lay.k, lay.v, torch.tensor(lens, dtype=torch.int32), wl.Hq, **kw)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_reorg_rows_are_the_cache_rows(orc, paged):
+    wl, lay, idx, n_idx = _two_segment_case(paged)
+    lens = lay.len0_host
+    idx = idx.clone()
+    idx[0, 0, 3] = -3                               # outside the sequence: zero rows, cpos -1
+    idx[1, 1, 5] = lens[1] + 2
+    n_idx = n_idx.clone()
+    n_idx[0, 1] -= 7                                # slots past the count: zero rows, cpos -1
+    ck, cv, cpos = orc.reorg(_orc_cache(orc, wl, lay, lens), idx, n_idx)
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            Kl, Vl = synth.logical_kv(lay, b, h, lens[b])
+            for s in range(idx.shape[-1]):
+                p = int(idx[b, h, s])
+                if s < int(n_idx[b, h]) and 0 <= p < lens[b]:
+                    assert cpos[b, h, s] == p
+                    np.testing.assert_array_equal(_as_f32(ck[b, h, s]), Kl[p].numpy())
+                    np.testing.assert_array_equal(_as_f32(cv[b, h, s]), Vl[p].numpy())
+                else:
+                    assert cpos[b, h, s] == -1
+                    assert not ck[b, h, s].any() and not cv[b, h, s].any()
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_two_segment_step_equals_gather_step(orc, paged):
+    wl, lay, idx, n_idx = _two_segment_case(paged)
+    ck, cv, cpos = orc.reorg(_orc_cache(orc, wl, lay, lay.len0_host), idx, n_idx)
+    hm = torch.zeros((wl.B, wl.Hq), dtype=torch.uint8)
+    hm[1, 2] = 1
+    for t in (1, 3, 5):                             # the recent window moves; the segment stays
+        lens = [n + t for n in lay.len0_host]
+        c = _orc_cache(orc, wl, lay, lens)
+        q = synth.make_query(wl, 0, t)
+        og, lg = orc.sparse(c, q, idx, n_idx, wl.n_recent, head_mask=hm)
+        oc, lc = orc.sparse_compact(c, q, ck, cv, cpos, n_idx, wl.n_recent, head_mask=hm)
+        np.testing.assert_array_equal(oc, og)
+        np.testing.assert_array_equal(lc, lg)
+        assert (oc[1, 2] == 0).all() and np.isneginf(lc[1, 2])
+
+
+def test_two_segment_step_reads_the_snapshot(orc):
+    wl, lay, idx, n_idx = _two_segment_case(False)
+    lens0 = lay.len0_host
+    ck, cv, cpos = orc.reorg(_orc_cache(orc, wl, lay, lens0), idx, n_idx)
+    K0, V0 = lay.k.clone(), lay.v.clone()
+    # overwrite the cache rows of some selected positions after the Reorg
+    g = torch.Generator().manual_seed(3)
+    for b in range(wl.B):
+        for h in range(wl.Hkv):
+            for p in idx[b, h, wl.n_sink:wl.n_sink + 6].tolist():
+                lay.k[b, h, p] = torch.randn(wl.d, generator=g).to(lay.k.dtype)
+                lay.v[b, h, p] = torch.randn(wl.d, generator=g).to(lay.v.dtype)
+    t = 2
+    lens = [n + t for n in lens0]
+    q = synth.make_query(wl, 0, t)
+    oc, lc = orc.sparse_compact(_orc_cache(orc, wl, lay, lens), q, ck, cv, cpos, n_idx,
+                                wl.n_recent)
+    og, _ = orc.sparse(_orc_cache(orc, wl, lay, lens), q, idx, n_idx, wl.n_recent)
+    assert np.abs(oc - og).max() > 1e-3            # the gather step sees the new rows
+    for b in range(wl.B):                           # the segment holds the rows of the Reorg
+        N = lens[b]
+        mask = torch.zeros((wl.Hkv, N), dtype=torch.bool)
+        for h in range(wl.Hkv):
+            sel = idx[b, h, :n_idx[b, h]].long()
+            mask[h, sel[sel < N - wl.n_recent]] = True
+            mask[h, N - wl.n_recent:] = True
+        ro, rl, _ = _sdpa_ref(q[b].float(), K0[b, :, :N].float(), V0[b, :, :N].float(), mask)
+        np.testing.assert_allclose(oc[b], ro.numpy(), atol=1e-12)
+        np.testing.assert_allclose(lc[b], rl.numpy(), atol=1e-12)
+
+
+def test_two_segment_drops_entries_past_the_reorg_length(orc):
+    wl, lay, idx, n_idx = _two_segment_case(False)
+    lens0 = lay.len0_host
+    # the Reorg sees shorter sequences: entries at or past its length are dropped, although
+    # the fast step's cache holds those positions below its recent window
+    short = [n - 100 for n in lens0]
+    dropped = sum(int(((idx[b, :, :] >= short[b]) & (idx[b] < lens0[b] - wl.n_recent)).sum())
+                  for b in range(wl.B))
+    assert dropped > 0
+    ck, cv, cpos = orc.reorg(_orc_cache(orc, wl, lay, short), idx, n_idx)
+    lens = [n + 1 for n in lens0]
+    q = synth.make_query(wl, 0, 1)
+    c = _orc_cache(orc, wl, lay, lens)
+    oc, lc = orc.sparse_compact(c, q, ck, cv, cpos, n_idx, wl.n_recent)
+    kept = idx.clone()
+    for b in range(wl.B):
+        kept[b][kept[b] >= short[b]] = -1           # the gather step skips negative entries
+    og, lg = orc.sparse(c, q, kept, n_idx, wl.n_recent)
+    np.testing.assert_array_equal(oc, og)
+    np.testing.assert_array_equal(lc, lg)
 
 
 # -------------------------------------------------------------------------------- mask
