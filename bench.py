@@ -53,6 +53,8 @@ def parse():
                          "logits, which a kernel trace would mix into the dense kernel's stats)")
     ap.add_argument("--no-routed", action="store_true",
                     help="skip the routed fast-step measurement on sink-dominated workloads")
+    ap.add_argument("--no-two-segment", action="store_true",
+                    help="skip the Reorg + two-segment fast-step measurement")
     ap.add_argument("--retention-sweep", action="store_true",
                     help="add dense-vs-sparse timings over retention ratios on a layer shaped "
                          "like the SFI page's retention table (KV 16K, batch 16, 32/8 heads)")
@@ -323,6 +325,60 @@ def synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, 
     return res
 
 
+def two_segment_steps(B, torch, wl, descs, queries, idxs, nidxs, masks, out, lse, ws,
+                      idx_stride, L):
+    """The two-segment layout: sfi_reorg of every rotated layer's selection (once per cycle),
+    then the cycle's fast steps on the compact segment (sfi_sparse_decode_compact), timed as
+    blocks over all layers beside the same fast steps gathered from the cache."""
+    dev = "cuda"
+    segs = []
+    for li in range(L):
+        ck = torch.empty((wl.B, wl.Hkv, idx_stride, wl.d), dtype=wl.torch_dtype, device=dev)
+        segs.append((ck, torch.empty_like(ck),
+                     torch.empty((wl.B, wl.Hkv, idx_stride), dtype=torch.int32, device=dev)))
+
+    def reorg():
+        for li in range(L):
+            B.sfi_reorg(descs[li][0], idxs[li], idx_stride, nidxs[li], *segs[li])
+
+    def compact():
+        for li in range(L):
+            for t in range(1, wl.cycle):
+                B.sfi_sparse_decode_compact(descs[li][t], queries[li][t], *segs[li], idx_stride,
+                                            nidxs[li], wl.n_recent, masks[li], out, lse, ws)
+
+    def gather():
+        for li in range(L):
+            for t in range(1, wl.cycle):
+                B.sfi_sparse_decode(descs[li][t], queries[li][t], idxs[li], idx_stride,
+                                    nidxs[li], wl.n_recent, masks[li], out, lse, ws)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / reps
+
+    reorg_us = timed(reorg) / L
+    compact_us = timed(compact) / (L * (wl.cycle - 1))
+    gather_us = timed(gather) / (L * (wl.cycle - 1))
+    n_sel = sum(int(x) for x in nidxs[0].flatten().tolist())
+    row = wl.d * wl.elem_bytes
+    units = wl.B * wl.Hkv
+    reorg_bytes = n_sel * 2 * row + units * idx_stride * 2 * row + n_sel * 4 + units * idx_stride * 4
+    del segs
+    return {"reorg_us": round(reorg_us, 2),
+            "reorg_gbps": round(reorg_bytes / (reorg_us * 1e-6) / 1e9, 1),
+            "reorg_bytes": int(reorg_bytes),
+            "fast_us": round(compact_us, 2), "gather_fast_us": round(gather_us, 2),
+            "fast_saving_per_cycle_us": round((gather_us - compact_us) * (wl.cycle - 1), 2)}
+
+
 def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
                       idx_stride, slots: int = 4, reps: int = 5):
     """The slow step over every rotated layer: the per-layer calls one after another, against
@@ -523,6 +579,12 @@ def main():
         layered = layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
                                     masks, ws, idx_stride)
 
+    two_seg = None
+    if not args.no_two_segment:
+        print("# two-segment layout", file=sys.stderr, flush=True)
+        two_seg = two_segment_steps(B, torch, wl, descs, queries, idxs, nidxs, masks, out, lse,
+                                    ws, idx_stride, L)
+
     print("# streaming-read yardstick", file=sys.stderr, flush=True)
     yard = read_yardstick(B, torch)
 
@@ -584,6 +646,11 @@ def main():
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
     result["read_yardstick"] = yard
+    if two_seg is not None:
+        two_seg["value_if_used_us"] = round(
+            (dense_us + select_us + mask_us + two_seg["reorg_us"] +
+             (wl.cycle - 1) * two_seg["fast_us"]) / wl.cycle, 3)
+        result["two_segment"] = two_seg
     result["roofline"]["frac_of_measured_read"] = round(dense_gbps / yard["gbps"], 4)
     result["fast_roofline"]["frac_of_measured_read"] = round(fast_gbps / yard["gbps"], 4)
     result["fast_synthetic_selections"] = synth_fast

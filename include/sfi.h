@@ -171,6 +171,38 @@ sfi_status sfi_sparse_decode_routed(const sfi_kv_desc* kv, const void* q,
                                     float* out, float* lse,
                                     void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Reorg for the two-segment fast-step layout.  SFI Sec. 4.1 (Reorg_i gathers the sink and
+ * selected KV entries of a layer into a contiguous compact buffer after its Selector) and
+ * Sec. 4.2 "Coalesced reads with a two-segment KV layout" (fast steps read that long-range
+ * segment in order and the recent tokens in place from the cache).  Per b and KV head h, with
+ * u = b*Hkv + h and n = n_idx[u] clamped to [0, idx_stride], for every slot s < idx_stride:
+ *   p = idx[u*idx_stride + s];  if s < n and 0 <= p < len[b]:  cpos[u*idx_stride + s] = p and
+ *   the key and value rows of position p are copied to row u*idx_stride + s of ck and cv;
+ *   otherwise cpos = -1 and the rows are zeros.
+ * ck, cv (device) [B][Hkv][idx_stride][d] of the cache's dtype, 16-byte aligned; cpos (device)
+ * int32 [B][Hkv][idx_stride].  idx and n_idx as for sfi_sparse_decode (e.g. sfi_select's
+ * output).  The segment is a snapshot: later writes to the cache do not reach it.  No
+ * workspace; one kernel launch.  SFI_E_UNSUPPORTED when B*Hkv*idx_stride >= 2^32. */
+sfi_status sfi_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
+                     const int32_t* n_idx, void* ck, void* cv, int32_t* cpos, hipStream_t stream);
+
+/* Fast step on the two-segment layout (SFI Sec. 4.2): as sfi_sparse_decode with idx = cpos,
+ * except that index slot s of (b, h) reads its key and value rows from row u*idx_stride + s of
+ * the compact segment ck, cv written by sfi_reorg instead of from the cache; the recent
+ * window [r0, N) is read in place from the cache as before:
+ *   I = { cpos[u*idx_stride + s] : s < n_idx[u], 0 <= entry < r0 }  u  [r0, N).
+ * With the segment written by sfi_reorg from idx (every entry of idx below len at that call)
+ * and the cache rows of those positions unchanged since, the result equals sfi_sparse_decode
+ * on idx bit for bit: the same slots in the same order with the same bytes.  n_idx is the
+ * array given to sfi_reorg; any value is safe (slots past the reorg's count hold zero rows
+ * and cpos -1).  Workspace, head_mask, out and lse as for sfi_sparse_decode (SFI_OP_SPARSE
+ * with this idx_stride).  SFI_E_UNSUPPORTED when B*Hkv*idx_stride >= 2^32. */
+sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
+                                     const void* ck, const void* cv, const int32_t* cpos,
+                                     int32_t idx_stride, const int32_t* n_idx, int32_t n_recent,
+                                     const uint8_t* head_mask, float* out, float* lse,
+                                     void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Slow step over the layers of a model with the Selector off the critical path.  SFI Sec. 4.1,
  * layer-wise asynchronous execution: the primary stream runs the dense step of layer after
  * layer while the Selector (and the sink mask) of each layer runs on a second stream, with a

@@ -20,8 +20,8 @@ SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE = 0, 1, 2
 
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
-            "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_workspace_bytes",
-            "sfi_stream_read", "sfi_status_string")
+            "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
+            "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_status_string")
 
 
 class SfiError(RuntimeError):
@@ -62,11 +62,15 @@ def lib():
                                            ctypes.c_float, P, P, P, P, P, P]
         L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
         L.sfi_workspace_bytes.restype = ctypes.c_size_t
+        L.sfi_reorg.argtypes = [D, P, i32, P, P, P, P, P]
+        L.sfi_sparse_decode_compact.argtypes = [D, P, P, P, P, i32, P, i32, P, P, P, P,
+                                                ctypes.c_size_t, P]
         L.sfi_stream_read.argtypes = [P, ctypes.c_uint64, i32, P, P]
         L.sfi_status_string.argtypes = [ctypes.c_int]
         L.sfi_status_string.restype = ctypes.c_char_p
         for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
-                  "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_stream_read"):
+                  "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_stream_read",
+                  "sfi_reorg", "sfi_sparse_decode_compact"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -195,6 +199,20 @@ def sfi_sparse_decode_routed(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_rec
                                           _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                           _stream(stream)),
            "sfi_sparse_decode_routed")
+
+
+def sfi_reorg(desc: KVDesc, idx, idx_stride: int, n_idx, ck, cv, cpos, stream=None):
+    _check(lib().sfi_reorg(desc.ref, _ptr(idx), int(idx_stride), _ptr(n_idx), _ptr(ck), _ptr(cv),
+                           _ptr(cpos), _stream(stream)), "sfi_reorg")
+
+
+def sfi_sparse_decode_compact(desc: KVDesc, q, ck, cv, cpos, idx_stride: int, n_idx,
+                              n_recent: int, head_mask, out, lse, ws, stream=None):
+    _check(lib().sfi_sparse_decode_compact(desc.ref, _ptr(q), _ptr(ck), _ptr(cv), _ptr(cpos),
+                                           int(idx_stride), _ptr(n_idx), int(n_recent),
+                                           _ptr(head_mask), _ptr(out), _ptr(lse), _ptr(ws),
+                                           ws.numel() * ws.element_size(), _stream(stream)),
+           "sfi_sparse_decode_compact")
 
 
 def _ptr_array(tensors):

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsfi.so")
-SOURCES = ["sfi_attention.hip", "sfi_select.hip", "sfi_stream.hip", "sfi_api.cpp"]
+SOURCES = ["sfi_attention.hip", "sfi_select.hip", "sfi_reorg.hip", "sfi_stream.hip", "sfi_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -164,6 +164,11 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     p->bytes = off;
 }
 
+// rows of a compact segment [B][Hkv][idx_stride] (row numbers are kept in 32 bits)
+int64_t segment_rows(const sfi_kv_desc& kv, int32_t idx_stride) {
+    return (int64_t)kv.batch * kv.num_kv_heads * idx_stride;
+}
+
 sfi_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
     if (!ws || !aligned(ws, kAlign) || ws_bytes < need) return SFI_E_WORKSPACE;
     return SFI_OK;
@@ -297,12 +302,17 @@ namespace {
 sfi_status sparse_impl(const sfi_kv_desc* kv, const void* q, const int32_t* idx,
                        int32_t idx_stride, const int32_t* n_idx, int32_t n_recent,
                        const uint8_t* head_mask, const float* route_lse, float gamma,
-                       uint8_t* routed, float* out, float* lse, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+                       uint8_t* routed, const void* ck, const void* cv, float* out, float* lse,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
     sfi_status st = check_desc(kv, true);
     if (st != SFI_OK) return st;
     if (!q || !out || !idx || !n_idx || !aligned(q, 16) || !aligned(out, 16)) return SFI_E_INVALID;
     if (idx_stride < 1 || n_recent < 0) return SFI_E_INVALID;
+    if ((ck != nullptr) != (cv != nullptr)) return SFI_E_INVALID;
+    if (ck) {
+        if (!aligned(ck, 16) || !aligned(cv, 16)) return SFI_E_INVALID;
+        if (segment_rows(*kv, idx_stride) >= (int64_t(1) << 32)) return SFI_E_UNSUPPORTED;
+    }
     AttnPlan plan;
     st = plan_attention(*kv, true, idx_stride, n_recent, &plan);
     if (st != SFI_OK) return st;
@@ -322,6 +332,8 @@ sfi_status sparse_impl(const sfi_kv_desc* kv, const void* q, const int32_t* idx,
     a.route_lse = route_lse;
     a.route_log_gamma = route_lse ? (float)log((double)gamma) : 0.f;
     a.routed = routed;
+    a.ck = ck;
+    a.cv = cv;
     const hipError_t e = launch_attention(a, kv->batch, kv->head_dim, kv->dtype == SFI_BF16,
                                           kv->block_table != nullptr, true, stream);
     return e == hipSuccess ? SFI_OK : SFI_E_HIP;
@@ -335,7 +347,47 @@ SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
                                         float* out, float* lse,
                                         void* ws, size_t ws_bytes, hipStream_t stream) {
     return sparse_impl(kv, q, idx, idx_stride, n_idx, n_recent, head_mask, nullptr, 1.f, nullptr,
-                       out, lse, ws, ws_bytes, stream);
+                       nullptr, nullptr, out, lse, ws, ws_bytes, stream);
+}
+
+SFI_EXPORT sfi_status sfi_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
+                                const int32_t* n_idx, void* ck, void* cv, int32_t* cpos,
+                                hipStream_t stream) {
+    const sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    if (!idx || !n_idx || !ck || !cv || !cpos || idx_stride < 1) return SFI_E_INVALID;
+    if (!aligned(ck, 16) || !aligned(cv, 16) || !aligned(cpos, 4)) return SFI_E_INVALID;
+    if (segment_rows(*kv, idx_stride) >= (int64_t(1) << 32)) return SFI_E_UNSUPPORTED;
+    ReorgArgs a;
+    a.k = kv->k;
+    a.v = kv->v;
+    a.len = kv->len;
+    a.block_table = kv->block_table;
+    a.n_cap = kv->n_cap;
+    a.block_shift = 0;
+    if (kv->block_table)
+        while ((1 << a.block_shift) < kv->block_size) ++a.block_shift;
+    a.max_blocks = kv->max_blocks;
+    a.Hkv = kv->num_kv_heads;
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.n_idx = n_idx;
+    a.ck = ck;
+    a.cv = cv;
+    a.cpos = cpos;
+    const int row_bytes = kv->head_dim * (kv->dtype == SFI_BF16 ? 2 : 4);
+    return launch_reorg(a, kv->batch, row_bytes, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
+SFI_EXPORT sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
+                                                const void* ck, const void* cv,
+                                                const int32_t* cpos, int32_t idx_stride,
+                                                const int32_t* n_idx, int32_t n_recent,
+                                                const uint8_t* head_mask, float* out, float* lse,
+                                                void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ck || !cv) return SFI_E_INVALID;
+    return sparse_impl(kv, q, cpos, idx_stride, n_idx, n_recent, head_mask, nullptr, 1.f, nullptr,
+                       ck, cv, out, lse, ws, ws_bytes, stream);
 }
 
 SFI_EXPORT sfi_status sfi_sparse_decode_routed(const sfi_kv_desc* kv, const void* q,
@@ -346,7 +398,7 @@ SFI_EXPORT sfi_status sfi_sparse_decode_routed(const sfi_kv_desc* kv, const void
                                                void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!route_lse || !(gamma > 0.f && gamma <= 1.f)) return SFI_E_INVALID;
     return sparse_impl(kv, q, idx, idx_stride, n_idx, n_recent, head_mask, route_lse, gamma, routed,
-                       out, lse, ws, ws_bytes, stream);
+                       nullptr, nullptr, out, lse, ws, ws_bytes, stream);
 }
 
 SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,

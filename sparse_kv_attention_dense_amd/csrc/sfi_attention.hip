@@ -362,6 +362,10 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     const int nslots = max(0, s1 - s0);
 
     const uint32_t base_row = PAGED ? 0u : (uint32_t)((int64_t)unit * a.n_cap);
+    // Two-segment fast step (compact long-range segment): index slot s of the unit reads row
+    // unit * idx_stride + s of ck / cv instead of gathering its position from the cache.
+    const bool compact = SPARSE && a.ck != nullptr;
+    const uint32_t crow0 = (uint32_t)unit * (uint32_t)a.idx_stride;
 
     const int bmask = (1 << a.block_shift) - 1;
     uint8_t* tab_ok = (uint8_t*)(tab + a.split_len);
@@ -380,7 +384,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
                     pos = r0 + (slot - n_sel);
                 }
                 tab_ok[t] = ok;
-                tab[t] = base_row + (uint32_t)pos;
+                tab[t] = (compact && slot < n_sel) ? crow0 + (uint32_t)slot : base_row + (uint32_t)pos;
             }
         }
         // Paged: slots are filled nfill per thread at a time; every index load of a batch is
@@ -411,10 +415,12 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             for (int u = 0; u < kFill; ++u) {
                 if constexpr (PAGED) {
                     const int t = t0 + u * kThreads + tid;
-                    const int blk = (u < nfill && t < nslots)
+                    const bool crow = compact && s0 + t < n_sel;     // compact row: no lookup
+                    const int blk = (u < nfill && t < nslots && !crow)
                         ? a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)] : 0;
-                    row[u] = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
-                             (uint32_t)(pos[u] & bmask);
+                    row[u] = crow ? crow0 + (uint32_t)(s0 + t)
+                                  : (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
+                                        (uint32_t)(pos[u] & bmask);
                 } else {
                     row[u] = base_row + (uint32_t)pos[u];
                 }
@@ -534,36 +540,39 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         if constexpr (kNtV) return __builtin_nontemporal_load((const u32x4*)p);
         else return *(const u32x4*)p;
     };
+    using Elem = typename std::conditional<BF, uint16_t, float>::type;
+    // first element of the key (or value) row of a slot: the compact segment for index slots
+    // of a two-segment step, else the cache
+    auto row_ptr = [&](int slot, const void* cache, const void* seg) -> const Elem* {
+        const void* base = cache;
+        if constexpr (SPARSE) {
+            if (compact && slot < n_sel) base = seg;
+        }
+        return (const Elem*)base + (uint64_t)slot_row(slot) * D;
+    };
     auto issue = [&](Regs& r, int tile) {
         const int sb = s0 + tile * kTile;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            const uint32_t row = slot_row(min(sb + 16 * st + n16, s1 - 1));
+            const Elem* kp = row_ptr(min(sb + 16 * st + n16, s1 - 1), a.k, a.ck);
 #pragma unroll
             for (int c = 0; c < C::kNQ; ++c) {
-                if constexpr (BF) {
-                    const uint16_t* kp = (const uint16_t*)a.k + (uint64_t)row * D;
-                    r.k[st][c] = load_k(kp + 32 * c + 8 * q4);
-                } else {
-                    const float* kp = (const float*)a.k + (uint64_t)row * D;
-                    r.k[st][c] = *(const f32x4*)(kp + 16 * c + 4 * q4);
-                }
+                if constexpr (BF) r.k[st][c] = load_k(kp + 32 * c + 8 * q4);
+                else r.k[st][c] = *(const f32x4*)(kp + 16 * c + 4 * q4);
             }
         }
         if constexpr (BF) {
 #pragma unroll
             for (int j = 0; j < C::kNV; ++j) {
                 const int rr = j * C::kRPI + lane / C::kLPR;
-                const uint32_t row = slot_row(min(sb + rr, s1 - 1));
-                r.v[j] = load_v((const uint16_t*)a.v + (uint64_t)row * D + (lane % C::kLPR) * 8);
+                r.v[j] = load_v(row_ptr(min(sb + rr, s1 - 1), a.v, a.cv) + (lane % C::kLPR) * 8);
             }
         } else {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const uint32_t row = slot_row(min(sb + 16 * st + 4 * q4 + i, s1 - 1));
-                    const float* vp = (const float*)a.v + (uint64_t)row * D;
+                    const float* vp = row_ptr(min(sb + 16 * st + 4 * q4 + i, s1 - 1), a.v, a.cv);
 #pragma unroll
                     for (int mb = 0; mb < D / 16; ++mb) r.v[(st * 4 + i) * (D / 16) + mb] = vp[16 * mb + n16];
                 }

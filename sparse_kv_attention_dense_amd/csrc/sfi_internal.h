@@ -44,6 +44,8 @@ struct AttnArgs {
     const float* route_lse;          // sparse only, may be null: per-head cached lse for routing
     float route_log_gamma;           // log(gamma) of the routing threshold
     uint8_t* routed;                 // may be null: [B][Hkv] routing decisions
+    const void* ck;                  // sparse only, may be null: compact segment of the
+    const void* cv;                  //   two-segment step, [B][Hkv][idx_stride][d]
     float* out;
     float* lse;                      // may be null
     float* part;                     // [units][nsplit][rec]: acc [G][d], then (m, l) [G]
@@ -91,6 +93,25 @@ struct MaskArgs {
 };
 
 hipError_t launch_sink_mask(const MaskArgs& a, hipStream_t stream);
+
+// Reorg of the two-segment layout (sfi_reorg.hip): copies the rows named by idx into the
+// compact segment ck / cv [B][Hkv][idx_stride][row_bytes] and their positions into cpos.
+struct ReorgArgs {
+    const void* k;
+    const void* v;
+    const int32_t* len;
+    const int32_t* block_table;      // null when contiguous
+    int64_t n_cap;
+    int32_t block_shift, max_blocks, Hkv;
+    const int32_t* idx;
+    int32_t idx_stride;
+    const int32_t* n_idx;
+    void* ck;
+    void* cv;
+    int32_t* cpos;
+};
+
+hipError_t launch_reorg(const ReorgArgs& a, int B, int row_bytes, hipStream_t stream);
 
 // Streaming-read yardstick (sfi_stream.hip): n_wg workgroups each read a contiguous chunk of
 // buf (bytes a multiple of 16); sink is a device buffer of kStreamSinkWords words.

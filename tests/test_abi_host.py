@@ -195,3 +195,27 @@ def test_stream_read_validation(L):
     assert L.sfi_stream_read(FAKE, 1 << 20, 1024, FAKE + 2, None) == B.SFI_E_INVALID
     assert L.sfi_stream_read(FAKE, 1 << 20, 0, FAKE, None) == B.SFI_E_INVALID
     assert L.sfi_stream_read(FAKE, 1 << 20, (1 << 20) + 1, FAKE, None) == B.SFI_E_INVALID
+
+
+def test_reorg_and_two_segment_validation(L):
+    d = _desc()
+    D = ctypes.byref(d)
+    ro = lambda **k: L.sfi_reorg(D, k.get("idx", FAKE), k.get("istride", 2052), FAKE,
+                                 k.get("ck", FAKE), k.get("cv", FAKE), k.get("cpos", FAKE), None)
+    assert ro(idx=None) == B.SFI_E_INVALID
+    assert ro(ck=None) == B.SFI_E_INVALID
+    assert ro(cpos=None) == B.SFI_E_INVALID
+    assert ro(cv=FAKE + 8) == B.SFI_E_INVALID
+    assert ro(cpos=FAKE + 2) == B.SFI_E_INVALID
+    assert ro(istride=0) == B.SFI_E_INVALID
+    assert ro(istride=1 << 30) == B.SFI_E_UNSUPPORTED          # 2*8*2^30 segment rows
+    assert L.sfi_reorg(None, FAKE, 2052, FAKE, FAKE, FAKE, FAKE, None) == B.SFI_E_INVALID
+    ws = L.sfi_workspace_bytes(D, B.SFI_OP_SPARSE, 2052, 256)
+    sc = lambda **k: L.sfi_sparse_decode_compact(
+        D, FAKE, k.get("ck", FAKE), k.get("cv", FAKE), k.get("cpos", FAKE),
+        k.get("istride", 2052), FAKE, 256, None, FAKE, None, FAKE, k.get("ws", ws), None)
+    assert sc(ck=None) == B.SFI_E_INVALID
+    assert sc(cv=None) == B.SFI_E_INVALID
+    assert sc(ck=FAKE + 4) == B.SFI_E_INVALID
+    assert sc(cpos=None) == B.SFI_E_INVALID
+    assert sc(ws=ws - 256) == B.SFI_E_WORKSPACE

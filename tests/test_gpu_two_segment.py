@@ -1,0 +1,169 @@
+"""Reorg and the two-segment fast step on the GPU.
+
+* sfi_reorg against the oracle's Reorg: positions and segment rows bit for bit, with entries
+  outside the sequence, counts below and above the stride, and an empty sequence;
+* sfi_sparse_decode_compact against the oracle's two-segment step (documented tolerance) and
+  against sfi_sparse_decode on the same index set, bit for bit, while the recent window moves;
+* the same bit-for-bit agreement at full size on the 128K batch and the ragged paged batch.
+"""
+import numpy as np
+import pytest
+import torch
+
+from sparse_kv_attention_dense_amd import binding as B
+from sparse_kv_attention_dense_amd import synth
+
+from gpu_util import (DEV, assert_close_out, assert_close_rel, desc_for, gpu_sparse,
+                      oracle_cache, say, tolerances)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy().view(np.uint32)
+
+
+def _orc_bits(a: np.ndarray) -> np.ndarray:
+    return a if a.dtype == np.uint16 else a.view(np.uint32)
+
+
+def gpu_reorg(lay, idx, n_idx, lens_host):
+    """sfi_reorg at the slow step's lengths; the outputs start as garbage."""
+    wl = lay.wl
+    lens = torch.tensor(lens_host, dtype=torch.int32, device=DEV)
+    desc = desc_for(lay, lens, max(max(lens_host), 1))
+    stride = idx.shape[-1]
+    ck = torch.full((wl.B, wl.Hkv, stride, wl.d), float("nan"), dtype=wl.torch_dtype, device=DEV)
+    cv = torch.full_like(ck, float("nan"))
+    cpos = torch.full((wl.B, wl.Hkv, stride), -9, dtype=torch.int32, device=DEV)
+    B.sfi_reorg(desc, idx.to(DEV), stride, n_idx.to(DEV), ck, cv, cpos)
+    torch.cuda.synchronize()
+    return ck, cv, cpos
+
+
+def gpu_compact(lay, q, t, ck, cv, cpos, n_idx, head_mask=None):
+    wl = lay.wl
+    lens = lay.len_at(t).to(DEV)
+    desc = desc_for(lay, lens, lay.max_len_at(t))
+    stride = cpos.shape[-1]
+    out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), device=DEV)
+    lse = torch.full((wl.B, wl.Hq), float("nan"), device=DEV)
+    ws = B.workspace(desc, idx_stride=stride, n_recent=wl.n_recent, device=DEV)
+    B.sfi_sparse_decode_compact(desc, q, ck, cv, cpos, stride, n_idx.to(DEV), wl.n_recent,
+                                None if head_mask is None else head_mask.to(DEV), out, lse, ws)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def _case(name):
+    if name == "d64_bf16":
+        wl = synth.Workload("ts_d64", 8300, 3, 14, 2, 64, "bf16", 2500, 4, 64, 300, 6)
+    elif name == "tiny_2k_f32":
+        wl = W[name]
+    elif name == "ragged_paged_b16":
+        wl = W[name].scaled(9000, B=4, len_lo=4000)
+    else:
+        base = W[name]
+        wl = base.scaled(base.n_sink + base.k_sel + base.n_recent + 3001, B=min(base.B, 2))
+    return wl
+
+
+@pytest.mark.parametrize("name", ["tiny_2k_f32", "gqa4_32k", "ragged_paged_b16", "d64_bf16"])
+def test_reorg_matches_oracle(orc, name):
+    wl = _case(name)
+    say(f"[reorg] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=31)
+    idx, n_idx = idx.clone(), n_idx.clone()
+    idx[0, 0, 2] = -5                                    # outside the sequence
+    idx[-1, -1, 1] = lay.len0_host[-1] + 3
+    n_idx[0, -1] -= 5                                    # fewer entries than the stride
+    n_idx[-1, 0] = idx.shape[-1] + 10                    # clamped to the stride
+    lens = lay.len0_host
+    ck, cv, cpos = gpu_reorg(lay, idx, n_idx, lens)
+    eck, ecv, ecpos = orc.reorg(oracle_cache(orc, lay, lens), idx, n_idx)
+    assert np.array_equal(cpos.cpu().numpy(), ecpos)
+    assert np.array_equal(_bits(ck), _orc_bits(eck))
+    assert np.array_equal(_bits(cv), _orc_bits(ecv))
+    say(f"    positions and {ck.numel() * 2} segment elements identical to the oracle")
+
+
+@pytest.mark.parametrize("name", ["tiny_2k_f32", "gqa4_32k", "sink_128k_b4", "ragged_paged_b16",
+                                  "d64_bf16"])
+def test_two_segment_step(orc, name):
+    wl = _case(name)
+    say(f"[two-segment] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    idx, n_idx = synth.synthetic_index_set(lay, "spans", seed=32)
+    ck, cv, cpos = gpu_reorg(lay, idx, n_idx, lay.len0_host)
+    hm = torch.zeros((wl.B, wl.Hq), dtype=torch.uint8)
+    hm[0, 1] = 1
+    ecv_host = orc.reorg(oracle_cache(orc, lay, lay.len0_host), idx, n_idx)
+    tol = tolerances(wl)
+    for t in (1, wl.cycle - 1):
+        q = synth.make_query(wl, 0, t, device=DEV, u=lay.u)
+        out, lse = gpu_compact(lay, q, t, ck, cv, cpos, n_idx, hm)
+        gout, glse = gpu_sparse(lay, q, t, idx.to(DEV), n_idx.to(DEV), hm.to(DEV))
+        assert torch.equal(out, gout) and torch.equal(lse, glse), "differs from the gather step"
+        lens = [n + t for n in lay.len0_host]
+        eo, el = orc.sparse_compact(oracle_cache(orc, lay, lens), q, *ecv_host, n_idx,
+                                    wl.n_recent, hm)
+        assert_close_out(out.cpu().numpy(), eo, tol["out"])
+        assert_close_rel(lse.cpu().numpy(), el, tol["rel"], "lse")
+        assert (out[0, 1] == 0).all() and torch.isneginf(lse[0, 1])
+    say("    bit-identical to sfi_sparse_decode on the same index set")
+
+
+def test_two_segment_edges(orc):
+    """An empty sequence, one shorter than the sink and recent windows, entries in the recent
+    window, and a count of zero."""
+    wl = synth.Workload("ts_edges", 8400, 3, 8, 2, 128, "bf16", 1500, 4, 100, 60, 4)
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[0, 90, 1500])
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=33)
+    idx, n_idx = idx.clone(), n_idx.clone()
+    idx[2, 1, int(n_idx[2, 1]) - 1] = 1500 - 30         # inside the recent window: skipped
+    n_idx[2, 0] = 0
+    ck, cv, cpos = gpu_reorg(lay, idx, n_idx, lay.len0_host)
+    eck, ecv, ecpos = orc.reorg(oracle_cache(orc, lay, lay.len0_host), idx, n_idx)
+    assert np.array_equal(cpos.cpu().numpy(), ecpos)
+    assert np.array_equal(_bits(ck), _orc_bits(eck))
+    for t in (0, 3):
+        q = synth.make_query(wl, 0, t, device=DEV)
+        out, lse = gpu_compact(lay, q, t, ck, cv, cpos, n_idx)
+        gout, glse = gpu_sparse(lay, q, t, idx.to(DEV), n_idx.to(DEV))
+        assert torch.equal(out, gout) and torch.equal(lse, glse)
+        lens = [n + t for n in lay.len0_host]
+        eo, el = orc.sparse_compact(oracle_cache(orc, lay, lens), q, eck, ecv, ecpos, n_idx,
+                                    wl.n_recent)
+        assert_close_out(out.cpu().numpy(), eo, 1e-2)
+        assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
+
+
+@pytest.mark.parametrize("name", ["sink_128k_b4", "ragged_paged_b16"])
+def test_two_segment_full_size_equals_gather(name):
+    wl = W[name]
+    say(f"[two-segment full size] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=34)
+    ck, cv, cpos = gpu_reorg(lay, idx, n_idx, lay.len0_host)
+    # spot-check segment rows against the cache
+    g = torch.Generator().manual_seed(4)
+    for _ in range(64):
+        b = int(torch.randint(wl.B, (1,), generator=g))
+        h = int(torch.randint(wl.Hkv, (1,), generator=g))
+        s = int(torch.randint(int(n_idx[b, h]), (1,), generator=g))
+        p = int(idx[b, h, s])
+        assert int(cpos[b, h, s]) == p
+        Kl, Vl = synth.logical_kv(lay, b, h, p + 1)
+        assert torch.equal(ck[b, h, s].float(), Kl[p]) and torch.equal(cv[b, h, s].float(), Vl[p])
+    for t in (1, wl.cycle - 1):
+        q = synth.make_query(wl, 0, t, device=DEV, u=lay.u)
+        out, lse = gpu_compact(lay, q, t, ck, cv, cpos, n_idx)
+        gout, glse = gpu_sparse(lay, q, t, idx.to(DEV), n_idx.to(DEV))
+        assert torch.equal(out, gout) and torch.equal(lse, glse)
+    say("    bit-identical to sfi_sparse_decode at full size")
