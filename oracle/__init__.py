@@ -31,6 +31,12 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+class _Refine(ctypes.Structure):
+    _fields_ = [("lambda_", ctypes.c_double), ("alpha_soft", ctypes.c_double),
+                ("alpha_cross", ctypes.c_double), ("prior_decay", ctypes.c_double),
+                ("tail_frac", ctypes.c_double), ("tail_brake", ctypes.c_double)]
+
+
 class _Cache(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("is_bf16", ctypes.c_int32),
@@ -58,9 +64,13 @@ def lib():
         L.orc_reorg.argtypes = [ctypes.POINTER(_Cache), P, ctypes.c_int32, P, P, P, P]
         L.orc_sparse_compact.argtypes = [ctypes.POINTER(_Cache), P, P, P, P, ctypes.c_int32, P,
                                          ctypes.c_int32, P, P, P]
+        L.orc_select_refined.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
+                                         ctypes.c_int64, P, ctypes.c_int64, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_Refine),
+                                         P, ctypes.c_int32, P, P, P]
         L.orc_threads.argtypes = []
         for f in (L.orc_dense, L.orc_select, L.orc_sparse, L.orc_sink_mask, L.orc_threads,
-                  L.orc_sparse_routed, L.orc_reorg, L.orc_sparse_compact):
+                  L.orc_sparse_routed, L.orc_reorg, L.orc_sparse_compact, L.orc_select_refined):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -154,6 +164,45 @@ def select(lens, Hq: int, Hkv: int, logits, n_sink: int, n_recent: int, k_sel: i
     if rc != 0:
         raise ValueError("idx_stride too small for sink + selected")
     return idx, n_idx, f
+
+
+REFINE_DEFAULTS = dict(lambda_=0.02, alpha_soft=0.5, alpha_cross=0.35, prior_decay=1.0,
+                       tail_frac=1.0 / 16, tail_brake=1.0)
+
+
+def select_refined(lens, Hq: int, Hkv: int, logits, n_sink: int, n_recent: int, k_sel: int,
+                   key_norm=None, params: dict | None = None, idx_stride: int | None = None,
+                   want_scores: bool = False):
+    """The full Selector (prior, reverse-KL fusion, Soft-NMS, cross-head exclusivity, Top-K).
+    logits [B][Hq][stride]; key_norm [B][Hkv][>= max len] or None; params override
+    REFINE_DEFAULTS.  Returns (idx, n_idx, fused, refined): the log-scores before and after the
+    refinements ([B][Hkv][stride], -inf outside J) when want_scores, else None."""
+    z = np.ascontiguousarray(np.asarray(logits.cpu() if torch.is_tensor(logits) else logits,
+                                        dtype=np.float64))
+    B, _, stride = z.shape
+    lens = _i32(lens)
+    kn = None
+    if key_norm is not None:
+        kn = np.ascontiguousarray(np.asarray(
+            key_norm.cpu() if torch.is_tensor(key_norm) else key_norm, dtype=np.float64))
+    pr = dict(REFINE_DEFAULTS)
+    pr.update(params or {})
+    rp = _Refine(pr["lambda_"], pr["alpha_soft"], pr["alpha_cross"], pr["prior_decay"],
+                 pr["tail_frac"], pr["tail_brake"])
+    idx_stride = int(idx_stride or (n_sink + k_sel))
+    idx = np.zeros((B, Hkv, idx_stride), np.int32)
+    n_idx = np.zeros((B, Hkv), np.int32)
+    fused = np.zeros((B, Hkv, stride), np.float64) if want_scores else None
+    refined = np.zeros((B, Hkv, stride), np.float64) if want_scores else None
+    rc = lib().orc_select_refined(B, Hq, Hkv, _ptr(lens), _ptr(z), stride,
+                                  _ptr(kn) if kn is not None else None,
+                                  kn.shape[-1] if kn is not None else 0, n_sink, n_recent, k_sel,
+                                  ctypes.byref(rp), _ptr(idx), idx_stride, _ptr(n_idx),
+                                  _ptr(fused) if fused is not None else None,
+                                  _ptr(refined) if refined is not None else None)
+    if rc != 0:
+        raise ValueError("idx_stride too small for sink + selected")
+    return idx, n_idx, fused, refined
 
 
 def sparse(cache: Cache, q, idx, n_idx, n_recent: int, head_mask=None):

@@ -174,6 +174,125 @@ int orc_select(int32_t B, int32_t Hq, int32_t Hkv, const int32_t* len,
     return bad ? -1 : 0;
 }
 
+/* ---- full Selector: prior, fusion and log-score refinements ------------------------- */
+
+/* Unnormalised prior weight of position j of J = [j0, j0 + nJ) for a KV head whose key norms
+ * are norm_row (NULL: no key-norm factor).  u is the position's place in J, in (0, 1). */
+static double prior_weight(const orc_refine* p, const double* norm_row, int64_t j, int64_t j0,
+                           int64_t nJ) {
+    double u = ((double)(j - j0) + 0.5) / (double)nJ;
+    double w = exp(-p->prior_decay * u);                          /* global decay */
+    double t0 = 1.0 - p->tail_frac;
+    if (p->tail_frac > 0.0 && u > t0) w *= exp(-p->tail_brake * (u - t0) / p->tail_frac);
+    if (norm_row) {                                               /* key-norm factor */
+        double n = norm_row[j] > 1e-6 ? norm_row[j] : 1e-6;
+        w /= n;
+    }
+    return w;
+}
+
+int orc_select_refined(int32_t B, int32_t Hq, int32_t Hkv, const int32_t* len,
+                       const double* logits, int64_t logit_stride,
+                       const double* key_norm, int64_t norm_stride,
+                       int32_t n_sink, int32_t n_recent, int32_t k_sel, const orc_refine* p,
+                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                       double* fused_out, double* refined_out) {
+    const int G = Hq / Hkv;
+    int bad = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t N = len[b];
+        int64_t ns = n_sink < N ? n_sink : N;
+        int64_t j0 = n_sink, j1 = N - n_recent;
+        int64_t nJ = j1 > j0 ? j1 - j0 : 0;
+        int64_t take = k_sel < nJ ? k_sel : nJ;
+        int64_t n1 = nJ > 0 ? nJ : 1;
+        double* ell = (double*)malloc(sizeof(double) * (size_t)(Hkv * n1));   /* log s_h */
+        double* ell1 = (double*)malloc(sizeof(double) * (size_t)(Hkv * n1));  /* after NMS */
+        /* 1. evidence f_h (the hot path's), 2. prior r_h, 3. fused s_h = f^(1-l) r^l / Z */
+        for (int h = 0; h < Hkv; ++h) {
+            double* e = ell + (int64_t)h * n1;
+            for (int64_t t = 0; t < nJ; ++t) e[t] = 0.0;
+            for (int g = 0; g < G; ++g) {
+                const double* z = logits + ((int64_t)b * Hq + h * G + g) * logit_stride;
+                double m = -INFINITY;
+                for (int64_t j = j0; j < j1; ++j) m = z[j] > m ? z[j] : m;
+                double l = 0.0;
+                for (int64_t j = j0; j < j1; ++j) l += exp(z[j] - m);
+                double lse_J = m + log(l);
+                for (int64_t t = 0; t < nJ; ++t) e[t] += exp(z[j0 + t] - lse_J) / G;   /* f */
+            }
+            const double* nrow = key_norm ? key_norm + ((int64_t)b * Hkv + h) * norm_stride : NULL;
+            double R = 0.0;
+            for (int64_t t = 0; t < nJ; ++t) R += prior_weight(p, nrow, j0 + t, j0, nJ);
+            double Z = 0.0;
+            for (int64_t t = 0; t < nJ; ++t) {
+                double r = prior_weight(p, nrow, j0 + t, j0, nJ) / R;
+                e[t] = pow(e[t], 1.0 - p->lambda) * pow(r, p->lambda);
+                Z += e[t];
+            }
+            for (int64_t t = 0; t < nJ; ++t) e[t] = log(e[t] / Z);
+            if (fused_out) {
+                double* fo = fused_out + ((int64_t)b * Hkv + h) * logit_stride;
+                for (int64_t j = 0; j < logit_stride; ++j) fo[j] = -INFINITY;
+                for (int64_t t = 0; t < nJ; ++t) fo[j0 + t] = e[t];
+            }
+            /* 4. Soft-NMS within the head: a position with a strictly higher neighbour in J is
+             *    decayed by log(1 - alpha_soft); local maxima keep their score */
+            double* e1 = ell1 + (int64_t)h * n1;
+            for (int64_t t = 0; t < nJ; ++t) {
+                int lower = (t > 0 && e[t - 1] > e[t]) || (t + 1 < nJ && e[t + 1] > e[t]);
+                e1[t] = e[t] + (lower ? log(1.0 - p->alpha_soft) : 0.0);
+            }
+        }
+        /* 5. cross-head exclusivity at each position: every head below the position's best
+         *    head is decayed by log(1 - alpha_cross) */
+        for (int64_t t = 0; t < nJ; ++t) {
+            double M = -INFINITY;
+            for (int h = 0; h < Hkv; ++h) M = ell1[(int64_t)h * n1 + t] > M ? ell1[(int64_t)h * n1 + t] : M;
+            for (int h = 0; h < Hkv; ++h) {
+                double* x = ell + (int64_t)h * n1 + t;            /* ell is reused for the result */
+                double v = ell1[(int64_t)h * n1 + t];
+                *x = v + (v < M ? log(1.0 - p->alpha_cross) : 0.0);
+            }
+        }
+        /* 6. Top-K per head on the refined log-scores (ties to the lower position), emitted in
+         *    ascending order after the sinks */
+        for (int h = 0; h < Hkv; ++h) {
+            int u = b * Hkv + h;
+            const double* e2 = ell + (int64_t)h * n1;
+            if (refined_out) {
+                double* ro = refined_out + (int64_t)u * logit_stride;
+                for (int64_t j = 0; j < logit_stride; ++j) ro[j] = -INFINITY;
+                for (int64_t t = 0; t < nJ; ++t) ro[j0 + t] = e2[t];
+            }
+            if (ns + take > idx_stride) {
+                bad = 1;
+                n_idx[u] = 0;
+                continue;
+            }
+            scored* sc = (scored*)malloc(sizeof(scored) * (size_t)n1);
+            for (int64_t t = 0; t < nJ; ++t) {
+                sc[t].f = e2[t];
+                sc[t].j = j0 + t;
+            }
+            qsort(sc, (size_t)nJ, sizeof(scored), by_score);
+            unsigned char* keep = (unsigned char*)calloc((size_t)n1, 1);
+            for (int64_t t = 0; t < take; ++t) keep[sc[t].j - j0] = 1;
+            int32_t* row = idx + (int64_t)u * idx_stride;
+            int64_t w = 0;
+            for (int64_t q = 0; q < ns; ++q) row[w++] = (int32_t)q;
+            for (int64_t t = 0; t < nJ; ++t)
+                if (keep[t]) row[w++] = (int32_t)(j0 + t);
+            n_idx[u] = (int32_t)w;
+            free(keep);
+            free(sc);
+        }
+        free(ell);
+        free(ell1);
+    }
+    return bad ? -1 : 0;
+}
+
 /* ---- sparse fast step ---------------------------------------------------------------- */
 
 int orc_sparse(const orc_cache* c, const void* q, const int32_t* idx, int32_t idx_stride,

@@ -56,6 +56,38 @@ int orc_select(int32_t B, int32_t Hq, int32_t Hkv, const int32_t* len,
                int32_t n_sink, int32_t n_recent, int32_t k_sel,
                int32_t* idx, int32_t idx_stride, int32_t* n_idx, double* f_out);
 
+/* Parameters of the full Selector.  lambda: fusion weight of the prior (SFI Sec. 5.1 clips it
+ * at 0.02); alpha_soft, alpha_cross: Soft-NMS and cross-head decays (0.5 and 0.35 there);
+ * prior_decay, tail_frac, tail_brake: shape of the position prior (not given on the page). */
+typedef struct orc_refine {
+    double lambda, alpha_soft, alpha_cross, prior_decay, tail_frac, tail_brake;
+} orc_refine;
+
+/* The full Selector (Slow-Fast Inference, Sec. 3.2 "Cache-aware prior", "Position factor",
+ * "Reverse-KL fusion", Sec. 3.3 "Soft-NMS", "Cross-head exclusivity", Top-K; the pages' formulas
+ * are lost, so each step below is a stated reading).  Per sequence b with J = [n_sink,
+ * N - n_recent) and u_j = (j - n_sink + 1/2)/|J|:
+ *   f_h        the evidence of orc_select
+ *   r_h(j)  ~  exp(-prior_decay u_j) * exp(-tail_brake max(0, u_j - 1 + tail_frac)/tail_frac)
+ *              / max(key_norm[b][h][j], 1e-6)          (the norm factor only if key_norm given)
+ *   s_h     =  argmin over distributions s on J of (1 - lambda) KL(s||f_h) + lambda KL(s||r_h)
+ *           =  f_h^(1-lambda) r_h^lambda / Z_h,   ell = log s_h
+ *   Soft-NMS:  ell1(j) = ell(j) + log(1 - alpha_soft) if a neighbour j-1 or j+1 in J has a
+ *              strictly larger ell, else ell(j)
+ *   exclusivity: ell2_h(j) = ell1_h(j) + log(1 - alpha_cross) if some other KV head of b has a
+ *              strictly larger ell1 at j, else ell1_h(j)
+ *   Top-K of ell2_h as in orc_select (ties to the lower position), emitted after the sinks.
+ * key_norm may be NULL ([B][Hkv][norm_stride] otherwise).  fused_out and refined_out (optional,
+ * [B][Hkv][logit_stride]) receive ell and ell2 on J and -inf elsewhere.  With lambda =
+ * alpha_soft = alpha_cross = 0 the result is that of orc_select.  Returns -1 when idx_stride
+ * is too small. */
+int orc_select_refined(int32_t B, int32_t Hq, int32_t Hkv, const int32_t* len,
+                       const double* logits, int64_t logit_stride,
+                       const double* key_norm, int64_t norm_stride,
+                       int32_t n_sink, int32_t n_recent, int32_t k_sel, const orc_refine* p,
+                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                       double* fused_out, double* refined_out);
+
 /* Sparse decode (Slow-Fast Inference, Sec. 1: a fast step attends only to sink + selected
  * + recent tokens, the recent window moving with every step).  Per (b, i), h = i / G,
  * N = len[b], r0 = max(0, N - n_recent):

@@ -56,7 +56,57 @@ def select_lse_j():
     }
 
 
+def select_soft_nms():
+    # one KV head, G = 1, no sinks or recent window: J = [0, 6) and f = softmax(z) over J.
+    # With z = ln f for an f that sums to one, the evidence is f itself.
+    f = [0.30, 0.25, 0.05, 0.20, 0.05, 0.15]
+    return {
+        "source": "Slow-Fast Inference Sec. 3.3 (Soft-NMS within a head keeps the local maximum "
+                  "of a neighbourhood and decays the lower-scoring candidates next to it, in "
+                  "log-score space; Top-K per KV head)",
+        "derivation": "f = (0.30, 0.25, 0.05, 0.20, 0.05, 0.15) on J = [0, 6), k_sel = 2, "
+                      "no prior (lambda = 0), alpha_soft = 0.5, neighbourhood j-1 and j+1. "
+                      "Local maxima: 0 (0.30 > 0.25), 3 (0.20 > 0.05, 0.05), 5 (0.15 > 0.05). "
+                      "Position 1 has the higher neighbour 0 and drops to 0.125, positions 2 "
+                      "and 4 drop to 0.025. Without Soft-NMS the two largest are {0, 1}; with "
+                      "it they are {0, 3} (0.30, 0.20 > 0.15 > 0.125).",
+        "N": 6, "n_sink": 0, "n_recent": 0, "k_sel": 2, "alpha_soft": 0.5,
+        "z": [math.log(x) for x in f],
+        "expected_idx_plain": [0, 1],
+        "expected_idx": [0, 3],
+        "expected_refined": [math.log(0.30), math.log(0.125), math.log(0.025),
+                             math.log(0.20), math.log(0.025), math.log(0.15)],
+        "tolerance": 1e-12,
+    }
+
+
+def select_cross_head():
+    # two KV heads with one query head each (G = 1), J = [0, 4), f_h = softmax(z_h) = f_h
+    fa = [0.35, 0.32, 0.23, 0.10]
+    fb = [0.36, 0.31, 0.05, 0.28]
+    keep = 1.0 - 0.35
+    ra = [fa[0] * keep, fa[1], fa[2], fa[3] * keep]
+    rb = [fb[0], fb[1] * keep, fb[2] * keep, fb[3]]
+    return {
+        "source": "Slow-Fast Inference Sec. 3.3 (cross-head exclusivity: a soft competition "
+                  "across heads at each fixed position, in log-score space, before Top-K)",
+        "derivation": "f_A = (0.35, 0.32, 0.23, 0.10), f_B = (0.36, 0.31, 0.05, 0.28), "
+                      "k_sel = 2, lambda = alpha_soft = 0, alpha_cross = 0.35. At j = 0 head B "
+                      "is larger, so A's score is multiplied by 0.65; at j = 1 and j = 2 head A "
+                      "is larger, so B's are; at j = 3 B is larger. Refined A = (0.2275, 0.32, "
+                      "0.23, 0.065), B = (0.36, 0.2015, 0.0325, 0.28). Without exclusivity "
+                      "both heads keep {0, 1}; with it A keeps {1, 2} and B keeps {0, 3}.",
+        "N": 4, "n_sink": 0, "n_recent": 0, "k_sel": 2, "alpha_cross": 0.35,
+        "z_head0": [math.log(x) for x in fa], "z_head1": [math.log(x) for x in fb],
+        "expected_idx_plain": [[0, 1], [0, 1]],
+        "expected_idx": [[1, 2], [0, 3]],
+        "expected_refined": [[math.log(x) for x in ra], [math.log(x) for x in rb]],
+        "tolerance": 1e-12,
+    }
+
+
 if __name__ == "__main__":
-    for name, fn in [("dense_two_token", dense_two_token), ("select_lse_j", select_lse_j)]:
+    for name, fn in [("dense_two_token", dense_two_token), ("select_lse_j", select_lse_j),
+                     ("select_soft_nms", select_soft_nms), ("select_cross_head", select_cross_head)]:
         with open(os.path.join(HERE, name + ".json"), "w") as fh:
             json.dump(fn(), fh, indent=1)

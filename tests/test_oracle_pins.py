@@ -12,7 +12,12 @@
 * the Reorg and the two-segment step: segment rows against the cache rows read by tensor
   indexing, exact agreement with the gather step on the same index set, snapshot semantics
   against the library attention on the original rows;
-* the sink-bypass mask against a library sort.
+* the sink-bypass mask against a library sort;
+* the full Selector (prior, fusion, Soft-NMS, cross-head exclusivity: readings of lost
+  equations): its reduction to the plain Selector, the fusion against a numerical minimum of
+  its defining objective, scale invariance and monotonicity of the key-norm factor, the
+  position factor's closed form, Soft-NMS against a library maximum filter, exclusivity under
+  a permutation of the heads, and two hand-derived golden cases.
 No test here needs a GPU.
 """
 import json
@@ -452,6 +457,154 @@ def test_two_segment_drops_entries_past_the_reorg_length(orc):
     og, lg = orc.sparse(c, q, kept, n_idx, wl.n_recent)
     np.testing.assert_array_equal(oc, og)
     np.testing.assert_array_equal(lc, lg)
+
+
+# ----------------------------------------------------------------- the full Selector
+
+NOREF = dict(lambda_=0.0, alpha_soft=0.0, alpha_cross=0.0)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,lens,k_sel", [(2, 8, 2, [700, 333], 50), (1, 4, 4, [260], 7),
+                                                 (3, 6, 3, [40, 1, 500], 30)])
+def test_refined_reduces_to_selector(orc, B, Hq, Hkv, lens, k_sel):
+    g = np.random.default_rng(5)
+    z = g.normal(size=(B, Hq, max(lens))) * 2.0
+    kn = g.uniform(0.5, 2.0, size=(B, Hkv, max(lens)))
+    a, na, _ = orc.select(lens, Hq, Hkv, z, 4, 16, k_sel)
+    b, nb, _, _ = orc.select_refined(lens, Hq, Hkv, z, 4, 16, k_sel, key_norm=kn, params=NOREF)
+    assert (a == b).all() and (na == nb).all()
+    # a uniform prior with lambda > 0 keeps the order of the evidence (s ~ f^(1-lambda))
+    flat = dict(lambda_=0.02, alpha_soft=0.0, alpha_cross=0.0, prior_decay=0.0, tail_brake=0.0)
+    c, nc, _, _ = orc.select_refined(lens, Hq, Hkv, z, 4, 16, k_sel, params=flat)
+    assert (a == c).all() and (na == nc).all()
+
+
+def test_fusion_minimises_the_kl_objective(orc):
+    from scipy.optimize import minimize
+    g = np.random.default_rng(6)
+    N, n_sink, n_recent, Hq = 14, 2, 2, 2                     # J = [2, 12), G = 2
+    z = g.normal(size=(1, Hq, N)) * 1.5
+    kn = g.uniform(0.5, 2.0, size=(1, 1, N))
+    base = dict(alpha_soft=0.0, alpha_cross=0.0, prior_decay=1.3, tail_frac=0.25, tail_brake=2.0)
+    _, _, f = orc.select([N], Hq, 1, z, n_sink, n_recent, 3, want_f=True)
+    fJ = f[0, 0, n_sink:N - n_recent]
+    # lambda = 1: the fused distribution is the prior itself
+    _, _, fr, _ = orc.select_refined([N], Hq, 1, z, n_sink, n_recent, 3, key_norm=kn,
+                                     params=dict(base, lambda_=1.0), want_scores=True)
+    r = np.exp(fr[0, 0, n_sink:N - n_recent])
+    assert abs(r.sum() - 1.0) < 1e-12
+    lam = 0.3
+    _, _, fs, _ = orc.select_refined([N], Hq, 1, z, n_sink, n_recent, 3, key_norm=kn,
+                                     params=dict(base, lambda_=lam), want_scores=True)
+    s = np.exp(fs[0, 0, n_sink:N - n_recent])
+
+    def objective(x):
+        q = np.exp(x - x.max())
+        q /= q.sum()
+        return (1 - lam) * np.sum(q * np.log(q / fJ)) + lam * np.sum(q * np.log(q / r))
+
+    res = minimize(objective, np.log(fJ), method="BFGS", options=dict(gtol=1e-12))
+    q = np.exp(res.x - res.x.max())
+    q /= q.sum()
+    np.testing.assert_allclose(s, q, atol=1e-6)
+    assert objective(np.log(s)) <= res.fun + 1e-12
+
+
+def test_prior_key_norm_and_position_factors(orc):
+    g = np.random.default_rng(7)
+    N, n_sink, n_recent, Hq, Hkv = 200, 4, 20, 4, 2
+    z = g.normal(size=(1, Hq, N))
+    kn = g.uniform(0.5, 2.0, size=(1, Hkv, N))
+    prm = dict(lambda_=0.02, alpha_soft=0.0, alpha_cross=0.0)
+    _, _, f1, _ = orc.select_refined([N], Hq, Hkv, z, n_sink, n_recent, 5, key_norm=kn,
+                                     params=prm, want_scores=True)
+    _, _, f3, _ = orc.select_refined([N], Hq, Hkv, z, n_sink, n_recent, 5, key_norm=3 * kn,
+                                     params=prm, want_scores=True)
+    J = slice(n_sink, N - n_recent)
+    np.testing.assert_allclose(f1[:, :, J], f3[:, :, J], atol=1e-12)     # only ratios matter
+    kn2 = kn.copy()
+    kn2[0, 0, 50] *= 4.0                                                  # a longer key
+    _, _, f4, _ = orc.select_refined([N], Hq, Hkv, z, n_sink, n_recent, 5, key_norm=kn2,
+                                     params=prm, want_scores=True)
+    assert f4[0, 0, 50] < f1[0, 0, 50]
+    others = np.delete(np.arange(n_sink, N - n_recent), 50 - n_sink)
+    assert (f4[0, 0, others] > f1[0, 0, others]).all()
+    np.testing.assert_allclose(f4[0, 1, J], f1[0, 1, J], atol=1e-12)     # the other head
+    # position factor on uniform evidence with lambda = 1 (s is the prior): consecutive
+    # log-ratios are -decay/|J| before the tail and -(decay + brake/tail_frac)/|J| inside it
+    nJ = N - n_recent - n_sink
+    pos = dict(lambda_=1.0, alpha_soft=0.0, alpha_cross=0.0, prior_decay=0.7, tail_frac=0.25,
+               tail_brake=1.5)
+    _, _, fu, _ = orc.select_refined([N], Hq, Hkv, np.zeros((1, Hq, N)), n_sink, n_recent, 5,
+                                     params=pos, want_scores=True)
+    d = np.diff(fu[0, 0, J])
+    u = (np.arange(nJ) + 0.5) / nJ
+    body = (u[1:] <= 0.75)
+    tail = (u[:-1] >= 0.75)
+    np.testing.assert_allclose(d[body], -0.7 / nJ, atol=1e-12)
+    np.testing.assert_allclose(d[tail], -(0.7 + 1.5 / 0.25) / nJ, atol=1e-12)
+
+
+def test_soft_nms_golden(orc):
+    gd = json.load(open(os.path.join(HERE, "golden", "select_soft_nms.json")))
+    z = np.array([[gd["z"]]])
+    plain, _, _ = orc.select([gd["N"]], 1, 1, z, gd["n_sink"], gd["n_recent"], gd["k_sel"])
+    assert plain[0, 0].tolist() == gd["expected_idx_plain"]
+    prm = dict(lambda_=0.0, alpha_soft=gd["alpha_soft"], alpha_cross=0.0)
+    idx, n_idx, _, ref = orc.select_refined([gd["N"]], 1, 1, z, gd["n_sink"], gd["n_recent"],
+                                            gd["k_sel"], params=prm, want_scores=True)
+    assert idx[0, 0, :n_idx[0, 0]].tolist() == gd["expected_idx"]
+    np.testing.assert_allclose(ref[0, 0], gd["expected_refined"], atol=gd["tolerance"])
+
+
+def test_cross_head_golden(orc):
+    gd = json.load(open(os.path.join(HERE, "golden", "select_cross_head.json")))
+    z = np.array([[gd["z_head0"], gd["z_head1"]]])
+    plain, _, _ = orc.select([gd["N"]], 2, 2, z, gd["n_sink"], gd["n_recent"], gd["k_sel"])
+    assert plain[0].tolist() == gd["expected_idx_plain"]
+    prm = dict(lambda_=0.0, alpha_soft=0.0, alpha_cross=gd["alpha_cross"])
+    idx, _, _, ref = orc.select_refined([gd["N"]], 2, 2, z, gd["n_sink"], gd["n_recent"],
+                                        gd["k_sel"], params=prm, want_scores=True)
+    assert idx[0].tolist() == gd["expected_idx"]
+    np.testing.assert_allclose(ref[0], gd["expected_refined"], atol=gd["tolerance"])
+
+
+def test_soft_nms_matches_a_library_maximum_filter(orc):
+    from scipy.ndimage import maximum_filter1d
+    g = np.random.default_rng(8)
+    N, n_sink, n_recent = 300, 4, 30
+    z = np.round(g.normal(size=(1, 2, N)) * 4) / 4            # exact ties between neighbours
+    prm = dict(lambda_=0.02, alpha_soft=0.5, alpha_cross=0.0)
+    _, _, fused, ref = orc.select_refined([N], 2, 1, z, n_sink, n_recent, 20, params=prm,
+                                          want_scores=True)
+    J = slice(n_sink, N - n_recent)
+    e = fused[0, 0, J]
+    lower = maximum_filter1d(e, size=3, mode="nearest") > e
+    assert lower.any() and (~lower).any()
+    np.testing.assert_allclose(ref[0, 0, J] - e, np.where(lower, np.log(0.5), 0.0), atol=1e-12)
+
+
+def test_cross_head_exclusivity_is_permutation_equivariant(orc):
+    g = np.random.default_rng(9)
+    N, Hkv, G = 400, 4, 2
+    z = g.normal(size=(1, Hkv * G, N)) * 2
+    kn = g.uniform(0.5, 2.0, size=(1, Hkv, N))
+    idx, n_idx, _, ref = orc.select_refined([N], Hkv * G, Hkv, z, 4, 40, 25, key_norm=kn,
+                                            want_scores=True)
+    perm = [2, 0, 3, 1]
+    zq = z.reshape(1, Hkv, G, N)[:, perm].reshape(1, Hkv * G, N)
+    idx2, n2, _, ref2 = orc.select_refined([N], Hkv * G, Hkv, zq, 4, 40, 25,
+                                           key_norm=kn[:, perm], want_scores=True)
+    assert (idx2[0] == idx[0, perm]).all() and (n2[0] == n_idx[0, perm]).all()
+    np.testing.assert_array_equal(ref2[0], ref[0, perm])
+    # against the same pipeline without exclusivity: at every position the best head keeps
+    # its score and every other head loses exactly log(1 - alpha_cross)
+    _, _, _, nms = orc.select_refined([N], Hkv * G, Hkv, z, 4, 40, 25, key_norm=kn,
+                                      params=dict(alpha_cross=0.0), want_scores=True)
+    J = slice(4, N - 40)
+    e, r = nms[0, :, J], ref[0, :, J]
+    best = e == e.max(axis=0, keepdims=True)
+    np.testing.assert_allclose(r - e, np.where(best, 0.0, np.log(0.65)), atol=1e-12)
 
 
 # -------------------------------------------------------------------------------- mask
