@@ -53,6 +53,8 @@ def parse():
                          "logits, which a kernel trace would mix into the dense kernel's stats)")
     ap.add_argument("--no-routed", action="store_true",
                     help="skip the routed fast-step measurement on sink-dominated workloads")
+    ap.add_argument("--no-refined", action="store_true",
+                    help="skip the full Selector (prior and refinements) measurement")
     ap.add_argument("--no-two-segment", action="store_true",
                     help="skip the Reorg + two-segment fast-step measurement")
     ap.add_argument("--retention-sweep", action="store_true",
@@ -325,6 +327,60 @@ def synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, 
     return res
 
 
+def key_norms(torch, wl, lay, n: int, stride: int):
+    """fp32 [B][Hkv][stride] norms of the cached keys at positions < n (the statistics the
+    full Selector's prior reads; computed once per layer with torch, outside any timing)."""
+    out = torch.ones((wl.B, wl.Hkv, stride), dtype=torch.float32, device=lay.k.device)
+    if not wl.paged:
+        for b in range(wl.B):
+            out[b, :, :n] = torch.linalg.vector_norm(lay.k[b, :, :n], dim=-1, dtype=torch.float32)
+        return out
+    phys = torch.linalg.vector_norm(lay.k, dim=-1, dtype=torch.float32)   # [n_blk][Hkv][bs]
+    pos = torch.arange(n, device=lay.k.device)
+    for b in range(wl.B):
+        blk = lay.block_table[b, pos // wl.block_size].long()
+        out[b, :, :n] = phys[blk, :, pos % wl.block_size].transpose(0, 1)
+    return out
+
+
+def refined_selector(B, torch, wl, layers, descs, logits, stride, idx_stride, L, reps=3):
+    """sfi_select_refined (prior, fusion, Soft-NMS, cross-head exclusivity) on every rotated
+    layer's slow-step logits, timed as a block beside the plain Selector."""
+    dev = "cuda"
+    n = layers[0].max_len_at(0)
+    norms = [key_norms(torch, wl, layers[li], n, stride) for li in range(L)]
+    ws = B.workspace(descs[0][0], idx_stride=idx_stride, n_recent=wl.n_recent, device=dev,
+                     refined=True)
+    idx = torch.empty((wl.B, wl.Hkv, idx_stride), dtype=torch.int32, device=dev)
+    n_idx = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)
+    params = dict(B.REFINE_DEFAULTS)
+
+    def refined():
+        for li in range(L):
+            B.sfi_select_refined(descs[li][0], logits[li], stride, norms[li], stride, wl.n_sink,
+                                 wl.n_recent, wl.k_sel, params, idx, idx_stride, n_idx, ws)
+
+    def plain():
+        for li in range(L):
+            B.sfi_select(descs[li][0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idx,
+                         idx_stride, n_idx, ws)
+
+    res = {}
+    for name, fn in (("select_refined_us", refined), ("select_plain_us", plain)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(1e3 * e0.elapsed_time(e1) / (reps * L), 2)
+    del norms, ws
+    res["params"] = {k.rstrip("_"): round(v, 4) for k, v in params.items()}
+    return res
+
+
 def two_segment_steps(B, torch, wl, descs, queries, idxs, nidxs, masks, out, lse, ws,
                       idx_stride, L):
     """The two-segment layout: sfi_reorg of every rotated layer's selection (once per cycle),
@@ -579,6 +635,11 @@ def main():
         layered = layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
                                     masks, ws, idx_stride)
 
+    refined = None
+    if not args.no_refined:
+        print("# full Selector", file=sys.stderr, flush=True)
+        refined = refined_selector(B, torch, wl, layers, descs, logits, stride, idx_stride, L)
+
     two_seg = None
     if not args.no_two_segment:
         print("# two-segment layout", file=sys.stderr, flush=True)
@@ -646,6 +707,11 @@ def main():
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
     result["read_yardstick"] = yard
+    if refined is not None:
+        refined["value_if_used_us"] = round(
+            (dense_us + refined["select_refined_us"] + mask_us + (wl.cycle - 1) * fast_us)
+            / wl.cycle, 3)
+        result["select_refined"] = refined
     if two_seg is not None:
         two_seg["value_if_used_us"] = round(
             (dense_us + select_us + mask_us + two_seg["reorg_us"] +

@@ -52,7 +52,21 @@ typedef enum sfi_status {
 
 typedef enum sfi_dtype { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
 
-typedef enum sfi_op { SFI_OP_DENSE = 0, SFI_OP_SELECT = 1, SFI_OP_SPARSE = 2 } sfi_op;
+typedef enum sfi_op {
+    SFI_OP_DENSE = 0, SFI_OP_SELECT = 1, SFI_OP_SPARSE = 2, SFI_OP_SELECT_REFINED = 3
+} sfi_op;
+
+/* Parameters of the full Selector (sfi_select_refined).  SFI Sec. 5.1 gives lambda_clip = 0.02,
+ * alpha_soft = 0.5 and alpha_cross = 0.35; the shape of the position prior is not given there
+ * (the tests and the benchmark use prior_decay 1, tail_frac 1/16, tail_brake 1). */
+typedef struct sfi_refine {
+    float lambda;        /* fusion weight of the prior, 0 <= lambda < 1 */
+    float alpha_soft;    /* Soft-NMS decay, 0 <= alpha_soft < 1 */
+    float alpha_cross;   /* cross-head exclusivity decay, 0 <= alpha_cross < 1 */
+    float prior_decay;   /* global decay of the position prior over J, >= 0 */
+    float tail_frac;     /* fraction of J at its end under the tail brake, in [0, 1] */
+    float tail_brake;    /* strength of the tail brake, >= 0 */
+} sfi_refine;
 
 /* The per-step cache descriptor (SFI Sec. 4.2: one packed description of cache bounds,
  * block tables and layout, read by every kernel of the step).
@@ -120,6 +134,32 @@ sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_
                       int32_t n_sink, int32_t n_recent, int32_t k_sel,
                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The full Selector: sfi_select with the cache-aware prior, reverse-KL fusion and the
+ * log-score refinements.  SFI Sec. 3.2 ("Cache-aware prior on allowed positions", "Position
+ * factor", "Reverse-KL fusion of evidence and prior", "Choosing lambda") and Sec. 3.3
+ * ("Soft-NMS", "Cross-head exclusivity", Top-K).  The page's formulas are lost; this call
+ * implements the following readings, per sequence b, KV head h, with J and the evidence f_h as
+ * for sfi_select and u_j = (j - n_sink + 1/2)/|J|:
+ *   r_h(j) ~ exp(-prior_decay u_j) exp(-tail_brake max(0, u_j - 1 + tail_frac)/tail_frac)
+ *            / max(key_norm[b][h][j], 1e-6)              (norm factor only when key_norm given)
+ *   s_h    = f_h^(1-lambda) r_h^lambda / Z_h             (the minimiser over distributions on J
+ *            of (1 - lambda) KL(s||f_h) + lambda KL(s||r_h))
+ *   Soft-NMS: s_h(j) *= 1 - alpha_soft when s_h(j-1) or s_h(j+1) (in J) is strictly larger
+ *   exclusivity: s_h(j) *= 1 - alpha_cross when another KV head of b has a strictly larger
+ *            score at j after Soft-NMS
+ *   then the Top-K of sfi_select on the refined scores (ties to the lower position).
+ * With lambda = alpha_soft = alpha_cross = 0 the indices equal sfi_select's.
+ * key_norm (device) fp32 [B][Hkv][norm_stride] with norm_stride >= max_len, or NULL: the norms
+ * of the cached keys (statistics kept with the cache).  ws: sfi_workspace_bytes(kv,
+ * SFI_OP_SELECT_REFINED, ...).  Every other argument as for sfi_select.  Seven kernel launches
+ * (the chunked Selector plus two refinement passes).  SFI_E_INVALID for parameters outside the
+ * stated ranges. */
+sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
+                              const float* key_norm, int64_t norm_stride,
+                              int32_t n_sink, int32_t n_recent, int32_t k_sel,
+                              const sfi_refine* params, int32_t* idx, int32_t idx_stride,
+                              int32_t* n_idx, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Sink-bypass mask.  SinkRouter Sec. 4.2: heads whose attention mass on token 0 is large
  * are in a low-impact regime and are bypassed with a zero surrogate.  Per b:
@@ -236,8 +276,8 @@ sfi_status sfi_slow_step_layers(
     hipEvent_t attn_event, hipEvent_t done_event);
 
 /* Workspace bytes needed by one call of `op` on this descriptor.  idx_stride and n_recent
- * (index capacity and recent window) are used by SFI_OP_SPARSE only; SFI_OP_DENSE and
- * SFI_OP_SELECT size from the descriptor (max_len) alone.  Returns 0 when the descriptor
+ * (index capacity and recent window) are used by SFI_OP_SPARSE only; SFI_OP_DENSE,
+ * SFI_OP_SELECT and SFI_OP_SELECT_REFINED size from the descriptor (max_len) alone.  Returns 0 when the descriptor
  * or op is invalid. */
 size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,
                            int32_t n_recent);

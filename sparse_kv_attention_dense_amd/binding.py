@@ -17,9 +17,10 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfi.so"
 
 SFI_OK, SFI_E_INVALID, SFI_E_UNSUPPORTED, SFI_E_WORKSPACE, SFI_E_HIP = 0, -1, -2, -3, -4
 SFI_F32, SFI_BF16 = 0, 1
-SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE = 0, 1, 2
+SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SELECT_REFINED = 0, 1, 2, 3
 
-EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
+EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_select_refined", "sfi_sink_bypass_mask",
+            "sfi_sparse_decode",
             "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
             "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_status_string")
 
@@ -28,6 +29,16 @@ class SfiError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {sfi_status_string(status)}")
+
+
+class sfi_refine(ctypes.Structure):
+    _fields_ = [("lambda_", ctypes.c_float), ("alpha_soft", ctypes.c_float),
+                ("alpha_cross", ctypes.c_float), ("prior_decay", ctypes.c_float),
+                ("tail_frac", ctypes.c_float), ("tail_brake", ctypes.c_float)]
+
+
+REFINE_DEFAULTS = dict(lambda_=0.02, alpha_soft=0.5, alpha_cross=0.35, prior_decay=1.0,
+                       tail_frac=1.0 / 16, tail_brake=1.0)
 
 
 class sfi_kv_desc(ctypes.Structure):
@@ -63,6 +74,9 @@ def lib():
         L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
         L.sfi_workspace_bytes.restype = ctypes.c_size_t
         L.sfi_reorg.argtypes = [D, P, i32, P, P, P, P, P]
+        L.sfi_select_refined.argtypes = [D, P, i64, P, i64, i32, i32, i32,
+                                         ctypes.POINTER(sfi_refine), P, i32, P, P,
+                                         ctypes.c_size_t, P]
         L.sfi_sparse_decode_compact.argtypes = [D, P, P, P, P, i32, P, i32, P, P, P, P,
                                                 ctypes.c_size_t, P]
         L.sfi_stream_read.argtypes = [P, ctypes.c_uint64, i32, P, P]
@@ -70,7 +84,7 @@ def lib():
         L.sfi_status_string.restype = ctypes.c_char_p
         for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
                   "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_stream_read",
-                  "sfi_reorg", "sfi_sparse_decode_compact"):
+                  "sfi_reorg", "sfi_sparse_decode_compact", "sfi_select_refined"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -175,6 +189,20 @@ def sfi_select(desc: KVDesc, logits, logit_stride: int, n_sink: int, n_recent: i
            "sfi_select")
 
 
+def sfi_select_refined(desc: KVDesc, logits, logit_stride: int, key_norm, norm_stride: int,
+                       n_sink: int, n_recent: int, k_sel: int, params: dict, idx,
+                       idx_stride: int, n_idx, ws, stream=None):
+    pr = dict(REFINE_DEFAULTS)
+    pr.update(params or {})
+    p = sfi_refine(pr["lambda_"], pr["alpha_soft"], pr["alpha_cross"], pr["prior_decay"],
+                   pr["tail_frac"], pr["tail_brake"])
+    _check(lib().sfi_select_refined(desc.ref, _ptr(logits), int(logit_stride), _ptr(key_norm),
+                                    int(norm_stride), int(n_sink), int(n_recent), int(k_sel),
+                                    ctypes.byref(p), _ptr(idx), int(idx_stride), _ptr(n_idx),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "sfi_select_refined")
+
+
 def sfi_sink_bypass_mask(desc: KVDesc, logits, logit_stride: int, lse, frac: float, head_mask,
                          stream=None):
     _check(lib().sfi_sink_bypass_mask(desc.ref, _ptr(logits), int(logit_stride), _ptr(lse),
@@ -251,11 +279,14 @@ def sfi_slow_step_layers(descs, qs, outs, lses, logits_slots, logit_stride: int,
         ctypes.c_void_p(_event_handle(done_event, side_stream))), "sfi_slow_step_layers")
 
 
-def workspace(desc: KVDesc, idx_stride: int = 1, n_recent: int = 0, device="cuda"):
+def workspace(desc: KVDesc, idx_stride: int = 1, n_recent: int = 0, device="cuda",
+              refined: bool = False):
     """A workspace large enough for every op on this descriptor (plumbing:
-    torch allocates it once; the library itself never allocates)."""
-    n = max(sfi_workspace_bytes(desc, op, idx_stride, n_recent)
-            for op in (SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE))
+    torch allocates it once; the library itself never allocates).  refined: also for
+    sfi_select_refined."""
+    ops = (SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE) + ((SFI_OP_SELECT_REFINED,) if refined
+                                                          else ())
+    n = max(sfi_workspace_bytes(desc, op, idx_stride, n_recent) for op in ops)
     if n == 0:
         raise SfiError(SFI_E_INVALID, "workspace")
     return torch.zeros(n, dtype=torch.uint8, device=device)

@@ -147,6 +147,7 @@ struct SelPlan {
     int nchunk = 0;
     size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0;
     size_t off_cand = 0, off_cand_n = 0, bytes = 0;
+    size_t off_zpart = 0, off_nms = 0, bytes_refined = 0;   // full Selector only
 };
 
 void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
@@ -162,6 +163,9 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     p->off_cand = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
     p->off_cand_n = off; off += align_up(B * Hkv * nc * sizeof(uint32_t));
     p->bytes = off;
+    p->off_zpart = off;  off += align_up(B * Hkv * nc * sizeof(float));
+    p->off_nms = off;    off += align_up(B * Hkv * nc * kSelChunk * sizeof(float));
+    p->bytes_refined = off;
 }
 
 // rows of a compact segment [B][Hkv][idx_stride] (row numbers are kept in 32 bits)
@@ -261,6 +265,14 @@ sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit
     a->cand = (uint32_t*)(base + plan.off_cand);
     a->cand_n = (uint32_t*)(base + plan.off_cand_n);
     a->unit_path = select_unit_path(*kv) ? 1 : 0;
+    a->refine = 0;
+    a->key_norm = nullptr;
+    a->norm_stride = 0;
+    a->lam = 0.f;
+    a->keep_soft = a->keep_cross = 1.f;
+    a->prior_decay = a->tail_frac = a->tail_brake = 0.f;
+    a->zpart = nullptr;
+    a->nms = nullptr;
     return SFI_OK;
 }
 
@@ -412,6 +424,42 @@ SFI_EXPORT sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int
     return launch_select(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
 }
 
+SFI_EXPORT sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* logits,
+                                         int64_t logit_stride, const float* key_norm,
+                                         int64_t norm_stride, int32_t n_sink, int32_t n_recent,
+                                         int32_t k_sel, const sfi_refine* params, int32_t* idx,
+                                         int32_t idx_stride, int32_t* n_idx, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+    if (!params) return SFI_E_INVALID;
+    const sfi_refine& p = *params;
+    if (!(p.lambda >= 0.f && p.lambda < 1.f) || !(p.alpha_soft >= 0.f && p.alpha_soft < 1.f) ||
+        !(p.alpha_cross >= 0.f && p.alpha_cross < 1.f) || !(p.prior_decay >= 0.f) ||
+        !(p.tail_frac >= 0.f && p.tail_frac <= 1.f) || !(p.tail_brake >= 0.f))
+        return SFI_E_INVALID;
+    if (key_norm && (norm_stride < kv->max_len || norm_stride < 1)) return SFI_E_INVALID;
+    SelArgs a;
+    sfi_status st = prep_select(kv, logits, logit_stride, n_sink, n_recent, k_sel, idx,
+                                idx_stride, n_idx, ws, ws_bytes, &a);
+    if (st != SFI_OK) return st;
+    SelPlan plan;
+    plan_select(*kv, &plan);
+    st = check_ws(ws, ws_bytes, plan.bytes_refined);
+    if (st != SFI_OK) return st;
+    a.unit_path = 0;                        // the exclusivity pass couples the KV heads
+    a.refine = 1;
+    a.key_norm = key_norm;
+    a.norm_stride = norm_stride;
+    a.lam = p.lambda;
+    a.keep_soft = 1.f - p.alpha_soft;
+    a.keep_cross = 1.f - p.alpha_cross;
+    a.prior_decay = p.prior_decay;
+    a.tail_frac = p.tail_frac;
+    a.tail_brake = p.tail_brake;
+    a.zpart = (float*)((unsigned char*)ws + plan.off_zpart);
+    a.nms = (float*)((unsigned char*)ws + plan.off_nms);
+    return launch_select(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
 SFI_EXPORT sfi_status sfi_sink_bypass_mask(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
                                            const float* lse, float frac, uint8_t* head_mask,
                                            hipStream_t stream) {
@@ -484,6 +532,12 @@ SFI_EXPORT size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t
         SelPlan p;
         plan_select(*kv, &p);
         return p.bytes;
+    }
+    if (op == SFI_OP_SELECT_REFINED) {
+        if (check_desc(kv, false) != SFI_OK) return 0;
+        SelPlan p;
+        plan_select(*kv, &p);
+        return p.bytes_refined;
     }
     if (op != SFI_OP_DENSE && op != SFI_OP_SPARSE) return 0;
     if (check_desc(kv, true) != SFI_OK) return 0;

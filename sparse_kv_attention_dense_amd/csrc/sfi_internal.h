@@ -79,6 +79,15 @@ struct SelArgs {
     uint32_t* cand;                  // [B][Hkv][nchunk][kSelChunk]: keys of the digit-0 bin
     uint32_t* cand_n;                // [B][Hkv][nchunk]: candidates per chunk
     int32_t unit_path;               // 1: one workgroup per (b, KV head) does everything
+    // full Selector (refine != 0): prior, reverse-KL fusion, Soft-NMS, cross-head exclusivity
+    int32_t refine;
+    const float* key_norm;           // [B][Hkv][norm_stride] or null (no key-norm factor)
+    int64_t norm_stride;
+    float lam;                       // fusion weight of the prior, in [0, 1)
+    float keep_soft, keep_cross;     // 1 - alpha_soft, 1 - alpha_cross
+    float prior_decay, tail_frac, tail_brake;
+    float* zpart;                    // [B][Hkv][nchunk]: partial sums of f^(1-lam) r^lam
+    float* nms;                      // [B][Hkv][nchunk*kSelChunk]: fused scores after Soft-NMS
 };
 
 hipError_t launch_select(const SelArgs& a, hipStream_t stream);

@@ -22,6 +22,16 @@
 //                          order after the sink positions [0, min(n_sink, N)).
 // The one-launch path (select_unit_kernel, short contexts) does the same in one workgroup per
 // (b, KV head).
+// Full Selector (refine mode, SFI Sec. 3.2 prior and reverse-KL fusion, Sec. 3.3 Soft-NMS and
+// cross-head exclusivity; the pages' formulas are lost and the library implements stated
+// readings of them): the evidence pass also sums f^(1-lam) r^lam per chunk instead of building
+// the histogram, then
+//   refine_nms_kernel    s = f^(1-lam) r^lam / Z per position of the chunk (and its two
+//                         neighbours), decayed by 1 - alpha_soft when a neighbour in J is larger
+//   refine_cross_kernel  per sequence and chunk: every KV head below the largest at a position
+//                         is decayed by 1 - alpha_cross; the results are the keys, and the
+//                         digit-0 histograms are built from them
+// before the candidate, resolve and emit passes, which are unchanged.
 // f is computed without the 1/G factor: a positive common scale does not change the order.
 //
 // Sink-bypass mask (SinkRouter Sec. 4.2): rank the query heads of each sequence by their
@@ -159,9 +169,26 @@ __global__ void __launch_bounds__(kThreads) lse_kernel(SelArgs a) {
     if (tid == 0) a.lse_part[((int64_t)b * a.Hq + i) * a.nchunk + c] = make_float2(m, s);
 }
 
+// log2 of the unnormalised prior weight of position j (J = [j0, j0 + nJ)) for unit `unit`:
+// a global decay over J, a brake over its last tail_frac, and the inverse key norm.
+__device__ __forceinline__ float prior_log2(const SelArgs& a, int unit, int j, int j0, int nJ) {
+    const float u = ((float)(j - j0) + 0.5f) / (float)nJ;
+    float e = -a.prior_decay * u;
+    if (a.tail_frac > 0.f) e -= a.tail_brake * fmaxf(0.f, u - (1.f - a.tail_frac)) / a.tail_frac;
+    float l = e * kLog2e;
+    if (a.key_norm) l -= __log2f(fmaxf(a.key_norm[(int64_t)unit * a.norm_stride + j], 1e-6f));
+    return l;
+}
+
+// log2 of f^(1-lam) r^lam (unnormalised; f without the 1/G factor, r without its sum)
+__device__ __forceinline__ float fused_log2(const SelArgs& a, float f, float lr) {
+    return (1.f - a.lam) * __log2f(f) + a.lam * lr;
+}
+
 __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     __shared__ float s_lse[kMaxG];
     __shared__ uint32_t lh[kCBins0];
+    __shared__ float sh[4];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int G = a.G;
@@ -187,6 +214,23 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     __syncthreads();
     uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
     const float* zb = a.logits + ((int64_t)b * a.Hq + h * G) * a.logit_stride;
+    if (a.refine) {
+        // keys of f for the refinement passes, and this chunk's share of the fusion normaliser
+        float zs = 0.f;
+        for (int k = 0; k < kPerThread; ++k) {
+            const int j = lo + k * kThreads + tid;
+            if (j < hi) {
+                float f = 0.f;
+                for (int g = 0; g < G; ++g)
+                    f += exp2_hw(fmaf(zb[(int64_t)g * a.logit_stride + j], kLog2e, -s_lse[g]));
+                keys[j - lo] = __float_as_uint(f);
+                zs += exp2_hw(fused_log2(a, f, prior_log2(a, unit, j, r.j0, r.nJ)));
+            }
+        }
+        zs = block_sum(zs, sh);
+        if (tid == 0) a.zpart[(int64_t)unit * a.nchunk + c] = zs;
+        return;
+    }
 #pragma unroll 4
     for (int k = 0; k < kPerThread; ++k) {
         const int j = lo + k * kThreads + tid;
@@ -203,6 +247,88 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
     for (int t = tid; t < kCBins0; t += kThreads)
         if (lh[t]) atomicAdd(&hg[t], lh[t]);
+}
+
+// Fused score and Soft-NMS for one (chunk, KV head, sequence).  The log2 scores of the chunk's
+// positions and of the neighbours just outside it are computed once, by one code path, into
+// LDS; a position is decayed by keep_soft when a neighbour in J has a strictly larger score.
+__global__ void __launch_bounds__(kThreads) refine_nms_kernel(SelArgs a) {
+    __shared__ float sh[4];
+    __shared__ float ls[kSelChunk + 2];             // positions lo - 1 ... hi
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    const Range r = j_range(a, b);
+    const int lo = r.j0 + c * kSelChunk;
+    const int hi = min(r.j1, lo + kSelChunk);
+    if (lo >= hi) return;
+    const int nc = (r.nJ + kSelChunk - 1) / kSelChunk;
+    float zs = 0.f;
+    for (int k = tid; k < nc; k += kThreads) zs += a.zpart[(int64_t)unit * a.nchunk + k];
+    const float l2z = __log2f(block_sum(zs, sh));
+    const uint32_t* keys_u = a.keys + (int64_t)unit * a.nchunk * kSelChunk;   // by j - j0
+    const int p0 = max(lo - 1, r.j0), p1 = min(hi + 1, r.j1);
+    for (int p = p0 + tid; p < p1; p += kThreads) {
+        const float f = __uint_as_float(keys_u[p - r.j0]);
+        ls[p - (lo - 1)] = fused_log2(a, f, prior_log2(a, unit, p, r.j0, r.nJ)) - l2z;
+    }
+    __syncthreads();
+    float* out = a.nms + (int64_t)unit * a.nchunk * kSelChunk;
+#pragma unroll 4
+    for (int k = 0; k < kPerThread; ++k) {
+        const int j = lo + k * kThreads + tid;
+        if (j < hi) {
+            const float v = ls[j - (lo - 1)];
+            const bool lower = (j > r.j0 && ls[j - 1 - (lo - 1)] > v) ||
+                               (j + 1 < r.j1 && ls[j + 1 - (lo - 1)] > v);
+            out[j - r.j0] = exp2_hw(v) * (lower ? a.keep_soft : 1.f);
+        }
+    }
+}
+
+// Cross-head exclusivity for one (chunk, sequence): at each position every KV head whose score
+// is below the largest is decayed by keep_cross.  The results become the keys, and the digit-0
+// histogram of each unit is built from them (one LDS histogram, reused head by head).
+__global__ void __launch_bounds__(kThreads) refine_cross_kernel(SelArgs a) {
+    __shared__ uint32_t lh[kCBins0];
+    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const Range r = j_range(a, b);
+    const int lo = r.j0 + c * kSelChunk;
+    const int hi = min(r.j1, lo + kSelChunk);
+    if (lo >= hi) return;
+    const int64_t chunk_off = (int64_t)c * kSelChunk;
+    float mx[kPerThread];
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) mx[k] = -INFINITY;
+    for (int h = 0; h < a.Hkv; ++h) {
+        const float* nu = a.nms + (int64_t)(b * a.Hkv + h) * a.nchunk * kSelChunk + chunk_off;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int t = k * kThreads + tid;
+            if (lo + t < hi) mx[k] = fmaxf(mx[k], nu[t]);
+        }
+    }
+    for (int h = 0; h < a.Hkv; ++h) {
+        const int unit = b * a.Hkv + h;
+        for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
+        __syncthreads();
+        const float* nu = a.nms + (int64_t)unit * a.nchunk * kSelChunk + chunk_off;
+        uint32_t* keys = a.keys + (int64_t)unit * a.nchunk * kSelChunk + chunk_off;
+#pragma unroll
+        for (int k = 0; k < kPerThread; ++k) {
+            const int t = k * kThreads + tid;
+            if (lo + t < hi) {
+                const float v = nu[t];
+                const uint32_t key = __float_as_uint(v < mx[k] ? v * a.keep_cross : v);
+                keys[t] = key;
+                atomicAdd(&lh[key >> kCShift[0]], 1u);
+            }
+        }
+        __syncthreads();
+        uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
+        for (int t = tid; t < kCBins0; t += kThreads)
+            if (lh[t]) atomicAdd(&hg[t], lh[t]);
+        __syncthreads();
+    }
 }
 
 // state: [0] prefix (bits of T decided so far), [1] k_rem, [2] nJ, [3] take_all
@@ -851,6 +977,10 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     const dim3 g_unit(a.Hkv, a.B);
     hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
     hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
+    if (a.refine) {
+        hipLaunchKernelGGL(refine_nms_kernel, g_group, blk, 0, s, a);
+        hipLaunchKernelGGL(refine_cross_kernel, dim3(a.nchunk, a.B), blk, 0, s, a);
+    }
     hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
     hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
     hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);

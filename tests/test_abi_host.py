@@ -219,3 +219,29 @@ def test_reorg_and_two_segment_validation(L):
     assert sc(ck=FAKE + 4) == B.SFI_E_INVALID
     assert sc(cpos=None) == B.SFI_E_INVALID
     assert sc(ws=ws - 256) == B.SFI_E_WORKSPACE
+
+
+def test_select_refined_validation(L):
+    d = _desc()
+    D = ctypes.byref(d)
+    ws = L.sfi_workspace_bytes(D, B.SFI_OP_SELECT_REFINED, 0, 0)
+    assert ws > L.sfi_workspace_bytes(D, B.SFI_OP_SELECT, 0, 0)
+
+    def call(ws_bytes=ws, norm=FAKE, nstride=4000, **kw):
+        pr = dict(B.REFINE_DEFAULTS)
+        pr.update(kw)
+        p = B.sfi_refine(pr["lambda_"], pr["alpha_soft"], pr["alpha_cross"], pr["prior_decay"],
+                         pr["tail_frac"], pr["tail_brake"])
+        return L.sfi_select_refined(D, FAKE, 4000, norm, nstride, 4, 64, 100, ctypes.byref(p),
+                                    FAKE, 104, FAKE, FAKE, ws_bytes, None)
+
+    assert call(lambda_=1.0) == B.SFI_E_INVALID
+    assert call(lambda_=-0.1) == B.SFI_E_INVALID
+    assert call(alpha_soft=1.0) == B.SFI_E_INVALID
+    assert call(alpha_cross=float("nan")) == B.SFI_E_INVALID
+    assert call(tail_frac=1.5) == B.SFI_E_INVALID
+    assert call(prior_decay=-1.0) == B.SFI_E_INVALID
+    assert call(nstride=3999) == B.SFI_E_INVALID
+    assert call(ws_bytes=ws - 256) == B.SFI_E_WORKSPACE
+    assert L.sfi_select_refined(D, FAKE, 4000, None, 0, 4, 64, 100, None, FAKE, 104, FAKE, FAKE,
+                                ws, None) == B.SFI_E_INVALID
