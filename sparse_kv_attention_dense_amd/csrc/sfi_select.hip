@@ -171,12 +171,19 @@ __global__ void __launch_bounds__(kThreads) lse_kernel(SelArgs a) {
 
 // log2 of the unnormalised prior weight of position j (J = [j0, j0 + nJ)) for unit `unit`:
 // a global decay over J, a brake over its last tail_frac, and the inverse key norm.
+__device__ __forceinline__ float prior_log2_n(const SelArgs& a, int j, int j0, int nJ, float nrm);
 __device__ __forceinline__ float prior_log2(const SelArgs& a, int unit, int j, int j0, int nJ) {
+    const float nrm = a.key_norm ? a.key_norm[(int64_t)unit * a.norm_stride + j] : 1.f;
+    return prior_log2_n(a, j, j0, nJ, nrm);
+}
+
+// the same with the key norm already loaded (1 when there are no norms)
+__device__ __forceinline__ float prior_log2_n(const SelArgs& a, int j, int j0, int nJ, float nrm) {
     const float u = ((float)(j - j0) + 0.5f) / (float)nJ;
     float e = -a.prior_decay * u;
     if (a.tail_frac > 0.f) e -= a.tail_brake * fmaxf(0.f, u - (1.f - a.tail_frac)) / a.tail_frac;
     float l = e * kLog2e;
-    if (a.key_norm) l -= __log2f(fmaxf(a.key_norm[(int64_t)unit * a.norm_stride + j], 1e-6f));
+    if (a.key_norm) l -= __log2f(fmaxf(nrm, 1e-6f));
     return l;
 }
 
@@ -217,6 +224,7 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     if (a.refine) {
         // keys of f for the refinement passes, and this chunk's share of the fusion normaliser
         float zs = 0.f;
+#pragma unroll 4
         for (int k = 0; k < kPerThread; ++k) {
             const int j = lo + k * kThreads + tid;
             if (j < hi) {
@@ -261,15 +269,27 @@ __global__ void __launch_bounds__(kThreads) refine_nms_kernel(SelArgs a) {
     const int lo = r.j0 + c * kSelChunk;
     const int hi = min(r.j1, lo + kSelChunk);
     if (lo >= hi) return;
+    const uint32_t* keys_u = a.keys + (int64_t)unit * a.nchunk * kSelChunk;   // by j - j0
+    const int p0 = max(lo - 1, r.j0), p1 = min(hi + 1, r.j1);
+    // every load of the thread first (evidence, key norm, the normaliser's parts), then the
+    // scores
+    constexpr int kM = kPerThread + 1;                  // covers kSelChunk + 2 positions
+    float fv[kM], nv[kM];
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+        const int p = p0 + m * kThreads + tid;
+        fv[m] = p < p1 ? __uint_as_float(keys_u[p - r.j0]) : 0.f;
+        nv[m] = (p < p1 && a.key_norm) ? a.key_norm[(int64_t)unit * a.norm_stride + p] : 1.f;
+    }
     const int nc = (r.nJ + kSelChunk - 1) / kSelChunk;
     float zs = 0.f;
     for (int k = tid; k < nc; k += kThreads) zs += a.zpart[(int64_t)unit * a.nchunk + k];
     const float l2z = __log2f(block_sum(zs, sh));
-    const uint32_t* keys_u = a.keys + (int64_t)unit * a.nchunk * kSelChunk;   // by j - j0
-    const int p0 = max(lo - 1, r.j0), p1 = min(hi + 1, r.j1);
-    for (int p = p0 + tid; p < p1; p += kThreads) {
-        const float f = __uint_as_float(keys_u[p - r.j0]);
-        ls[p - (lo - 1)] = fused_log2(a, f, prior_log2(a, unit, p, r.j0, r.nJ)) - l2z;
+#pragma unroll
+    for (int m = 0; m < kM; ++m) {
+        const int p = p0 + m * kThreads + tid;
+        if (p < p1)
+            ls[p - (lo - 1)] = fused_log2(a, fv[m], prior_log2_n(a, p, r.j0, r.nJ, nv[m])) - l2z;
     }
     __syncthreads();
     float* out = a.nms + (int64_t)unit * a.nchunk * kSelChunk;
@@ -285,40 +305,64 @@ __global__ void __launch_bounds__(kThreads) refine_nms_kernel(SelArgs a) {
     }
 }
 
-// Cross-head exclusivity for one (chunk, sequence): at each position every KV head whose score
-// is below the largest is decayed by keep_cross.  The results become the keys, and the digit-0
-// histogram of each unit is built from them (one LDS histogram, reused head by head).
+// Cross-head exclusivity for one (part of a chunk, sequence): at each position every KV head
+// whose score is below the largest is decayed by keep_cross.  The results become the keys, and
+// the digit-0 histogram of each unit is built from them (one LDS histogram, reused head by
+// head).  A chunk is split over kCrossParts workgroups so the launch fills the chip.
+#ifndef SFI_CROSS_PARTS
+#define SFI_CROSS_PARTS 4
+#endif
+constexpr int kCrossParts = SFI_CROSS_PARTS;
+constexpr int kCrossPer = kPerThread / kCrossParts;    // positions per thread
+constexpr int kCrossRegHeads = 16;                      // heads whose scores stay in registers
 __global__ void __launch_bounds__(kThreads) refine_cross_kernel(SelArgs a) {
     __shared__ uint32_t lh[kCBins0];
-    const int c = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int c = blockIdx.x / kCrossParts, part = blockIdx.x % kCrossParts;
+    const int b = blockIdx.y, tid = threadIdx.x;
     const Range r = j_range(a, b);
-    const int lo = r.j0 + c * kSelChunk;
-    const int hi = min(r.j1, lo + kSelChunk);
+    const int lo = r.j0 + c * kSelChunk + part * (kSelChunk / kCrossParts);
+    const int hi = min(r.j1, lo + kSelChunk / kCrossParts);
     if (lo >= hi) return;
-    const int64_t chunk_off = (int64_t)c * kSelChunk;
-    float mx[kPerThread];
+    const int64_t chunk_off = (int64_t)c * kSelChunk + part * (kSelChunk / kCrossParts);
+    const int64_t unit_len = (int64_t)a.nchunk * kSelChunk;
+    const float* nms_b = a.nms + (int64_t)b * a.Hkv * unit_len + chunk_off;
+    // the scores of the first kCrossRegHeads heads are loaded once, all in flight together
+    float v[kCrossRegHeads][kCrossPer];
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k) mx[k] = -INFINITY;
-    for (int h = 0; h < a.Hkv; ++h) {
-        const float* nu = a.nms + (int64_t)(b * a.Hkv + h) * a.nchunk * kSelChunk + chunk_off;
+    for (int h = 0; h < kCrossRegHeads; ++h)
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
+        for (int k = 0; k < kCrossPer; ++k) {
             const int t = k * kThreads + tid;
-            if (lo + t < hi) mx[k] = fmaxf(mx[k], nu[t]);
+            v[h][k] = (h < a.Hkv && lo + t < hi) ? nms_b[h * unit_len + t] : -INFINITY;
         }
+    float mx[kCrossPer];
+#pragma unroll
+    for (int k = 0; k < kCrossPer; ++k) {
+        mx[k] = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < kCrossRegHeads; ++h) mx[k] = fmaxf(mx[k], v[h][k]);
     }
+    for (int h = kCrossRegHeads; h < a.Hkv; ++h)
+#pragma unroll
+        for (int k = 0; k < kCrossPer; ++k) {
+            const int t = k * kThreads + tid;
+            if (lo + t < hi) mx[k] = fmaxf(mx[k], nms_b[h * unit_len + t]);
+        }
     for (int h = 0; h < a.Hkv; ++h) {
         const int unit = b * a.Hkv + h;
         for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
         __syncthreads();
-        const float* nu = a.nms + (int64_t)unit * a.nchunk * kSelChunk + chunk_off;
-        uint32_t* keys = a.keys + (int64_t)unit * a.nchunk * kSelChunk + chunk_off;
+        uint32_t* keys = a.keys + (int64_t)unit * unit_len + chunk_off;
 #pragma unroll
-        for (int k = 0; k < kPerThread; ++k) {
+        for (int k = 0; k < kCrossPer; ++k) {
             const int t = k * kThreads + tid;
             if (lo + t < hi) {
-                const float v = nu[t];
-                const uint32_t key = __float_as_uint(v < mx[k] ? v * a.keep_cross : v);
+                float x = 0.f;
+#pragma unroll
+                for (int hh = 0; hh < kCrossRegHeads; ++hh)
+                    if (hh == h) x = v[hh][k];
+                if (h >= kCrossRegHeads) x = nms_b[h * unit_len + t];
+                const uint32_t key = __float_as_uint(x < mx[k] ? x * a.keep_cross : x);
                 keys[t] = key;
                 atomicAdd(&lh[key >> kCShift[0]], 1u);
             }
@@ -979,7 +1023,7 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
     if (a.refine) {
         hipLaunchKernelGGL(refine_nms_kernel, g_group, blk, 0, s, a);
-        hipLaunchKernelGGL(refine_cross_kernel, dim3(a.nchunk, a.B), blk, 0, s, a);
+        hipLaunchKernelGGL(refine_cross_kernel, dim3(a.nchunk * kCrossParts, a.B), blk, 0, s, a);
     }
     hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
     hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
