@@ -189,7 +189,7 @@ def test_refined_full_size(orc):
 
 def test_refined_edges(orc):
     """Empty J, J shorter than k, k = 0, one KV head (no competition), no tail brake, no
-    key norms, G = 1."""
+    key norms, G = 1, and 20 KV heads (beyond the 16 kept in registers)."""
     wl = synth.Workload("ref_edges", 1, 6, 6, 6, 64, "bf16", 3000, 4, 64, 100, 1)
     g = torch.Generator().manual_seed(9)
     lens = [3, 68, 150, 3000, 1, 2000]
@@ -201,6 +201,14 @@ def test_refined_edges(orc):
         n_diff, n_amb, _, _ = _compare(orc, wl, lens, z, None, params, wl.n_sink, wl.n_recent,
                                        k_sel, ig, ng)
         assert n_diff <= n_amb
+    # more KV heads than the exclusivity pass holds in registers
+    many = synth.Workload("ref_many", 1, 2, 40, 20, 128, "bf16", 6000, 4, 64, 200, 1)
+    zm = torch.randn((2, 40, 6000), generator=g) * 2
+    km = torch.rand((2, 20, 6000), generator=g) + 0.5
+    ig, ng = _gpu_refined(many, [6000, 5000], zm, km, dict(B.REFINE_DEFAULTS), 4, 64, 200)
+    n_diff, n_amb, _, _ = _compare(orc, many, [6000, 5000], zm, km, dict(B.REFINE_DEFAULTS), 4,
+                                   64, 200, ig, ng)
+    assert n_diff <= n_amb
     one = synth.Workload("ref_one", 1, 2, 3, 1, 128, "bf16", 9000, 4, 64, 300, 1)
     z1 = torch.randn((2, 3, 9000), generator=g) * 2
     ig, ng = _gpu_refined(one, [9000, 7000], z1, None, dict(B.REFINE_DEFAULTS), 4, 64, 300)
