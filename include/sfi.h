@@ -253,11 +253,14 @@ sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
  *   on `side_stream`: wait for that dense step (attn_event); sfi_select(&kv[l], logits[s], ...)
  *                     into idx[l], n_idx[l] with workspace sel_ws[s]; when head_mask is not NULL,
  *                     sfi_sink_bypass_mask(&kv[l], logits[s], lse[l], mask_frac, head_mask[l]);
- *                     then record slot_events[s] (slot s free again).
+ *                     then record slot_events[s] (slot s free again); when seg_k is not
+ *                     NULL, sfi_reorg(&kv[l], idx[l], ..., seg_k[l], seg_v[l], seg_pos[l])
+ *                     (SFI Sec. 4.1: Reorg_i follows Sel_i on the maintenance stream).
  * Finally `stream` waits for everything queued on `side_stream` (done_event), so work queued on
- * `stream` after this call sees every layer's indices and masks.  Every result equals that of
- * the per-layer calls made one after another.
- * Arguments: kv, q, out, lse, idx, n_idx (and head_mask, or NULL) are host arrays of n_layers
+ * `stream` after this call sees every layer's indices, masks and compact segments.  Every
+ * result equals that of the per-layer calls made one after another.
+ * Arguments: kv, q, out, lse, idx, n_idx (and head_mask, or NULL; seg_k, seg_v, seg_pos, all
+ * NULL or all given, laid out as for sfi_reorg with idx_stride) are host arrays of n_layers
  * entries; logits and sel_ws are host arrays of n_slots entries; all the pointers in them are
  * device buffers laid out as for the single calls (lse is required here).  dense_ws (at least
  * SFI_OP_DENSE bytes for every layer) serves the dense steps one after another; each sel_ws[s]
@@ -272,6 +275,7 @@ sfi_status sfi_slow_step_layers(
     void* const* sel_ws, size_t sel_ws_bytes, void* dense_ws, size_t dense_ws_bytes,
     int32_t n_sink, int32_t n_recent, int32_t k_sel, int32_t* const* idx, int32_t idx_stride,
     int32_t* const* n_idx, float mask_frac, uint8_t* const* head_mask,
+    void* const* seg_k, void* const* seg_v, int32_t* const* seg_pos,
     hipStream_t stream, hipStream_t side_stream, hipEvent_t* slot_events,
     hipEvent_t attn_event, hipEvent_t done_event);
 

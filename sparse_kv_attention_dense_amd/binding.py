@@ -70,7 +70,7 @@ def lib():
                                                P, P, P, ctypes.c_size_t, P]
         L.sfi_slow_step_layers.argtypes = [i32, D, P, P, P, i32, P, i64, P, ctypes.c_size_t, P,
                                            ctypes.c_size_t, i32, i32, i32, P, i32, P,
-                                           ctypes.c_float, P, P, P, P, P, P]
+                                           ctypes.c_float, P, P, P, P, P, P, P, P, P]
         L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
         L.sfi_workspace_bytes.restype = ctypes.c_size_t
         L.sfi_reorg.argtypes = [D, P, i32, P, P, P, P, P]
@@ -260,10 +260,11 @@ def _event_handle(ev, stream):
 def sfi_slow_step_layers(descs, qs, outs, lses, logits_slots, logit_stride: int, sel_ws_slots,
                          dense_ws, n_sink: int, n_recent: int, k_sel: int, idxs, idx_stride: int,
                          n_idxs, mask_frac: float, head_masks, stream, side_stream, slot_events,
-                         attn_event, done_event):
+                         attn_event, done_event, segments=None):
     """Layer-wise slow step (see include/sfi.h).  descs, qs, outs, lses, idxs, n_idxs,
     head_masks: one per layer (head_masks may be None); logits_slots, sel_ws_slots and
-    slot_events: one per ring slot; streams are torch.cuda.Stream, events torch.cuda.Event."""
+    slot_events: one per ring slot; streams are torch.cuda.Stream, events torch.cuda.Event.
+    segments: None, or one (seg_k, seg_v, seg_pos) per layer for a Reorg after each Selector."""
     n, r = len(descs), len(logits_slots)
     darr = (sfi_kv_desc * n)(*[d.c for d in descs])
     evs = (ctypes.c_void_p * r)(*[_event_handle(e, side_stream) for e in slot_events])
@@ -274,6 +275,9 @@ def sfi_slow_step_layers(descs, qs, outs, lses, logits_slots, logit_stride: int,
         dense_ws.numel() * dense_ws.element_size(), int(n_sink), int(n_recent), int(k_sel),
         _ptr_array(idxs), int(idx_stride), _ptr_array(n_idxs), float(mask_frac),
         None if head_masks is None else _ptr_array(head_masks),
+        None if segments is None else _ptr_array([t[0] for t in segments]),
+        None if segments is None else _ptr_array([t[1] for t in segments]),
+        None if segments is None else _ptr_array([t[2] for t in segments]),
         ctypes.c_void_p(stream.cuda_stream), ctypes.c_void_p(side_stream.cuda_stream), evs,
         ctypes.c_void_p(_event_handle(attn_event, stream)),
         ctypes.c_void_p(_event_handle(done_event, side_stream))), "sfi_slow_step_layers")

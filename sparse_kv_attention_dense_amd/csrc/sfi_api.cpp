@@ -362,15 +362,16 @@ SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
                        nullptr, nullptr, out, lse, ws, ws_bytes, stream);
 }
 
-SFI_EXPORT sfi_status sfi_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
-                                const int32_t* n_idx, void* ck, void* cv, int32_t* cpos,
-                                hipStream_t stream) {
+namespace {
+
+sfi_status prep_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
+                      const int32_t* n_idx, void* ck, void* cv, int32_t* cpos, ReorgArgs* out) {
     const sfi_status st = check_desc(kv, true);
     if (st != SFI_OK) return st;
     if (!idx || !n_idx || !ck || !cv || !cpos || idx_stride < 1) return SFI_E_INVALID;
     if (!aligned(ck, 16) || !aligned(cv, 16) || !aligned(cpos, 4)) return SFI_E_INVALID;
     if (segment_rows(*kv, idx_stride) >= (int64_t(1) << 32)) return SFI_E_UNSUPPORTED;
-    ReorgArgs a;
+    ReorgArgs& a = *out;
     a.k = kv->k;
     a.v = kv->v;
     a.len = kv->len;
@@ -387,8 +388,22 @@ SFI_EXPORT sfi_status sfi_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32
     a.ck = ck;
     a.cv = cv;
     a.cpos = cpos;
-    const int row_bytes = kv->head_dim * (kv->dtype == SFI_BF16 ? 2 : 4);
-    return launch_reorg(a, kv->batch, row_bytes, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
+    return SFI_OK;
+}
+
+hipError_t launch_reorg_for(const sfi_kv_desc* kv, const ReorgArgs& a, hipStream_t stream) {
+    return launch_reorg(a, kv->batch, kv->head_dim * (kv->dtype == SFI_BF16 ? 2 : 4), stream);
+}
+
+}  // namespace
+
+SFI_EXPORT sfi_status sfi_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
+                                const int32_t* n_idx, void* ck, void* cv, int32_t* cpos,
+                                hipStream_t stream) {
+    ReorgArgs a;
+    const sfi_status st = prep_reorg(kv, idx, idx_stride, n_idx, ck, cv, cpos, &a);
+    if (st != SFI_OK) return st;
+    return launch_reorg_for(kv, a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
 }
 
 SFI_EXPORT sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
@@ -475,11 +490,14 @@ SFI_EXPORT sfi_status sfi_slow_step_layers(
         void* const* sel_ws, size_t sel_ws_bytes, void* dense_ws, size_t dense_ws_bytes,
         int32_t n_sink, int32_t n_recent, int32_t k_sel, int32_t* const* idx, int32_t idx_stride,
         int32_t* const* n_idx, float mask_frac, uint8_t* const* head_mask,
+        void* const* seg_k, void* const* seg_v, int32_t* const* seg_pos,
         hipStream_t stream, hipStream_t side_stream, hipEvent_t* slot_events,
         hipEvent_t attn_event, hipEvent_t done_event) {
     if (n_layers < 1 || n_slots < 1 || !kv || !q || !out || !lse || !logits || !sel_ws || !idx ||
         !n_idx || !slot_events || !attn_event || !done_event || stream == side_stream)
         return SFI_E_INVALID;
+    const bool reorg = seg_k != nullptr;
+    if (reorg != (seg_v != nullptr) || reorg != (seg_pos != nullptr)) return SFI_E_INVALID;
     for (int s = 0; s < n_slots; ++s)
         if (!slot_events[s]) return SFI_E_INVALID;
     // Every layer's arguments pass validation before anything is queued.
@@ -497,6 +515,10 @@ SFI_EXPORT sfi_status sfi_slow_step_layers(
                              idx_stride, n_idx[l], sel_ws[s], sel_ws_bytes, &sa);
         if (st == SFI_OK && head_mask)
             st = prep_mask(&kv[l], logits[s], logit_stride, lse[l], mask_frac, head_mask[l], &ma);
+        ReorgArgs ra;
+        if (st == SFI_OK && reorg)
+            st = prep_reorg(&kv[l], idx[l], idx_stride, n_idx[l], seg_k[l], seg_v[l], seg_pos[l],
+                            &ra);
         if (st != SFI_OK) return st;
     }
     for (int l = 0; l < n_layers; ++l) {
@@ -518,6 +540,13 @@ SFI_EXPORT sfi_status sfi_slow_step_layers(
             if (launch_sink_mask(ma, side_stream) != hipSuccess) return SFI_E_HIP;
         }
         if (hipEventRecord(slot_events[s], side_stream) != hipSuccess) return SFI_E_HIP;
+        // Reorg reads the layer's own cache and indices, not the slot, so it runs after the
+        // slot is released
+        if (reorg) {
+            ReorgArgs ra;
+            prep_reorg(&kv[l], idx[l], idx_stride, n_idx[l], seg_k[l], seg_v[l], seg_pos[l], &ra);
+            if (launch_reorg_for(&kv[l], ra, side_stream) != hipSuccess) return SFI_E_HIP;
+        }
     }
     // one completion barrier: later work on `stream` sees every layer's indices and masks
     if (hipEventRecord(done_event, side_stream) != hipSuccess) return SFI_E_HIP;

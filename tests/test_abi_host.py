@@ -165,12 +165,12 @@ def test_slow_step_layers_validation(L):
     sws = L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_SELECT, 0, 0)
 
     def call(n_layers=n, descs=descs, n_slots=2, stride=4000, dws_b=dws, sws_b=sws, side=FAKE + 16,
-             lse=None, ks=2048, events=None, head_mask=None, frac=0.25):
+             lse=None, ks=2048, events=None, head_mask=None, frac=0.25, seg=(None, None, None)):
         return L.sfi_slow_step_layers(
             n_layers, descs, ptrs(n), ptrs(n), lse if lse is not None else ptrs(n), n_slots,
             ptrs(2), stride, ptrs(2), sws_b, FAKE, dws_b, 4, 256, ks, ptrs(n), 2052, ptrs(n),
-            ctypes.c_float(frac), head_mask, FAKE, side, events if events is not None else ptrs(2),
-            FAKE, FAKE)
+            ctypes.c_float(frac), head_mask, *seg, FAKE, side,
+            events if events is not None else ptrs(2), FAKE, FAKE)
 
     assert call(n_layers=0) == B.SFI_E_INVALID
     assert call(n_slots=0) == B.SFI_E_INVALID
@@ -184,6 +184,9 @@ def test_slow_step_layers_validation(L):
     assert call(head_mask=ptrs(n), frac=1.5) == B.SFI_E_INVALID
     bad = (B.sfi_kv_desc * n)(_desc(), _desc(), _desc(head_dim=96))
     assert call(descs=bad) == B.SFI_E_UNSUPPORTED             # the last layer is checked too
+    assert call(seg=(ptrs(n), None, ptrs(n))) == B.SFI_E_INVALID       # all three or none
+    assert call(seg=(ptrs(n), ptrs(n), (ctypes.c_void_p * n)(FAKE, FAKE, None))) == B.SFI_E_INVALID
+    assert call(seg=(ptrs(n), ptrs(n, FAKE + 8), ptrs(n))) == B.SFI_E_INVALID   # alignment
 
 
 def test_stream_read_validation(L):

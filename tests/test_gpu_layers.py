@@ -1,9 +1,9 @@
 """The layer-wise slow step (sfi_slow_step_layers) against the per-layer calls in sequence.
 
-Five layers share two ring slots, so every slot is reused; the Selector and the mask run on a
-second stream.  Every output must equal the sequential result bit for bit (the kernels are
-deterministic), and a fast step queued on the primary stream right after the call must see
-the last layer's indices (the completion barrier).
+Five layers share two ring slots, so every slot is reused; the Selector, the mask and (when
+asked) the Reorg run on a second stream.  Every output must equal the sequential result bit for
+bit (the kernels are deterministic), and a fast step queued on the primary stream right after
+the call must see the last layer's indices and compact segment (the completion barrier).
 """
 import pytest
 import torch
@@ -16,13 +16,13 @@ from gpu_util import DEV, desc_for, round4, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,n_slots", [("gqa8_512k", 2), ("ragged_paged_b16", 2),
-                                          ("gqa4_32k", 1)])
-def test_layered_slow_step_matches_sequential(name, n_slots):
+@pytest.mark.parametrize("name,n_slots,reorg", [("gqa8_512k", 2, False), ("ragged_paged_b16", 2, True),
+                                                ("gqa4_32k", 1, True)])
+def test_layered_slow_step_matches_sequential(name, n_slots, reorg):
     base = synth.WORKLOADS[name]
     wl = base.scaled(7001, B=min(base.B, 3), len_lo=3000 if base.len_lo else None)
     n_layers = 5
-    say(f"[layers] {wl.name} layers={n_layers} slots={n_slots}")
+    say(f"[layers] {wl.name} layers={n_layers} slots={n_slots} reorg={reorg}")
     lays = [synth.make_layer(wl, li, device=DEV) for li in range(n_layers)]
     lens = lays[0].len_at(0).to(DEV)
     max_len = lays[0].max_len_at(0)
@@ -41,6 +41,12 @@ def test_layered_slow_step_matches_sequential(name, n_slots):
             n_idx=[torch.full((wl.B, wl.Hkv), -3, dtype=torch.int32, device=DEV) for _ in lays],
             mask=[torch.full((wl.B, wl.Hq), 7, dtype=torch.uint8, device=DEV) for _ in lays],
             logits=[torch.empty((wl.B, wl.Hq, stride), device=DEV) for _ in range(n_slots)],
+            seg=[(torch.full((wl.B, wl.Hkv, istride, wl.d), float("nan"), dtype=wl.torch_dtype,
+                             device=DEV),
+                  torch.full((wl.B, wl.Hkv, istride, wl.d), float("nan"), dtype=wl.torch_dtype,
+                             device=DEV),
+                  torch.full((wl.B, wl.Hkv, istride), -9, dtype=torch.int32, device=DEV))
+                 for _ in lays],
             sel_ws=[B.workspace(descs[0], idx_stride=istride, n_recent=wl.n_recent, device=DEV)
                     for _ in range(n_slots)])
 
@@ -54,6 +60,8 @@ def test_layered_slow_step_matches_sequential(name, n_slots):
                      ref["idx"][l], istride, ref["n_idx"][l], ref["sel_ws"][s])
         B.sfi_sink_bypass_mask(descs[l], ref["logits"][s], stride, ref["lse"][l], frac,
                                ref["mask"][l])
+        if reorg:
+            B.sfi_reorg(descs[l], ref["idx"][l], istride, ref["n_idx"][l], *ref["seg"][l])
     torch.cuda.synchronize()
 
     got = bufs()
@@ -63,7 +71,8 @@ def test_layered_slow_step_matches_sequential(name, n_slots):
     B.sfi_slow_step_layers(descs, qs, got["out"], got["lse"], got["logits"], stride,
                            got["sel_ws"], dense_ws, wl.n_sink, wl.n_recent, wl.k_sel, got["idx"],
                            istride, got["n_idx"], frac, got["mask"], stream, side, events,
-                           torch.cuda.Event(), torch.cuda.Event())
+                           torch.cuda.Event(), torch.cuda.Event(),
+                           segments=got["seg"] if reorg else None)
     # queued on the primary stream right after: must see the last layer's indices and mask
     lens1 = lays[0].len_at(1).to(DEV)
     d1 = desc_for(lays[-1], lens1, lays[0].max_len_at(1))
@@ -71,6 +80,10 @@ def test_layered_slow_step_matches_sequential(name, n_slots):
     fast_got = torch.empty((wl.B, wl.Hq, wl.d), device=DEV)
     B.sfi_sparse_decode(d1, q1, got["idx"][-1], istride, got["n_idx"][-1], wl.n_recent,
                         got["mask"][-1], fast_got, None, dense_ws)
+    seg_got = torch.empty_like(fast_got)
+    if reorg:
+        B.sfi_sparse_decode_compact(d1, q1, *got["seg"][-1], istride, got["n_idx"][-1],
+                                    wl.n_recent, got["mask"][-1], seg_got, None, dense_ws)
     torch.cuda.synchronize()
     fast_ref = torch.empty_like(fast_got)
     B.sfi_sparse_decode(d1, q1, ref["idx"][-1], istride, ref["n_idx"][-1], wl.n_recent,
@@ -81,4 +94,10 @@ def test_layered_slow_step_matches_sequential(name, n_slots):
         for l in range(n_layers):
             assert torch.equal(got[key][l], ref[key][l]), f"{key} differs at layer {l}"
     assert torch.equal(fast_got, fast_ref)
+    if reorg:
+        for l in range(n_layers):
+            for a, b_ in zip(got["seg"][l], ref["seg"][l]):
+                assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
+                                   b_.view(torch.int16) if b_.dtype == torch.bfloat16 else b_)
+        assert torch.equal(seg_got, fast_ref)     # the compact segment of the last layer
     say(f"    {n_layers} layers identical to the sequential calls; fast step after the call too")
