@@ -4,7 +4,9 @@
 // attention_kernel: one workgroup (4 wavefronts) owns one (batch b, KV head h, split s): a
 // contiguous range of "slots".  A slot is a key position: in the dense step slot ==
 // position; in the sparse step slot k < n_idx is idx[k] and the remaining slots walk the
-// recent window [r0, len).  Each wavefront takes 32-slot tiles (round-robin, or a contiguous
+// recent window [r0, len).  In the two-segment fast step (SFI Sec. 4.2) index slot k reads
+// its rows from row (b*Hkv + h)*idx_stride + k of the compact segment written by the Reorg;
+// the recent window is still read in place.  Each wavefront takes 32-slot tiles (round-robin, or a contiguous
 // quarter of the split when the dense step stages its logits) and keeps an online softmax
 // (m, l, acc) for the G query heads of the group:
 //   - S^T = K_tile * Q^T on MFMA (v_mfma_f32_16x16x32_bf16, or 16x16x4 f32): the 16 rows of

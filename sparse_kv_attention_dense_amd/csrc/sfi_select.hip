@@ -314,6 +314,7 @@ __global__ void __launch_bounds__(kThreads) refine_nms_kernel(SelArgs a) {
 #endif
 constexpr int kCrossParts = SFI_CROSS_PARTS;
 constexpr int kCrossPer = kPerThread / kCrossParts;    // positions per thread
+static_assert(kPerThread % kCrossParts == 0, "a chunk part holds whole rows of threads");
 constexpr int kCrossRegHeads = 16;                      // heads whose scores stay in registers
 __global__ void __launch_bounds__(kThreads) refine_cross_kernel(SelArgs a) {
     __shared__ uint32_t lh[kCBins0];
