@@ -552,11 +552,16 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         }
         return (const Elem*)base + (uint64_t)slot_row(slot) * D;
     };
+    // tile < 0: past the wavefront's last tile.  Every lane then reads the split's first row,
+    // so the number of loads is the same on every path (the wait before the math covers only
+    // the current tile) while the extra loads touch a few cache lines instead of a whole tile.
     auto issue = [&](Regs& r, int tile) {
-        const int sb = s0 + tile * kTile;
+        const bool idle = tile < 0;
+        const int sb = s0 + (idle ? 0 : tile * kTile);
+        auto pick = [&](int slot) { return idle ? s0 : min(slot, s1 - 1); };
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            const Elem* kp = row_ptr(min(sb + 16 * st + n16, s1 - 1), a.k, a.ck);
+            const Elem* kp = row_ptr(pick(sb + 16 * st + n16), a.k, a.ck);
 #pragma unroll
             for (int c = 0; c < C::kNQ; ++c) {
                 if constexpr (BF) r.k[st][c] = load_k(kp + 32 * c + 8 * q4);
@@ -567,14 +572,14 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 #pragma unroll
             for (int j = 0; j < C::kNV; ++j) {
                 const int rr = j * C::kRPI + lane / C::kLPR;
-                r.v[j] = load_v(row_ptr(min(sb + rr, s1 - 1), a.v, a.cv) + (lane % C::kLPR) * 8);
+                r.v[j] = load_v(row_ptr(pick(sb + rr), a.v, a.cv) + (lane % C::kLPR) * 8);
             }
         } else {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float* vp = row_ptr(min(sb + 16 * st + 4 * q4 + i, s1 - 1), a.v, a.cv);
+                    const float* vp = row_ptr(pick(sb + 16 * st + 4 * q4 + i), a.v, a.cv);
 #pragma unroll
                     for (int mb = 0; mb < D / 16; ++mb) r.v[(st * 4 + i) * (D / 16) + mb] = vp[16 * mb + n16];
                 }
@@ -732,22 +737,21 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     };
 
     // ---- main loop over [t_begin, t_end) in steps of t_step; loads run one tile ahead --------
-    // The next tile's loads are issued unconditionally (past the end the wavefront re-reads
-    // its current tile, which hits in cache), so the number of loads younger than the
-    // current tile's is the same on every path and the wait before the math only covers
-    // the current tile.
+    // The next tile's loads are issued unconditionally (past the end as idle loads of one
+    // row, see issue), so the number of loads younger than the current tile's is the same on
+    // every path and the wait before the math only covers the current tile.
     if (t_begin < t_end) {
         Regs ra, rb;
         int t = t_begin;
         issue(ra, t);
         for (;;) {
             int tn = t + t_step;
-            issue(rb, tn < t_end ? tn : t);
+            issue(rb, tn < t_end ? tn : -1);
             compute(ra, t);
             if (tn >= t_end) break;
             t = tn;
             tn = t + t_step;
-            issue(ra, tn < t_end ? tn : t);
+            issue(ra, tn < t_end ? tn : -1);
             compute(rb, t);
             if (tn >= t_end) break;
             t = tn;
