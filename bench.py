@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
-"""Benchmark of one Slow-Fast decode-attention layer on one MI355X.
+"""Benchmark of Slow-Fast decode attention on one MI355X.
 
-A step is one slow-fast cycle of the workload: the dense slow step with fp32 logit write
-(sfi_dense_decode), the Selector (sfi_select), the sink-bypass mask when the workload has
-one (sfi_sink_bypass_mask), then cycle-1 fast steps (sfi_sparse_decode) whose recent
-window moves by one token per step.  Steps rotate over --layers distinct layer buffers
-(own K/V, logits, indices) so repeated reads are not served from the 256 MB Infinity Cache.
-Inputs are resident in HBM before the timed region.
+A step is one slow-fast cycle of a stack of --layers layers of the workload, each with its own
+K/V, logits and indices, run in decode order: token 0 runs the slow step of every layer in turn
+(the dense step with fp32 logit write, sfi_dense_decode; the Selector, sfi_select; the
+sink-bypass mask when the workload has one, sfi_sink_bypass_mask), then each of the cycle-1
+later tokens runs the fast step (sfi_sparse_decode) of every layer in turn, with the recent
+window one token further on.  Between two calls on one layer the other layers' calls run, so
+repeated reads are not served from the 256 MB Infinity Cache.  Inputs are resident in HBM
+before the timed region.
 
-Prints one JSON line.  value = microseconds per decode step, amortised over the cycle
-(slow + (cycle-1) fast) / cycle, from the host clock around whole cycles run back to back.
-roofline = the dense slow step's algorithmic HBM bytes per launch / its mean time, measured
-with HIP events on the launch stream inside the timed region (the only events there).
-The per-call breakdown (select, mask, fast) comes from separate instrumented cycles;
+Prints one JSON line.  value = microseconds per decode step of one layer, amortised over the
+cycle: stack-cycle time / (cycle * layers), from the host clock around whole stack cycles run
+back to back.  roofline = the dense slow step's algorithmic HBM bytes per launch / its mean
+time, measured with HIP events on the launch stream inside the timed region (the only events
+there).  The per-call breakdown (select, mask, fast) comes from separate instrumented cycles;
 spread_us gives p10/p50/p90 over single calls each bracketed by its own events (an event pair
 adds about 1.5 us to a call, so these sit above the block means), and dense_nolog_us the dense
 step without its logit write.
@@ -41,8 +43,8 @@ ATTN_SRC = os.path.join(ROOT, "sparse_kv_attention_dense_amd", "csrc", "sfi_atte
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="sink_128k_b4")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -202,35 +204,37 @@ def read_yardstick(B, torch, gib: int = 4, grids=(1024, 2048, 4096), reps: int =
 
 def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
                       idx_stride, L, gamma: float = 0.65):
-    """Fast steps with inline group routing (sfi_sparse_decode_routed), the slow step's lse as
-    the cached normaliser: per layer one slow step, then the cycle's fast steps timed as one
-    block.  Reports µs per fast step and the fraction of (sequence, KV head) groups bypassed."""
+    """Fast steps with inline group routing (sfi_sparse_decode_routed), each layer's slow-step
+    lse as its cached normaliser: the slow step of every layer, then the cycle's fast steps in
+    decode order (token by token, every layer in turn) timed as one block, twice.  Reports µs
+    per fast step and the fraction of (sequence, KV head) groups bypassed."""
     dev = "cuda"
     stream = torch.cuda.current_stream()
     out = torch.empty((wl.B, wl.Hq, wl.d), device=dev)
     lse_f = torch.empty((wl.B, wl.Hq), device=dev)
-    slow_lse = torch.empty((wl.B, wl.Hq), device=dev)
-    routed = torch.zeros((wl.B, wl.Hkv), dtype=torch.uint8, device=dev)
-    frac_sum, times = 0.0, []
+    slow_lse = [torch.empty((wl.B, wl.Hq), device=dev) for _ in range(L)]
+    routed = [torch.zeros((wl.B, wl.Hkv), dtype=torch.uint8, device=dev) for _ in range(L)]
     print("# routed fast steps", file=sys.stderr, flush=True)
-    for li in list(range(L)) * 2:
+    for li in range(L):
         d = descs[li]
-        B.sfi_dense_decode(d[0], queries[li][0], out, slow_lse, logits[li], stride, ws)
+        B.sfi_dense_decode(d[0], queries[li][0], out, slow_lse[li], logits[li], stride, ws)
         B.sfi_select(d[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
                      idx_stride, nidxs[li], ws)
+    times, frac = [], []
+    for rep in range(2):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for t in range(1, wl.cycle):
-            B.sfi_sparse_decode_routed(d[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
-                                       wl.n_recent, masks[li], slow_lse, gamma, routed, out,
-                                       lse_f, ws)
+            for li in range(L):
+                B.sfi_sparse_decode_routed(descs[li][t], queries[li][t], idxs[li], idx_stride,
+                                           nidxs[li], wl.n_recent, masks[li], slow_lse[li],
+                                           gamma, routed[li], out, lse_f, ws)
         e1.record(stream)
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e3 / (wl.cycle - 1))
-        frac_sum += float(routed.float().mean())
-    n = 2 * L
-    return {"gamma": gamma, "fast_us": round(sum(times) / n, 2),
-            "groups_routed_frac": round(frac_sum / n, 4),
+        times.append(e0.elapsed_time(e1) * 1e3 / (L * (wl.cycle - 1)))
+        frac += [float(r.float().mean()) for r in routed]
+    return {"gamma": gamma, "fast_us": round(sum(times) / len(times), 2),
+            "groups_routed_frac": round(sum(frac) / len(frac), 4),
             "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
 
 
@@ -302,7 +306,8 @@ def synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, 
                                    idx_stride, L):
     """Fast steps on the workload's synthetic selections instead of the Selector's: sentence-
     like spans of 10-40 positions, and uniformly scattered positions (the two variants the
-    ragged workload is stated with), each timed over whole cycles of every rotated layer."""
+    ragged workload is stated with), each timed over the fast steps of a whole cycle of every
+    rotated layer in decode order."""
     dev = "cuda"
     res = {}
     for kind in ("spans", "scattered"):
@@ -312,8 +317,8 @@ def synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, 
             sets.append((i.to(dev), n.to(dev)))
 
         def run():
-            for li in range(L):
-                for t in range(1, wl.cycle):
+            for t in range(1, wl.cycle):
+                for li in range(L):
                     B.sfi_sparse_decode(descs[li][t], queries[li][t], sets[li][0], idx_stride,
                                         sets[li][1], wl.n_recent, None, out, lse, ws)
         run()
@@ -384,8 +389,9 @@ def refined_selector(B, torch, wl, layers, descs, logits, stride, idx_stride, L,
 def two_segment_steps(B, torch, wl, descs, queries, idxs, nidxs, masks, out, lse, ws,
                       idx_stride, L):
     """The two-segment layout: sfi_reorg of every rotated layer's selection (once per cycle),
-    then the cycle's fast steps on the compact segment (sfi_sparse_decode_compact), timed as
-    blocks over all layers beside the same fast steps gathered from the cache."""
+    then the cycle's fast steps on the compact segment (sfi_sparse_decode_compact) in decode
+    order (token by token, every layer in turn), timed as blocks beside the same fast steps
+    gathered from the cache."""
     dev = "cuda"
     segs = []
     for li in range(L):
@@ -398,14 +404,14 @@ def two_segment_steps(B, torch, wl, descs, queries, idxs, nidxs, masks, out, lse
             B.sfi_reorg(descs[li][0], idxs[li], idx_stride, nidxs[li], *segs[li])
 
     def compact():
-        for li in range(L):
-            for t in range(1, wl.cycle):
+        for t in range(1, wl.cycle):
+            for li in range(L):
                 B.sfi_sparse_decode_compact(descs[li][t], queries[li][t], *segs[li], idx_stride,
                                             nidxs[li], wl.n_recent, masks[li], out, lse, ws)
 
     def gather():
-        for li in range(L):
-            for t in range(1, wl.cycle):
+        for t in range(1, wl.cycle):
+            for li in range(L):
                 B.sfi_sparse_decode(descs[li][t], queries[li][t], idxs[li], idx_stride,
                                     nidxs[li], wl.n_recent, masks[li], out, lse, ws)
 
@@ -534,85 +540,106 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
-    def cycle(li, rec):
-        """One slow-fast cycle of layer li.  rec = "none": no events; "dense": events around
-        the dense call only (the timed region); "all": events around every call."""
-        d0 = descs[li]
-        e = [ev() for _ in range(5)] if rec != "none" else None
-        if e:
-            e[0].record(stream)
-        B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
-        if e:
-            e[1].record(stream)
-        B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
-                     idx_stride, nidxs[li], ws)
-        if rec == "all":
-            e[2].record(stream)
-        if masks[li] is not None:
-            B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
-        if rec == "all":
-            e[3].record(stream)
+    def cycle(rec):
+        """One slow-fast cycle of the L-layer stack in decode order: token 0 runs the slow step
+        of every layer in turn (dense with logits, Selector, mask), then each later token runs
+        the fast step of every layer in turn.  Between two fast steps of one layer the other
+        layers' steps run, as when a decode step passes through a model's layers, so a layer's
+        selected rows are not still in the 256 MB Infinity Cache from its previous step.
+        rec = "none": no events; "dense": events around each dense call only (the timed
+        region); "all": events around each slow-step call and around the block of fast steps."""
+        marks = []
+        for li in range(L):
+            d0 = descs[li]
+            e = [ev() for _ in range(4)] if rec != "none" else None
+            if e:
+                e[0].record(stream)
+            B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
+            if e:
+                e[1].record(stream)
+            B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
+                         idx_stride, nidxs[li], ws)
+            if rec == "all":
+                e[2].record(stream)
+            if masks[li] is not None:
+                B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
+            if rec == "all":
+                e[3].record(stream)
+            marks.append(e)
+        fe = [ev(), ev()] if rec == "all" else None
+        if fe:
+            fe[0].record(stream)
         for t in range(1, wl.cycle):
-            B.sfi_sparse_decode(d0[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
-                                wl.n_recent, masks[li], out, lse, ws)
-        if rec == "all":
-            e[4].record(stream)
-        return e
+            for li in range(L):
+                B.sfi_sparse_decode(descs[li][t], queries[li][t], idxs[li], idx_stride,
+                                    nidxs[li], wl.n_recent, masks[li], out, lse, ws)
+        if fe:
+            fe[1].record(stream)
+        return marks, fe
 
     print("# warmup", file=sys.stderr, flush=True)
     for s in range(args.warmup):
-        cycle(s % L, "none")
+        cycle("none")
     torch.cuda.synchronize()
-    # Timed region: whole cycles back to back; the only events are the two around each dense
-    # call (the roofline kernel), so the wall clock is not inflated by event records.
+    # Timed region: whole stack cycles back to back; the only events are the two around each
+    # dense call (the roofline kernel), so the wall clock is not inflated by event records.
     print("# timed region", file=sys.stderr, flush=True)
     evs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        evs.append(cycle(s % L, "dense"))
+        evs.append(cycle("dense"))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     mean = lambda x: sum(x) / len(x)
-    dense_us = 1e3 * mean([e[0].elapsed_time(e[1]) for e in evs])
-    # Breakdown: separate cycles with events around the Selector, the mask and the block of
-    # fast steps (each event pair adds a few µs of its own, so the breakdown is not used for
+    dense_us = 1e3 * mean([e[0].elapsed_time(e[1]) for marks, _ in evs for e in marks])
+    # Breakdown: separate stack cycles with events around the Selector, the mask and the block
+    # of fast steps (each event pair adds a few µs of its own, so the breakdown is not used for
     # value; the fast steps are timed as one block and divided by their number).
     print("# breakdown", file=sys.stderr, flush=True)
-    evs = [cycle(s % L, "all") for s in range(max(1, min(args.steps, 2 * L)))]
+    evs = [cycle("all") for s in range(max(1, min(args.steps, 2)))]
     torch.cuda.synchronize()
-    select_us = 1e3 * mean([e[1].elapsed_time(e[2]) for e in evs])
-    mask_us = 1e3 * mean([e[2].elapsed_time(e[3]) for e in evs]) if wl.mask_frac > 0 else 0.0
-    fast_us = 1e3 * mean([e[3].elapsed_time(e[4]) / (wl.cycle - 1) for e in evs])
+    select_us = 1e3 * mean([e[1].elapsed_time(e[2]) for marks, _ in evs for e in marks])
+    mask_us = (1e3 * mean([e[2].elapsed_time(e[3]) for marks, _ in evs for e in marks])
+               if wl.mask_frac > 0 else 0.0)
+    fast_us = 1e3 * mean([fe[0].elapsed_time(fe[1]) / (L * (wl.cycle - 1)) for _, fe in evs])
 
-    # Spread: one more pass with events around every single call (p10 / p50 / p90), and the
-    # dense step without its logit write as a reference for the cost of the logits.
+    # Spread: one more stack cycle in decode order with events around every single call
+    # (p10 / p50 / p90), and the dense step without its logit write as a reference for the
+    # cost of the logits.
     dense_calls, nolog_calls, fast_calls = [], [], []
     if not args.no_spread:
         print("# per-call spread", file=sys.stderr, flush=True)
-    for li in range(0 if args.no_spread else L):
-        d0 = descs[li]
-        e = [ev() for _ in range(2 * wl.cycle + 2)]
-        e[0].record(stream)
-        B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
-        e[1].record(stream)
-        B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
-                     idx_stride, nidxs[li], ws)
-        if masks[li] is not None:
-            B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
+        pairs = {"dense": [], "nolog": [], "fast": []}
+
+        def timed_call(kind, fn):
+            e = (ev(), ev())
+            e[0].record(stream)
+            fn()
+            e[1].record(stream)
+            pairs[kind].append(e)
+
+        for li in range(L):
+            d0 = descs[li]
+            timed_call("dense", lambda: B.sfi_dense_decode(d0[0], queries[li][0], out, lse,
+                                                           logits[li], stride, ws))
+            B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
+                         idx_stride, nidxs[li], ws)
+            if masks[li] is not None:
+                B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
         for t in range(1, wl.cycle):
-            e[2 * t].record(stream)
-            B.sfi_sparse_decode(d0[t], queries[li][t], idxs[li], idx_stride, nidxs[li],
-                                wl.n_recent, masks[li], out, lse, ws)
-            e[2 * t + 1].record(stream)
-        e[2 * wl.cycle].record(stream)
-        B.sfi_dense_decode(d0[0], queries[li][0], out, lse, None, stride, ws)
-        e[2 * wl.cycle + 1].record(stream)
+            for li in range(L):
+                timed_call("fast", lambda: B.sfi_sparse_decode(
+                    descs[li][t], queries[li][t], idxs[li], idx_stride, nidxs[li], wl.n_recent,
+                    masks[li], out, lse, ws))
+        for li in range(L):
+            timed_call("nolog", lambda: B.sfi_dense_decode(descs[li][0], queries[li][0], out,
+                                                           lse, None, stride, ws))
         torch.cuda.synchronize()
-        dense_calls.append(1e3 * e[0].elapsed_time(e[1]))
-        nolog_calls.append(1e3 * e[2 * wl.cycle].elapsed_time(e[2 * wl.cycle + 1]))
-        fast_calls += [1e3 * e[2 * t].elapsed_time(e[2 * t + 1]) for t in range(1, wl.cycle)]
+        dense_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["dense"]]
+        nolog_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["nolog"]]
+        fast_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["fast"]]
 
     def pct(xs):
         if not xs:
@@ -661,7 +688,7 @@ def main():
     dense_gbps = d_bytes / (dense_us * 1e-6) / 1e9
     fast_gbps = f_bytes / (fast_us * 1e-6) / 1e9
     select_gbps = s_bytes / (select_us * 1e-6) / 1e9
-    value = ms_per_step * 1e3 / wl.cycle
+    value = ms_per_step * 1e3 / (wl.cycle * L)
     traffic = counter_traffic(wl.name)
 
     result = {
@@ -681,8 +708,8 @@ def main():
                    "head_dim": wl.d, "context": wl.n0, "n_sink": wl.n_sink,
                    "n_recent": wl.n_recent, "k_sel": wl.k_sel, "cycle": wl.cycle,
                    "mask_frac": wl.mask_frac, "layers_rotated": L,
-                   "step": f"1 slow (dense+select{'+mask' if wl.mask_frac else ''}) + "
-                           f"{wl.cycle - 1} fast"},
+                   "step": f"{L} layers x (1 slow (dense+select{'+mask' if wl.mask_frac else ''}) + "
+                           f"{wl.cycle - 1} fast), token-major"},
         "slow_us": round(dense_us + select_us + mask_us, 2),
         "fast_us": round(fast_us, 2),
         "dense_us": round(dense_us, 2),

@@ -254,23 +254,32 @@ __device__ bool route_decide(const AttnArgs& a, int b, int hq0, const RoutePre<B
     return all;
 }
 
+// Wavefronts per workgroup: 4 in the dense step (two workgroups per CU); kSparseWaves in the
+// fast step, whose launch has about one workgroup per CU, except fp32 at d = 128, whose tile
+// registers allow one wavefront per SIMD only.
+constexpr int waves_of(bool bf, int d, bool sparse) {
+    return (sparse && (bf || d == 64)) ? kSparseWaves : kWaves;
+}
+
 template <bool BF, int D, bool PAGED, bool SPARSE>
 struct Cfg {
+    static constexpr int kNW = waves_of(BF, D, SPARSE);
+    static constexpr int kNT = 64 * kNW;
     static constexpr int kVRow = D * 2 + 16;                       // staged bf16 row, bytes
     // The dense step stages V half a tile at a time (16 slots, k = 16 MFMAs) so that its LDS
     // holds longer logit runs; the fast step stages whole tiles (k = 32 MFMAs), which measured
     // faster there (20.2 vs 21.0 us at 128K).
     static constexpr bool kHalfV = BF && !SPARSE;
     static constexpr int kVRows = kHalfV ? kTile / 2 : kTile;      // V rows staged at a time
-    static constexpr int kVStage = BF ? kWaves * kVRows * kVRow : 0;
-    static constexpr int kRed = kWaves * kMaxG * (D + 2) * 4;      // cross-wave merge
+    static constexpr int kVStage = BF ? kNW * kVRows * kVRow : 0;
+    static constexpr int kRed = kNW * kMaxG * (D + 2) * 4;         // cross-wave merge
     // dense: per-wavefront staging of fp32 logits, kZRows (head, tile) rows of 32 positions;
     // 120 rows (15 KB) for bf16 d = 128 keeps two workgroups per CU in 160 KB of LDS
     static constexpr int kZRows = (BF && D == 128) ? 120 : 64;
     static constexpr int kZWave = SPARSE ? 4 : kZRows * kTile;     // floats per wavefront
     // the cross-wave merge reuses the logit staging area when that is large enough (it runs
     // after the last run has been written), else the V staging area
-    static constexpr bool kRedInZ = !SPARSE && kWaves * kZWave * 4 >= kRed;
+    static constexpr bool kRedInZ = !SPARSE && kNW * kZWave * 4 >= kRed;
     static constexpr int kRaw0 = kRedInZ ? kVStage : (kVStage > kRed ? kVStage : kRed);
     static constexpr int kRaw = kRaw0 > 64 ? kRaw0 : 64;
     static constexpr int kNQ = BF ? D / 32 : D / 16;               // Q / K fragments per row
@@ -289,11 +298,14 @@ struct TileRegs {
 };
 
 template <bool BF, int D, bool PAGED, bool SPARSE>
-__global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(64 * waves_of(BF, D, SPARSE),
+                                  (BF || D == 64) ? 8 / waves_of(BF, D, SPARSE) : 1)
+attention_kernel(AttnArgs a) {
     using C = Cfg<BF, D, PAGED, SPARSE>;
+    static_assert(SPARSE || C::kNW == kWaves, "the dense split lookup assumes four wavefronts");
     using Regs = TileRegs<BF, D, PAGED, SPARSE>;
     __shared__ __attribute__((aligned(16))) unsigned char raw[C::kRaw];
-    __shared__ __attribute__((aligned(16))) float zstage[kWaves * C::kZWave];
+    __shared__ __attribute__((aligned(16))) float zstage[C::kNW * C::kZWave];
     // Row table in dynamic LDS, sized by the host for this launch's split length:
     //   sparse: one row per slot, then one "attend" flag byte per slot;
     //   dense paged: one base row per KV block the split touches.
@@ -319,18 +331,18 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     const int hq0 = h * G;
     const int unit = b * a.Hkv + h;
     const int s0 = split * a.split_len;
-    // The index entries of the first kFill * kThreads slots depend only on the slot, so their
+    // The index entries of the first kFill * C::kNT slots depend only on the slot, so their
     // loads are issued before the lengths arrive and the latencies overlap.
     int idx_pre[kFill];
     // Table slots per thread in one batch: what the split needs, at most kFill (paged only).
-    const int nfill = min(kFill, (a.split_len + kThreads - 1) / kThreads);
+    const int nfill = min(kFill, (a.split_len + C::kNT - 1) / C::kNT);
     if constexpr (SPARSE && !PAGED) {
         idx_pre[0] = s0 + tid < a.idx_stride ? a.idx[(int64_t)unit * a.idx_stride + s0 + tid] : 0;
     } else if constexpr (SPARSE) {
         const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
 #pragma unroll
         for (int u = 0; u < kFill; ++u) {
-            const int slot = s0 + u * kThreads + tid;
+            const int slot = s0 + u * C::kNT + tid;
             idx_pre[u] = (u < nfill && slot < a.idx_stride) ? irow[slot] : 0;
         }
     }
@@ -374,7 +386,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     if constexpr (SPARSE) {
         const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
         if constexpr (!PAGED) {
-            for (int t = tid; t < nslots; t += kThreads) {
+            for (int t = tid; t < nslots; t += C::kNT) {
                 const int slot = s0 + t;
                 int pos;
                 bool ok = true;
@@ -393,12 +405,12 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         // issued before any is used, then every block-table load, so a batch costs two memory
         // round trips however many slots it holds (3% faster fast steps on a ragged batch;
         // on a contiguous cache the plain loop above measured faster).
-        for (int t0 = 0; PAGED && t0 < nslots; t0 += nfill * kThreads) {
+        for (int t0 = 0; PAGED && t0 < nslots; t0 += nfill * C::kNT) {
             int pos[kFill];
             bool ok[kFill];
 #pragma unroll
             for (int u = 0; u < kFill; ++u) {
-                const int t = t0 + u * kThreads + tid;
+                const int t = t0 + u * C::kNT + tid;
                 const int slot = s0 + t;
                 ok[u] = true;
                 pos[u] = 0;
@@ -416,7 +428,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 #pragma unroll
             for (int u = 0; u < kFill; ++u) {
                 if constexpr (PAGED) {
-                    const int t = t0 + u * kThreads + tid;
+                    const int t = t0 + u * C::kNT + tid;
                     const bool crow = compact && s0 + t < n_sel;     // compact row: no lookup
                     const int blk = (u < nfill && t < nslots && !crow)
                         ? a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)] : 0;
@@ -429,7 +441,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             }
 #pragma unroll
             for (int u = 0; u < kFill; ++u) {
-                const int t = t0 + u * kThreads + tid;
+                const int t = t0 + u * C::kNT + tid;
                 if (u < nfill && t < nslots) {
                     tab_ok[t] = ok[u];
                     tab[t] = row[u];
@@ -441,7 +453,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
         // blocks [s0 >> shift, (s1 - 1) >> shift] of sequence b
         const int blk0 = s0 >> a.block_shift;
         const int nblk = nslots > 0 ? ((s1 - 1) >> a.block_shift) - blk0 + 1 : 0;
-        for (int t = tid; t < nblk; t += kThreads) {
+        for (int t = tid; t < nblk; t += C::kNT) {
             const int blk = a.block_table[(int64_t)b * a.max_blocks + blk0 + t];
             tab[t] = ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift;
         }
@@ -499,10 +511,10 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     const bool quarters = !SPARSE && zF >= 8;
     const bool staged = quarters && a.logits;
     const int ntiles = (nslots + kTile - 1) / kTile;
-    const int tpw = (ntiles + kWaves - 1) / kWaves;
+    const int tpw = (ntiles + C::kNW - 1) / C::kNW;
     const int t_begin = quarters ? min(ntiles, w * tpw) : w;
     const int t_end = quarters ? min(ntiles, t_begin + tpw) : ntiles;
-    const int t_step = quarters ? 1 : kWaves;
+    const int t_step = quarters ? 1 : C::kNW;
     float* zst = staged ? zstage + w * C::kZWave : nullptr;
     float* logit_row = nullptr;                       // unstaged logits of head n16
     if constexpr (!SPARSE) {
@@ -762,7 +774,7 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
 
     // ---- merge the four wavefronts, write this split's partial -----------------------------
     __syncthreads();
-    float* red = C::kRedInZ ? zstage : (float*)raw;   // [kWaves][kMaxG][D+2]
+    float* red = C::kRedInZ ? zstage : (float*)raw;   // [kNW][kMaxG][D+2]
     if (n16 < G) {
         float* rp = red + (w * kMaxG + n16) * (D + 2);
 #pragma unroll
@@ -777,15 +789,15 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
     __syncthreads();
     {
         float* part = a.part + ((int64_t)unit * a.nsplit + split) * a.rec_floats;
-        for (int e = tid; e < G * D; e += kThreads) {
+        for (int e = tid; e < G * D; e += C::kNT) {
             const int g = e / D, dim = e - g * D;
             float M = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
+            for (int ww = 0; ww < C::kNW; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
             const float Mu = (M == -INFINITY) ? 0.f : M;
             float s = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww)
+            for (int ww = 0; ww < C::kNW; ++ww)
                 s += exp2_fast(red[(ww * kMaxG + g) * (D + 2) + D] - Mu) * red[(ww * kMaxG + g) * (D + 2) + dim];
             part[e] = s;
         }
@@ -793,11 +805,11 @@ __global__ void __launch_bounds__(kThreads, (BF || D == 64) ? 2 : 1) attention_k
             const int g = tid;
             float M = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
+            for (int ww = 0; ww < C::kNW; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
             const float Mu = (M == -INFINITY) ? 0.f : M;
             float L = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww)
+            for (int ww = 0; ww < C::kNW; ++ww)
                 L += exp2_fast(red[(ww * kMaxG + g) * (D + 2) + D] - Mu) * red[(ww * kMaxG + g) * (D + 2) + D + 1];
             part[G * D + 2 * g] = M;
             part[G * D + 2 * g + 1] = L;
@@ -815,7 +827,8 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
 template <bool BF, int D, bool PAGED, bool SPARSE>
 hipError_t launch_one(const AttnArgs& a, int B, hipStream_t stream) {
     const dim3 grid = SPARSE ? dim3(a.nsplit, a.Hkv, B) : dim3(a.nsplit * a.Hkv * B);
-    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), grid, dim3(kThreads),
+    hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), grid,
+                       dim3(Cfg<BF, D, PAGED, SPARSE>::kNT),
                        (size_t)a.tab_bytes, stream, a);
     hipLaunchKernelGGL((combine_kernel<D, SPARSE>), dim3(a.Hq, B), dim3(kThreads), 0, stream, a);
     return hipGetLastError();

@@ -12,6 +12,10 @@ namespace sfi {
 
 constexpr int kThreads = 256;        // 4 wavefronts of 64
 constexpr int kWaves = 4;
+#ifndef SFI_SPARSE_WAVES
+#define SFI_SPARSE_WAVES 4
+#endif
+constexpr int kSparseWaves = SFI_SPARSE_WAVES;   // wavefronts of a fast-step workgroup
 constexpr int kTile = 32;            // slots per wavefront iteration (two 16-row MFMA blocks)
 constexpr int kSplitQuantum = kTile * kWaves;
 constexpr int kTabMax = 4096;        // row-table entries per workgroup (dynamic LDS)
