@@ -58,6 +58,37 @@ def test_sparse_contiguous(orc, name):
         assert torch.isneginf(lse.cpu()[hm.bool()]).all()
 
 
+@pytest.mark.parametrize("dtype,d,G,block", [("bf16", 64, 1, 0), ("bf16", 128, 16, 64),
+                                             ("f32", 128, 2, 0), ("f32", 64, 8, 1),
+                                             ("bf16", 128, 3, 16), ("bf16", 64, 7, 0)])
+def test_sparse_head_shapes(orc, dtype, d, G, block):
+    """Group sizes 1 to 16, d 64 and 128, fp32 and bf16, contiguous and paged caches with
+    pages of 1, 16 and 64 positions; two steps of the moving recent window."""
+    wl = synth.Workload(f"sparse_shape_{dtype}_{d}_{G}_{block}", 7400 + d + G + block, 2, 2 * G,
+                        2, d, dtype, 1500, 4, 64, 128, 4, paged=block > 0,
+                        block_size=max(block, 1))
+    say(f"[sparse] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[1500, 777])
+    idx, n_idx = synth.synthetic_index_set(lay, "spans", seed=31)
+    for t in (1, 3):
+        q = synth.make_query(wl, 0, t, device=DEV)
+        _check(orc, lay, q, t, idx, n_idx)
+
+
+def test_sparse_largest_split(orc):
+    """An index set long enough that each fast-step workgroup holds the largest split its row
+    table allows (4096 slots): 1,049,068 slots for the one (sequence, KV head) unit, 257
+    workgroups."""
+    n = 1_050_000
+    wl = synth.Workload("sparse_largest_split", 7600, 1, 2, 1, 64, "bf16", n, 4, 64, 1_049_000, 2)
+    say(f"[sparse] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=32)
+    assert int(n_idx[0, 0]) + wl.n_recent > 256 * 4096
+    q = synth.make_query(wl, 0, 1, device=DEV)
+    _check(orc, lay, q, 1, idx, n_idx)
+
+
 def test_sparse_full_set_equals_dense(orc):
     """idx = every position before the recent window: the fast step is the dense step."""
     wl = W["gqa4_32k"].scaled(7001)
