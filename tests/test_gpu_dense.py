@@ -56,6 +56,24 @@ def test_dense_head_shapes(orc, dtype, d, G):
     assert_logits(logits, ez, lay.len0_host, tol["rel"])
 
 
+@pytest.mark.parametrize("dtype,d,G,block", [("bf16", 128, 4, 1), ("bf16", 64, 8, 64),
+                                             ("f32", 128, 2, 256), ("bf16", 128, 16, 1024)])
+def test_dense_paged_page_sizes(orc, dtype, d, G, block):
+    """Paged caches with pages of 1 to 1024 positions (block-table lookups per position, per
+    page and spanning whole splits)."""
+    wl = synth.Workload(f"dense_paged_{dtype}_{d}_{G}_{block}", 7200 + d + G + block, 2, 2 * G, 2,
+                        d, dtype, 2600, 4, 64, 128, 2, paged=True, block_size=block)
+    say(f"[dense] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[2600, 1333])
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    out, lse, logits, _ = gpu_dense(lay, q)
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lay.len0_host), q)
+    tol = tolerances(wl)
+    assert_close_out(out.cpu().numpy(), eo, tol["out"])
+    assert_close_rel(lse.cpu().numpy(), el, tol["rel"], "lse")
+    assert_logits(logits, ez, lay.len0_host, tol["rel"])
+
+
 def test_dense_edge_lengths(orc):
     """Lengths 0, 1, a tile minus one, a split plus one; logits past len stay untouched."""
     wl = synth.Workload("edges", 7300, 5, 8, 2, 128, "bf16", 4200, 4, 16, 32, 1)
