@@ -17,7 +17,8 @@ time, measured with HIP events on the launch stream inside the timed region (the
 there).  The per-call breakdown (select, mask, fast) comes from separate instrumented cycles;
 spread_us gives p10/p50/p90 over single calls each bracketed by its own events (an event pair
 adds about 1.5 us to a call, so these sit above the block means), and dense_nolog_us the dense
-step without its logit write.
+step without its logit write.  graph_cycle = the same stack cycle captured once in a HIP graph
+and replayed, next to the eager value.
 cpu_baseline = the fp64 CPU oracle timed on the host on whole cycles of one layer.
 read_yardstick = a plain sequential read of 4 GiB (sfi_stream_read) on the same box; the
 rooflines also give the dense and fast rates as a fraction of it, next to the 8 TB/s peak.
@@ -59,6 +60,8 @@ def parse():
                     help="skip the full Selector (prior and refinements) measurement")
     ap.add_argument("--no-two-segment", action="store_true",
                     help="skip the Reorg + two-segment fast-step measurement")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the stack cycle replayed from a captured HIP graph")
     ap.add_argument("--retention-sweep", action="store_true",
                     help="add dense-vs-sparse timings over retention ratios on a layer shaped "
                          "like the SFI page's retention table (KV 16K, batch 16, 32/8 heads)")
@@ -236,6 +239,30 @@ def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
     return {"gamma": gamma, "fast_us": round(sum(times) / len(times), 2),
             "groups_routed_frac": round(sum(frac) / len(frac), 4),
             "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
+
+
+def graph_replay(torch, run, per_replay: int, reps: int = 3):
+    """The stack cycle run() captured once in a HIP graph (torch.cuda.CUDAGraph: the library's
+    calls queue kernels only) and replayed back to back, timed on the host clock like the
+    eager timed region.  Returns µs per decode step of one layer (per_replay steps a replay)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()                                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) * 1e6 / (reps * per_replay)
+    del g
+    return round(us, 3)
 
 
 def retention_sweep(B, torch, synth, ratios=(0.016, 0.031, 0.0625, 0.125, 0.25, 0.5, 1.0),
@@ -648,6 +675,11 @@ def main():
         at = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
         return [round(at(0.1), 2), round(at(0.5), 2), round(at(0.9), 2)]
 
+    graph_us = None
+    if not args.no_graph:
+        print("# stack cycle replayed from a HIP graph", file=sys.stderr, flush=True)
+        graph_us = graph_replay(torch, lambda: cycle("none"), wl.cycle * L)
+
     print("# fast steps on synthetic selections", file=sys.stderr, flush=True)
     synth_fast = synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out,
                                                 lse, ws, idx_stride, L)
@@ -734,6 +766,10 @@ def main():
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
     result["read_yardstick"] = yard
+    if graph_us is not None:
+        result["graph_cycle"] = {"us_per_step": graph_us, "eager_us_per_step": round(value, 3),
+                                 "what": "the same stack cycle captured once in a HIP graph "
+                                         "and replayed (no host launch cost)"}
     if refined is not None:
         refined["value_if_used_us"] = round(
             (dense_us + refined["select_refined_us"] + mask_us + (wl.cycle - 1) * fast_us)
