@@ -107,6 +107,32 @@ def _check(status: int, where: str):
         raise SfiError(status, where)
 
 
+_F32, _I32, _U8 = torch.float32, torch.int32, torch.uint8
+_CACHE_DTYPES = {torch.float32: SFI_F32, torch.bfloat16: SFI_BF16}
+
+
+def _buf(t, name: str, dtype=None, numel: int = 0, optional: bool = False,
+         device: bool = True):
+    """Checks a tensor before its pointer crosses the C ABI.  The library sees only the
+    address, so a buffer of another dtype, a strided view or one smaller than the call's
+    sizes would be read or written past its end by a kernel; such calls raise here instead.
+    Checked in this order: type, dtype, contiguity, size, then that it lives in GPU memory."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name}: a tensor is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: holds {t.numel()} elements, the call needs {numel}")
+    if device and t.device.type != "cuda":
+        raise ValueError(f"{name}: must be in GPU memory, is on {t.device}")
+
+
 class KVDesc:
     """Builds an ``sfi_kv_desc`` from tensors and keeps them alive while it is in use.
 
@@ -118,13 +144,36 @@ class KVDesc:
     def __init__(self, k, v, lens, max_len: int, num_q_heads: int, block_table=None,
                  block_size: int = 0, batch: Optional[int] = None):
         self._keep = (k, v, lens, block_table)
+        n_batch = int(batch if batch is not None else lens.shape[0])
+        _buf(lens, "lens", _I32, n_batch, device=False)
         if k is not None:
-            dtype = {torch.float32: SFI_F32, torch.bfloat16: SFI_BF16}.get(k.dtype, 99)
+            if k.dtype not in _CACHE_DTYPES:
+                raise TypeError(f"k: dtype {k.dtype}, expected torch.float32 or torch.bfloat16")
+            if k.dim() != 4:
+                raise ValueError("k: expected [B][Hkv][n_cap][d] or [num_blocks][Hkv][block_size][d]")
+            _buf(k, "k", k.dtype, device=False)
+            _buf(v, "v", k.dtype, device=False)
+            if tuple(v.shape) != tuple(k.shape):
+                raise ValueError(f"v: shape {tuple(v.shape)} differs from k {tuple(k.shape)}")
+            if block_table is None and int(k.shape[0]) < n_batch:
+                raise ValueError(f"k: {int(k.shape[0])} sequences, the batch has {n_batch}")
+            if block_table is not None:
+                if block_table.dim() != 2:
+                    raise ValueError("block_table: expected [B][max_blocks]")
+                _buf(block_table, "block_table", _I32, n_batch * int(block_table.shape[1]),
+                     device=False)
+                if int(k.shape[2]) != int(block_size):
+                    raise ValueError(f"k: pages of {int(k.shape[2])} positions, block_size "
+                                     f"says {block_size}")
+            dtype = _CACHE_DTYPES[k.dtype]
             hkv, d = int(k.shape[1]), int(k.shape[-1])
         else:
             dtype, hkv, d = SFI_F32, 0, 0
+        for name, t in (("lens", lens), ("k", k), ("v", v), ("block_table", block_table)):
+            _buf(t, name, optional=True)                     # GPU residence, checked last
+        self.cache_dtype = k.dtype if k is not None else None
         self.c = sfi_kv_desc()
-        self.c.batch = int(batch if batch is not None else lens.shape[0])
+        self.c.batch = n_batch
         self.c.num_q_heads = int(num_q_heads)
         self.c.num_kv_heads = hkv
         self.c.head_dim = d
@@ -143,14 +192,18 @@ class KVDesc:
         """Descriptor for calls that read no cache (sfi_select, sfi_sink_bypass_mask)."""
         d = cls(None, None, lens, max_len, num_q_heads)
         d.c.num_kv_heads = int(num_kv_heads)
+        if int(num_kv_heads) < 1:
+            raise ValueError("num_kv_heads must be at least 1")
         d.c.head_dim = int(head_dim)
         d.c.dtype = SFI_BF16
         return d
 
     def with_lens(self, lens, max_len: int) -> "KVDesc":
         """Same cache, other lengths (a later decode step)."""
+        _buf(lens, "lens", _I32, self.c.batch)
         d = object.__new__(KVDesc)
         d._keep = self._keep + (lens,)
+        d.cache_dtype = self.cache_dtype
         d.c = sfi_kv_desc.from_buffer_copy(self.c)
         d.c.len = lens.data_ptr()
         d.c.max_len = int(max_len)
@@ -159,6 +212,19 @@ class KVDesc:
     @property
     def ref(self):
         return ctypes.byref(self.c)
+
+    # sizes that the calls' buffers must cover (elements)
+    @property
+    def heads(self) -> int:                 # query heads over the batch
+        return self.c.batch * self.c.num_q_heads
+
+    @property
+    def units(self) -> int:                 # (sequence, KV head) units over the batch
+        return self.c.batch * self.c.num_kv_heads
+
+    def need_cache(self, what: str):
+        if self.cache_dtype is None:
+            raise ValueError(f"{what}: the descriptor has no cache (KVDesc.for_logits)")
 
 
 def sfi_status_string(status: int) -> str:
@@ -171,18 +237,34 @@ def sfi_workspace_bytes(desc: KVDesc, op: int, idx_stride: int = 0, n_recent: in
 
 def sfi_stream_read(buf, n_workgroups: int, sink, stream=None):
     """Sequential read of the whole of `buf` (a measurement yardstick); sink: >= 64 int32."""
+    _buf(buf, "buf")
+    _buf(sink, "sink", _I32, 64)
     _check(lib().sfi_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(n_workgroups),
                                  _ptr(sink), _stream(stream)), "sfi_stream_read")
 
 
 def sfi_dense_decode(desc: KVDesc, q, out, lse, logits, logit_stride: int, ws, stream=None):
+    desc.need_cache("sfi_dense_decode")
+    _buf(q, "q", desc.cache_dtype, desc.heads * desc.c.head_dim)
+    _buf(out, "out", _F32, desc.heads * desc.c.head_dim)
+    _buf(lse, "lse", _F32, desc.heads, optional=True)
+    _buf(logits, "logits", _F32, desc.heads * int(logit_stride), optional=True)
+    _buf(ws, "ws")
     _check(lib().sfi_dense_decode(desc.ref, _ptr(q), _ptr(out), _ptr(lse), _ptr(logits),
                                   int(logit_stride), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)), "sfi_dense_decode")
 
 
+def _selector_bufs(desc: KVDesc, logits, logit_stride: int, idx, idx_stride: int, n_idx, ws):
+    _buf(logits, "logits", _F32, desc.heads * int(logit_stride))
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
+    _buf(n_idx, "n_idx", _I32, desc.units)
+    _buf(ws, "ws")
+
+
 def sfi_select(desc: KVDesc, logits, logit_stride: int, n_sink: int, n_recent: int, k_sel: int,
                idx, idx_stride: int, n_idx, ws, stream=None):
+    _selector_bufs(desc, logits, logit_stride, idx, idx_stride, n_idx, ws)
     _check(lib().sfi_select(desc.ref, _ptr(logits), int(logit_stride), int(n_sink),
                             int(n_recent), int(k_sel), _ptr(idx), int(idx_stride), _ptr(n_idx),
                             _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
@@ -192,6 +274,8 @@ def sfi_select(desc: KVDesc, logits, logit_stride: int, n_sink: int, n_recent: i
 def sfi_select_refined(desc: KVDesc, logits, logit_stride: int, key_norm, norm_stride: int,
                        n_sink: int, n_recent: int, k_sel: int, params: dict, idx,
                        idx_stride: int, n_idx, ws, stream=None):
+    _selector_bufs(desc, logits, logit_stride, idx, idx_stride, n_idx, ws)
+    _buf(key_norm, "key_norm", _F32, desc.units * int(norm_stride), optional=True)
     pr = dict(REFINE_DEFAULTS)
     pr.update(params or {})
     p = sfi_refine(pr["lambda_"], pr["alpha_soft"], pr["alpha_cross"], pr["prior_decay"],
@@ -205,13 +289,28 @@ def sfi_select_refined(desc: KVDesc, logits, logit_stride: int, key_norm, norm_s
 
 def sfi_sink_bypass_mask(desc: KVDesc, logits, logit_stride: int, lse, frac: float, head_mask,
                          stream=None):
+    _buf(logits, "logits", _F32, (desc.heads - 1) * int(logit_stride) + 1)
+    _buf(lse, "lse", _F32, desc.heads)
+    _buf(head_mask, "head_mask", _U8, desc.heads)
     _check(lib().sfi_sink_bypass_mask(desc.ref, _ptr(logits), int(logit_stride), _ptr(lse),
                                       float(frac), _ptr(head_mask), _stream(stream)),
            "sfi_sink_bypass_mask")
 
 
+def _fast_bufs(desc: KVDesc, what: str, q, n_idx, head_mask, out, lse, ws):
+    desc.need_cache(what)
+    _buf(q, "q", desc.cache_dtype, desc.heads * desc.c.head_dim)
+    _buf(n_idx, "n_idx", _I32, desc.units)
+    _buf(head_mask, "head_mask", _U8, desc.heads, optional=True)
+    _buf(out, "out", _F32, desc.heads * desc.c.head_dim)
+    _buf(lse, "lse", _F32, desc.heads, optional=True)
+    _buf(ws, "ws")
+
+
 def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int, head_mask,
                       out, lse, ws, stream=None):
+    _fast_bufs(desc, "sfi_sparse_decode", q, n_idx, head_mask, out, lse, ws)
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
     _check(lib().sfi_sparse_decode(desc.ref, _ptr(q), _ptr(idx), int(idx_stride), _ptr(n_idx),
                                    int(n_recent), _ptr(head_mask), _ptr(out), _ptr(lse),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
@@ -221,6 +320,10 @@ def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: in
 def sfi_sparse_decode_routed(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int,
                              head_mask, route_lse, gamma: float, routed, out, lse, ws,
                              stream=None):
+    _fast_bufs(desc, "sfi_sparse_decode_routed", q, n_idx, head_mask, out, lse, ws)
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
+    _buf(route_lse, "route_lse", _F32, desc.heads)
+    _buf(routed, "routed", _U8, desc.units, optional=True)
     _check(lib().sfi_sparse_decode_routed(desc.ref, _ptr(q), _ptr(idx), int(idx_stride),
                                           _ptr(n_idx), int(n_recent), _ptr(head_mask),
                                           _ptr(route_lse), float(gamma), _ptr(routed), _ptr(out),
@@ -229,13 +332,26 @@ def sfi_sparse_decode_routed(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_rec
            "sfi_sparse_decode_routed")
 
 
+def _segment_bufs(desc: KVDesc, idx_stride: int, ck, cv, cpos):
+    rows = desc.units * int(idx_stride)
+    _buf(ck, "seg_k", desc.cache_dtype, rows * desc.c.head_dim)
+    _buf(cv, "seg_v", desc.cache_dtype, rows * desc.c.head_dim)
+    _buf(cpos, "seg_pos", _I32, rows)
+
+
 def sfi_reorg(desc: KVDesc, idx, idx_stride: int, n_idx, ck, cv, cpos, stream=None):
+    desc.need_cache("sfi_reorg")
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
+    _buf(n_idx, "n_idx", _I32, desc.units)
+    _segment_bufs(desc, idx_stride, ck, cv, cpos)
     _check(lib().sfi_reorg(desc.ref, _ptr(idx), int(idx_stride), _ptr(n_idx), _ptr(ck), _ptr(cv),
                            _ptr(cpos), _stream(stream)), "sfi_reorg")
 
 
 def sfi_sparse_decode_compact(desc: KVDesc, q, ck, cv, cpos, idx_stride: int, n_idx,
                               n_recent: int, head_mask, out, lse, ws, stream=None):
+    _fast_bufs(desc, "sfi_sparse_decode_compact", q, n_idx, head_mask, out, lse, ws)
+    _segment_bufs(desc, idx_stride, ck, cv, cpos)
     _check(lib().sfi_sparse_decode_compact(desc.ref, _ptr(q), _ptr(ck), _ptr(cv), _ptr(cpos),
                                            int(idx_stride), _ptr(n_idx), int(n_recent),
                                            _ptr(head_mask), _ptr(out), _ptr(lse), _ptr(ws),
@@ -266,6 +382,27 @@ def sfi_slow_step_layers(descs, qs, outs, lses, logits_slots, logit_stride: int,
     slot_events: one per ring slot; streams are torch.cuda.Stream, events torch.cuda.Event.
     segments: None, or one (seg_k, seg_v, seg_pos) per layer for a Reorg after each Selector."""
     n, r = len(descs), len(logits_slots)
+    for name, xs, want in (("qs", qs, n), ("outs", outs, n), ("lses", lses, n), ("idxs", idxs, n),
+                           ("n_idxs", n_idxs, n), ("sel_ws_slots", sel_ws_slots, r),
+                           ("slot_events", slot_events, r)):
+        if len(xs) != want:
+            raise ValueError(f"{name}: {len(xs)} entries, expected {want}")
+    for li, d in enumerate(descs):
+        d.need_cache("sfi_slow_step_layers")
+        _buf(qs[li], f"qs[{li}]", d.cache_dtype, d.heads * d.c.head_dim)
+        _buf(outs[li], f"outs[{li}]", _F32, d.heads * d.c.head_dim)
+        _buf(lses[li], f"lses[{li}]", _F32, d.heads)
+        _buf(idxs[li], f"idxs[{li}]", _I32, d.units * int(idx_stride))
+        _buf(n_idxs[li], f"n_idxs[{li}]", _I32, d.units)
+        if head_masks is not None:
+            _buf(head_masks[li], f"head_masks[{li}]", _U8, d.heads, optional=True)
+        if segments is not None:
+            _segment_bufs(d, idx_stride, *segments[li])
+        for si, lg in enumerate(logits_slots):
+            _buf(lg, f"logits_slots[{si}]", _F32, d.heads * int(logit_stride))
+    for si, w in enumerate(sel_ws_slots):
+        _buf(w, f"sel_ws_slots[{si}]")
+    _buf(dense_ws, "dense_ws")
     darr = (sfi_kv_desc * n)(*[d.c for d in descs])
     evs = (ctypes.c_void_p * r)(*[_event_handle(e, side_stream) for e in slot_events])
     sel_bytes = min(w.numel() * w.element_size() for w in sel_ws_slots)

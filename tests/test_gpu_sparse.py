@@ -267,3 +267,26 @@ def test_sparse_routed_edges(paged):
     ref_o, ref_l = gpu_sparse(lay, q, 0, idx.to(DEV), n_idx.to(DEV))
     assert torch.equal(out.nan_to_num(7.0), ref_o.nan_to_num(7.0))
     assert torch.equal(lse, ref_l)
+
+
+def test_binding_rejects_misused_device_buffers():
+    """The binding raises before the call for a wrong dtype or a strided view (cases chosen
+    so that even an unchecked call would stay inside the tensors' storage)."""
+    wl = W["gqa4_32k"].scaled(3000, B=1)
+    lay = synth.make_layer(wl, 0, device=DEV)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=23)
+    idx, n_idx = idx.to(DEV), n_idx.to(DEV)
+    lens = lay.len_at(1).to(DEV)
+    desc = desc_for(lay, lens, lay.max_len_at(1))
+    q = synth.make_query(wl, 0, 1, device=DEV)
+    ws = B.workspace(desc, idx_stride=idx.shape[-1], n_recent=wl.n_recent, device=DEV)
+    out64 = torch.zeros((wl.B, wl.Hq, wl.d), dtype=torch.float64, device=DEV)
+    with pytest.raises(TypeError, match="out"):
+        B.sfi_sparse_decode(desc, q, idx, idx.shape[-1], n_idx, wl.n_recent, None, out64, None, ws)
+    wide = torch.zeros((wl.B, wl.Hkv, 2 * idx.shape[-1]), dtype=torch.int32, device=DEV)
+    out = torch.zeros((wl.B, wl.Hq, wl.d), device=DEV)
+    with pytest.raises(ValueError, match="contiguous"):
+        B.sfi_sparse_decode(desc, q, wide[:, :, ::2], idx.shape[-1], n_idx, wl.n_recent, None,
+                            out, None, ws)
+    torch.cuda.synchronize()
+    assert (out == 0).all(), "a rejected call must not have queued work"
