@@ -91,14 +91,25 @@ def lib():
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # a plain int: the argtypes turn it into a void* without a ctypes object per argument
+    return None if t is None else t.data_ptr()
+
+
+def _current_raw_stream():
+    """torch's current HIP stream on the current device, as an address.  torch's raw-stream
+    query avoids building a torch.cuda.Stream object on every call; the public path is the
+    fallback."""
+    try:
+        return torch._C._cuda_getCurrentRawStream(torch._C._cuda_getDevice())
+    except AttributeError:
+        return torch.cuda.current_stream().cuda_stream
 
 
 def _stream(stream):
     if stream is not None:
-        return ctypes.c_void_p(int(stream))
+        return int(stream)
     if torch.cuda.is_available():
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return _current_raw_stream()
     return None
 
 
@@ -116,11 +127,18 @@ def _buf(t, name: str, dtype=None, numel: int = 0, optional: bool = False,
     """Checks a tensor before its pointer crosses the C ABI.  The library sees only the
     address, so a buffer of another dtype, a strided view or one smaller than the call's
     sizes would be read or written past its end by a kernel; such calls raise here instead.
-    Checked in this order: type, dtype, contiguity, size, then that it lives in GPU memory."""
+    The common case is one combined test; a failure is then diagnosed in this order: type,
+    dtype, contiguity, size, GPU residence."""
     if t is None:
         if optional:
             return
         raise ValueError(f"{name}: a tensor is required")
+    try:
+        if ((dtype is None or t.dtype is dtype) and t.is_contiguous() and t.numel() >= numel
+                and (t.is_cuda or not device)):
+            return
+    except AttributeError:
+        pass
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
     if dtype is not None and t.dtype != dtype:
@@ -129,8 +147,7 @@ def _buf(t, name: str, dtype=None, numel: int = 0, optional: bool = False,
         raise ValueError(f"{name}: must be contiguous")
     if t.numel() < numel:
         raise ValueError(f"{name}: holds {t.numel()} elements, the call needs {numel}")
-    if device and t.device.type != "cuda":
-        raise ValueError(f"{name}: must be in GPU memory, is on {t.device}")
+    raise ValueError(f"{name}: must be in GPU memory, is on {t.device}")
 
 
 class KVDesc:
