@@ -62,6 +62,9 @@ def parse():
                     help="skip the Reorg + two-segment fast-step measurement")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the stack cycle replayed from a captured HIP graph")
+    ap.add_argument("--context-sweep", action="store_true",
+                    help="add dense, Selector and fast-step timings of an 8B-shaped layer at "
+                         "contexts of 32K to 512K")
     ap.add_argument("--retention-sweep", action="store_true",
                     help="add dense-vs-sparse timings over retention ratios on a layer shaped "
                          "like the SFI page's retention table (KV 16K, batch 16, 32/8 heads)")
@@ -327,6 +330,82 @@ def retention_sweep(B, torch, synth, ratios=(0.016, 0.031, 0.0625, 0.125, 0.25, 
         del sets, wsr
     return {"shape": "B 16, 32/8 heads, d 128, bf16, N 16384, sink 4, recent 256, spans",
             "dense_us": round(dense_us, 2), "dense_nolog_us": round(nolog_us, 2), "rows": rows}
+
+
+def context_sweep(B, torch, synth, contexts=(32768, 65536, 131072, 262144, 524288), L=4,
+                  reps=3):
+    """Dense step, Selector and fast step of one Llama-3.1-8B-shaped layer (batch 1, 32/8
+    heads, d 128, bf16, sink 4 + recent 256 + k 2048) over contexts of 32K to 512K, each call
+    timed over L rotated layers (fast steps in decode order) so no layer's rows are re-read from
+    the Infinity Cache.  fast_us is the fast-step block replayed from a captured graph,
+    fast_eager_us the same block launched from Python, which the host paces at this size."""
+    dev = "cuda"
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rows = []
+    for N in contexts:
+        wl = synth.Workload(f"ctx_{N}", 8000 + N // 1024, 1, 32, 8, 128, "bf16", N, 4, 256, 2048, 16)
+        lays = [synth.make_layer(wl, li, device=dev) for li in range(L)]
+        T = wl.cycle
+        lens = [lays[0].len_at(t).to(dev) for t in range(T)]
+        descs = [[B.KVDesc(lay.k, lay.v, lens[t], lay.max_len_at(t), wl.Hq) for t in range(T)]
+                 for lay in lays]
+        qs = [[synth.make_query(wl, li, t, device=dev) for t in range(T)] for li in range(L)]
+        stride = (N + 3) // 4 * 4
+        istride = wl.n_sink + wl.k_sel
+        logits = [torch.empty((1, wl.Hq, stride), device=dev) for _ in range(L)]
+        idx = [torch.empty((1, wl.Hkv, istride), dtype=torch.int32, device=dev) for _ in range(L)]
+        nidx = [torch.empty((1, wl.Hkv), dtype=torch.int32, device=dev) for _ in range(L)]
+        out = torch.empty((1, wl.Hq, wl.d), device=dev)
+        lse = torch.empty((1, wl.Hq), device=dev)
+        ws = B.workspace(descs[0][T - 1], idx_stride=istride, n_recent=wl.n_recent, device=dev)
+
+        def dense(with_logits):
+            for li in range(L):
+                B.sfi_dense_decode(descs[li][0], qs[li][0], out, lse,
+                                   logits[li] if with_logits else None, stride, ws)
+
+        def select():
+            for li in range(L):
+                B.sfi_select(descs[li][0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel,
+                             idx[li], istride, nidx[li], ws)
+
+        def fast():
+            for t in range(1, T):
+                for li in range(L):
+                    B.sfi_sparse_decode(descs[li][t], qs[li][t], idx[li], istride, nidx[li],
+                                        wl.n_recent, None, out, lse, ws)
+
+        def timed(fn, per):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return 1e3 * e0.elapsed_time(e1) / (reps * per)
+
+        d_us = timed(lambda: dense(True), L)
+        n_us = timed(lambda: dense(False), L)
+        s_us = timed(select, L)
+        # back-to-back fast steps of a small layer outrun the host's launches from Python, so
+        # the block is also replayed from a captured graph (the GPU's own time)
+        fe_us = timed(fast, L * (T - 1))
+        f_us = graph_replay(torch, fast, L * (T - 1))
+        d_bytes = dense_bytes(wl, [N])
+        f_bytes = fast_bytes(wl, [N + 1], nidx[0].cpu().tolist(), None)
+        rows.append({"context": N, "dense_us": round(d_us, 1), "dense_nolog_us": round(n_us, 1),
+                     "dense_gbps": round(d_bytes / (d_us * 1e-6) / 1e9, 1),
+                     "select_us": round(s_us, 1), "fast_us": round(f_us, 2),
+                     "fast_eager_us": round(fe_us, 2),
+                     "fast_gbps": round(f_bytes / (f_us * 1e-6) / 1e9, 1),
+                     "value_us": round((d_us + s_us + (T - 1) * f_us) / T, 2)})
+        print(f"#   context {N}: {rows[-1]}", file=sys.stderr, flush=True)
+        del lays, descs, qs, logits, idx, nidx, ws
+        torch.cuda.empty_cache()
+    return {"shape": "B 1, 32/8 heads, d 128, bf16, sink 4, recent 256, k 2048, cycle 16, "
+                     f"{L} rotated layers", "rows": rows}
 
 
 def synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out, lse, ws,
@@ -793,11 +872,15 @@ def main():
         print("# cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         host_q = [q.cpu() for q in queries[0]]
         result["cpu_baseline"] = cpu_baseline(wl, layers[0], host_q, lens0)
-    if args.retention_sweep:
-        print("# retention sweep", file=sys.stderr, flush=True)
+    if args.retention_sweep or args.context_sweep:
         del layers, descs, queries, logits, idxs, nidxs, masks
         torch.cuda.empty_cache()
+    if args.retention_sweep:
+        print("# retention sweep", file=sys.stderr, flush=True)
         result["retention_sweep"] = retention_sweep(B, torch, synth)
+    if args.context_sweep:
+        print("# context sweep", file=sys.stderr, flush=True)
+        result["context_sweep"] = context_sweep(B, torch, synth)
     print(json.dumps(result), flush=True)
 
 
