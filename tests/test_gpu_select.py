@@ -98,6 +98,8 @@ def test_select_edges(orc, path):
     _run(orc, wl, lens, z, exact=True, k_sel=0, idx_stride=8, max_len=ml)
     _run(orc, wl, lens, z, exact=True, n_sink=0, k_sel=37, max_len=ml)
     _run(orc, wl, lens, z, exact=True, n_sink=3, n_recent=5, k_sel=101, max_len=ml)
+    # no recent window: J runs to the end of the sequence
+    _run(orc, wl, lens, z, exact=True, n_recent=0, k_sel=90, max_len=ml)
     # many exact ties: quantised logits, lowest positions win
     zq = torch.randint(-2, 2, z.shape, generator=g).float()
     _run(orc, wl, lens, zq, exact=True, max_len=ml)

@@ -127,6 +127,19 @@ def test_sparse_window_only_and_skipped_entries(orc):
     _check(orc, lay, q, 1, idx, n_idx)
 
 
+def test_sparse_without_recent_window(orc):
+    """n_recent = 0: only the index set is attended; a unit with an empty index set attends to
+    nothing (zero output, lse = -inf)."""
+    wl = synth.Workload("sp_no_recent", 8200, 3, 8, 2, 128, "bf16", 3000, 4, 0, 300, 3)
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[3000, 700, 5])
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=25)
+    n_idx[1, 1] = 0
+    for t in (0, 2):
+        q = synth.make_query(wl, 0, t, device=DEV)
+        out, lse = _check(orc, lay, q, t, idx, n_idx, n_recent=0)
+        assert (out[1, 4:8] == 0).all() and torch.isneginf(lse[1, 4:8]).all()
+
+
 def test_sparse_all_heads_masked_and_group_skip(orc):
     wl = W["gqa8_512k"].scaled(12000)
     lay = synth.make_layer(wl, 0, device=DEV)
