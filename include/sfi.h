@@ -72,6 +72,8 @@ typedef struct sfi_refine {
  * block tables and layout, read by every kernel of the step).
  *
  *   batch, num_q_heads, num_kv_heads : B, Hq, Hkv; Hq % Hkv == 0 and G = Hq / Hkv <= 16
+ *                                     (<= 64 for the calls that read no cache: the Selectors
+ *                                     and the mask)
  *   head_dim                          : d, 64 or 128
  *   dtype                             : element type of k, v and q (SFI_F32 or SFI_BF16)
  *   k, v      (device) contiguous: [B][Hkv][n_cap][d]; paged: [num_blocks][Hkv][block_size][d];
@@ -129,7 +131,11 @@ sfi_status sfi_dense_decode(const sfi_kv_desc* kv, const void* q, float* out, fl
  * logit_stride >= max_len and a multiple of 4.
  * idx (device) int32 [B][Hkv][idx_stride], idx_stride >= n_sink + k_sel.
  * n_idx (device) int32 [B][Hkv] = min(n_sink, N) + min(k_sel, |J|).
- * n_sink, n_recent >= 0, k_sel >= 0.  kv->k and kv->v are not read. */
+ * n_sink, n_recent >= 0, k_sel >= 0.  kv->k and kv->v are not read.
+ * Observation window (SFI Sec. 3.2 and Sec. 5.1: evidence averaged over the last W queries, W
+ * = 1 at decode, 16 at the end of prefill): pass the logits of W queries per query head as
+ * rows i*W + w, w < W, with num_q_heads = Hq*W; the group of KV head h is then its G*W rows
+ * and f is their mean.  G*W <= 64. */
 sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
                       int32_t n_sink, int32_t n_recent, int32_t k_sel,
                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,

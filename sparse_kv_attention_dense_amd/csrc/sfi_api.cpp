@@ -60,7 +60,9 @@ sfi_status check_desc(const sfi_kv_desc* kv, bool need_cache) {
     if (!kv) return SFI_E_INVALID;
     if (kv->batch < 1 || kv->num_q_heads < 1 || kv->num_kv_heads < 1) return SFI_E_INVALID;
     if (kv->num_q_heads % kv->num_kv_heads != 0) return SFI_E_INVALID;
-    if (kv->num_q_heads / kv->num_kv_heads > kMaxG) return SFI_E_UNSUPPORTED;
+    // the attention kernels hold a group in one MFMA N dimension; the Selector and the mask
+    // only read logit rows
+    if (kv->num_q_heads / kv->num_kv_heads > (need_cache ? kMaxG : kMaxSelG)) return SFI_E_UNSUPPORTED;
     if (kv->batch > 65535 || kv->num_kv_heads > 65535 || kv->num_q_heads > 65535) return SFI_E_UNSUPPORTED;
     if (kv->head_dim != 64 && kv->head_dim != 128) return SFI_E_UNSUPPORTED;
     if (kv->dtype != SFI_F32 && kv->dtype != SFI_BF16) return SFI_E_UNSUPPORTED;

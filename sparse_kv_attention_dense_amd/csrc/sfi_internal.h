@@ -21,6 +21,8 @@ constexpr int kSplitQuantum = kTile * kWaves;
 constexpr int kTabMax = 4096;        // row-table entries per workgroup (dynamic LDS)
 constexpr int kMaxSplits = 1024;     // partial records per (b, h) that the combine merges
 constexpr int kMaxG = 16;            // query heads per KV head (MFMA N dimension)
+constexpr int kMaxSelG = 64;         // logit rows per KV head that the Selector and the mask
+                                     // take (query heads, or query heads x window queries)
 
 struct AttnArgs {
     const void* k;

@@ -193,7 +193,7 @@ __device__ __forceinline__ float fused_log2(const SelArgs& a, float f, float lr)
 }
 
 __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
-    __shared__ float s_lse[kMaxG];
+    __shared__ float s_lse[kMaxSelG];
     __shared__ uint32_t lh[kCBins0];
     __shared__ float sh[4];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -586,7 +586,7 @@ struct UnitShared {
     uint32_t hist[kRadixBins];
     uint32_t wtot[kUW];
     float2 red[4 * kUW];
-    float lse[kMaxG];
+    float lse[kMaxSelG];
     uint32_t sel[2];
 };
 

@@ -115,6 +115,21 @@ def test_select_and_mask_validation(L):
     assert ok_ptr(-0.1) == B.SFI_E_INVALID
 
 
+def test_group_size_limits(L):
+    """The attention calls hold a KV group in one 16-wide MFMA dimension; the Selector and the
+    mask read logit rows only and take up to 64 per KV head (query heads x window queries)."""
+    big = 1 << 40
+    for G, sel_ok in ((16, True), (64, True), (65, False)):
+        d = _desc(k=None, v=None, num_q_heads=2 * G, num_kv_heads=2)
+        st = L.sfi_select(ctypes.byref(d), FAKE, 4000, 4, 256, 2048, FAKE, 2052, FAKE, FAKE, 0,
+                          None)
+        assert st == (B.SFI_E_WORKSPACE if sel_ok else B.SFI_E_UNSUPPORTED), G
+        assert (L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SELECT, 0, 0) > 0) == sel_ok
+    d = _desc(num_q_heads=64, num_kv_heads=2)                      # G = 32
+    assert _dense(L, d, big) == B.SFI_E_UNSUPPORTED
+    assert L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_DENSE, 0, 0) == 0
+
+
 def test_sparse_validation(L):
     d = _desc()
     ws = L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 2052, 256)

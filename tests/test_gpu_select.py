@@ -108,6 +108,31 @@ def test_select_edges(orc, path):
     _run(orc, wl, lens, torch.zeros_like(z), exact=True, max_len=ml)
 
 
+@pytest.mark.parametrize("path", ["unit", "chunked"])
+def test_select_observation_window(orc, path):
+    """Evidence over an observation window of W = 16 queries per head: the window's logits as
+    rows i*W + w, 64 rows per KV head at G = 4, planted (exact) and random (tie band); and
+    every head's row repeated W times selects what the row alone selects."""
+    G, Hkv, Wn = 4, 2, 16
+    wl = synth.Workload("sel_window", 1, 2, G * Hkv * Wn, Hkv, 128, "bf16", 20000, 4, 256, 300, 1)
+    lens = [1000, 900] if path == "unit" else [20000, 15000]
+    ml = CHUNKED_MAX_LEN if path == "chunked" else None
+    say(f"[select window] {path} rows per KV head {G * Wn}")
+    z, _ = _planted(wl, lens, seed=91)
+    _run(orc, wl, lens, z, exact=True, max_len=ml)
+    g = torch.Generator().manual_seed(92)
+    _run(orc, wl, lens, torch.randn((2, wl.Hq, max(lens)), generator=g) * 2.0, exact=False,
+         max_len=ml)
+    one = synth.Workload("sel_window_1", 1, 2, G * Hkv, Hkv, 128, "bf16", 20000, 4, 256, 300, 1)
+    z1, ranks = _planted(one, lens, seed=93)
+    idx, n_idx, _ = _run(orc, wl, lens, z1.repeat_interleave(Wn, dim=1), exact=True, max_len=ml)
+    ig = idx.cpu().numpy()
+    for b, N in enumerate(lens):
+        for h in range(Hkv):
+            keep = sorted((torch.nonzero(ranks[b][h] < one.k_sel).flatten() + one.n_sink).tolist())
+            assert ig[b, h, :n_idx[b, h]].tolist() == list(range(min(one.n_sink, N))) + keep
+
+
 @pytest.mark.parametrize("G,path", [(1, "unit"), (16, "unit"), (1, "chunked"), (16, "chunked"),
                                     (5, "unit")])
 def test_select_group_sizes(orc, G, path):

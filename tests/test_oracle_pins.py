@@ -232,6 +232,31 @@ def test_select_single_head_is_library_topk(orc):
         assert idx[0, h, :n_idx[0, h]].tolist() == exp
 
 
+def test_select_observation_window_is_the_mean_over_queries(orc):
+    """Evidence over a window of W queries per head (rows i*W + w of the logits, so KV head h
+    owns G*W rows) is the mean of the W single-query evidences, each over its G rows; a window
+    of W copies of one query gives that query's evidence and selection."""
+    g = torch.Generator().manual_seed(12)
+    B, Hq, Hkv, Wn, N = 2, 8, 2, 4, 600
+    n_sink, n_recent, k_sel = 4, 40, 90
+    lens = [N, 437]
+    z = torch.randn((B, Hq * Wn, N), generator=g) * 2.0
+    _, _, fw = orc.select(lens, Hq * Wn, Hkv, z, n_sink, n_recent, k_sel, want_f=True)
+    f_each = []
+    for w in range(Wn):
+        _, _, f = orc.select(lens, Hq, Hkv, z[:, w::Wn], n_sink, n_recent, k_sel, want_f=True)
+        f_each.append(f)
+    for b, n in enumerate(lens):
+        J = slice(n_sink, n - n_recent)
+        mean = sum(f[b][:, J] for f in f_each) / Wn
+        assert np.allclose(fw[b][:, J], mean, rtol=1e-12, atol=0.0)
+    z1 = torch.randn((B, Hq, N), generator=g)
+    i1, n1, _ = orc.select(lens, Hq, Hkv, z1, n_sink, n_recent, k_sel)
+    iw, nw, _ = orc.select(lens, Hq * Wn, Hkv, z1.repeat_interleave(Wn, dim=1), n_sink, n_recent,
+                           k_sel)
+    assert (n1 == nw).all() and (i1 == iw).all()
+
+
 def test_select_brute_force_rank_counting(orc):
     """O(n^2) rank counting on tiny inputs with ties: j is kept iff fewer than k_sel
     positions beat it ((f larger) or (f equal and position lower))."""
