@@ -15,6 +15,13 @@
  *                                                                        -> sfi_sparse_decode_routed
  *   - the slow step over a model's layers with the Selector on a second stream
  *     (SFI Sec. 4.1, layer-wise asynchronous execution)                  -> sfi_slow_step_layers
+ *   - the Selector with the cache-aware prior, fusion and refinements
+ *     (SFI Sec. 3.2-3.3)                                                  -> sfi_select_refined
+ *   - the two-segment layout: copy sink + selected rows into a compact segment, then fast
+ *     steps that read it (SFI Sec. 4.1-4.2, Reorg and the coalesced
+ *     sparse kernel)                          -> sfi_reorg, sfi_sparse_decode_compact
+ *   - a plain streaming read, the measured bandwidth yardstick (not a step of the method)
+ *                                                                        -> sfi_stream_read
  *
  * Conventions shared by every call
  *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
