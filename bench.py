@@ -105,10 +105,11 @@ def fast_bytes(wl, lens_t, n_idx_host, mask_host):
     return tot + wl.B * wl.Hq * wl.d * (wl.elem_bytes + 4) + wl.B * wl.Hq * 4
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per dense launch from the committed rocprofv3 counter summary of this workload
-    (FETCH_SIZE and WRITE_SIZE, each scaled by a known-size copy), or None when there is none or
-    the kernel source changed since the counters were taken."""
+def counter_traffic(workload: str, key: str = "traffic_bytes_per_launch"):
+    """HBM bytes from the committed rocprofv3 counter summary of this workload (FETCH_SIZE and
+    WRITE_SIZE, each scaled by a known-size copy): per dense launch, or with key
+    "fast_traffic_bytes_per_step" per fast step (partials kernel and combine).  None when there
+    is none or the kernel source changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_counters.md")
     try:
         text = open(path).read()
@@ -116,10 +117,10 @@ def counter_traffic(workload: str):
     except OSError:
         return None
     for line in text.splitlines():
-        if line.startswith("traffic_bytes_per_launch="):
+        if line.startswith(key + "="):
             fields = dict(kv.split("=", 1) for kv in line.split())
             if fields.get("source_sha256") == sha:
-                return int(fields["traffic_bytes_per_launch"])
+                return int(fields[key])
     return None
 
 
@@ -841,6 +842,7 @@ def main():
                      "algorithmic_bytes": d_bytes},
         "fast_roofline": {"bound": "hbm", "achieved": round(fast_gbps, 1), "peak": PEAK_HBM_GBS,
                           "unit": "GB/s", "frac": round(fast_gbps / PEAK_HBM_GBS, 4),
+                          "traffic": counter_traffic(wl.name, "fast_traffic_bytes_per_step"),
                           "algorithmic_bytes": int(f_bytes),
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
