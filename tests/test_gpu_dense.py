@@ -74,6 +74,32 @@ def test_dense_paged_page_sizes(orc, dtype, d, G, block):
     assert_logits(logits, ez, lay.len0_host, tol["rel"])
 
 
+def test_dense_loose_length_bound(orc):
+    """max_len is only a host-side bound for the launch plan: a bound three times the longest
+    sequence (as a captured step that must serve later, longer steps would declare) gives the
+    same results against the oracle."""
+    wl = synth.Workload("dense_loose_bound", 7350, 3, 16, 4, 128, "bf16", 6000, 4, 64, 128, 2)
+    lay = synth.make_layer(wl, 0, device=DEV, lens=[6000, 2500, 777])
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    lens = lay.len_at(0).to(DEV)
+    stride = round4(3 * 6000)
+    out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), device=DEV)
+    lse = torch.full((wl.B, wl.Hq), float("nan"), device=DEV)
+    logits = torch.full((wl.B, wl.Hq, stride), float("nan"), device=DEV)
+    kbig = torch.zeros((wl.B, wl.Hkv, 3 * 6000, wl.d), dtype=lay.k.dtype, device=DEV)
+    vbig = torch.zeros_like(kbig)
+    kbig[:, :, :lay.k.shape[2]] = lay.k
+    vbig[:, :, :lay.v.shape[2]] = lay.v
+    desc = B.KVDesc(kbig, vbig, lens, 3 * 6000, wl.Hq)
+    ws = B.workspace(desc, device=DEV)
+    B.sfi_dense_decode(desc, q, out, lse, logits, stride, ws)
+    torch.cuda.synchronize()
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lay.len0_host), q)
+    assert_close_out(out.cpu().numpy(), eo, 1e-2)
+    assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
+    assert_logits(logits, ez, lay.len0_host, 1e-3)
+
+
 def test_dense_edge_lengths(orc):
     """Lengths 0, 1, a tile minus one, a split plus one; logits past len stay untouched."""
     wl = synth.Workload("edges", 7300, 5, 8, 2, 128, "bf16", 4200, 4, 16, 32, 1)

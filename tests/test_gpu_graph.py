@@ -84,3 +84,54 @@ def test_graph_replay_matches_eager(name):
         for k, (x, y) in enumerate(zip(got, eager)):
             assert torch.equal(x.nan_to_num(7.0), y.nan_to_num(7.0)), f"replay {rep}, buffer {k}"
         say(f"    replay {rep}: identical to eager")
+
+
+def test_graph_fast_step_follows_device_state():
+    """One captured fast step replayed for successive decode steps: the lengths (so the recent
+    window) and the query are rewritten in device memory between replays, as a per-step
+    descriptor is; the launch plan depends on max_len, idx_stride and n_recent only, so each
+    replay equals, bit for bit, the eager call for that step."""
+    base = synth.WORKLOADS["sink_128k_b4"]
+    wl = base.scaled(9001, B=2)
+    say(f"[graph] per-step device state {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    T = wl.cycle
+    max_len = lay.max_len_at(T - 1)                 # one bound for every step of the cycle
+    lens_buf = lay.len_at(1).to(DEV).clone()
+    q_buf = synth.make_query(wl, 0, 1, device=DEV, u=lay.u).clone()
+    desc = desc_for(lay, lens_buf, max_len)
+    idx, n_idx = synth.synthetic_index_set(lay, "spans", seed=41)
+    idx, n_idx = idx.to(DEV), n_idx.to(DEV)
+    istride = idx.shape[-1]
+    ws = B.workspace(desc, idx_stride=istride, n_recent=wl.n_recent, device=DEV)
+    out = torch.empty((wl.B, wl.Hq, wl.d), device=DEV)
+    lse = torch.empty((wl.B, wl.Hq), device=DEV)
+
+    def step():
+        B.sfi_sparse_decode(desc, q_buf, idx, istride, n_idx, wl.n_recent, None, out, lse, ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    ref_out = torch.empty_like(out)
+    ref_lse = torch.empty_like(lse)
+    for t in (1, 2, 7, T - 1):
+        q_t = synth.make_query(wl, 0, t, device=DEV, u=lay.u)
+        lens_t = lay.len_at(t).to(DEV)
+        lens_buf.copy_(lens_t)
+        q_buf.copy_(q_t)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        B.sfi_sparse_decode(desc_for(lay, lens_t, max_len), q_t, idx, istride, n_idx,
+                            wl.n_recent, None, ref_out, ref_lse, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), f"step {t}"
+        say(f"    step {t}: replay identical to the eager call")
