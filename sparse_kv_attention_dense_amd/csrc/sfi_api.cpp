@@ -105,8 +105,9 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
     if ((sparse || paged) && split > kTabMax) split = kTabMax;
     int64_t nsplit = ceil_div(slots, split);
     if (nsplit > kMaxSplits) {
-        if (sparse || paged) return SFI_E_UNSUPPORTED;   // more than kMaxSplits * kTabMax slots
-        split = ceil_div(ceil_div(slots, kMaxSplits), kSplitQuantum) * kSplitQuantum;
+        // longer splits, up to the row table's capacity where there is one
+        split = ceil_div(ceil_div(slots, kMaxSplits), quantum) * quantum;
+        if ((sparse || paged) && split > kTabMax) return SFI_E_UNSUPPORTED;   // > kMaxSplits * kTabMax slots
         nsplit = ceil_div(slots, split);
     }
     if (!sparse && nsplit * units >= (int64_t(1) << 31)) return SFI_E_UNSUPPORTED;   // 1-D grid

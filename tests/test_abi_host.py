@@ -130,6 +130,17 @@ def test_group_size_limits(L):
     assert L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_DENSE, 0, 0) == 0
 
 
+def test_single_unit_paged_dense_up_to_the_table_capacity(L):
+    """One (sequence, KV head) unit on a paged cache: splits grow up to the row table's 4096
+    positions, so contexts up to 1024 x 4096 positions are planned; one more is rejected."""
+    def desc(n):
+        return _desc(batch=1, num_q_heads=2, num_kv_heads=1, head_dim=64, n_cap=0, max_len=n,
+                     block_table=FAKE, block_size=16, max_blocks=(n + 15) // 16)
+    for n in (2_200_000, 3_000_000, 1024 * 4096):
+        assert L.sfi_workspace_bytes(ctypes.byref(desc(n)), B.SFI_OP_DENSE, 0, 0) > 0, n
+    assert L.sfi_workspace_bytes(ctypes.byref(desc(1024 * 4096 + 1)), B.SFI_OP_DENSE, 0, 0) == 0
+
+
 def test_sparse_validation(L):
     d = _desc()
     ws = L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 2052, 256)

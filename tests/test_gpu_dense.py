@@ -100,6 +100,22 @@ def test_dense_loose_length_bound(orc):
     assert_logits(logits, ez, lay.len0_host, 1e-3)
 
 
+def test_dense_longest_single_unit_paged(orc):
+    """One sequence, one KV head, 3M positions in 16-position pages: more positions than 1024
+    splits of the default length cover, so the plan lengthens the splits (to 2944 positions)
+    within the row table's capacity."""
+    wl = synth.Workload("dense_3m_paged", 7500, 1, 2, 1, 64, "bf16", 3_000_000, 4, 64, 128, 1,
+                        paged=True, block_size=16)
+    say(f"[dense] {wl.name}")
+    lay = synth.make_layer(wl, 0, device=DEV)
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    out, lse, logits, _ = gpu_dense(lay, q)
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lay.len0_host), q)
+    assert_close_out(out.cpu().numpy(), eo, 1e-2)
+    assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
+    assert_logits(logits, ez, lay.len0_host, 1e-3)
+
+
 def test_dense_edge_lengths(orc):
     """Lengths 0, 1, a tile minus one, a split plus one; logits past len stay untouched."""
     wl = synth.Workload("edges", 7300, 5, 8, 2, 128, "bf16", 4200, 4, 16, 32, 1)
