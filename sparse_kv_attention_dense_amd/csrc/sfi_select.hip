@@ -564,14 +564,8 @@ __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
 // (greater, equal) scan per block.  Keys are kept per position in the workspace (L2-resident
 // between the passes).
 
-// merge of two partial log-sum-exp pairs (max, sum of exp(x - max)); max = -inf is empty
-__device__ __forceinline__ float2 lse_merge(float2 p, float2 q) {
-    const float m = fmaxf(p.x, q.x);
-    if (m == -INFINITY) return make_float2(m, 0.f);
-    return make_float2(m, p.y * expf(p.x - m) + q.y * expf(q.x - m));
-}
-
-// lse_merge in log2 units
+// merge of two partial log-sum-exp pairs (max, sum of 2^(x - max)) in log2 units; max = -inf
+// is empty
 __device__ __forceinline__ float2 lse2_merge(float2 p, float2 q) {
     const float m = fmaxf(p.x, q.x);
     if (m == -INFINITY) return make_float2(m, 0.f);
