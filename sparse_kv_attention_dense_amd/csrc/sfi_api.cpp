@@ -82,7 +82,7 @@ sfi_status check_desc(const sfi_kv_desc* kv, bool need_cache) {
 }
 
 struct AttnPlan {
-    int split_len = 0, nsplit = 0, rec = 0, tab_bytes = 0;
+    int split_len = 0, nsplit = 0, rec = 0, tab_bytes = 0, bt_off = -1;
     size_t bytes = 0;
 };
 
@@ -123,6 +123,11 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
         tab = ((split >> shift) + 2) * 4;                   // one base row per block touched
     }
     p->tab_bytes = (int)(ceil_div(tab, 16) * 16);
+    // fast step on a paged cache: the sequence's block table staged in LDS when it is short
+    if (sparse && paged && kv.max_blocks <= kBtPer * kThreads) {
+        p->bt_off = p->tab_bytes;                           // the sequence's block table
+        p->tab_bytes += (int)(ceil_div((int64_t)kv.max_blocks * 4, 16) * 16);
+    }
     // Partial records are sized for a bound on nsplit that never decreases as the length
     // grows (the split itself is rounded, so nsplit alone can), so a workspace sized for the
     // longest step of a cycle serves every shorter one.
@@ -210,6 +215,7 @@ void fill_plan_args(const AttnPlan& p, void* ws, AttnArgs* a) {
     a->split_len = p.split_len;
     a->nsplit = p.nsplit;
     a->tab_bytes = p.tab_bytes;
+    a->bt_off = p.bt_off;
     a->rec_floats = p.rec;
     a->part = (float*)ws;
 }

@@ -358,6 +358,20 @@ attention_kernel(AttnArgs a) {
     if constexpr (SPARSE) {
         if (a.route_lse) route_load<BF, D, PAGED>(a, b, h, hq0, unit, 0, route);
     }
+    // fast step on a paged cache with a short block table: the sequence's whole table is
+    // loaded here, beside the index entries, and staged in LDS below, so the row table costs
+    // one memory round trip instead of two (index, then block)
+    int bt_pre[kBtPer];
+    const bool bt_staged = SPARSE && PAGED && a.bt_off >= 0;
+    if constexpr (SPARSE && PAGED) {
+        if (bt_staged) {
+#pragma unroll
+            for (int u = 0; u < kBtPer; ++u) {
+                const int e = u * C::kNT + tid;
+                bt_pre[u] = e < a.max_blocks ? a.block_table[(int64_t)b * a.max_blocks + e] : 0;
+            }
+        }
+    }
     const int len_b = a.len[b];
 
     // ---- slot range of this workgroup -------------------------------------------------
@@ -391,6 +405,17 @@ attention_kernel(AttnArgs a) {
 
     const int bmask = (1 << a.block_shift) - 1;
     uint8_t* tab_ok = (uint8_t*)(tab + a.split_len);
+    int32_t* s_bt = (int32_t*)((unsigned char*)tab + (a.bt_off > 0 ? a.bt_off : 0));
+    if constexpr (SPARSE && PAGED) {
+        if (bt_staged) {
+#pragma unroll
+            for (int u = 0; u < kBtPer; ++u) {
+                const int e = u * C::kNT + tid;
+                if (e < a.max_blocks) s_bt[e] = bt_pre[u];
+            }
+        }
+        __syncthreads();
+    }
     if constexpr (SPARSE) {
         const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
         if constexpr (!PAGED) {
@@ -447,7 +472,9 @@ attention_kernel(AttnArgs a) {
                     const int t = t0 + u * C::kNT + tid;
                     const bool crow = compact && s0 + t < n_sel;     // compact row: no lookup
                     const int blk = (u < nfill && t < nslots && !crow)
-                        ? a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)] : 0;
+                        ? (bt_staged ? s_bt[pos[u] >> a.block_shift]
+                                     : a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)])
+                        : 0;
                     row[u] = crow ? crow0 + (uint32_t)(s0 + t)
                                   : (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
                                         (uint32_t)(pos[u] & bmask);

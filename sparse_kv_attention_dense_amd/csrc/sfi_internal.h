@@ -16,6 +16,7 @@ constexpr int kWaves = 4;
 #define SFI_SPARSE_WAVES 4
 #endif
 constexpr int kSparseWaves = SFI_SPARSE_WAVES;   // wavefronts of a fast-step workgroup
+constexpr int kBtPer = 12;           // staged block-table entries per thread (fast step, paged)
 constexpr int kTile = 32;            // slots per wavefront iteration (two 16-row MFMA blocks)
 constexpr int kSplitQuantum = kTile * kWaves;
 constexpr int kTabMax = 4096;        // row-table entries per workgroup (dynamic LDS)
@@ -41,6 +42,8 @@ struct AttnArgs {
     int32_t split_len;               // slots per workgroup, a multiple of kTile
     int32_t nsplit;                  // workgroups per (b, h)
     int32_t tab_bytes;               // dynamic LDS of the row table
+    int32_t bt_off;                  // sparse paged: byte offset of the staged block table in
+                                     //   the dynamic LDS, or -1 when it is not staged
     int32_t rec_floats;              // floats per partial record (G*(d+2) rounded to 4)
     const int32_t* idx;              // sparse only
     int32_t idx_stride;
