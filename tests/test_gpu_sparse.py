@@ -75,6 +75,20 @@ def test_sparse_head_shapes(orc, dtype, d, G, block):
         _check(orc, lay, q, t, idx, n_idx)
 
 
+@pytest.mark.parametrize("lens", [[5000, 3100], [3073, 40]])
+def test_sparse_paged_long_block_table(orc, lens):
+    """A block table longer than the 3072 entries a fast-step workgroup stages in LDS (pages of
+    one position): the rows are then looked up in the table directly."""
+    wl = synth.Workload("sparse_long_bt", 7700, 2, 8, 2, 128, "bf16", max(lens), 4, 64, 300, 2,
+                        paged=True, block_size=1)
+    say(f"[sparse] {wl.name} lens={lens}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=lens)
+    assert lay.max_blocks > 3072
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=33)
+    q = synth.make_query(wl, 0, 1, device=DEV)
+    _check(orc, lay, q, 1, idx, n_idx)
+
+
 def test_sparse_largest_split(orc):
     """An index set long enough that each fast-step workgroup holds the largest split its row
     table allows (4096 slots): 1,049,068 slots for the one (sequence, KV head) unit, 257
