@@ -226,6 +226,20 @@ def test_sparse_routed_planted_decisions(orc, name):
     base = W[name]
     wl = base if name == "tiny_2k_f32" else base.scaled(9001, B=min(base.B, 2),
                                                          len_lo=4000 if base.len_lo else None)
+    _routed_planted(orc, wl)
+
+
+@pytest.mark.parametrize("dtype,d,G,block", [("bf16", 128, 16, 0), ("f32", 64, 16, 16),
+                                             ("bf16", 64, 1, 1)])
+def test_sparse_routed_head_shapes(orc, dtype, d, G, block):
+    """Routing with every thread of the prologue busy (16 heads x 16 lanes at d = 128), fp32 at
+    d = 64 on a paged cache, and single-head groups on one-position pages."""
+    wl = synth.Workload(f"routed_{dtype}_{d}_{G}_{block}", 7800 + d + G + block, 2, 2 * G, 2, d,
+                        dtype, 3000, 4, 64, 300, 3, paged=block > 0, block_size=max(block, 1))
+    _routed_planted(orc, wl)
+
+
+def _routed_planted(orc, wl):
     say(f"[sparse routed planted] {wl.name}")
     lay = synth.make_layer(wl, 0, device=DEV)
     t = 2
