@@ -63,6 +63,11 @@ def gpu_compact(lay, q, t, ck, cv, cpos, n_idx, head_mask=None):
 def _case(name):
     if name == "d64_bf16":
         wl = synth.Workload("ts_d64", 8300, 3, 14, 2, 64, "bf16", 2500, 4, 64, 300, 6)
+    elif name == "f32_d128_paged":
+        wl = synth.Workload("ts_f32_d128", 8310, 2, 4, 2, 128, "f32", 2500, 4, 64, 300, 4,
+                            paged=True, block_size=64)
+    elif name == "g16_bf16":
+        wl = synth.Workload("ts_g16", 8320, 2, 32, 2, 128, "bf16", 2500, 4, 64, 300, 4)
     elif name == "tiny_2k_f32":
         wl = W[name]
     elif name == "ragged_paged_b16":
@@ -73,7 +78,8 @@ def _case(name):
     return wl
 
 
-@pytest.mark.parametrize("name", ["tiny_2k_f32", "gqa4_32k", "ragged_paged_b16", "d64_bf16"])
+@pytest.mark.parametrize("name", ["tiny_2k_f32", "gqa4_32k", "ragged_paged_b16", "d64_bf16",
+                                  "f32_d128_paged"])
 def test_reorg_matches_oracle(orc, name):
     wl = _case(name)
     say(f"[reorg] {wl.name}")
@@ -94,7 +100,7 @@ def test_reorg_matches_oracle(orc, name):
 
 
 @pytest.mark.parametrize("name", ["tiny_2k_f32", "gqa4_32k", "sink_128k_b4", "ragged_paged_b16",
-                                  "d64_bf16"])
+                                  "d64_bf16", "f32_d128_paged", "g16_bf16"])
 def test_two_segment_step(orc, name):
     wl = _case(name)
     say(f"[two-segment] {wl.name}")
