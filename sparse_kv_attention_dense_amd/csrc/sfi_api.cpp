@@ -18,10 +18,11 @@ using namespace sfi;
 // Workgroups a launch aims for.  The attention kernel holds two tile buffers in registers
 // (about 240 VGPRs), so two 4-wavefront workgroups are resident per CU: 512 on a 256-CU
 // MI355X.  Dense steps on a contiguous cache use 1024 equal workgroups (two even rounds; 512
-// and 2048 measured slower at 128K), or 512 (one round) when the whole step holds at most
-// 2^20 (sequence, KV head, position) triples: each workgroup then has only a few tiles and a
-// second round costs more than it balances (32K, one sequence: 31-33 vs 36.6 us; 128K and
-// 512K keep 1024).  The dense grid lists only splits that hold positions,
+// and 2048 measured slower at 128K), or 256 (one workgroup per CU, one round) when the whole
+// step holds at most 2^20 (sequence, KV head, position) triples: each workgroup then has
+// only a few tiles, a second round costs more than it balances and fewer, longer workgroups
+// amortise their start (one sequence of 32K: 512 workgroups 33.3-33.9 us, 256: 32.0-32.5;
+// 64K 56.5 vs 54.8; 128K 105 vs 100.5; 1024 at 32K: 36.6; 128K and 512K batches keep 1024).  The dense grid lists only splits that hold positions,
 // so on a paged cache, which usually holds sequences of unequal length, smaller splits
 // (about 2048 workgroups at the longest length) even out the rounds: 292 vs 309 us for a
 // ragged batch of 16 at 8K-32K.  A fast step moves little data and is bound by latency, so it
@@ -41,6 +42,9 @@ using namespace sfi;
 #define SFI_SPARSE_QUANTUM 32
 #endif
 constexpr int64_t kTargetWorkgroups = SFI_TARGET_WG;
+#ifndef SFI_SMALL_WG
+#define SFI_SMALL_WG 256
+#endif
 constexpr int64_t kSmallDenseRows = int64_t(1) << 20;    // one round of workgroups below this
 constexpr int64_t kPagedTargetWorkgroups = SFI_PAGED_TARGET_WG;
 constexpr int64_t kSparseTargetWorkgroups = SFI_SPARSE_TARGET_WG;
@@ -99,7 +103,7 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
     const bool small = units * (int64_t)kv.max_len <= kSmallDenseRows;
     const int64_t target = sparse ? kSparseTargetWorkgroups
                                   : (paged ? kPagedTargetWorkgroups
-                                           : (small ? kTargetWorkgroups / 2 : kTargetWorkgroups));
+                                           : (small ? SFI_SMALL_WG : kTargetWorkgroups));
     const int64_t per_unit = ceil_div(target, units);
     int64_t split = ceil_div(ceil_div(slots, per_unit), quantum) * quantum;
     if ((sparse || paged) && split > kTabMax) split = kTabMax;
