@@ -38,7 +38,18 @@ if ROOT not in sys.path:
 
 METRIC = "fast/slow decode-attn µs/step + achieved HBM GB/s (% of peak) at 32K–512K ctx"
 PEAK_HBM_GBS = 8000.0
-ATTN_SRC = os.path.join(ROOT, "sparse_kv_attention_dense_amd", "csrc", "sfi_attention.hip")
+# The sources that decide the attention kernels' HBM traffic: the kernels, and the launch plan
+# (grid, split lengths) with its constants.  Committed counter figures carry their hash.
+ATTN_SRCS = [os.path.join(ROOT, "sparse_kv_attention_dense_amd", "csrc", f)
+             for f in ("sfi_attention.hip", "sfi_api.cpp", "sfi_internal.h")]
+
+
+def attention_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for path in ATTN_SRCS:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def parse():
@@ -109,11 +120,12 @@ def counter_traffic(workload: str, key: str = "traffic_bytes_per_launch"):
     """HBM bytes from the committed rocprofv3 counter summary of this workload (FETCH_SIZE and
     WRITE_SIZE, each scaled by a known-size copy): per dense launch, or with key
     "fast_traffic_bytes_per_step" per fast step (partials kernel and combine).  None when there
-    is none or the kernel source changed since the counters were taken."""
+    is none, or when the attention kernels or their launch plan (ATTN_SRCS) changed since the
+    counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{workload}_counters.md")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        sha = attention_sources_sha256()
     except OSError:
         return None
     for line in text.splitlines():

@@ -29,26 +29,12 @@ using namespace sfi;
 // uses about 256 larger workgroups with 32-slot granularity (608 workgroups of 256 slots
 // measured 27% slower at 128K).  The plan depends only on the descriptor, so workspace sizes
 // are the same on every device.
-#ifndef SFI_TARGET_WG
-#define SFI_TARGET_WG 1024
-#endif
-#ifndef SFI_PAGED_TARGET_WG
-#define SFI_PAGED_TARGET_WG 2048
-#endif
-#ifndef SFI_SPARSE_TARGET_WG
-#define SFI_SPARSE_TARGET_WG 256
-#endif
-#ifndef SFI_SPARSE_QUANTUM
-#define SFI_SPARSE_QUANTUM 32
-#endif
-constexpr int64_t kTargetWorkgroups = SFI_TARGET_WG;
-#ifndef SFI_SMALL_WG
-#define SFI_SMALL_WG 256
-#endif
+constexpr int64_t kTargetWorkgroups = 1024;
+constexpr int64_t kSmallTargetWorkgroups = 256;
 constexpr int64_t kSmallDenseRows = int64_t(1) << 20;    // one round of workgroups below this
-constexpr int64_t kPagedTargetWorkgroups = SFI_PAGED_TARGET_WG;
-constexpr int64_t kSparseTargetWorkgroups = SFI_SPARSE_TARGET_WG;
-constexpr int64_t kSparseQuantum = SFI_SPARSE_QUANTUM;
+constexpr int64_t kPagedTargetWorkgroups = 2048;
+constexpr int64_t kSparseTargetWorkgroups = 256;
+constexpr int64_t kSparseQuantum = kTile;
 constexpr size_t kAlign = 256;
 constexpr double kUnitFixedUs = 14.7;           // Selector path estimates, see select_unit_path
 constexpr double kUnitUsPerPos = 6.0e-4;
@@ -103,7 +89,7 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
     const bool small = units * (int64_t)kv.max_len <= kSmallDenseRows;
     const int64_t target = sparse ? kSparseTargetWorkgroups
                                   : (paged ? kPagedTargetWorkgroups
-                                           : (small ? SFI_SMALL_WG : kTargetWorkgroups));
+                                           : (small ? kSmallTargetWorkgroups : kTargetWorkgroups));
     const int64_t per_unit = ceil_div(target, units);
     int64_t split = ceil_div(ceil_div(slots, per_unit), quantum) * quantum;
     if ((sparse || paged) && split > kTabMax) split = kTabMax;
@@ -149,11 +135,7 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
 // 18 us at 2K positions (G = 4), 42 us at 32K, 126 us at 128K, 209 us at 128K with G = 8,
 // 66 us at 64K with G = 1; chunked 30 us at 32 KB of logits in all, 35 us at 4 MB, 37 us at
 // 17 MB, 57 us at 67 MB, 81 us at 134 MB.
-#ifndef SFI_SELECT_PATH
-#define SFI_SELECT_PATH -1                      // -1: estimate; 0: chunked; 1: one per unit
-#endif
 bool select_unit_path(const sfi_kv_desc& kv) {
-    if (SFI_SELECT_PATH >= 0) return SFI_SELECT_PATH == 1;
     const double G = (double)kv.num_q_heads / kv.num_kv_heads;
     const double all_mb = (double)kv.batch * kv.num_q_heads * kv.max_len * 4.0 / 1e6;
     const double t_unit = kUnitFixedUs + (kUnitUsPerPos + kUnitUsPerPosHead * G) * kv.max_len;

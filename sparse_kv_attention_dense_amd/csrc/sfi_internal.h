@@ -12,10 +12,7 @@ namespace sfi {
 
 constexpr int kThreads = 256;        // 4 wavefronts of 64
 constexpr int kWaves = 4;
-#ifndef SFI_SPARSE_WAVES
-#define SFI_SPARSE_WAVES 4
-#endif
-constexpr int kSparseWaves = SFI_SPARSE_WAVES;   // wavefronts of a fast-step workgroup
+constexpr int kSparseWaves = 4;      // wavefronts of a fast-step workgroup
 constexpr int kBtPer = 12;           // staged block-table entries per thread (fast step, paged)
 constexpr int kTile = 32;            // slots per wavefront iteration (two 16-row MFMA blocks)
 constexpr int kSplitQuantum = kTile * kWaves;
@@ -24,6 +21,11 @@ constexpr int kMaxSplits = 1024;     // partial records per (b, h) that the comb
 constexpr int kMaxG = 16;            // query heads per KV head (MFMA N dimension)
 constexpr int kMaxSelG = 64;         // logit rows per KV head that the Selector and the mask
                                      // take (query heads, or query heads x window queries)
+// The host stages a fast step's block table when it has at most kBtPer * kThreads entries, and
+// the kernel loads kBtPer entries per thread of its own workgroup; the routing prologue gives
+// each of the kMaxG * d / 8 (head, 8-element piece) pairs of a group one thread.
+static_assert(kSparseWaves * 64 >= kThreads, "a fast-step workgroup stages the whole block table");
+static_assert(kSparseWaves * 64 >= kMaxG * 128 / 8, "routing needs one thread per head piece");
 
 struct AttnArgs {
     const void* k;

@@ -309,10 +309,7 @@ __global__ void __launch_bounds__(kThreads) refine_nms_kernel(SelArgs a) {
 // whose score is below the largest is decayed by keep_cross.  The results become the keys, and
 // the digit-0 histogram of each unit is built from them (one LDS histogram, reused head by
 // head).  A chunk is split over kCrossParts workgroups so the launch fills the chip.
-#ifndef SFI_CROSS_PARTS
-#define SFI_CROSS_PARTS 4
-#endif
-constexpr int kCrossParts = SFI_CROSS_PARTS;
+constexpr int kCrossParts = 4;
 constexpr int kCrossPer = kPerThread / kCrossParts;    // positions per thread
 static_assert(kPerThread % kCrossParts == 0, "a chunk part holds whole rows of threads");
 constexpr int kCrossRegHeads = 16;                      // heads whose scores stay in registers

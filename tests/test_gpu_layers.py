@@ -1,26 +1,34 @@
-"""The layer-wise slow step (sfi_slow_step_layers) against the per-layer calls in sequence.
+"""The layer-wise slow step (sfi_slow_step_layers) against the fp64 oracle and against the
+per-layer calls in sequence.
 
-Five layers share two ring slots, so every slot is reused; the Selector, the mask and (when
-asked) the Reorg run on a second stream.  Every output must equal the sequential result bit for
-bit (the kernels are deterministic), and a fast step queued on the primary stream right after
-the call must see the last layer's indices and compact segment (the completion barrier).
+Five layers share the ring slots, so every slot is reused; the Selector, the mask and (when
+asked) the Reorg run on a second stream.  Every layer's out and lse are compared with the
+oracle's dense step, its selection with the oracle's Selector run on the oracle's own logits
+(sets equal up to near-ties at the Top-K boundary), its mask with the oracle's mask and its
+compact segment with the oracle's Reorg of the selection; then every output must also equal
+the sequential result bit for bit (the kernels are deterministic), and a fast step queued on
+the primary stream right after the call must see the last layer's indices and compact segment
+(the completion barrier) and match the oracle's fast step.
 """
+import numpy as np
 import pytest
 import torch
 
 from sparse_kv_attention_dense_amd import binding as B
 from sparse_kv_attention_dense_amd import synth
 
-from gpu_util import DEV, desc_for, round4, say
+from gpu_util import (DEV, assert_close_out, assert_close_rel, compare_index_sets, desc_for,
+                      oracle_cache, round4, say, tolerances)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,n_slots,reorg", [("gqa8_512k", 2, False), ("ragged_paged_b16", 2, True),
-                                                ("gqa4_32k", 1, True)])
-def test_layered_slow_step_matches_sequential(name, n_slots, reorg):
+@pytest.mark.parametrize("name,n_slots,reorg,k_sel", [("gqa8_512k", 2, False, 1024),
+                                                      ("ragged_paged_b16", 2, True, None),
+                                                      ("gqa4_32k", 1, True, None)])
+def test_layered_slow_step_matches_oracle_and_sequential(orc, name, n_slots, reorg, k_sel):
     base = synth.WORKLOADS[name]
-    wl = base.scaled(7001, B=min(base.B, 3), len_lo=3000 if base.len_lo else None)
+    wl = base.scaled(7001, B=min(base.B, 3), len_lo=3000 if base.len_lo else None, k_sel=k_sel)
     n_layers = 5
     say(f"[layers] {wl.name} layers={n_layers} slots={n_slots} reorg={reorg}")
     lays = [synth.make_layer(wl, li, device=DEV) for li in range(n_layers)]
@@ -89,6 +97,37 @@ def test_layered_slow_step_matches_sequential(name, n_slots, reorg):
     B.sfi_sparse_decode(d1, q1, ref["idx"][-1], istride, ref["n_idx"][-1], wl.n_recent,
                         ref["mask"][-1], fast_ref, None, dense_ws)
     torch.cuda.synchronize()
+
+    # every layer against the oracle
+    tol = tolerances(wl)
+    lens_host = lays[0].len0_host
+    swaps = 0
+    for l in range(n_layers):
+        cache = oracle_cache(orc, lays[l], lens_host)
+        eo, el, ez = orc.dense(cache, qs[l])
+        assert_close_out(got["out"][l].cpu().numpy(), eo, tol["out"], f"layer {l} out")
+        assert_close_rel(got["lse"][l].cpu().numpy(), el, tol["rel"], f"layer {l} lse")
+        eidx, en, f = orc.select(lens_host, wl.Hq, wl.Hkv, ez, wl.n_sink, wl.n_recent, wl.k_sel,
+                                 istride, want_f=True)
+        swaps += compare_index_sets(got["idx"][l], got["n_idx"][l], eidx, en, f, lens_host,
+                                    wl.n_sink, wl.n_recent, wl.k_sel, exact=False)
+        ehm = orc.sink_mask(ez[:, :, 0], el, frac)
+        assert (got["mask"][l].cpu().numpy() == ehm).all(), f"mask differs at layer {l}"
+        if reorg:
+            ck, cv, cpos = orc.reorg(cache, got["idx"][l], got["n_idx"][l])
+            gk, gv, gp = (x.cpu() for x in got["seg"][l])
+            as_bits = (lambda t: t.view(torch.int16).numpy().view(np.uint16)) \
+                if gk.dtype == torch.bfloat16 else (lambda t: t.numpy())
+            assert (gp.numpy() == cpos).all(), f"segment positions differ at layer {l}"
+            live = cpos >= 0
+            assert (as_bits(gk)[live] == ck[live]).all(), f"segment keys differ at layer {l}"
+            assert (as_bits(gv)[live] == cv[live]).all(), f"segment values differ at layer {l}"
+        if l == n_layers - 1:
+            lens_t = [n + 1 for n in lens_host]
+            xo, _ = orc.sparse(oracle_cache(orc, lays[l], lens_t), q1, eidx, en, wl.n_recent, ehm)
+            assert_close_out(fast_got.cpu().numpy(), xo, tol["out"], "fast step after the call")
+    say(f"    oracle: every layer's out, lse, selection ({swaps} near-tie swaps), mask"
+        f"{' and segment' if reorg else ''} agree")
 
     for key in ("out", "lse", "idx", "n_idx", "mask"):
         for l in range(n_layers):
