@@ -25,7 +25,9 @@
  *
  * Conventions shared by every call
  *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
- *     never allocates, keeps no pointer after a call returns, and holds no global state.
+ *     never allocates, keeps no pointer after a call returns, and holds no global state;
+ *     the one exception is sfi_sparse_decode_noalloc, which runs on a static device array of
+ *     the library instead of a caller workspace (see its declaration).
  *   - Calls are asynchronous on `stream` (0 = the null stream) and never synchronise the
  *     host.  A returned SFI_OK means the arguments passed host-side validation and the
  *     launches were queued; device data (lengths, block tables, indices) is trusted.
@@ -54,7 +56,9 @@ typedef enum sfi_status {
     SFI_E_INVALID = -1,      /* null pointer, inconsistent sizes, bad alignment */
     SFI_E_UNSUPPORTED = -2,  /* well-formed but not built: head_dim, dtype, group size */
     SFI_E_WORKSPACE = -3,    /* ws is NULL, misaligned or smaller than sfi_workspace_bytes() */
-    SFI_E_HIP = -4           /* the HIP runtime reported an error while launching */
+    SFI_E_HIP = -4,          /* the HIP runtime reported an error while launching */
+    SFI_E_SCRATCH = -5       /* sfi_sparse_decode_noalloc: the step needs more than the
+                                library's static scratch array holds */
 } sfi_status;
 
 typedef enum sfi_dtype { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
@@ -202,6 +206,24 @@ sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
                              int32_t n_recent, const uint8_t* head_mask,
                              float* out, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The fast step for callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same computation, arguments and kernels as
+ * sfi_sparse_decode, but the partial records live in a library-owned static device array of
+ * SFI_NOALLOC_SCRATCH_BYTES per GPU instead of a caller workspace: no allocation of any kind
+ * happens in the call.  The first call on a device (that device current) looks up the array's
+ * device address once; each GPU holds its own array until the process ends.
+ *   SFI_E_SCRATCH when the step's partial records need more than SFI_NOALLOC_SCRATCH_BYTES
+ *   (sfi_workspace_bytes(kv, SFI_OP_SPARSE, idx_stride, n_recent) tells the need); every
+ *   other error as for sfi_sparse_decode.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a GPU (other streams,
+ * other threads) race and must be ordered by the caller.  The records are written in full by
+ * every call before they are read, so nothing needs clearing between calls. */
+#define SFI_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+sfi_status sfi_sparse_decode_noalloc(const sfi_kv_desc* kv, const void* q,
+                                     const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
+                                     int32_t n_recent, const uint8_t* head_mask,
+                                     float* out, float* lse, hipStream_t stream);
 
 /* Sparse decode step with inline group routing.  SinkRouter Sec. 4 (decide per KV group,
  * before loading the group's history, whether it is in the sink-dominant regime, and if so

@@ -16,11 +16,13 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsfi.so")
 
 SFI_OK, SFI_E_INVALID, SFI_E_UNSUPPORTED, SFI_E_WORKSPACE, SFI_E_HIP = 0, -1, -2, -3, -4
+SFI_E_SCRATCH = -5
+SFI_NOALLOC_SCRATCH_BYTES = 8 << 20
 SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SELECT_REFINED = 0, 1, 2, 3
 
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_select_refined", "sfi_sink_bypass_mask",
-            "sfi_sparse_decode",
+            "sfi_sparse_decode", "sfi_sparse_decode_noalloc",
             "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
             "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_status_string")
 
@@ -66,6 +68,7 @@ def lib():
         L.sfi_select.argtypes = [D, P, i64, i32, i32, i32, P, i32, P, P, ctypes.c_size_t, P]
         L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
         L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.sfi_sparse_decode_noalloc.argtypes = [D, P, P, i32, P, i32, P, P, P, P]
         L.sfi_sparse_decode_routed.argtypes = [D, P, P, i32, P, i32, P, P, ctypes.c_float, P,
                                                P, P, P, ctypes.c_size_t, P]
         L.sfi_slow_step_layers.argtypes = [i32, D, P, P, P, i32, P, i64, P, ctypes.c_size_t, P,
@@ -332,6 +335,21 @@ def sfi_sparse_decode(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: in
                                    int(n_recent), _ptr(head_mask), _ptr(out), _ptr(lse),
                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "sfi_sparse_decode")
+
+
+def sfi_sparse_decode_noalloc(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int,
+                              head_mask, out, lse, stream=None):
+    desc.need_cache("sfi_sparse_decode_noalloc")
+    _buf(q, "q", desc.cache_dtype, desc.heads * desc.c.head_dim)
+    _buf(n_idx, "n_idx", _I32, desc.units)
+    _buf(head_mask, "head_mask", _U8, desc.heads, optional=True)
+    _buf(out, "out", _F32, desc.heads * desc.c.head_dim)
+    _buf(lse, "lse", _F32, desc.heads, optional=True)
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
+    _check(lib().sfi_sparse_decode_noalloc(desc.ref, _ptr(q), _ptr(idx), int(idx_stride),
+                                           _ptr(n_idx), int(n_recent), _ptr(head_mask), _ptr(out),
+                                           _ptr(lse), _stream(stream)),
+           "sfi_sparse_decode_noalloc")
 
 
 def sfi_sparse_decode_routed(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int,

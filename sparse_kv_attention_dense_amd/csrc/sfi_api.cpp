@@ -5,6 +5,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "sfi.h"
 #include "sfi_internal.h"
@@ -365,6 +367,59 @@ SFI_EXPORT sfi_status sfi_sparse_decode(const sfi_kv_desc* kv, const void* q,
 
 namespace {
 
+// ---- the fast step on a library-owned scratch array (sfi_sparse_decode_noalloc) ------------
+// Each GPU the library runs on holds its own copy of `scratch` until the process ends.  Host
+// code never uses the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kScratchBytes = SFI_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kScratchDevices = 256;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mutex;
+
+sfi_status scratch_of_current_device(void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SFI_E_HIP;
+    if (dev >= kScratchDevices) return SFI_E_UNSUPPORTED;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SFI_E_HIP;
+            if (((uintptr_t)p % kAlign) != 0) return SFI_E_HIP;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *addr = p;
+    return SFI_OK;
+}
+
+}  // namespace
+
+SFI_EXPORT sfi_status sfi_sparse_decode_noalloc(const sfi_kv_desc* kv, const void* q,
+                                                const int32_t* idx, int32_t idx_stride,
+                                                const int32_t* n_idx, int32_t n_recent,
+                                                const uint8_t* head_mask, float* out, float* lse,
+                                                hipStream_t stream) {
+    // host-side validation and the size check come before any HIP call
+    sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    if (!q || !out || !idx || !n_idx || !aligned(q, 16) || !aligned(out, 16)) return SFI_E_INVALID;
+    if (idx_stride < 1 || n_recent < 0) return SFI_E_INVALID;
+    AttnPlan plan;
+    st = plan_attention(*kv, true, idx_stride, n_recent, &plan);
+    if (st != SFI_OK) return st;
+    if (plan.bytes > kScratchBytes) return SFI_E_SCRATCH;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != SFI_OK) return st;
+    return sparse_impl(kv, q, idx, idx_stride, n_idx, n_recent, head_mask, nullptr, 1.f, nullptr,
+                       nullptr, nullptr, out, lse, ws, kScratchBytes, stream);
+}
+
+namespace {
+
 sfi_status prep_reorg(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
                       const int32_t* n_idx, void* ck, void* cv, int32_t* cpos, ReorgArgs* out) {
     const sfi_status st = check_desc(kv, true);
@@ -593,6 +648,8 @@ SFI_EXPORT const char* sfi_status_string(sfi_status s) {
         case SFI_E_UNSUPPORTED: return "SFI_E_UNSUPPORTED: head_dim, dtype, group size or length not supported";
         case SFI_E_WORKSPACE: return "SFI_E_WORKSPACE: workspace missing, misaligned or too small";
         case SFI_E_HIP: return "SFI_E_HIP: HIP runtime error at launch";
+        case SFI_E_SCRATCH:
+            return "SFI_E_SCRATCH: the step needs more than the library's static scratch array holds";
     }
     return "unknown sfi_status";
 }

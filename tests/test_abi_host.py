@@ -154,8 +154,28 @@ def test_sparse_validation(L):
     assert L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 1 << 30, 0) == 0
 
 
+def test_noalloc_fast_step_validation(L):
+    """The fast step on the library's static scratch array validates like sfi_sparse_decode and
+    rejects, before any HIP call, a step whose partial records would not fit the array."""
+    na = lambda dd, **k: L.sfi_sparse_decode_noalloc(ctypes.byref(dd), FAKE, k.get("idx", FAKE),
+                                                     k.get("istride", 2052), FAKE,
+                                                     k.get("nr", 256), None, FAKE, None, None)
+    d = _desc()
+    assert L.sfi_workspace_bytes(ctypes.byref(d), B.SFI_OP_SPARSE, 2052, 256) <= \
+        B.SFI_NOALLOC_SCRATCH_BYTES
+    assert na(d, idx=None) == B.SFI_E_INVALID
+    assert na(d, istride=0) == B.SFI_E_INVALID
+    assert na(d, nr=-1) == B.SFI_E_INVALID
+    assert na(_desc(head_dim=96)) == B.SFI_E_UNSUPPORTED
+    big = _desc(batch=4096, n_cap=4096)                 # 32768 units: records far past 8 MiB
+    need = L.sfi_workspace_bytes(ctypes.byref(big), B.SFI_OP_SPARSE, 2052, 256)
+    assert need > B.SFI_NOALLOC_SCRATCH_BYTES
+    assert na(big) == B.SFI_E_SCRATCH
+
+
 def test_status_strings(L):
-    for s in (B.SFI_OK, B.SFI_E_INVALID, B.SFI_E_UNSUPPORTED, B.SFI_E_WORKSPACE, B.SFI_E_HIP):
+    for s in (B.SFI_OK, B.SFI_E_INVALID, B.SFI_E_UNSUPPORTED, B.SFI_E_WORKSPACE, B.SFI_E_HIP,
+              B.SFI_E_SCRATCH):
         assert B.sfi_status_string(s).startswith("SFI_")
     assert "unknown" in B.sfi_status_string(42)
 
