@@ -64,7 +64,8 @@ typedef enum sfi_status {
 typedef enum sfi_dtype { SFI_F32 = 0, SFI_BF16 = 1 } sfi_dtype;
 
 typedef enum sfi_op {
-    SFI_OP_DENSE = 0, SFI_OP_SELECT = 1, SFI_OP_SPARSE = 2, SFI_OP_SELECT_REFINED = 3
+    SFI_OP_DENSE = 0, SFI_OP_SELECT = 1, SFI_OP_SPARSE = 2, SFI_OP_SELECT_REFINED = 3,
+    SFI_OP_SLOW = 4
 } sfi_op;
 
 /* Parameters of the full Selector (sfi_select_refined).  SFI Sec. 5.1 gives lambda_clip = 0.02,
@@ -151,6 +152,29 @@ sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_
                       int32_t n_sink, int32_t n_recent, int32_t k_sel,
                       int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole slow step in one call: sfi_dense_decode with logits, then sfi_select, then (when
+ * head_mask is not NULL) sfi_sink_bypass_mask, with the same arguments and results as those
+ * three calls up to rounding.  SFI Sec. 4.2 (slow-step kernels expose what the GPU-resident
+ * Selector needs) and Sec. 3.2 (the evidence is each head's softmax renormalised over the
+ * allowed set J): the dense kernels also keep each split's log-sum-exp over J, so the Selector
+ * does not read the logits a second time for it (one pass over the logits of J and one
+ * launch fewer than the separate calls).  Because the Selector's normaliser over J comes from
+ * the dense accumulators instead of the written logits, its evidence can differ from
+ * sfi_select's in the last bits: selections agree except at exact-tie precision.
+ * logits and lse are required.  G <= 16 (the dense step's limit).  ws: at least
+ * sfi_workspace_bytes(kv, SFI_OP_SLOW, 0, 0) bytes, no initialisation needed.
+ * dense_done: a HIP event created by the caller, or NULL; when given it is recorded on
+ * `stream` after the dense step's kernels and before the Selector's (for callers that time
+ * the dense step or start other work after it, as the layer-wise schedule of SFI Sec. 4.1
+ * does).  Launches: the dense step's two, the Selector's four (or one on short contexts), the
+ * mask's one. */
+sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
+                         float* logits, int64_t logit_stride,
+                         int32_t n_sink, int32_t n_recent, int32_t k_sel,
+                         int32_t* idx, int32_t idx_stride, int32_t* n_idx,
+                         float mask_frac, uint8_t* head_mask,
+                         void* ws, size_t ws_bytes, hipEvent_t dense_done, hipStream_t stream);
 
 /* The full Selector: sfi_select with the cache-aware prior, reverse-KL fusion and the
  * log-score refinements.  SFI Sec. 3.2 ("Cache-aware prior on allowed positions", "Position
@@ -316,7 +340,8 @@ sfi_status sfi_slow_step_layers(
 
 /* Workspace bytes needed by one call of `op` on this descriptor.  idx_stride and n_recent
  * (index capacity and recent window) are used by SFI_OP_SPARSE only; SFI_OP_DENSE,
- * SFI_OP_SELECT and SFI_OP_SELECT_REFINED size from the descriptor (max_len) alone.  Returns 0 when the descriptor
+ * SFI_OP_SELECT, SFI_OP_SELECT_REFINED and SFI_OP_SLOW (sfi_slow_step) size from the
+ * descriptor (max_len) alone.  Returns 0 when the descriptor
  * or op is invalid. */
 size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,
                            int32_t n_recent);

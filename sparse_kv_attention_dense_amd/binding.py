@@ -19,9 +19,9 @@ SFI_OK, SFI_E_INVALID, SFI_E_UNSUPPORTED, SFI_E_WORKSPACE, SFI_E_HIP = 0, -1, -2
 SFI_E_SCRATCH = -5
 SFI_NOALLOC_SCRATCH_BYTES = 8 << 20
 SFI_F32, SFI_BF16 = 0, 1
-SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SELECT_REFINED = 0, 1, 2, 3
+SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SELECT_REFINED, SFI_OP_SLOW = 0, 1, 2, 3, 4
 
-EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_select_refined", "sfi_sink_bypass_mask",
+EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_slow_step", "sfi_select_refined", "sfi_sink_bypass_mask",
             "sfi_sparse_decode", "sfi_sparse_decode_noalloc",
             "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
             "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_status_string")
@@ -66,6 +66,8 @@ def lib():
         D = ctypes.POINTER(sfi_kv_desc)
         L.sfi_dense_decode.argtypes = [D, P, P, P, P, i64, P, ctypes.c_size_t, P]
         L.sfi_select.argtypes = [D, P, i64, i32, i32, i32, P, i32, P, P, ctypes.c_size_t, P]
+        L.sfi_slow_step.argtypes = [D, P, P, P, P, i64, i32, i32, i32, P, i32, P, ctypes.c_float,
+                                    P, P, ctypes.c_size_t, P, P]
         L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
         L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.sfi_sparse_decode_noalloc.argtypes = [D, P, P, i32, P, i32, P, P, P, P]
@@ -275,6 +277,25 @@ def sfi_dense_decode(desc: KVDesc, q, out, lse, logits, logit_stride: int, ws, s
                                   _stream(stream)), "sfi_dense_decode")
 
 
+def sfi_slow_step(desc: KVDesc, q, out, lse, logits, logit_stride: int, n_sink: int,
+                  n_recent: int, k_sel: int, idx, idx_stride: int, n_idx, mask_frac: float,
+                  head_mask, ws, dense_done=None, stream=None):
+    """dense_done: a torch.cuda.Event (recorded after the dense kernels) or None."""
+    desc.need_cache("sfi_slow_step")
+    _buf(q, "q", desc.cache_dtype, desc.heads * desc.c.head_dim)
+    _buf(out, "out", _F32, desc.heads * desc.c.head_dim)
+    _buf(lse, "lse", _F32, desc.heads)
+    _selector_bufs(desc, logits, logit_stride, idx, idx_stride, n_idx, ws)
+    _buf(head_mask, "head_mask", _U8, desc.heads, optional=True)
+    st = _stream(stream)
+    ev = _event_handle(dense_done, stream) if dense_done is not None else None
+    _check(lib().sfi_slow_step(desc.ref, _ptr(q), _ptr(out), _ptr(lse), _ptr(logits),
+                               int(logit_stride), int(n_sink), int(n_recent), int(k_sel),
+                               _ptr(idx), int(idx_stride), _ptr(n_idx), float(mask_frac),
+                               _ptr(head_mask), _ptr(ws), ws.numel() * ws.element_size(),
+                               ev, st), "sfi_slow_step")
+
+
 def _selector_bufs(desc: KVDesc, logits, logit_stride: int, idx, idx_stride: int, n_idx, ws):
     _buf(logits, "logits", _F32, desc.heads * int(logit_stride))
     _buf(idx, "idx", _I32, desc.units * int(idx_stride))
@@ -460,8 +481,8 @@ def workspace(desc: KVDesc, idx_stride: int = 1, n_recent: int = 0, device="cuda
     """A workspace large enough for every op on this descriptor (plumbing:
     torch allocates it once; the library itself never allocates).  refined: also for
     sfi_select_refined."""
-    ops = (SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE) + ((SFI_OP_SELECT_REFINED,) if refined
-                                                          else ())
+    ops = (SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SLOW) + (
+        (SFI_OP_SELECT_REFINED,) if refined else ())
     n = max(sfi_workspace_bytes(desc, op, idx_stride, n_recent) for op in ops)
     if n == 0:
         raise SfiError(SFI_E_INVALID, "workspace")

@@ -81,7 +81,7 @@ struct AttnPlan {
 // Split plan: per (b, KV head) unit, nsplit workgroups of split_len slots each, about
 // kTargetWorkgroups (dense) or kSparseTargetWorkgroups (sparse) per launch in total.
 sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride, int64_t n_recent,
-                          AttnPlan* p) {
+                          AttnPlan* p, bool lse_j = false) {
     const bool paged = kv.block_table != nullptr;
     const int64_t units = (int64_t)kv.batch * kv.num_kv_heads;
     const int64_t G = kv.num_q_heads / kv.num_kv_heads;
@@ -105,7 +105,8 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
     if (!sparse && nsplit * units >= (int64_t(1) << 31)) return SFI_E_UNSUPPORTED;   // 1-D grid
     p->split_len = (int)split;
     p->nsplit = (int)nsplit;
-    p->rec = (int)(ceil_div(G * (kv.head_dim + 2), 4) * 4);
+    // records: acc [G][d], (m, l) [G], and for the fused slow step (m, l) over J [G]
+    p->rec = (int)(ceil_div(G * (kv.head_dim + (lse_j ? 4 : 2)), 4) * 4);
     int64_t tab = 0;
     if (sparse) {
         tab = split * 4 + split;                            // rows, then attend flags
@@ -276,6 +277,7 @@ sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit
     a->prior_decay = a->tail_frac = a->tail_brake = 0.f;
     a->zpart = nullptr;
     a->nms = nullptr;
+    a->lse_j = nullptr;
     return SFI_OK;
 }
 
@@ -610,8 +612,79 @@ SFI_EXPORT sfi_status sfi_slow_step_layers(
     return SFI_OK;
 }
 
+namespace {
+
+// Workspace of the fused slow step: the dense records (with the pairs over J), then lse_j
+// [B][Hq], then the Selector's own layout.
+struct SlowLayout {
+    AttnPlan dense;
+    SelPlan sel;
+    size_t off_lse_j = 0, off_sel = 0, bytes = 0;
+};
+
+sfi_status plan_slow(const sfi_kv_desc& kv, SlowLayout* p) {
+    const sfi_status st = plan_attention(kv, false, 0, 0, &p->dense, true);
+    if (st != SFI_OK) return st;
+    plan_select(kv, &p->sel);
+    p->off_lse_j = p->dense.bytes;
+    p->off_sel = p->off_lse_j + align_up((size_t)kv.batch * kv.num_q_heads * sizeof(float));
+    p->bytes = p->off_sel + p->sel.bytes;
+    return SFI_OK;
+}
+
+}  // namespace
+
+SFI_EXPORT sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
+                                    float* logits, int64_t logit_stride, int32_t n_sink,
+                                    int32_t n_recent, int32_t k_sel, int32_t* idx,
+                                    int32_t idx_stride, int32_t* n_idx, float mask_frac,
+                                    uint8_t* head_mask, void* ws, size_t ws_bytes,
+                                    hipEvent_t dense_done, hipStream_t stream) {
+    sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    if (!logits || !lse) return SFI_E_INVALID;
+    if (kv->num_q_heads / kv->num_kv_heads > kMaxG) return SFI_E_UNSUPPORTED;
+    SlowLayout lay;
+    st = plan_slow(*kv, &lay);
+    if (st != SFI_OK) return st;
+    st = check_ws(ws, ws_bytes, lay.bytes);
+    if (st != SFI_OK) return st;
+    unsigned char* base = (unsigned char*)ws;
+    AttnArgs da;
+    // the dense step validates against its own part of the workspace
+    st = prep_dense(kv, q, out, lse, logits, logit_stride, ws, lay.off_lse_j, &da);
+    if (st != SFI_OK) return st;
+    SelArgs sa;
+    st = prep_select(kv, logits, logit_stride, n_sink, n_recent, k_sel, idx, idx_stride, n_idx,
+                     base + lay.off_sel, lay.sel.bytes, &sa);
+    if (st != SFI_OK) return st;
+    MaskArgs ma;
+    if (head_mask) {
+        st = prep_mask(kv, logits, logit_stride, lse, mask_frac, head_mask, &ma);
+        if (st != SFI_OK) return st;
+    }
+    fill_plan_args(lay.dense, ws, &da);
+    da.lse_j = (float*)(base + lay.off_lse_j);
+    da.n_sink = n_sink;
+    da.n_recent = n_recent;
+    da.sel_hist = sa.hist;
+    sa.lse_j = da.lse_j;
+    if (launch_dense(kv, da, stream) != SFI_OK) return SFI_E_HIP;
+    if (dense_done && hipEventRecord(dense_done, stream) != hipSuccess) return SFI_E_HIP;
+    if (launch_select(sa, stream) != hipSuccess) return SFI_E_HIP;
+    if (head_mask && launch_sink_mask(ma, stream) != hipSuccess) return SFI_E_HIP;
+    return SFI_OK;
+}
+
 SFI_EXPORT size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride,
                                       int32_t n_recent) {
+    if (op == SFI_OP_SLOW) {
+        if (check_desc(kv, true) != SFI_OK) return 0;
+        if (kv->num_q_heads / kv->num_kv_heads > kMaxG) return 0;
+        SlowLayout lay;
+        if (plan_slow(*kv, &lay) != SFI_OK) return 0;
+        return lay.bytes;
+    }
     if (op == SFI_OP_SELECT) {
         if (check_desc(kv, false) != SFI_OK) return 0;
         SelPlan p;

@@ -163,6 +163,32 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
         a.out[((int64_t)b * a.Hq + i) * D + tid] = zero ? 0.f : At / Lt;
         if (tid == 0 && a.lse) a.lse[b * a.Hq + i] = zero ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
     }
+    if constexpr (!SPARSE) {
+        if (a.lse_j) {
+            // log-sum-exp over the Selector's allowed set: the same merge over the (m, l) pairs
+            // the splits kept for positions of J, by the last wavefront
+            const int w = tid >> 6, lane = tid & 63;
+            if (w == kThreads / 64 - 1) {
+                float Mj = -INFINITY;
+                for (int s = lane; s < S; s += 64)
+                    Mj = fmaxf(Mj, base[(int64_t)s * rec + G * D + 2 * G + 2 * g]);
+                for (int o = 32; o >= 1; o >>= 1) Mj = fmaxf(Mj, __shfl_xor(Mj, o));
+                const float Mu = (Mj == -INFINITY) ? 0.f : Mj;
+                float Lj = 0.f;
+                for (int s = lane; s < S; s += 64) {
+                    const float* r = base + (int64_t)s * rec + G * D + 2 * G + 2 * g;
+                    Lj += exp2_fast(r[0] - Mu) * r[1];
+                }
+                for (int o = 32; o >= 1; o >>= 1) Lj += __shfl_xor(Lj, o);
+                if (lane == 0) a.lse_j[b * a.Hq + i] = Lj > 0.f ? (Mj + log2f(Lj)) * kLn2 : -INFINITY;
+            }
+            // the Selector's digit-0 histogram of this head's KV group starts empty
+            if (g == 0 && a.sel_hist) {
+                uint32_t* hh = a.sel_hist + (int64_t)(b * a.Hkv + h) * kSelHistBins;
+                for (int t = tid; t < kSelHistBins; t += kThreads) hh[t] = 0u;
+            }
+        }
+    }
     __syncthreads();
 }
 
@@ -273,7 +299,7 @@ struct Cfg {
     static constexpr bool kHalfV = BF && !SPARSE;
     static constexpr int kVRows = kHalfV ? kTile / 2 : kTile;      // V rows staged at a time
     static constexpr int kVStage = BF ? kNW * kVRows * kVRow : 0;
-    static constexpr int kRed = kNW * kMaxG * (D + 2) * 4;         // cross-wave merge
+    static constexpr int kRed = kNW * kMaxG * (D + 4) * 4;         // cross-wave merge
     // dense: per-wavefront staging of fp32 logits, kZRows (head, tile) rows of 32 positions;
     // 120 rows (15 KB) for bf16 d = 128 keeps two workgroups per CU in 160 KB of LDS
     static constexpr int kZRows = (BF && D == 128) ? 120 : 64;
@@ -533,6 +559,11 @@ attention_kernel(AttnArgs a) {
     }
 
     float m_run = -INFINITY, l_run = 0.f;
+    // dense step of sfi_slow_step: the same online sums over the positions of the Selector's
+    // allowed set J = [n_sink, len_b - n_recent) only (for its log-sum-exp over J)
+    const bool track_j = !SPARSE && a.lse_j != nullptr;
+    const int j_lo = a.n_sink, j_hi = len_b - a.n_recent;
+    float mj_run = -INFINITY, lj_run = 0.f;
     f32x4 acc[D / 16];
 #pragma unroll
     for (int mb = 0; mb < D / 16; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -720,6 +751,32 @@ attention_kernel(AttnArgs a) {
                 p[st][i] = exp2_fast(sv[st][i] - m_use);
                 l_run += p[st][i];
             }
+        if (track_j) {
+            float tj = -INFINITY;
+            bool inj[2][4];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int slot = sb + 16 * st + 4 * q4 + i;
+                    inj[st][i] = slot >= j_lo && slot < j_hi && sv[st][i] != -INFINITY;
+                    if (inj[st][i]) tj = fmaxf(tj, sv[st][i]);
+                }
+            tj = fmaxf(tj, __shfl_xor(tj, 16));
+            tj = fmaxf(tj, __shfl_xor(tj, 32));
+            const float mj_new = fmaxf(mj_run, tj);
+            const float mj_use = (mj_new == -INFINITY) ? 0.f : mj_new;
+            lj_run *= exp2_fast(mj_run - mj_use);
+            mj_run = mj_new;
+            // where J's running maximum is the overall one (every split without sink or recent
+            // positions) the weights are the ones just computed
+            const bool same = mj_use == m_use;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (inj[st][i]) lj_run += same ? p[st][i] : exp2_fast(sv[st][i] - mj_use);
+        }
         if constexpr (BF && !C::kHalfV) {
             // P^T as the B operand: virtual k = 8*q4 + e maps to slot 4*q4 + e of block 0
             // (e < 4) or of block 1 (e >= 4); the V^T A operand uses the same map.
@@ -814,12 +871,16 @@ attention_kernel(AttnArgs a) {
     }
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    lj_run += __shfl_xor(lj_run, 16);
+    lj_run += __shfl_xor(lj_run, 32);
 
     // ---- merge the four wavefronts, write this split's partial -----------------------------
+    // per wavefront and head: acc [D], (m, l), (m, l) over J
+    constexpr int kRS = D + 4;
     __syncthreads();
-    float* red = C::kRedInZ ? zstage : (float*)raw;   // [kNW][kMaxG][D+2]
+    float* red = C::kRedInZ ? zstage : (float*)raw;   // [kNW][kMaxG][D+4]
     if (n16 < G) {
-        float* rp = red + (w * kMaxG + n16) * (D + 2);
+        float* rp = red + (w * kMaxG + n16) * kRS;
 #pragma unroll
         for (int mb = 0; mb < D / 16; ++mb)
 #pragma unroll
@@ -827,6 +888,8 @@ attention_kernel(AttnArgs a) {
         if (q4 == 0) {
             rp[D] = m_run;
             rp[D + 1] = l_run;
+            rp[D + 2] = mj_run;
+            rp[D + 3] = lj_run;
         }
     }
     __syncthreads();
@@ -836,26 +899,28 @@ attention_kernel(AttnArgs a) {
             const int g = e / D, dim = e - g * D;
             float M = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < C::kNW; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
+            for (int ww = 0; ww < C::kNW; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * kRS + D]);
             const float Mu = (M == -INFINITY) ? 0.f : M;
             float s = 0.f;
 #pragma unroll
             for (int ww = 0; ww < C::kNW; ++ww)
-                s += exp2_fast(red[(ww * kMaxG + g) * (D + 2) + D] - Mu) * red[(ww * kMaxG + g) * (D + 2) + dim];
+                s += exp2_fast(red[(ww * kMaxG + g) * kRS + D] - Mu) * red[(ww * kMaxG + g) * kRS + dim];
             part[e] = s;
         }
-        if (tid < G) {
-            const int g = tid;
+        // (m, l) of every head, and with lse_j the (m, l) over J after them
+        const int npair = track_j ? 2 * G : G;
+        if (tid < npair) {
+            const int g = tid % G, off = tid < G ? D : D + 2;
             float M = -INFINITY;
 #pragma unroll
-            for (int ww = 0; ww < C::kNW; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * (D + 2) + D]);
+            for (int ww = 0; ww < C::kNW; ++ww) M = fmaxf(M, red[(ww * kMaxG + g) * kRS + off]);
             const float Mu = (M == -INFINITY) ? 0.f : M;
             float L = 0.f;
 #pragma unroll
             for (int ww = 0; ww < C::kNW; ++ww)
-                L += exp2_fast(red[(ww * kMaxG + g) * (D + 2) + D] - Mu) * red[(ww * kMaxG + g) * (D + 2) + D + 1];
-            part[G * D + 2 * g] = M;
-            part[G * D + 2 * g + 1] = L;
+                L += exp2_fast(red[(ww * kMaxG + g) * kRS + off] - Mu) * red[(ww * kMaxG + g) * kRS + off + 1];
+            part[G * D + 2 * tid] = M;
+            part[G * D + 2 * tid + 1] = L;
         }
     }
 }

@@ -59,7 +59,14 @@ struct AttnArgs {
     const void* cv;                  //   two-segment step, [B][Hkv][idx_stride][d]
     float* out;
     float* lse;                      // may be null
-    float* part;                     // [units][nsplit][rec]: acc [G][d], then (m, l) [G]
+    float* part;                     // [units][nsplit][rec]: acc [G][d], then (m, l) [G], then
+                                     //   (m, l) over the Selector's allowed set [G] (lse_j only)
+    // dense step of sfi_slow_step: the log-sum-exp of each query head's logits over the
+    // Selector's allowed set J = [n_sink, len - n_recent) goes to lse_j [B][Hq] (natural log),
+    // and the combine clears the Selector's digit-0 histograms sel_hist [B*Hkv][kSelHistBins]
+    float* lse_j;                    // null: not computed
+    int32_t n_sink;                  // with n_recent above: the bounds of J
+    uint32_t* sel_hist;
 };
 
 hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool paged, bool sparse,
@@ -89,6 +96,8 @@ struct SelArgs {
                                      // candidates > T, kept keys == T, per chunk
     uint32_t* cand;                  // [B][Hkv][nchunk][kSelChunk]: keys of the digit-0 bin
     uint32_t* cand_n;                // [B][Hkv][nchunk]: candidates per chunk
+    const float* lse_j;              // [B][Hq] log-sum-exp over J from the dense step (natural
+                                     //   log; the histograms are then already cleared), or null
     int32_t unit_path;               // 1: one workgroup per (b, KV head) does everything
     // full Selector (refine != 0): prior, reverse-KL fusion, Soft-NMS, cross-head exclusivity
     int32_t refine;

@@ -4,7 +4,9 @@
 // window of one query; Sec. 3.3, Top-K per KV head; prior and refinements off).  Chunked path
 // (long contexts):
 //   1. lse_kernel         partial log-sum-exp of each query head's logits over a 4096-wide
-//                          chunk of J (also clears the digit-0 histogram of the group)
+//                          chunk of J (also clears the digit-0 histogram of the group); not
+//                          launched in the fused slow step, whose dense step already gives the
+//                          log-sum-exp over J and clears the histograms
 //   2. evidence_kernel    f(j) = sum_{i in group} exp(z_ij - LSE_J,i) for the chunk, stored as
 //                          uint32 keys (the bit pattern of a non-negative float orders like
 //                          the float), plus a histogram of digit 0 (key bits 30..19)
@@ -205,7 +207,11 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     const int hi = min(r.j1, lo + kSelChunk);
     if (lo >= hi) return;
     for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
-    for (int g = w; g < G; g += kWaves) {
+    if (a.lse_j) {
+        // the dense step of the slow step gave the log-sum-exp over J
+        if (tid < G) s_lse[tid] = a.lse_j[(int64_t)b * a.Hq + h * G + tid] * kLog2e;
+    }
+    for (int g = w; !a.lse_j && g < G; g += kWaves) {
         const float2* lp = a.lse_part + ((int64_t)b * a.Hq + h * G + g) * a.nchunk;
         float M = -INFINITY;
         for (int k = lane; k < a.nchunk; k += 64) M = fmaxf(M, lp[k].x);
@@ -785,7 +791,12 @@ __global__ void __launch_bounds__(kUT) select_unit_kernel(SelArgs a) {
     auto in_j = [&](int qi, int e) { const int j = 4 * qi + e; return qi < q1 && j >= j0 && j < j1; };
 
     // 1. log-sum-exp over J of each query head, four heads and kUQ quads per thread at a time
-    for (int g0 = 0; g0 < G; g0 += 4) {
+    //    (given by the dense step in the fused slow step)
+    if (a.lse_j) {
+        for (int g = tid; g < G; g += kUT) sm.lse[g] = a.lse_j[(int64_t)b * a.Hq + h * G + g] * kLog2e;
+        __syncthreads();
+    }
+    for (int g0 = 0; !a.lse_j && g0 < G; g0 += 4) {
         float m[4], sum[4];
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
@@ -1011,7 +1022,8 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     const dim3 g_head(a.nchunk, a.Hq, a.B);
     const dim3 g_group(a.nchunk, a.Hkv, a.B);
     const dim3 g_unit(a.Hkv, a.B);
-    hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
+    // with lse_j the dense step computed the log-sum-exp over J and cleared the histograms
+    if (!a.lse_j) hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
     hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
     if (a.refine) {
         hipLaunchKernelGGL(refine_nms_kernel, g_group, blk, 0, s, a);
