@@ -96,12 +96,15 @@ def dense_bytes(wl, lens):
 
 
 def select_bytes(wl, lens):
+    """HBM bytes the Selector of the fused slow step (sfi_slow_step) must move: the logits over J
+    read once (its normaliser over J comes from the dense step), one 4-byte key written per
+    (KV head, position of J) and read back by the candidate pass and by the emit, and the index
+    rows written.  (The survey's plan counts a second logit read and the keys four times, an
+    upper bound for a Selector that computes its own normaliser.)  The candidates, well under
+    1 % of J, and the 16 KB histograms are not counted."""
     nJ = sum(max(0, n - wl.n_recent - wl.n_sink) for n in lens)
-    # logits over J read twice (log-sum-exp pass, evidence pass); one key written per
-    # (KV head, position) and read back by the candidate pass and the emit (the candidates
-    # themselves, well under 1 % of J, are not counted)
-    return 2 * wl.Hq * nJ * 4 + 3 * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
-                                                         for _ in lens)
+    return wl.Hq * nJ * 4 + 3 * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
+                                                      for _ in lens)
 
 
 def fast_bytes(wl, lens_t, n_idx_host, mask_host):
@@ -670,20 +673,16 @@ def main():
         marks = []
         for li in range(L):
             d0 = descs[li]
-            e = [ev() for _ in range(4)] if rec != "none" else None
+            e = [ev() for _ in range(3)] if rec != "none" else None
             if e:
                 e[0].record(stream)
-            B.sfi_dense_decode(d0[0], queries[li][0], out, lse, logits[li], stride, ws)
-            if e:
-                e[1].record(stream)
-            B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
-                         idx_stride, nidxs[li], ws)
+            # the slow step in one call: dense with logits, Selector (its normaliser over J from
+            # the dense kernels), mask; e[1] is recorded by the library after the dense kernels
+            B.sfi_slow_step(d0[0], queries[li][0], out, lse, logits[li], stride, wl.n_sink,
+                            wl.n_recent, wl.k_sel, idxs[li], idx_stride, nidxs[li],
+                            wl.mask_frac, masks[li], ws, dense_done=e[1] if e else None)
             if rec == "all":
                 e[2].record(stream)
-            if masks[li] is not None:
-                B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
-            if rec == "all":
-                e[3].record(stream)
             marks.append(e)
         fe = [ev(), ev()] if rec == "all" else None
         if fe:
@@ -719,18 +718,18 @@ def main():
     print("# breakdown", file=sys.stderr, flush=True)
     evs = [cycle("all") for s in range(max(1, min(args.steps, 2)))]
     torch.cuda.synchronize()
+    # Selector and (when the workload has one) mask: from the library's event after the dense
+    # kernels to the end of the slow-step call
     select_us = 1e3 * mean([e[1].elapsed_time(e[2]) for marks, _ in evs for e in marks])
-    mask_us = (1e3 * mean([e[2].elapsed_time(e[3]) for marks, _ in evs for e in marks])
-               if wl.mask_frac > 0 else 0.0)
     fast_us = 1e3 * mean([fe[0].elapsed_time(fe[1]) / (L * (wl.cycle - 1)) for _, fe in evs])
 
     # Spread: one more stack cycle in decode order with events around every single call
     # (p10 / p50 / p90), and the dense step without its logit write as a reference for the
     # cost of the logits.
-    dense_calls, nolog_calls, fast_calls = [], [], []
+    dense_calls, nolog_calls, fast_calls, sep_calls, mask_calls = [], [], [], [], []
     if not args.no_spread:
         print("# per-call spread", file=sys.stderr, flush=True)
-        pairs = {"dense": [], "nolog": [], "fast": []}
+        pairs = {"dense": [], "nolog": [], "fast": [], "select_sep": [], "mask": []}
 
         def timed_call(kind, fn):
             e = (ev(), ev())
@@ -739,14 +738,18 @@ def main():
             e[1].record(stream)
             pairs[kind].append(e)
 
+        # the separate calls of the slow step, each timed on its own: the dense step, the
+        # Selector with its own log-sum-exp pass (sfi_select), the mask
         for li in range(L):
             d0 = descs[li]
             timed_call("dense", lambda: B.sfi_dense_decode(d0[0], queries[li][0], out, lse,
                                                            logits[li], stride, ws))
-            B.sfi_select(d0[0], logits[li], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[li],
-                         idx_stride, nidxs[li], ws)
+            timed_call("select_sep", lambda: B.sfi_select(d0[0], logits[li], stride, wl.n_sink,
+                                                          wl.n_recent, wl.k_sel, idxs[li],
+                                                          idx_stride, nidxs[li], ws))
             if masks[li] is not None:
-                B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse, wl.mask_frac, masks[li])
+                timed_call("mask", lambda: B.sfi_sink_bypass_mask(d0[0], logits[li], stride, lse,
+                                                                  wl.mask_frac, masks[li]))
         for t in range(1, wl.cycle):
             for li in range(L):
                 timed_call("fast", lambda: B.sfi_sparse_decode(
@@ -759,6 +762,8 @@ def main():
         dense_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["dense"]]
         nolog_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["nolog"]]
         fast_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["fast"]]
+        sep_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["select_sep"]]
+        mask_calls = [1e3 * a.elapsed_time(b) for a, b in pairs["mask"]]
 
     def pct(xs):
         if not xs:
@@ -823,6 +828,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_cycle": round(ms_per_step, 4),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -834,11 +840,12 @@ def main():
                    "mask_frac": wl.mask_frac, "layers_rotated": L,
                    "step": f"{L} layers x (1 slow (dense+select{'+mask' if wl.mask_frac else ''}) + "
                            f"{wl.cycle - 1} fast), token-major"},
-        "slow_us": round(dense_us + select_us + mask_us, 2),
+        "slow_us": round(dense_us + select_us, 2),
         "fast_us": round(fast_us, 2),
         "dense_us": round(dense_us, 2),
         "select_us": round(select_us, 2),
-        "mask_us": round(mask_us, 2),
+        "mask_us": round(mean(mask_calls), 2) if mask_calls else 0.0,
+        "select_separate_us": round(mean(sep_calls), 2) if sep_calls else None,
         "dense_gbps": round(dense_gbps, 1),
         "fast_gbps": round(fast_gbps, 1),
         "select_gbps": round(select_gbps, 1),
@@ -848,6 +855,12 @@ def main():
                       "dense_nolog": pct(nolog_calls), "fast": pct(fast_calls),
                       "calls": {"dense": len(dense_calls), "fast": len(fast_calls)}},
         "tokens_per_s": round(wl.B * 1e6 / value, 1),
+        "steps_explained": "value is us per decode step of one layer (amortised over the cycle); "
+                           "ms_per_step = ms_per_cycle is one timed bench step: a whole stack "
+                           f"cycle of {L} layers x {wl.cycle} decode steps",
+        "hbm_frac_by_step": {"dense": round(dense_gbps / PEAK_HBM_GBS, 4),
+                             "selector": round(select_gbps / PEAK_HBM_GBS, 4),
+                             "fast": round(fast_gbps / PEAK_HBM_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(dense_gbps, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(dense_gbps / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel": "sfi_dense_decode (attention_kernel)",
@@ -865,12 +878,13 @@ def main():
                                          "and replayed (no host launch cost)"}
     if refined is not None:
         refined["value_if_used_us"] = round(
-            (dense_us + refined["select_refined_us"] + mask_us + (wl.cycle - 1) * fast_us)
+            (dense_us + refined["select_refined_us"] + (mean(mask_calls) if mask_calls else 0.0)
+             + (wl.cycle - 1) * fast_us)
             / wl.cycle, 3)
         result["select_refined"] = refined
     if two_seg is not None:
         two_seg["value_if_used_us"] = round(
-            (dense_us + select_us + mask_us + two_seg["reorg_us"] +
+            (dense_us + select_us + two_seg["reorg_us"] +
              (wl.cycle - 1) * two_seg["fast_us"]) / wl.cycle, 3)
         result["two_segment"] = two_seg
     result["roofline"]["frac_of_measured_read"] = round(dense_gbps / yard["gbps"], 4)
