@@ -194,6 +194,11 @@ __device__ __forceinline__ float fused_log2(const SelArgs& a, float f, float lr)
     return (1.f - a.lam) * __log2f(f) + a.lam * lr;
 }
 
+// Evidence of one 4096-position chunk of J for one (KV head, sequence): thread t takes the
+// position quads t, t + 256, ... (16-byte loads from the multiple of 4 at or below the chunk's
+// start), four query heads at a time with every load of the four heads issued before any is
+// used; positions outside the chunk are masked.
+constexpr int kEvQ = kPerThread / 4 + 1;               // quads per thread (kSelChunk + 3 positions)
 __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     __shared__ float s_lse[kMaxSelG];
     __shared__ uint32_t lh[kCBins0];
@@ -206,7 +211,25 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     const int lo = r.j0 + c * kSelChunk;
     const int hi = min(r.j1, lo + kSelChunk);
     if (lo >= hi) return;
-    for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
+    const float* zb = a.logits + ((int64_t)b * a.Hq + h * G) * a.logit_stride;
+    const int base = lo & ~3;
+    const int n4 = (hi - base + 3) >> 2;
+    // the first four heads' quads are in flight before the normalisers are known
+    f32x4 v[4][kEvQ];
+    auto load4 = [&](int g0) {
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            const float* z = zb + (int64_t)min(g0 + gg, G - 1) * a.logit_stride + base;
+#pragma unroll
+            for (int k = 0; k < kEvQ; ++k) {
+                const int f = k * kThreads + tid;
+                v[gg][k] = f < n4 ? *(const f32x4*)(z + 4 * f) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    };
+    load4(0);
+    if (!a.refine)
+        for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
     if (a.lse_j) {
         // the dense step of the slow step gave the log-sum-exp over J
         if (tid < G) s_lse[tid] = a.lse_j[(int64_t)b * a.Hq + h * G + tid] * kLog2e;
@@ -225,38 +248,53 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
         if (lane == 0) s_lse[g] = (M + logf(S)) * kLog2e;   // log2 units
     }
     __syncthreads();
+    // f(j) = sum over the group's rows of exp(z - LSE_J) (no 1/G: the order is the same)
+    float f[kEvQ][4];
+#pragma unroll
+    for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[k][e] = 0.f;
+    for (int g0 = 0; g0 < G; g0 += 4) {
+        if (g0 > 0) load4(g0);
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+            if (g0 + gg >= G) continue;
+            const float l = s_lse[g0 + gg];
+#pragma unroll
+            for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) f[k][e] += exp2_hw(fmaf(v[gg][k][e], kLog2e, -l));
+        }
+    }
     uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
-    const float* zb = a.logits + ((int64_t)b * a.Hq + h * G) * a.logit_stride;
     if (a.refine) {
         // keys of f for the refinement passes, and this chunk's share of the fusion normaliser
         float zs = 0.f;
-#pragma unroll 4
-        for (int k = 0; k < kPerThread; ++k) {
-            const int j = lo + k * kThreads + tid;
-            if (j < hi) {
-                float f = 0.f;
-                for (int g = 0; g < G; ++g)
-                    f += exp2_hw(fmaf(zb[(int64_t)g * a.logit_stride + j], kLog2e, -s_lse[g]));
-                keys[j - lo] = __float_as_uint(f);
-                zs += exp2_hw(fused_log2(a, f, prior_log2(a, unit, j, r.j0, r.nJ)));
+#pragma unroll
+        for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = base + 4 * (k * kThreads + tid) + e;
+                if (j >= lo && j < hi) {
+                    keys[j - lo] = __float_as_uint(f[k][e]);
+                    zs += exp2_hw(fused_log2(a, f[k][e], prior_log2(a, unit, j, r.j0, r.nJ)));
+                }
             }
-        }
         zs = block_sum(zs, sh);
         if (tid == 0) a.zpart[(int64_t)unit * a.nchunk + c] = zs;
         return;
     }
-#pragma unroll 4
-    for (int k = 0; k < kPerThread; ++k) {
-        const int j = lo + k * kThreads + tid;
-        if (j < hi) {
-            float f = 0.f;
-            for (int g = 0; g < G; ++g)
-                f += exp2_hw(fmaf(zb[(int64_t)g * a.logit_stride + j], kLog2e, -s_lse[g]));
-            const uint32_t key = __float_as_uint(f);
-            keys[j - lo] = key;
-            atomicAdd(&lh[key >> kCShift[0]], 1u);
+#pragma unroll
+    for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int j = base + 4 * (k * kThreads + tid) + e;
+            if (j >= lo && j < hi) {
+                const uint32_t key = __float_as_uint(f[k][e]);
+                keys[j - lo] = key;
+                atomicAdd(&lh[key >> kCShift[0]], 1u);
+            }
         }
-    }
     __syncthreads();
     uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
     for (int t = tid; t < kCBins0; t += kThreads)
