@@ -11,6 +11,8 @@
  *     (SinkRouter Sec. 4.2, target regime and execution policy)          -> sfi_sink_bypass_mask
  *   - a fast step attends only to sink + selected + recent positions
  *     (SFI Sec. 1, the compact cache of fast steps)                       -> sfi_sparse_decode
+ *   - the same with its per-step state read from a device step descriptor
+ *     (SFI Sec. 4.2, the packed per-step descriptor)                     -> sfi_sparse_decode_step
  *   - the same with SinkRouter's inline group routing (SinkRouter Sec. 4.2-4.3)
  *                                                                        -> sfi_sparse_decode_routed
  *   - the slow step over a model's layers with the Selector on a second stream
@@ -248,6 +250,61 @@ sfi_status sfi_sparse_decode_noalloc(const sfi_kv_desc* kv, const void* q,
                                      const int32_t* idx, int32_t idx_stride, const int32_t* n_idx,
                                      int32_t n_recent, const uint8_t* head_mask,
                                      float* out, float* lse, hipStream_t stream);
+
+/* Step descriptor of the fast step (SFI Sec. 4.2: the host writes a compact packed descriptor
+ * once per decoding step, and every kernel of the step reads its per-request cache bounds,
+ * block-table pointer and layout offsets from device memory, so steps need no dynamic
+ * allocation or extra synchronisation).  One sfi_step lives in device memory (8-byte aligned,
+ * caller-owned); the caller writes it before each step, e.g. by a copy from the host, and
+ * sfi_sparse_decode_step reads it.  A call captured once in a HIP graph therefore serves every
+ * fast step of a cycle: between replays only the descriptor (lengths, query, outputs, index
+ * set, mask, segment, recent window) changes.  Field meanings as for sfi_sparse_decode and
+ * sfi_sparse_decode_compact:
+ *   k, v         cache base pointers, laid out as the host descriptor says (contiguous
+ *                [B][Hkv][n_cap][d] or paged [num_blocks][Hkv][block_size][d])
+ *   block_table  [B][max_blocks] int32 when the host descriptor is paged, else NULL
+ *   len          [B] int32 lengths at this step
+ *   q            [B][Hq][d] query of this step; out fp32 [B][Hq][d]; lse fp32 [B][Hq] or NULL
+ *   idx, n_idx   index set [B][Hkv][idx_stride] and counts [B][Hkv] (for a two-segment step:
+ *                the positions cpos written by sfi_reorg)
+ *   head_mask    [B][Hq] uint8 or NULL
+ *   seg_k, seg_v compact segment of the two-segment layout ([B][Hkv][idx_stride][d]) or NULL
+ *                (both or neither): index slots then read the segment instead of the cache
+ *   n_recent     recent window of this step, 0 <= n_recent <= the call's max_recent
+ * The device data is trusted, as the other calls trust lengths and indices. */
+typedef struct sfi_step {
+    const void* k;
+    const void* v;
+    const int32_t* block_table;
+    const int32_t* len;
+    const void* q;
+    const int32_t* idx;
+    const int32_t* n_idx;
+    const uint8_t* head_mask;
+    const void* seg_k;
+    const void* seg_v;
+    float* out;
+    float* lse;
+    int32_t n_recent;
+    int32_t reserved;        /* 0 */
+} sfi_step;
+
+/* Fast step whose per-step state comes from a device step descriptor (see sfi_step).  The
+ * host arguments fix only what the launch plan needs and every step of a cycle shares: kv
+ * gives batch, heads, head_dim, dtype and the cache's capacity (n_cap, or block_size and
+ * max_blocks with any non-NULL kv->block_table marking a paged cache); kv->k, kv->v,
+ * kv->block_table and kv->len are not read (the descriptor's are), and kv->max_len is not
+ * used.  idx_stride is the index rows' stride and max_recent bounds the descriptor's
+ * n_recent.  step (device) points to the descriptor.  Workspace: sfi_workspace_bytes(kv,
+ * SFI_OP_SPARSE, idx_stride, max_recent).  With the descriptor's n_recent equal to max_recent
+ * the result equals sfi_sparse_decode (or sfi_sparse_decode_compact, with a segment) called
+ * with the descriptor's values bit for bit; a smaller n_recent gives the same attention with the
+ * splits planned for max_recent (equal up to rounding).  Two kernel launches, each reading the
+ * descriptor at entry.  SFI_E_INVALID for a NULL or misaligned step, idx_stride < 1 or
+ * max_recent < 0. */
+sfi_status sfi_sparse_decode_step(const sfi_kv_desc* kv, const sfi_step* step,
+                                  int32_t idx_stride, int32_t max_recent,
+                                  void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Sparse decode step with inline group routing.  SinkRouter Sec. 4 (decide per KV group,
  * before loading the group's history, whether it is in the sink-dominant regime, and if so

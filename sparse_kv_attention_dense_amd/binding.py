@@ -22,7 +22,7 @@ SFI_F32, SFI_BF16 = 0, 1
 SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SELECT_REFINED, SFI_OP_SLOW = 0, 1, 2, 3, 4
 
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_slow_step", "sfi_select_refined", "sfi_sink_bypass_mask",
-            "sfi_sparse_decode", "sfi_sparse_decode_noalloc",
+            "sfi_sparse_decode", "sfi_sparse_decode_noalloc", "sfi_sparse_decode_step",
             "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
             "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_status_string")
 
@@ -41,6 +41,14 @@ class sfi_refine(ctypes.Structure):
 
 REFINE_DEFAULTS = dict(lambda_=0.02, alpha_soft=0.5, alpha_cross=0.35, prior_decay=1.0,
                        tail_frac=1.0 / 16, tail_brake=1.0)
+
+
+class sfi_step(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+                ("len", ctypes.c_void_p), ("q", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("n_idx", ctypes.c_void_p), ("head_mask", ctypes.c_void_p),
+                ("seg_k", ctypes.c_void_p), ("seg_v", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("n_recent", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class sfi_kv_desc(ctypes.Structure):
@@ -71,6 +79,7 @@ def lib():
         L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
         L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.sfi_sparse_decode_noalloc.argtypes = [D, P, P, i32, P, i32, P, P, P, P]
+        L.sfi_sparse_decode_step.argtypes = [D, P, i32, i32, P, ctypes.c_size_t, P]
         L.sfi_sparse_decode_routed.argtypes = [D, P, P, i32, P, i32, P, P, ctypes.c_float, P,
                                                P, P, P, ctypes.c_size_t, P]
         L.sfi_slow_step_layers.argtypes = [i32, D, P, P, P, i32, P, i64, P, ctypes.c_size_t, P,
@@ -371,6 +380,47 @@ def sfi_sparse_decode_noalloc(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_re
                                            _ptr(n_idx), int(n_recent), _ptr(head_mask), _ptr(out),
                                            _ptr(lse), _stream(stream)),
            "sfi_sparse_decode_noalloc")
+
+
+def step_descriptor(device="cuda") -> torch.Tensor:
+    """Device memory for one sfi_step (plumbing: torch allocates it once)."""
+    return torch.zeros(256, dtype=torch.uint8, device=device)
+
+
+def write_step(step_buf, desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int,
+               head_mask, out, lse, segment=None, stream=None):
+    """Checks this step's buffers as sfi_sparse_decode does (desc gives the cache, the lengths
+    and, when paged, the block table of the step), packs an sfi_step on the host and copies it
+    into step_buf on the stream.  segment: (ck, cv) of the two-segment layout, with idx its
+    cpos, or None."""
+    desc.need_cache("write_step")
+    _fast_bufs(desc, "write_step", q, n_idx, head_mask, out, lse, step_buf)
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
+    ck = cv = None
+    if segment is not None:
+        ck, cv = segment
+        rows = desc.units * int(idx_stride) * desc.c.head_dim
+        _buf(ck, "seg_k", desc.cache_dtype, rows)
+        _buf(cv, "seg_v", desc.cache_dtype, rows)
+    c = desc.c
+    st = sfi_step(c.k, c.v, c.block_table, c.len, _ptr(q), _ptr(idx), _ptr(n_idx),
+                  _ptr(head_mask), _ptr(ck), _ptr(cv), _ptr(out), _ptr(lse), int(n_recent), 0)
+    raw = torch.frombuffer(bytearray(bytes(st)), dtype=torch.uint8)
+    s = torch.cuda.current_stream() if stream is None else stream
+    with torch.cuda.stream(s):
+        step_buf[:raw.numel()].copy_(raw)
+
+
+def sfi_sparse_decode_step(desc: KVDesc, step_buf, idx_stride: int, max_recent: int, ws,
+                           stream=None):
+    """desc gives the shapes and the cache's capacity; the step's pointers come from
+    step_buf (written by write_step)."""
+    desc.need_cache("sfi_sparse_decode_step")
+    _buf(step_buf, "step", _U8, ctypes.sizeof(sfi_step))
+    _buf(ws, "ws")
+    _check(lib().sfi_sparse_decode_step(desc.ref, _ptr(step_buf), int(idx_stride),
+                                        int(max_recent), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)), "sfi_sparse_decode_step")
 
 
 def sfi_sparse_decode_routed(desc: KVDesc, q, idx, idx_stride: int, n_idx, n_recent: int,

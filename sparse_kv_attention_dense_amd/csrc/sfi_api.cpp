@@ -475,6 +475,36 @@ SFI_EXPORT sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const voi
                        ck, cv, out, lse, ws, ws_bytes, stream);
 }
 
+SFI_EXPORT sfi_status sfi_sparse_decode_step(const sfi_kv_desc* kv, const sfi_step* step,
+                                             int32_t idx_stride, int32_t max_recent, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+    if (!kv || !step || ((uintptr_t)step % 8) != 0) return SFI_E_INVALID;
+    // shapes and capacities from the host descriptor; its pointers are not read (the device
+    // descriptor's are), so stand-ins let the common checks run
+    sfi_kv_desc hk = *kv;
+    hk.k = hk.v = (const void*)kAlign;
+    hk.len = (const int32_t*)kAlign;
+    hk.max_len = 0;
+    sfi_status st = check_desc(&hk, true);
+    if (st != SFI_OK) return st;
+    if (idx_stride < 1 || max_recent < 0) return SFI_E_INVALID;
+    if (segment_rows(hk, idx_stride) >= (int64_t(1) << 32)) return SFI_E_UNSUPPORTED;
+    AttnPlan plan;
+    st = plan_attention(hk, true, idx_stride, max_recent, &plan);
+    if (st != SFI_OK) return st;
+    st = check_ws(ws, ws_bytes, plan.bytes);
+    if (st != SFI_OK) return st;
+    AttnArgs a;
+    fill_cache_args(hk, &a);
+    fill_plan_args(plan, ws, &a);
+    a.idx_stride = idx_stride;
+    a.n_recent = max_recent;
+    a.step = step;
+    const hipError_t e = launch_attention(a, kv->batch, kv->head_dim, kv->dtype == SFI_BF16,
+                                          kv->block_table != nullptr, true, stream);
+    return e == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
 SFI_EXPORT sfi_status sfi_sparse_decode_routed(const sfi_kv_desc* kv, const void* q,
                                                const int32_t* idx, int32_t idx_stride,
                                                const int32_t* n_idx, int32_t n_recent,

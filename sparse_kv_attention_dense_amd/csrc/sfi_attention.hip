@@ -192,6 +192,25 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
     __syncthreads();
 }
 
+// Fast step on a device step descriptor: the per-step pointers and the recent window replace
+// the launch arguments' (uniform scalar loads at kernel entry).
+__device__ __forceinline__ void apply_step(AttnArgs& a) {
+    const sfi_step* s = a.step;
+    a.k = s->k;
+    a.v = s->v;
+    a.block_table = s->block_table;
+    a.len = s->len;
+    a.q = s->q;
+    a.idx = s->idx;
+    a.n_idx = s->n_idx;
+    a.head_mask = s->head_mask;
+    a.ck = s->seg_k;
+    a.cv = s->seg_v;
+    a.out = s->out;
+    a.lse = s->lse;
+    a.n_recent = s->n_recent;
+}
+
 // Orders this wavefront's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -327,8 +346,12 @@ struct TileRegs {
 template <bool BF, int D, bool PAGED, bool SPARSE>
 __global__ void __launch_bounds__(64 * waves_of(BF, D, SPARSE),
                                   (BF || D == 64) ? 8 / waves_of(BF, D, SPARSE) : 1)
-attention_kernel(AttnArgs a) {
+attention_kernel(AttnArgs a_in) {
     using C = Cfg<BF, D, PAGED, SPARSE>;
+    AttnArgs a = a_in;
+    if constexpr (SPARSE) {
+        if (a.step) apply_step(a);
+    }
     static_assert(SPARSE || C::kNW == kWaves, "the dense split lookup assumes four wavefronts");
     using Regs = TileRegs<BF, D, PAGED, SPARSE>;
     __shared__ __attribute__((aligned(16))) unsigned char raw[C::kRaw];
@@ -927,8 +950,12 @@ attention_kernel(AttnArgs a) {
 
 // One workgroup per query head (blockIdx.x) of batch blockIdx.y merges the split records.
 template <int D, bool SPARSE>
-__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a_in) {
     __shared__ float s_m[kThreads], s_l[kThreads], s_a[kThreads];
+    AttnArgs a = a_in;
+    if constexpr (SPARSE) {
+        if (a.step) apply_step(a);
+    }
     merge_head<D, SPARSE>(a, blockIdx.y, blockIdx.x, s_m, s_l, s_a);
 }
 

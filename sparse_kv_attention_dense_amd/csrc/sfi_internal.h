@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "sfi.h"
+
 namespace sfi {
 
 // ---- attention kernels (dense slow step and sparse fast step share one kernel) ----------
@@ -67,6 +69,9 @@ struct AttnArgs {
     float* lse_j;                    // null: not computed
     int32_t n_sink;                  // with n_recent above: the bounds of J
     uint32_t* sel_hist;
+    // fast step of sfi_sparse_decode_step: the per-step pointers and the recent window are
+    // read from this device descriptor at kernel entry (null: the fields above hold them)
+    const sfi_step* step;
 };
 
 hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool paged, bool sparse,

@@ -173,6 +173,24 @@ def test_noalloc_fast_step_validation(L):
     assert na(big) == B.SFI_E_SCRATCH
 
 
+def test_step_descriptor_validation(L):
+    """sfi_sparse_decode_step validates the host side (shapes, capacities, bounds, workspace)
+    before any HIP call; the descriptor's own pointers are device data."""
+    d = _desc(k=None, v=None, len=None, max_len=10 ** 9)    # pointers and max_len are not read
+    ws = L.sfi_workspace_bytes(ctypes.byref(_desc()), B.SFI_OP_SPARSE, 2052, 256)
+    st = lambda dd=d, step=FAKE, istride=2052, nr=256, w=ws: L.sfi_sparse_decode_step(
+        ctypes.byref(dd) if dd is not None else None, step, istride, nr, FAKE if w else None, w,
+        None)
+    assert st(dd=None) == B.SFI_E_INVALID
+    assert st(step=None) == B.SFI_E_INVALID
+    assert st(step=FAKE + 4) == B.SFI_E_INVALID             # not 8-byte aligned
+    assert st(istride=0) == B.SFI_E_INVALID
+    assert st(nr=-1) == B.SFI_E_INVALID
+    assert st(w=ws - 256) == B.SFI_E_WORKSPACE
+    assert st(dd=_desc(head_dim=96)) == B.SFI_E_UNSUPPORTED
+    assert ctypes.sizeof(B.sfi_step) == 12 * 8 + 8
+
+
 def test_status_strings(L):
     for s in (B.SFI_OK, B.SFI_E_INVALID, B.SFI_E_UNSUPPORTED, B.SFI_E_WORKSPACE, B.SFI_E_HIP,
               B.SFI_E_SCRATCH):
