@@ -260,6 +260,73 @@ def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
             "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
 
 
+def routed_sink_heavy(B, torch, synth, wl, layers, descs, stride, idx_stride, L, ws,
+                      gamma: float = 0.65, extra: float = 2.1972245773362196):
+    """The routed fast step at an operating point where most KV groups reach gamma: the sink
+    recipe with token 0's key steadied (its part orthogonal to u scaled by 0.1, so its logit
+    varies little between queries; restored afterwards) and its logit raised by ln 9 (token-0
+    mass near 0.9), its own queries for every step, each layer's slow step (fused call) giving
+    the index set and the cached normaliser.
+    The same cycle's fast steps run in decode order once unrouted (sfi_sparse_decode) and once
+    routed (sfi_sparse_decode_routed), each timed as one block, twice.  Bytes: the fast step's
+    algorithmic bytes without and with the bypassed groups' rows and indices."""
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    print("# routed fast steps, sink-heavy queries", file=sys.stderr, flush=True)
+    saved = [synth.steady_sink(lay, 0.1) for lay in layers]
+    qs = [[synth.make_query(wl, li, t, device=dev, u=layers[li].u, sink_extra=extra)
+           for t in range(wl.cycle)] for li in range(L)]
+    out = torch.empty((wl.B, wl.Hq, wl.d), device=dev)
+    lse_f = torch.empty((wl.B, wl.Hq), device=dev)
+    slow_lse = [torch.empty((wl.B, wl.Hq), device=dev) for _ in range(L)]
+    logits = torch.empty((wl.B, wl.Hq, stride), device=dev)
+    idxs = [torch.empty((wl.B, wl.Hkv, idx_stride), dtype=torch.int32, device=dev) for _ in range(L)]
+    nidxs = [torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev) for _ in range(L)]
+    routed = [torch.zeros((wl.B, wl.Hkv), dtype=torch.uint8, device=dev) for _ in range(L)]
+    for li in range(L):
+        B.sfi_slow_step(descs[li][0], qs[li][0], out, slow_lse[li], logits, stride, wl.n_sink,
+                        wl.n_recent, wl.k_sel, idxs[li], idx_stride, nidxs[li], 0.0, None, ws)
+
+    def block(route):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for t in range(1, wl.cycle):
+            for li in range(L):
+                if route:
+                    B.sfi_sparse_decode_routed(descs[li][t], qs[li][t], idxs[li], idx_stride,
+                                               nidxs[li], wl.n_recent, None, slow_lse[li], gamma,
+                                               routed[li], out, lse_f, ws)
+                else:
+                    B.sfi_sparse_decode(descs[li][t], qs[li][t], idxs[li], idx_stride, nidxs[li],
+                                        wl.n_recent, None, out, lse_f, ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (L * (wl.cycle - 1))
+
+    plain, rout, frac = [], [], []
+    for rep in range(2):
+        plain.append(block(False))
+        rout.append(block(True))
+        frac += [float(r.float().mean()) for r in routed]
+    for lay, sv in zip(layers, saved):
+        synth.restore_sink(lay, sv)
+    lens0 = layers[0].len0_host
+    n_idx_host = nidxs[0].cpu().tolist()
+    mean = lambda x: sum(x) / len(x)
+    full = mean([fast_bytes(wl, [n + t for n in lens0], n_idx_host, None)
+                 for t in range(1, wl.cycle)])
+    # the last step's decisions of layer 0, spread to its heads, as the bypassed groups' mask
+    rmask = routed[0].repeat_interleave(wl.G, dim=1).cpu().tolist()
+    kept = mean([fast_bytes(wl, [n + t for n in lens0], n_idx_host, rmask)
+                 for t in range(1, wl.cycle)])
+    return {"gamma": gamma, "token0_logit_raised_by": round(extra, 4),
+            "token0_key_orthogonal_scale": 0.1,
+            "groups_routed_frac": round(mean(frac), 4),
+            "fast_us_unrouted": round(mean(plain), 2), "fast_us_routed": round(mean(rout), 2),
+            "algorithmic_bytes_unrouted": int(full), "algorithmic_bytes_routed": int(kept),
+            "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
+
+
 def graph_replay(torch, run, per_replay: int, reps: int = 3):
     """The stack cycle run() captured once in a HIP graph (torch.cuda.CUDAGraph: the library's
     calls queue kernels only) and replayed back to back, timed on the host clock like the
@@ -781,10 +848,12 @@ def main():
     synth_fast = synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out,
                                                 lse, ws, idx_stride, L)
 
-    routed = None
+    routed = routed_heavy = None
     if wl.sink and not args.no_routed:
         routed = routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
                                    masks, ws, idx_stride, L)
+        routed_heavy = routed_sink_heavy(B, torch, synth, wl, layers, descs, stride, idx_stride,
+                                         L, ws)
 
     layered = None
     if L >= 2 and not args.no_layered:
@@ -892,6 +961,8 @@ def main():
     result["fast_synthetic_selections"] = synth_fast
     if routed is not None:
         result["routed_fast"] = routed
+    if routed_heavy is not None:
+        result["routed_fast_sink_heavy"] = routed_heavy
     if layered is not None:
         result["slow_step_layers"] = layered
     if args.copy_calibration > 0:

@@ -212,14 +212,48 @@ def make_layer(wl: Workload, layer: int = 0, device="cpu", lens=None) -> Layer:
                  len_host, max(caps), block_table=bt_dev, max_blocks=max_blocks, u=u)
 
 
-def make_query(wl: Workload, layer: int, t: int, device="cpu", u=None, n_for_sink=None):
-    """Query for decode step t of a cycle ([B][Hq][d])."""
+def steady_sink(layer: Layer, scale: float = 0.1):
+    """Sink-heavy variant of the sink recipe (sink workloads): token 0's key keeps its 8u offset
+    but its part orthogonal to u is scaled by `scale`, so its logit varies little from query to
+    query (the stable first-token anchor that routing on a cached normaliser relies on).
+    Rewrites the key rows of position 0 in place; returns what restore_sink puts back."""
+    wl = layer.wl
+    assert wl.sink and layer.u is not None
+    saved = []
+    for b in range(wl.B):
+        rows = (layer.k[layer.block_table[b, 0].long(), :, 0, :] if wl.paged
+                else layer.k[b, :, 0, :])                       # [Hkv][d]
+        saved.append(rows.clone())
+        k0 = rows.float()
+        along = (k0 * layer.u).sum(-1, keepdim=True) * layer.u
+        new = (scale * (k0 - along) + along).to(rows.dtype)
+        if wl.paged:
+            layer.k[layer.block_table[b, 0].long(), :, 0, :] = new
+        else:
+            layer.k[b, :, 0, :] = new
+    return saved
+
+
+def restore_sink(layer: Layer, saved):
+    wl = layer.wl
+    for b in range(wl.B):
+        if wl.paged:
+            layer.k[layer.block_table[b, 0].long(), :, 0, :] = saved[b]
+        else:
+            layer.k[b, :, 0, :] = saved[b]
+
+
+def make_query(wl: Workload, layer: int, t: int, device="cpu", u=None, n_for_sink=None,
+               sink_extra: float = 0.0):
+    """Query for decode step t of a cycle ([B][Hq][d]).  sink_extra (sink workloads): raise
+    token 0's logit by this many nats above the recipe's (ln 9 turns the recipe's even odds into
+    about nine to one, a token-0 mass near 0.9)."""
     g = _gen(device, wl.seed_base + layer + 100 + t)
     q = torch.randn((wl.B, wl.Hq, wl.d), generator=g, device=device, dtype=torch.float32)
     if wl.sink:
         assert u is not None
         uq = u.repeat_interleave(wl.G, dim=0)[None]            # [1,Hq,d], head i -> KV head i//G
-        s = sink_query_shift(wl.d, n_for_sink or wl.n0)
+        s = sink_query_shift(wl.d, n_for_sink or wl.n0) + math.sqrt(wl.d) / 8.0 * sink_extra
         q = q - (q * uq).sum(-1, keepdim=True) * uq + s * uq
     return q.to(wl.torch_dtype)
 

@@ -289,6 +289,41 @@ def test_sparse_routed_with_slow_step_lse(orc):
     assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
 
 
+@pytest.mark.parametrize("name", ["sink_128k_b4", "gqa8_512k"])
+def test_sparse_routed_sink_heavy_operating_point(orc, name):
+    """The sink recipe with token 0's key steadied (its part orthogonal to the sink direction
+    scaled by 0.1, so its logit varies little between queries) and its logit raised by ln 9
+    (token-0 mass near 0.9): most KV groups reach gamma = 0.65 with the slow step's lse as
+    normaliser, so the routed step skips their rows.  Decisions agree with the oracle's
+    wherever rounding cannot flip them, outputs agree with the oracle given the GPU's decisions,
+    and most groups are bypassed."""
+    base = W[name]
+    wl = base.scaled(16001, B=min(base.B, 2), k_sel=1024)
+    lay = synth.make_layer(wl, 0, device=DEV)
+    synth.steady_sink(lay, 0.1)
+    extra = float(np.log(9.0))
+    q0 = synth.make_query(wl, 0, 0, device=DEV, u=lay.u, sink_extra=extra)
+    _, lse0, _, _ = gpu_dense(lay, q0, 0, logits=False)
+    t = 5
+    q = synth.make_query(wl, 0, t, device=DEV, u=lay.u, sink_extra=extra)
+    idx, n_idx = synth.synthetic_index_set(lay, "scattered", seed=34)
+    out, lse, routed = _routed_gpu(lay, q, t, idx, n_idx, lse0.cpu().double(), 0.65)
+    lens = [n + t for n in lay.len0_host]
+    c = oracle_cache(orc, lay, lens)
+    _, _, er, margin = orc.sparse_routed(c, q, idx, n_idx, wl.n_recent, lse0.cpu().double(), 0.65)
+    rg = routed.cpu().numpy()
+    clear = np.abs(margin) > 1e-3
+    assert (rg[clear] == er[clear]).all()
+    frac = float(rg.mean())
+    say(f"    groups routed: {int(rg.sum())} of {rg.size} ({100 * frac:.0f} %); "
+        f"near-threshold: {int((~clear).sum())}")
+    assert frac >= 0.5
+    hm = torch.tensor(rg).repeat_interleave(wl.G, dim=1).to(torch.uint8)
+    eo, el = orc.sparse(c, q, idx, n_idx, wl.n_recent, hm)
+    assert_close_out(out.cpu().numpy(), eo, 1e-2)
+    assert_close_rel(lse.cpu().numpy(), el, 1e-3, "lse")
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_sparse_routed_edges(paged):
     """Lengths 0, 1 and 300: routing everything yields zeros (and no routing for the empty
