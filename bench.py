@@ -632,9 +632,10 @@ def two_segment_steps(B, torch, wl, descs, queries, idxs, nidxs, masks, out, lse
 
 def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
                       idx_stride, slots: int = 4, reps: int = 5):
-    """The slow step over every rotated layer: the per-layer calls one after another, against
-    sfi_slow_step_layers (Selector and mask of each layer on a second stream, a ring of
-    `slots` logits buffers and Selector workspaces).  Host clock around whole slow steps."""
+    """The slow step over every rotated layer: sfi_slow_step layer after layer, against
+    sfi_slow_step_layers (the same kernels, the Selector and mask of each layer on a second
+    stream, a ring of `slots` logits buffers and Selector workspaces).  Host clock around whole
+    slow steps."""
     L = len(descs)
     R = min(slots, L)
     dev = "cuda"
@@ -652,11 +653,9 @@ def layered_slow_step(B, torch, wl, descs, queries, logits, stride, idxs, nidxs,
     def sequential():
         for l in range(L):
             s = l % R
-            B.sfi_dense_decode(d0[l], queries[l][0], outs[l], lses[l], logits[s], stride, dense_ws)
-            B.sfi_select(d0[l], logits[s], stride, wl.n_sink, wl.n_recent, wl.k_sel, idxs[l],
-                         idx_stride, nidxs[l], sel_ws[s])
-            if has_mask:
-                B.sfi_sink_bypass_mask(d0[l], logits[s], stride, lses[l], wl.mask_frac, masks[l])
+            B.sfi_slow_step(d0[l], queries[l][0], outs[l], lses[l], logits[s], stride, wl.n_sink,
+                            wl.n_recent, wl.k_sel, idxs[l], idx_stride, nidxs[l], wl.mask_frac,
+                            masks[l] if has_mask else None, sel_ws[s])
 
     def pipelined():
         B.sfi_slow_step_layers(d0, [queries[l][0] for l in range(L)], outs, lses, logits[:R],

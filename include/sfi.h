@@ -365,8 +365,10 @@ sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
  * ring of n_slots maintenance slots and one completion barrier at the end.  For l = 0 ..
  * n_layers - 1, with slot s = l % n_slots:
  *   on `stream`:      if l >= n_slots, wait until slot s is free (slot_events[s]); then
- *                     sfi_dense_decode(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride)
- *   on `side_stream`: wait for that dense step (attn_event); sfi_select(&kv[l], logits[s], ...)
+ *                     the dense step of sfi_slow_step(&kv[l], q[l], out[l], lse[l], logits[s],
+ *                     logit_stride, ...), its records in dense_ws and its normaliser over J in
+ *                     sel_ws[s]
+ *   on `side_stream`: wait for that dense step (attn_event); the Selector of sfi_slow_step
  *                     into idx[l], n_idx[l] with workspace sel_ws[s]; when head_mask is not NULL,
  *                     sfi_sink_bypass_mask(&kv[l], logits[s], lse[l], mask_frac, head_mask[l]);
  *                     then record slot_events[s] (slot s free again); when seg_k is not
@@ -374,13 +376,16 @@ sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
  *                     (SFI Sec. 4.1: Reorg_i follows Sel_i on the maintenance stream).
  * Finally `stream` waits for everything queued on `side_stream` (done_event), so work queued on
  * `stream` after this call sees every layer's indices, masks and compact segments.  Every
- * result equals that of the per-layer calls made one after another.
+ * result equals that of sfi_slow_step (and sfi_reorg) called layer after layer, bit for bit.
  * Arguments: kv, q, out, lse, idx, n_idx (and head_mask, or NULL; seg_k, seg_v, seg_pos, all
  * NULL or all given, laid out as for sfi_reorg with idx_stride) are host arrays of n_layers
  * entries; logits and sel_ws are host arrays of n_slots entries; all the pointers in them are
- * device buffers laid out as for the single calls (lse is required here).  dense_ws (at least
- * SFI_OP_DENSE bytes for every layer) serves the dense steps one after another; each sel_ws[s]
- * needs at least SFI_OP_SELECT bytes.  slot_events (n_slots), attn_event and done_event are
+ * device buffers laid out as for the single calls (lse is required here).  dense_ws serves the
+ * dense steps one after another and each sel_ws[s] holds a slot's normaliser and Selector
+ * workspace: sfi_workspace_bytes(&kv[l], SFI_OP_SLOW, 0, 0) bytes suffice for both (G <= 16).
+ * Measured on MI355X, pipelining only pays for mid-sized slow steps (a ragged batch of 16 at
+ * 8K-32K, one 32K sequence); at 128K x 4 and at 512K, where the dense step alone keeps HBM busy,
+ * a concurrent Selector competes with it and sfi_slow_step layer after layer is faster.  slot_events (n_slots), attn_event and done_event are
  * HIP events created by the caller; the library only records them and waits on them.
  * stream and side_stream must differ; calls that share buffers or events must not overlap.
  * Every layer is validated before anything is queued; on an error nothing has been queued

@@ -572,6 +572,48 @@ SFI_EXPORT sfi_status sfi_sink_bypass_mask(const sfi_kv_desc* kv, const float* l
     return launch_sink_mask(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
 }
 
+namespace {
+
+// Slot layout of the layered slow step: the Selector's normaliser over J [B][Hq], then the
+// Selector's workspace.
+size_t slot_lse_bytes(const sfi_kv_desc& kv) {
+    return align_up((size_t)kv.batch * kv.num_q_heads * sizeof(float));
+}
+
+// Validation and argument packing of one layer of the layered slow step (the fused form of
+// sfi_slow_step, with the dense records in dense_ws and the normaliser and Selector in the
+// slot's workspace).
+sfi_status prep_layer(const sfi_kv_desc* kv, const void* q, float* out, float* lse, float* logits,
+                      int64_t logit_stride, void* dense_ws, size_t dense_ws_bytes, void* sel_ws,
+                      size_t sel_ws_bytes, int32_t n_sink, int32_t n_recent, int32_t k_sel,
+                      int32_t* idx, int32_t idx_stride, int32_t* n_idx, AttnArgs* da,
+                      SelArgs* sa) {
+    if (!lse || !logits) return SFI_E_INVALID;
+    sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    AttnPlan plan;
+    st = plan_attention(*kv, false, 0, 0, &plan, true);
+    if (st != SFI_OK) return st;
+    st = check_ws(dense_ws, dense_ws_bytes, plan.bytes);
+    if (st != SFI_OK) return st;
+    st = prep_dense(kv, q, out, lse, logits, logit_stride, dense_ws, dense_ws_bytes, da);
+    if (st != SFI_OK) return st;
+    const size_t lse_bytes = slot_lse_bytes(*kv);
+    if (!sel_ws || sel_ws_bytes < lse_bytes) return SFI_E_WORKSPACE;
+    st = prep_select(kv, logits, logit_stride, n_sink, n_recent, k_sel, idx, idx_stride, n_idx,
+                     (unsigned char*)sel_ws + lse_bytes, sel_ws_bytes - lse_bytes, sa);
+    if (st != SFI_OK) return st;
+    fill_plan_args(plan, dense_ws, da);
+    da->lse_j = (float*)sel_ws;
+    da->n_sink = n_sink;
+    da->n_recent = n_recent;
+    da->sel_hist = sa->hist;
+    sa->lse_j = da->lse_j;
+    return SFI_OK;
+}
+
+}  // namespace
+
 SFI_EXPORT sfi_status sfi_slow_step_layers(
         int32_t n_layers, const sfi_kv_desc* kv, const void* const* q, float* const* out,
         float* const* lse, int32_t n_slots, float* const* logits, int64_t logit_stride,
@@ -594,13 +636,9 @@ SFI_EXPORT sfi_status sfi_slow_step_layers(
         AttnArgs da;
         SelArgs sa;
         MaskArgs ma;
-        if (!lse[l]) return SFI_E_INVALID;
-        sfi_status st = prep_dense(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride,
-                                   dense_ws, dense_ws_bytes, &da);
-        if (st == SFI_OK && !logits[s]) st = SFI_E_INVALID;
-        if (st == SFI_OK)
-            st = prep_select(&kv[l], logits[s], logit_stride, n_sink, n_recent, k_sel, idx[l],
-                             idx_stride, n_idx[l], sel_ws[s], sel_ws_bytes, &sa);
+        sfi_status st = prep_layer(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride,
+                                   dense_ws, dense_ws_bytes, sel_ws[s], sel_ws_bytes, n_sink,
+                                   n_recent, k_sel, idx[l], idx_stride, n_idx[l], &da, &sa);
         if (st == SFI_OK && head_mask)
             st = prep_mask(&kv[l], logits[s], logit_stride, lse[l], mask_frac, head_mask[l], &ma);
         ReorgArgs ra;
@@ -614,9 +652,9 @@ SFI_EXPORT sfi_status sfi_slow_step_layers(
         AttnArgs da;
         SelArgs sa;
         MaskArgs ma;
-        prep_dense(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride, dense_ws, dense_ws_bytes, &da);
-        prep_select(&kv[l], logits[s], logit_stride, n_sink, n_recent, k_sel, idx[l], idx_stride,
-                    n_idx[l], sel_ws[s], sel_ws_bytes, &sa);
+        prep_layer(&kv[l], q[l], out[l], lse[l], logits[s], logit_stride, dense_ws, dense_ws_bytes,
+                   sel_ws[s], sel_ws_bytes, n_sink, n_recent, k_sel, idx[l], idx_stride, n_idx[l],
+                   &da, &sa);
         // the slot's logits and Selector workspace are free once layer l - n_slots is selected
         if (l >= n_slots && hipStreamWaitEvent(stream, slot_events[s], 0) != hipSuccess) return SFI_E_HIP;
         if (launch_dense(&kv[l], da, stream) != SFI_OK) return SFI_E_HIP;

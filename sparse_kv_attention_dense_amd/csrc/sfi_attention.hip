@@ -102,6 +102,20 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
     const int S = SPARSE ? a.nsplit : splits_of(a, a.len[b]), rec = a.rec_floats;
     const float* base = a.part + (int64_t)(b * a.Hkv + h) * a.nsplit * rec;   // nsplit records per unit
     const int dim = tid % D, ph = tid / D;
+    // dense step of the fused slow step: the last wavefront folds the splits' (m, l) pairs over
+    // J with the same rule, its first batch of loads issued before the main merge
+    constexpr int kJB = 4;                           // pairs per lane per batch
+    const bool j_merge = !SPARSE && a.lse_j != nullptr && (tid >> 6) == kThreads / 64 - 1;
+    float jm[kJB], jl[kJB];
+    if (j_merge) {
+#pragma unroll
+        for (int u = 0; u < kJB; ++u) {
+            const int sp = (tid & 63) + 64 * u;
+            const float* r = base + (int64_t)(sp < S ? sp : 0) * rec + G * D + 2 * G + 2 * g;
+            jm[u] = sp < S ? r[0] : -INFINITY;
+            jl[u] = sp < S ? r[1] : 0.f;
+        }
+    }
     // Records are merged kMB per thread at a time, all loaded before any is used (one memory
     // round trip per batch); records past S read record 0 and count as empty.  Few splits (a
     // ragged batch has 2 per sequence) take small batches, so no loads are wasted.
@@ -166,20 +180,23 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
     if constexpr (!SPARSE) {
         if (a.lse_j) {
             // log-sum-exp over the Selector's allowed set: the same merge over the (m, l) pairs
-            // the splits kept for positions of J, by the last wavefront
-            const int w = tid >> 6, lane = tid & 63;
-            if (w == kThreads / 64 - 1) {
-                float Mj = -INFINITY;
-                for (int s = lane; s < S; s += 64)
-                    Mj = fmaxf(Mj, base[(int64_t)s * rec + G * D + 2 * G + 2 * g]);
-                for (int o = 32; o >= 1; o >>= 1) Mj = fmaxf(Mj, __shfl_xor(Mj, o));
-                const float Mu = (Mj == -INFINITY) ? 0.f : Mj;
-                float Lj = 0.f;
-                for (int s = lane; s < S; s += 64) {
-                    const float* r = base + (int64_t)s * rec + G * D + 2 * G + 2 * g;
-                    Lj += exp2_fast(r[0] - Mu) * r[1];
+            // the splits kept for positions of J, by the last wavefront (one pass)
+            const int lane = tid & 63;
+            if (j_merge) {
+                float Mj = -INFINITY, Lj = 0.f;
+                auto fold = [&](float m, float l) {
+                    const float Mn = fmaxf(Mj, m);
+                    if (Mn == -INFINITY) return;
+                    Lj = Lj * exp2_fast(Mj - Mn) + l * exp2_fast(m - Mn);
+                    Mj = Mn;
+                };
+#pragma unroll
+                for (int u = 0; u < kJB; ++u) fold(jm[u], jl[u]);
+                for (int sp = lane + 64 * kJB; sp < S; sp += 64) {
+                    const float* r = base + (int64_t)sp * rec + G * D + 2 * G + 2 * g;
+                    fold(r[0], r[1]);
                 }
-                for (int o = 32; o >= 1; o >>= 1) Lj += __shfl_xor(Lj, o);
+                for (int o = 32; o >= 1; o >>= 1) fold(__shfl_xor(Mj, o), __shfl_xor(Lj, o));
                 if (lane == 0) a.lse_j[b * a.Hq + i] = Lj > 0.f ? (Mj + log2f(Lj)) * kLn2 : -INFINITY;
             }
             // the Selector's digit-0 histogram of this head's KV group starts empty
@@ -759,6 +776,7 @@ attention_kernel(AttnArgs a_in) {
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_run_prev = m_run;
         const float m_new = fmaxf(m_run, tmax);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = exp2_fast(m_run - m_use);
@@ -767,14 +785,23 @@ attention_kernel(AttnArgs a_in) {
 #pragma unroll
         for (int mb = 0; mb < D / 16; ++mb) acc[mb] *= alpha;
         float p[2][4];
+        float psum = 0.f;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[st][i] = exp2_fast(sv[st][i] - m_use);
-                l_run += p[st][i];
+                psum += p[st][i];
             }
-        if (track_j) {
+        l_run += psum;
+        // a tile wholly inside J whose head's J maximum so far is the overall one (every tile
+        // of a split without sink or recent positions) updates the J sums exactly as the
+        // plain ones: same maximum, same weights
+        const bool j_same = track_j && sb >= j_lo && sb + kTile <= j_hi && mj_run == m_run_prev;
+        if (j_same) {
+            lj_run = lj_run * alpha + psum;
+            mj_run = m_new;
+        } else if (track_j) {
             float tj = -INFINITY;
             bool inj[2][4];
 #pragma unroll

@@ -225,8 +225,9 @@ def test_slow_step_layers_validation(L):
     n = 3
     descs = (B.sfi_kv_desc * n)(*[_desc() for _ in range(n)])
     ptrs = lambda k, v=FAKE: (ctypes.c_void_p * k)(*([v] * k))
-    dws = L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_DENSE, 0, 0)
-    sws = L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_SELECT, 0, 0)
+    # SFI_OP_SLOW bytes suffice for the dense workspace and for each Selector slot
+    dws = sws = L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_SLOW, 0, 0)
+    assert dws >= L.sfi_workspace_bytes(ctypes.byref(descs[0]), B.SFI_OP_SELECT, 0, 0)
 
     def call(n_layers=n, descs=descs, n_slots=2, stride=4000, dws_b=dws, sws_b=sws, side=FAKE + 16,
              lse=None, ks=2048, events=None, head_mask=None, frac=0.25, seg=(None, None, None)):
@@ -241,8 +242,8 @@ def test_slow_step_layers_validation(L):
     assert call(side=FAKE) == B.SFI_E_INVALID                 # the two streams must differ
     assert call(events=(ctypes.c_void_p * 2)(FAKE, None)) == B.SFI_E_INVALID
     assert call(lse=(ctypes.c_void_p * n)(FAKE, None, FAKE)) == B.SFI_E_INVALID
-    assert call(dws_b=dws - 1) == B.SFI_E_WORKSPACE
-    assert call(sws_b=sws - 1) == B.SFI_E_WORKSPACE
+    assert call(dws_b=4096) == B.SFI_E_WORKSPACE
+    assert call(sws_b=4096) == B.SFI_E_WORKSPACE
     assert call(stride=4002) == B.SFI_E_INVALID               # logits stride not a multiple of 4
     assert call(ks=5000) == B.SFI_E_INVALID                   # idx_stride < n_sink + k_sel
     assert call(head_mask=ptrs(n), frac=1.5) == B.SFI_E_INVALID

@@ -1,5 +1,5 @@
 """The layer-wise slow step (sfi_slow_step_layers) against the fp64 oracle and against the
-per-layer calls in sequence.
+fused slow step (sfi_slow_step) called layer after layer.
 
 Five layers share the ring slots, so every slot is reused; the Selector, the mask and (when
 asked) the Reorg run on a second stream.  Every layer's out and lse are compared with the
@@ -58,16 +58,13 @@ def test_layered_slow_step_matches_oracle_and_sequential(orc, name, n_slots, reo
             sel_ws=[B.workspace(descs[0], idx_stride=istride, n_recent=wl.n_recent, device=DEV)
                     for _ in range(n_slots)])
 
-    # sequential reference: the single calls, one layer after another
+    # sequential reference: the fused slow step, one layer after another
     ref = bufs()
     for l in range(n_layers):
         s = l % n_slots
-        B.sfi_dense_decode(descs[l], qs[l], ref["out"][l], ref["lse"][l], ref["logits"][s], stride,
-                           dense_ws)
-        B.sfi_select(descs[l], ref["logits"][s], stride, wl.n_sink, wl.n_recent, wl.k_sel,
-                     ref["idx"][l], istride, ref["n_idx"][l], ref["sel_ws"][s])
-        B.sfi_sink_bypass_mask(descs[l], ref["logits"][s], stride, ref["lse"][l], frac,
-                               ref["mask"][l])
+        B.sfi_slow_step(descs[l], qs[l], ref["out"][l], ref["lse"][l], ref["logits"][s], stride,
+                        wl.n_sink, wl.n_recent, wl.k_sel, ref["idx"][l], istride,
+                        ref["n_idx"][l], frac, ref["mask"][l], ref["sel_ws"][s])
         if reorg:
             B.sfi_reorg(descs[l], ref["idx"][l], istride, ref["n_idx"][l], *ref["seg"][l])
     torch.cuda.synchronize()
