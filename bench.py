@@ -327,6 +327,47 @@ def routed_sink_heavy(B, torch, synth, wl, layers, descs, stride, idx_stride, L,
             "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
 
 
+def fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L, grids=(256, 1024)):
+    """Floor of the fast step's access pattern: sfi_gather_read (the same rows, read once with
+    no arithmetic, one launch) over the cycle's fast steps in decode order, timed as one block at
+    each workgroup count, and the GPU-side cost of one launch with almost nothing to do (a 16 KB
+    read by one workgroup, replayed from a captured graph).  The fast step itself needs two launches: its split-K
+    partials and their merge."""
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    tiny = torch.zeros(4096, dtype=torch.int32, device="cuda")
+
+    def block(fn):
+        fn()
+        torch.cuda.synchronize()
+        best = None
+        for rep in range(2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (L * (wl.cycle - 1))
+            best = us if best is None else min(best, us)
+        return best
+
+    gather = {}
+    for g in grids:
+        gather[g] = block(lambda: [B.sfi_gather_read(descs[li][t], idxs[li], idx_stride,
+                                                     nidxs[li], wl.n_recent, g, sink)
+                                   for t in range(1, wl.cycle) for li in range(L)])
+    # one launch with almost nothing to do, replayed from a captured graph so that the host's
+    # own call overhead (larger than the GPU's per-launch cost) does not set the pace
+    n_launch = L * (wl.cycle - 1)
+    launch = graph_replay(torch, lambda: [B.sfi_stream_read(tiny, 1, sink) for _ in range(n_launch)],
+                          n_launch)
+    best = min(gather, key=gather.get)
+    return {"gather_read_us": round(gather[best], 2), "gather_read_workgroups": best,
+            "gather_read_us_by_workgroups": {str(g): round(v, 2) for g, v in gather.items()},
+            "one_launch_us": round(launch, 2),
+            "two_launch_floor_us": round(gather[best] + launch, 2)}
+
+
 def graph_replay(torch, run, per_replay: int, reps: int = 3):
     """The stack cycle run() captured once in a HIP graph (torch.cuda.CUDAGraph: the library's
     calls queue kernels only) and replayed back to back, timed on the host clock like the
@@ -843,6 +884,9 @@ def main():
         print("# stack cycle replayed from a HIP graph", file=sys.stderr, flush=True)
         graph_us = graph_replay(torch, lambda: cycle("none"), wl.cycle * L)
 
+    print("# fast-step floor (gather read, one launch)", file=sys.stderr, flush=True)
+    floor = fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L)
+
     print("# fast steps on synthetic selections", file=sys.stderr, flush=True)
     synth_fast = synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out,
                                                 lse, ws, idx_stride, L)
@@ -957,6 +1001,12 @@ def main():
         result["two_segment"] = two_seg
     result["roofline"]["frac_of_measured_read"] = round(dense_gbps / yard["gbps"], 4)
     result["fast_roofline"]["frac_of_measured_read"] = round(fast_gbps / yard["gbps"], 4)
+    floor["gather_read_frac_of_peak"] = round(f_bytes / (floor["gather_read_us"] * 1e-6) / 1e9
+                                              / PEAK_HBM_GBS, 4)
+    floor["two_launch_floor_frac_of_peak"] = round(
+        f_bytes / (floor["two_launch_floor_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+    floor["fast_us_over_two_launch_floor"] = round(fast_us / floor["two_launch_floor_us"], 3)
+    result["fast_roofline"]["floor"] = floor
     result["fast_synthetic_selections"] = synth_fast
     if routed is not None:
         result["routed_fast"] = routed

@@ -24,6 +24,8 @@
  *     sparse kernel)                          -> sfi_reorg, sfi_sparse_decode_compact
  *   - a plain streaming read, the measured bandwidth yardstick (not a step of the method)
  *                                                                        -> sfi_stream_read
+ *   - a read of exactly the rows a fast step gathers, its floor (not a step of the method)
+ *                                                                        -> sfi_gather_read
  *
  * Conventions shared by every call
  *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
@@ -418,6 +420,18 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride
  *                  equals a fixed constant (practically never), so its contents are undefined
  *   n_workgroups   1 ... 2^20
  * SFI_E_INVALID for a null pointer, a bad size, alignment or count; asynchronous on stream. */
+/* Measurement yardstick, not a step of the method: the key and value rows that
+ * sfi_sparse_decode reads for these arguments (index entries below the recent window, a
+ * stand-in row for each skipped entry, then the recent window, through the block table when
+ * paged), read once each with 16-byte loads by about n_workgroups workgroups in one launch,
+ * with no arithmetic.  Timed with events it is the floor of the fast step's access pattern in
+ * one launch (the fast step itself also computes, and merges its splits in a second launch).
+ * kv, idx, idx_stride, n_idx, n_recent as for sfi_sparse_decode; sink as for sfi_stream_read.
+ * SFI_E_INVALID for a null pointer, a bad size or count; asynchronous on stream. */
+sfi_status sfi_gather_read(const sfi_kv_desc* kv, const int32_t* idx, int32_t idx_stride,
+                           const int32_t* n_idx, int32_t n_recent, int32_t n_workgroups,
+                           uint32_t* sink, hipStream_t stream);
+
 sfi_status sfi_stream_read(const void* buf, uint64_t bytes, int32_t n_workgroups, uint32_t* sink,
                            hipStream_t stream);
 

@@ -24,7 +24,8 @@ SFI_OP_DENSE, SFI_OP_SELECT, SFI_OP_SPARSE, SFI_OP_SELECT_REFINED, SFI_OP_SLOW =
 EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_slow_step", "sfi_select_refined", "sfi_sink_bypass_mask",
             "sfi_sparse_decode", "sfi_sparse_decode_noalloc", "sfi_sparse_decode_step",
             "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
-            "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_status_string")
+            "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_gather_read",
+            "sfi_status_string")
 
 
 class SfiError(RuntimeError):
@@ -85,6 +86,7 @@ def lib():
         L.sfi_slow_step_layers.argtypes = [i32, D, P, P, P, i32, P, i64, P, ctypes.c_size_t, P,
                                            ctypes.c_size_t, i32, i32, i32, P, i32, P,
                                            ctypes.c_float, P, P, P, P, P, P, P, P, P]
+        L.sfi_gather_read.argtypes = [D, P, i32, P, i32, i32, P, P]
         L.sfi_workspace_bytes.argtypes = [D, i32, i32, i32]
         L.sfi_workspace_bytes.restype = ctypes.c_size_t
         L.sfi_reorg.argtypes = [D, P, i32, P, P, P, P, P]
@@ -272,6 +274,17 @@ def sfi_stream_read(buf, n_workgroups: int, sink, stream=None):
     _buf(sink, "sink", _I32, 64)
     _check(lib().sfi_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(n_workgroups),
                                  _ptr(sink), _stream(stream)), "sfi_stream_read")
+
+
+def sfi_gather_read(desc: KVDesc, idx, idx_stride: int, n_idx, n_recent: int,
+                    n_workgroups: int, sink, stream=None):
+    desc.need_cache("sfi_gather_read")
+    _buf(idx, "idx", _I32, desc.units * int(idx_stride))
+    _buf(n_idx, "n_idx", _I32, desc.units)
+    _buf(sink, "sink", _I32, 64)
+    _check(lib().sfi_gather_read(desc.ref, _ptr(idx), int(idx_stride), _ptr(n_idx),
+                                 int(n_recent), int(n_workgroups), _ptr(sink), _stream(stream)),
+           "sfi_gather_read")
 
 
 def sfi_dense_decode(desc: KVDesc, q, out, lse, logits, logit_stride: int, ws, stream=None):

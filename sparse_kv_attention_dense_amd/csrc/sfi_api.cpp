@@ -782,6 +782,41 @@ SFI_EXPORT sfi_status sfi_stream_read(const void* buf, uint64_t bytes, int32_t n
                                                                                      : SFI_E_HIP;
 }
 
+SFI_EXPORT sfi_status sfi_gather_read(const sfi_kv_desc* kv, const int32_t* idx,
+                                      int32_t idx_stride, const int32_t* n_idx, int32_t n_recent,
+                                      int32_t n_workgroups, uint32_t* sink, hipStream_t stream) {
+    const sfi_status st = check_desc(kv, true);
+    if (st != SFI_OK) return st;
+    if (!idx || !n_idx || !sink || idx_stride < 1 || n_recent < 0 || !aligned(sink, 4) ||
+        n_workgroups < 1 || n_workgroups > (1 << 20))
+        return SFI_E_INVALID;
+    const int64_t units = (int64_t)kv->batch * kv->num_kv_heads;
+    const int64_t slots = (int64_t)idx_stride + n_recent;
+    const int64_t per_unit = ceil_div(n_workgroups, units);
+    const int64_t split = ceil_div(ceil_div(slots, per_unit), kTile) * kTile;
+    const int64_t nsplit = ceil_div(slots, split);
+    if (nsplit > 65535) return SFI_E_UNSUPPORTED;
+    GatherArgs a;
+    memset(&a, 0, sizeof a);
+    a.k = kv->k;
+    a.v = kv->v;
+    a.len = kv->len;
+    a.block_table = kv->block_table;
+    a.n_cap = kv->n_cap;
+    if (kv->block_table)
+        while ((1 << a.block_shift) < kv->block_size) ++a.block_shift;
+    a.max_blocks = kv->max_blocks;
+    a.Hkv = kv->num_kv_heads;
+    a.row_bytes = kv->head_dim * (kv->dtype == SFI_BF16 ? 2 : 4);
+    a.idx = idx;
+    a.idx_stride = idx_stride;
+    a.n_idx = n_idx;
+    a.n_recent = n_recent;
+    a.split_len = (int32_t)split;
+    a.sink = sink;
+    return launch_gather_read(a, (int)nsplit, kv->batch, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
 SFI_EXPORT const char* sfi_status_string(sfi_status s) {
     switch (s) {
         case SFI_OK: return "SFI_OK: success";

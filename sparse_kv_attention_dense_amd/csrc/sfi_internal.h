@@ -153,4 +153,22 @@ constexpr int kStreamSinkWords = 64;
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, int n_wg, uint32_t* sink,
                               hipStream_t stream);
 
+// Gather yardstick (sfi_stream.hip): the key and value rows of a fast step, no arithmetic.
+struct GatherArgs {
+    const void* k;
+    const void* v;
+    const int32_t* len;
+    const int32_t* block_table;      // null when contiguous
+    int64_t n_cap;
+    int32_t block_shift, max_blocks, Hkv;
+    int32_t row_bytes;               // d * element bytes
+    const int32_t* idx;
+    int32_t idx_stride;
+    const int32_t* n_idx;
+    int32_t n_recent;
+    int32_t split_len;               // slots per workgroup
+    uint32_t* sink;
+};
+hipError_t launch_gather_read(const GatherArgs& a, int nsplit, int B, hipStream_t stream);
+
 }  // namespace sfi

@@ -265,6 +265,19 @@ def test_stream_read_validation(L):
     assert L.sfi_stream_read(FAKE, 1 << 20, (1 << 20) + 1, FAKE, None) == B.SFI_E_INVALID
 
 
+def test_gather_read_validation(L):
+    d = _desc()
+    gr = lambda dd=d, idx=FAKE, istride=2052, nidx=FAKE, nr=256, wg=256, sink=FAKE: \
+        L.sfi_gather_read(ctypes.byref(dd), idx, istride, nidx, nr, wg, sink, None)
+    assert gr(idx=None) == B.SFI_E_INVALID
+    assert gr(nidx=None) == B.SFI_E_INVALID
+    assert gr(sink=None) == B.SFI_E_INVALID
+    assert gr(istride=0) == B.SFI_E_INVALID
+    assert gr(nr=-1) == B.SFI_E_INVALID
+    assert gr(wg=0) == B.SFI_E_INVALID
+    assert gr(dd=_desc(head_dim=96)) == B.SFI_E_UNSUPPORTED
+
+
 def test_reorg_and_two_segment_validation(L):
     d = _desc()
     D = ctypes.byref(d)

@@ -41,3 +41,55 @@ def test_stream_read_reads_every_word(nbytes, wg):
     B.sfi_stream_read(buf, wg, sink)
     torch.cuda.synchronize()
     assert torch.equal(sink, torch.full_like(sink, 5))
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_gather_read_reads_the_fast_steps_rows(paged):
+    """The gather yardstick (sfi_gather_read) reads the rows of the selected positions and of
+    the recent window, and no other: over a zeroed cache with the kernel's constant planted in
+    one key row, a sink word changes exactly when that row is one the fast step attends."""
+    Bsz, Hkv, Hq, d, N, n_recent, bs = 2, 2, 8, 128, 3000, 64, 16
+    g = torch.Generator().manual_seed(5)
+    sel = [[sorted(torch.randperm(N - n_recent, generator=g)[:100].tolist()) for _ in range(Hkv)]
+           for _ in range(Bsz)]
+    idx = torch.zeros((Bsz, Hkv, 100), dtype=torch.int32)
+    for b in range(Bsz):
+        for h in range(Hkv):
+            idx[b, h] = torch.tensor(sel[b][h], dtype=torch.int32)
+    idx = idx.to(DEV)
+    n_idx = torch.full((Bsz, Hkv), 100, dtype=torch.int32, device=DEV)
+    lens = torch.full((Bsz,), N, dtype=torch.int32, device=DEV)
+    nblk = (N + bs - 1) // bs
+    if paged:
+        perm = torch.randperm(Bsz * nblk, generator=g).to(torch.int32)
+        bt = perm.view(Bsz, nblk).to(DEV)
+        K = torch.zeros((Bsz * nblk, Hkv, bs, d), dtype=torch.bfloat16, device=DEV)
+        desc = B.KVDesc(K, torch.zeros_like(K), lens, N, Hq, block_table=bt, block_size=bs)
+    else:
+        K = torch.zeros((Bsz, Hkv, N, d), dtype=torch.bfloat16, device=DEV)
+        desc = B.KVDesc(K, torch.zeros_like(K), lens, N, Hq)
+    words = K.view(torch.int32)                      # two bf16 per word, 64 words per row
+
+    def row_words(b, h, pos):
+        if paged:
+            return words[int(bt[b, pos // bs]), h, pos % bs]
+        return words[b, h, pos]
+
+    sink = torch.zeros(64, dtype=torch.int32, device=DEV)
+    cases = []
+    for b in range(Bsz):
+        for h in range(Hkv):
+            s_set = set(sel[b][h])
+            cases.append((b, h, sel[b][h][37], True))                       # selected
+            cases.append((b, h, next(p for p in range(5, N) if p not in s_set and p < N - n_recent),
+                          False))                                          # not selected
+            cases.append((b, h, N - 5, True))                               # recent window
+    for b, h, pos, hit in cases:
+        K.zero_()
+        row_words(b, h, pos)[3] = MAGIC
+        sink.zero_()
+        B.sfi_gather_read(desc, idx, 100, n_idx, n_recent, 64, sink)
+        torch.cuda.synchronize()
+        changed = bool((sink != 0).any())
+        assert changed == hit, f"position {pos} of ({b},{h}): read {changed}, expected {hit}"
+    say(f"    {len(cases)} planted rows: read exactly the fast step's rows")
