@@ -150,7 +150,7 @@ struct SelPlan {
     int nchunk = 0;
     size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0;
     size_t off_cand = 0, off_cand_n = 0, bytes = 0;
-    size_t off_zpart = 0, off_nms = 0, bytes_refined = 0;   // full Selector only
+    size_t off_zpart = 0, off_lfused = 0, bytes_refined = 0;   // full Selector only
 };
 
 void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
@@ -167,7 +167,7 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     p->off_cand_n = off; off += align_up(B * Hkv * nc * sizeof(uint32_t));
     p->bytes = off;
     p->off_zpart = off;  off += align_up(B * Hkv * nc * sizeof(float));
-    p->off_nms = off;    off += align_up(B * Hkv * nc * kSelChunk * sizeof(float));
+    p->off_lfused = off; off += align_up(B * Hkv * nc * kSelChunk * sizeof(float));
     p->bytes_refined = off;
 }
 
@@ -276,7 +276,7 @@ sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit
     a->keep_soft = a->keep_cross = 1.f;
     a->prior_decay = a->tail_frac = a->tail_brake = 0.f;
     a->zpart = nullptr;
-    a->nms = nullptr;
+    a->lfused = nullptr;
     a->lse_j = nullptr;
     return SFI_OK;
 }
@@ -559,7 +559,7 @@ SFI_EXPORT sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* log
     a.tail_frac = p.tail_frac;
     a.tail_brake = p.tail_brake;
     a.zpart = (float*)((unsigned char*)ws + plan.off_zpart);
-    a.nms = (float*)((unsigned char*)ws + plan.off_nms);
+    a.lfused = (float*)((unsigned char*)ws + plan.off_lfused);
     return launch_select(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
 }
 

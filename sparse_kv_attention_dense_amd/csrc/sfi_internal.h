@@ -112,7 +112,8 @@ struct SelArgs {
     float keep_soft, keep_cross;     // 1 - alpha_soft, 1 - alpha_cross
     float prior_decay, tail_frac, tail_brake;
     float* zpart;                    // [B][Hkv][nchunk]: partial sums of f^(1-lam) r^lam
-    float* nms;                      // [B][Hkv][nchunk*kSelChunk]: fused scores after Soft-NMS
+    float* lfused;                   // [B][Hkv][nchunk*kSelChunk]: log2 of f^(1-lam) r^lam by
+                                     //   j - j0 (unnormalised), written by the evidence pass
 };
 
 hipError_t launch_select(const SelArgs& a, hipStream_t stream);

@@ -26,13 +26,14 @@
 // (b, KV head).
 // Full Selector (refine mode, SFI Sec. 3.2 prior and reverse-KL fusion, Sec. 3.3 Soft-NMS and
 // cross-head exclusivity; the pages' formulas are lost and the library implements stated
-// readings of them): the evidence pass also sums f^(1-lam) r^lam per chunk instead of building
-// the histogram, then
-//   refine_nms_kernel    s = f^(1-lam) r^lam / Z per position of the chunk (and its two
-//                         neighbours), decayed by 1 - alpha_soft when a neighbour in J is larger
-//   refine_cross_kernel  per sequence and chunk: every KV head below the largest at a position
-//                         is decayed by 1 - alpha_cross; the results are the keys, and the
-//                         digit-0 histograms are built from them
+// readings of them): the evidence pass stores log2(f^(1-lam) r^lam) per position and sums
+// f^(1-lam) r^lam per chunk instead of building the histogram, then
+//   refine_kernel        per sequence and quarter chunk, for every KV head: s = f^(1-lam) r^lam / Z
+//                         per position (from the log2 scores the evidence pass stored, and its two
+//                         neighbours'), decayed by 1 - alpha_soft
+//                         when a neighbour in J is larger; then every KV head below the largest
+//                         at a position is decayed by 1 - alpha_cross; the results are the
+//                         keys, and the digit-0 histograms are built from them
 // before the candidate, resolve and emit passes, which are unchanged.
 // f is computed without the 1/G factor: a positive common scale does not change the order.
 //
@@ -228,6 +229,21 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
         }
     };
     load4(0);
+    // the key norms of the full Selector's prior, with the first quads (clamped into the chunk)
+    float nrm[kEvQ][4];
+    if (a.refine && a.key_norm) {
+        const float* kn = a.key_norm + (int64_t)unit * a.norm_stride;
+#pragma unroll
+        for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                nrm[k][e] = kn[min(max(base + 4 * (k * kThreads + tid) + e, lo), hi - 1)];
+    } else {
+#pragma unroll
+        for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) nrm[k][e] = 1.f;
+    }
     if (!a.refine)
         for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
     if (a.lse_j) {
@@ -268,7 +284,9 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     }
     uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
     if (a.refine) {
-        // keys of f for the refinement passes, and this chunk's share of the fusion normaliser
+        // log2 of the unnormalised fused score for the refinement pass, and this chunk's share
+        // of the fusion normaliser
+        float* lf = a.lfused + ((int64_t)unit * a.nchunk + c) * kSelChunk;
         float zs = 0.f;
 #pragma unroll
         for (int k = 0; k < kEvQ; ++k)
@@ -276,8 +294,9 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
             for (int e = 0; e < 4; ++e) {
                 const int j = base + 4 * (k * kThreads + tid) + e;
                 if (j >= lo && j < hi) {
-                    keys[j - lo] = __float_as_uint(f[k][e]);
-                    zs += exp2_hw(fused_log2(a, f[k][e], prior_log2(a, unit, j, r.j0, r.nJ)));
+                    const float l = fused_log2(a, f[k][e], prior_log2_n(a, j, r.j0, r.nJ, nrm[k][e]));
+                    lf[j - lo] = l;
+                    zs += exp2_hw(l);
                 }
             }
         zs = block_sum(zs, sh);
@@ -297,123 +316,177 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
         }
     __syncthreads();
     uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
-    for (int t = tid; t < kCBins0; t += kThreads)
-        if (lh[t]) atomicAdd(&hg[t], lh[t]);
-}
-
-// Fused score and Soft-NMS for one (chunk, KV head, sequence).  The log2 scores of the chunk's
-// positions and of the neighbours just outside it are computed once, by one code path, into
-// LDS; a position is decayed by keep_soft when a neighbour in J has a strictly larger score.
-__global__ void __launch_bounds__(kThreads) refine_nms_kernel(SelArgs a) {
-    __shared__ float sh[4];
-    __shared__ float ls[kSelChunk + 2];             // positions lo - 1 ... hi
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
-    const int unit = b * a.Hkv + h;
-    const Range r = j_range(a, b);
-    const int lo = r.j0 + c * kSelChunk;
-    const int hi = min(r.j1, lo + kSelChunk);
-    if (lo >= hi) return;
-    const uint32_t* keys_u = a.keys + (int64_t)unit * a.nchunk * kSelChunk;   // by j - j0
-    const int p0 = max(lo - 1, r.j0), p1 = min(hi + 1, r.j1);
-    // every load of the thread first (evidence, key norm, the normaliser's parts), then the
-    // scores
-    constexpr int kM = kPerThread + 1;                  // covers kSelChunk + 2 positions
-    float fv[kM], nv[kM];
-#pragma unroll
-    for (int m = 0; m < kM; ++m) {
-        const int p = p0 + m * kThreads + tid;
-        fv[m] = p < p1 ? __uint_as_float(keys_u[p - r.j0]) : 0.f;
-        nv[m] = (p < p1 && a.key_norm) ? a.key_norm[(int64_t)unit * a.norm_stride + p] : 1.f;
-    }
-    const int nc = (r.nJ + kSelChunk - 1) / kSelChunk;
-    float zs = 0.f;
-    for (int k = tid; k < nc; k += kThreads) zs += a.zpart[(int64_t)unit * a.nchunk + k];
-    const float l2z = __log2f(block_sum(zs, sh));
-#pragma unroll
-    for (int m = 0; m < kM; ++m) {
-        const int p = p0 + m * kThreads + tid;
-        if (p < p1)
-            ls[p - (lo - 1)] = fused_log2(a, fv[m], prior_log2_n(a, p, r.j0, r.nJ, nv[m])) - l2z;
-    }
-    __syncthreads();
-    float* out = a.nms + (int64_t)unit * a.nchunk * kSelChunk;
-#pragma unroll 4
-    for (int k = 0; k < kPerThread; ++k) {
-        const int j = lo + k * kThreads + tid;
-        if (j < hi) {
-            const float v = ls[j - (lo - 1)];
-            const bool lower = (j > r.j0 && ls[j - 1 - (lo - 1)] > v) ||
-                               (j + 1 < r.j1 && ls[j + 1 - (lo - 1)] > v);
-            out[j - r.j0] = exp2_hw(v) * (lower ? a.keep_soft : 1.f);
-        }
+    // bins 2t and 2t + 1 as one 64-bit add (the low and high halves of a little-endian word;
+    // no count reaches 2^32, so no carry crosses between them)
+    for (int t = tid; t < kCBins0 / 2; t += kThreads) {
+        const uint2 n = *(const uint2*)&lh[2 * t];
+        if (n.x | n.y)
+            atomicAdd((unsigned long long*)hg + t,
+                      (unsigned long long)n.x | ((unsigned long long)n.y << 32));
     }
 }
 
-// Cross-head exclusivity for one (part of a chunk, sequence): at each position every KV head
-// whose score is below the largest is decayed by keep_cross.  The results become the keys, and
-// the digit-0 histogram of each unit is built from them (one LDS histogram, reused head by
-// head).  A chunk is split over kCrossParts workgroups so the launch fills the chip.
-constexpr int kCrossParts = 4;
-constexpr int kCrossPer = kPerThread / kCrossParts;    // positions per thread
-static_assert(kPerThread % kCrossParts == 0, "a chunk part holds whole rows of threads");
-constexpr int kCrossRegHeads = 16;                      // heads whose scores stay in registers
-__global__ void __launch_bounds__(kThreads) refine_cross_kernel(SelArgs a) {
-    __shared__ uint32_t lh[kCBins0];
+// Fused score, Soft-NMS and cross-head exclusivity for one quarter of a chunk of J of one
+// sequence, every KV head of it.  Thread t takes the 4 consecutive positions lo + 4t ... and
+// forms, from the evidence pass's log2 fused scores of those positions and the one on each side,
+// the normalised log2 score s = log2(f^(1-lam) r^lam) - log2 Z_h, then the Soft-NMS score
+// exp2(s), times keep_soft where a neighbour in J has a strictly larger s.  The loads of up to
+// kRefHeads heads (one 16-byte load per lane and the neighbours of the wave's ends, clamped into
+// J, per head; the other neighbours come from the adjacent lanes) and of the heads' chunk sums
+// are issued together at entry, and the normalisers take one barrier.  At each
+// position every head below the largest is then decayed by keep_cross; the results are the keys.
+// Each unit's digit-0 histogram is built from them in LDS with two 16-bit counts per word (a
+// workgroup counts at most kRefSpan keys per head), every head of the group in one pass, then
+// added to the unit's histogram in global memory.  The scores are read from their own buffer, so
+// the neighbours' keys written by other workgroups never feed a score.
+constexpr int kCrossParts = 2;                         // workgroups per chunk
+constexpr int kRefSpan = kSelChunk / kCrossParts;      // positions per workgroup
+constexpr int kRefThreads = kRefSpan / 4;              // four positions per thread
+constexpr int kRefWaves = kRefThreads / 64;
+constexpr int kRefHeads = 8;                           // heads held in registers at a time
+constexpr int kRefWords = kCBins0 / 2;                 // packed histogram words per head
+static_assert(kRefThreads % 64 == 0 && kRefThreads <= 1024, "whole waves, one workgroup");
+static_assert(kRefSpan < 65536, "a 16-bit count holds every key of a workgroup");
+static_assert(kSelChunk % 4 == 0, "16-byte loads of the score buffer");
+static_assert((kRefHeads * kRefWords) % (4 * kRefThreads) == 0, "16-byte clears of the histograms");
+__global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
+    __shared__ float s_z[kRefWaves][kRefHeads];
+    __shared__ uint32_t lh[kRefHeads][kRefWords];
     const int c = blockIdx.x / kCrossParts, part = blockIdx.x % kCrossParts;
-    const int b = blockIdx.y, tid = threadIdx.x;
+    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const Range r = j_range(a, b);
-    const int lo = r.j0 + c * kSelChunk + part * (kSelChunk / kCrossParts);
-    const int hi = min(r.j1, lo + kSelChunk / kCrossParts);
+    const int lo = r.j0 + c * kSelChunk + part * kRefSpan;
+    const int hi = min(r.j1, lo + kRefSpan);
     if (lo >= hi) return;
-    const int64_t chunk_off = (int64_t)c * kSelChunk + part * (kSelChunk / kCrossParts);
     const int64_t unit_len = (int64_t)a.nchunk * kSelChunk;
-    const float* nms_b = a.nms + (int64_t)b * a.Hkv * unit_len + chunk_off;
-    // the scores of the first kCrossRegHeads heads are loaded once, all in flight together
-    float v[kCrossRegHeads][kCrossPer];
+    const int nc = (r.nJ + kSelChunk - 1) / kSelChunk;
+    const int pb = lo + 4 * tid;                       // first of this thread's positions
+    // offsets into a unit's score buffer: the quad (a multiple of 4, inside the chunk's region
+    // even past hi), and the neighbours of the wave's first and last positions, clamped into J
+    // (the other neighbours come from the adjacent lanes)
+    const int jq = pb - r.j0;
+    const int pw = lo + 4 * (tid & ~63);
+    const int jl = max(pw - 1, r.j0) - r.j0;
+    const int jr = min(pw + 4 * 64, r.j1 - 1) - r.j0;
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    float sc[kRefHeads][4];
+    // heads are taken kRefHeads at a time; with more heads than that, the scores are computed
+    // twice (once for the maxima, once for the keys)
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int h0 = 0; h0 < a.Hkv; h0 += kRefHeads) {
+            const int nh = min(kRefHeads, a.Hkv - h0);
+            if (pass == 1 && a.Hkv <= kRefHeads) {
+                // the scores of pass 0 are still in registers
+            } else {
+                f32x4 q[kRefHeads];
+                float ql[kRefHeads], qr[kRefHeads], zs[kRefHeads];
 #pragma unroll
-    for (int h = 0; h < kCrossRegHeads; ++h)
+                for (int hh = 0; hh < kRefHeads; ++hh) {
+                    const int unit = b * a.Hkv + h0 + min(hh, nh - 1);
+                    const float* lf = a.lfused + (int64_t)unit * unit_len;
+                    q[hh] = *(const f32x4*)(lf + jq);
+                    ql[hh] = lf[jl];                   // the same address in every lane
+                    qr[hh] = lf[jr];
+                    zs[hh] = 0.f;
+                }
+                for (int k = tid; k < nc; k += kRefThreads)
 #pragma unroll
-        for (int k = 0; k < kCrossPer; ++k) {
-            const int t = k * kThreads + tid;
-            v[h][k] = (h < a.Hkv && lo + t < hi) ? nms_b[h * unit_len + t] : -INFINITY;
-        }
-    float mx[kCrossPer];
+                    for (int hh = 0; hh < kRefHeads; ++hh)
+                        zs[hh] += a.zpart[(int64_t)(b * a.Hkv + h0 + min(hh, nh - 1)) * a.nchunk + k];
+                if (pass == 1) {
+                    // the histograms of this group start from zero; the barrier below orders the
+                    // clear after the previous group's flush and before any count
+                    u32x4* l4 = (u32x4*)&lh[0][0];
+                    for (int t = tid; t < kRefHeads * kRefWords / 4; t += kRefThreads)
+                        l4[t] = u32x4{0u, 0u, 0u, 0u};
+                }
 #pragma unroll
-    for (int k = 0; k < kCrossPer; ++k) {
-        mx[k] = -INFINITY;
+                for (int hh = 0; hh < kRefHeads; ++hh) zs[hh] = wave_sum(zs[hh]);
+                if (lane == 0)
 #pragma unroll
-        for (int h = 0; h < kCrossRegHeads; ++h) mx[k] = fmaxf(mx[k], v[h][k]);
-    }
-    for (int h = kCrossRegHeads; h < a.Hkv; ++h)
+                    for (int hh = 0; hh < kRefHeads; ++hh) s_z[w][hh] = zs[hh];
+                __syncthreads();
 #pragma unroll
-        for (int k = 0; k < kCrossPer; ++k) {
-            const int t = k * kThreads + tid;
-            if (lo + t < hi) mx[k] = fmaxf(mx[k], nms_b[h * unit_len + t]);
-        }
-    for (int h = 0; h < a.Hkv; ++h) {
-        const int unit = b * a.Hkv + h;
-        for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
-        __syncthreads();
-        uint32_t* keys = a.keys + (int64_t)unit * unit_len + chunk_off;
+                for (int hh = 0; hh < kRefHeads; ++hh) {
+                    float z = 0.f;
 #pragma unroll
-        for (int k = 0; k < kCrossPer; ++k) {
-            const int t = k * kThreads + tid;
-            if (lo + t < hi) {
-                float x = 0.f;
+                    for (int v = 0; v < kRefWaves; ++v) z += s_z[v][hh];
+                    const float l2z = __log2f(z);
+                    const float up = __shfl_up(q[hh][3], 1), dn = __shfl_down(q[hh][0], 1);
+                    const float left = lane == 0 ? ql[hh] : up;
+                    const float right = lane == 63 ? qr[hh] : dn;
+                    const float ls[6] = {left - l2z,      q[hh][0] - l2z, q[hh][1] - l2z,
+                                         q[hh][2] - l2z, q[hh][3] - l2z, right - l2z};
 #pragma unroll
-                for (int hh = 0; hh < kCrossRegHeads; ++hh)
-                    if (hh == h) x = v[hh][k];
-                if (h >= kCrossRegHeads) x = nms_b[h * unit_len + t];
-                const uint32_t key = __float_as_uint(x < mx[k] ? x * a.keep_cross : x);
-                keys[t] = key;
-                atomicAdd(&lh[key >> kCShift[0]], 1u);
+                    for (int e = 1; e < 5; ++e) {
+                        const int j = pb - 1 + e;
+                        const bool lower = (j > r.j0 && ls[e - 1] > ls[e]) ||
+                                           (j + 1 < r.j1 && ls[e + 1] > ls[e]);
+                        sc[hh][e - 1] = (j < hi) ? exp2_hw(ls[e]) * (lower ? a.keep_soft : 1.f)
+                                                 : -INFINITY;
+                    }
+                }
+                if (a.Hkv > kRefHeads) __syncthreads();    // s_z is reused by the next group
             }
+            if (pass == 0) {
+#pragma unroll
+                for (int hh = 0; hh < kRefHeads; ++hh)
+                    if (hh < nh)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) mx[e] = fmaxf(mx[e], sc[hh][e]);
+                if (a.Hkv <= kRefHeads) {
+                    // pass 1 loads nothing: clear the histograms here, ordered by the barrier
+                    // after the maxima
+                    u32x4* l4 = (u32x4*)&lh[0][0];
+                    for (int t = tid; t < kRefHeads * kRefWords / 4; t += kRefThreads)
+                        l4[t] = u32x4{0u, 0u, 0u, 0u};
+                    __syncthreads();
+                }
+                continue;
+            }
+            // pass 1: exclusivity, keys and the packed histograms of the group
+#pragma unroll
+            for (int hh = 0; hh < kRefHeads; ++hh) {
+                if (hh >= nh) continue;
+                const int unit = b * a.Hkv + h0 + hh;
+                uint32_t* keys = a.keys + (int64_t)unit * unit_len;
+                u32x4 kk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x = sc[hh][e];
+                    kk[e] = __float_as_uint(x < mx[e] ? x * a.keep_cross : x);
+                }
+                if (pb + 3 < hi) {
+                    *(u32x4*)(keys + jq) = kk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (pb + e < hi) keys[jq + e] = kk[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (pb + e < hi) {
+                        const uint32_t bin = kk[e] >> kCShift[0];
+                        atomicAdd(&lh[hh][bin >> 1], 1u << (16 * (bin & 1u)));
+                    }
+            }
+            __syncthreads();
+            // the two counts of a word go to the unit's histogram as one 64-bit add (bins 2i and
+            // 2i + 1 are the low and high halves of a little-endian 64-bit word; a count stays far
+            // below 2^32, so no carry crosses between them).  One word per lane keeps each wave's
+            // adds on the fewest cache lines.
+            for (int t = tid; t < kRefHeads * kRefWords; t += kRefThreads) {
+                const int hh = t / kRefWords;
+                const uint32_t n = (&lh[0][0])[t];
+                if (hh < nh && n) {
+                    unsigned long long* hg = (unsigned long long*)(a.hist +
+                        (int64_t)(b * a.Hkv + h0 + hh) * kCBins0) + t % kRefWords;
+                    atomicAdd(hg, (unsigned long long)(n & 0xffffu) |
+                                  ((unsigned long long)(n >> 16) << 32));
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
-        for (int t = tid; t < kCBins0; t += kThreads)
-            if (lh[t]) atomicAdd(&hg[t], lh[t]);
-        __syncthreads();
     }
 }
 
@@ -1063,10 +1136,8 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     // with lse_j the dense step computed the log-sum-exp over J and cleared the histograms
     if (!a.lse_j) hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
     hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
-    if (a.refine) {
-        hipLaunchKernelGGL(refine_nms_kernel, g_group, blk, 0, s, a);
-        hipLaunchKernelGGL(refine_cross_kernel, dim3(a.nchunk * kCrossParts, a.B), blk, 0, s, a);
-    }
+    if (a.refine)
+        hipLaunchKernelGGL(refine_kernel, dim3(a.nchunk * kCrossParts, a.B), dim3(kRefThreads), 0, s, a);
     hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
     hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
     hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);
