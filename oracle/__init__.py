@@ -18,7 +18,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "sfi_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A prebuilt oracle library to load instead (the sanitizer test points this at a build with
+# AddressSanitizer and UndefinedBehaviorSanitizer); never built here.
+_LIB_OVERRIDE = os.environ.get("SFI_ORACLE_LIB")
 _lib = None
+
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
 
 
 def build(force: bool = True) -> str:
@@ -29,6 +35,14 @@ def build(force: bool = True) -> str:
                                "-Wall", "-Wextra", "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(path: str) -> str:
+    """Compile the oracle with AddressSanitizer and UndefinedBehaviorSanitizer into `path`
+    (CPU only; the library must be loaded with the sanitizer runtimes preloaded)."""
+    subprocess.check_call(["gcc", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+                           "-fno-fast-math"] + SANITIZE_FLAGS + ["-o", path, _SRC, "-lm"])
+    return path
 
 
 class _Refine(ctypes.Structure):
@@ -48,9 +62,12 @@ class _Cache(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         L.orc_dense.argtypes = [ctypes.POINTER(_Cache), P, P, P, P, ctypes.c_int64]
         L.orc_select.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P,
