@@ -35,6 +35,20 @@
 namespace sfi {
 namespace {
 
+// Loads and stores of device memory through the global address space.  The pointers of a
+// step descriptor are read from device memory, so the compiler cannot tell that they point to
+// global memory and would emit flat accesses for them; a flat load also counts against the LDS
+// wait counter, so every LDS wait of the tile loop would then wait for the prefetched tile too.
+template <class T>
+__device__ __forceinline__ T gld(const T* p) {
+    return *(const __attribute__((address_space(1))) T*)p;
+}
+template <class T>
+__device__ __forceinline__ void gst(T* p, T x) {
+    *(__attribute__((address_space(1))) T*)p = x;
+}
+
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -172,10 +186,10 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
         }
         bool zero = !(Lt > 0.f);
         if constexpr (SPARSE) {
-            if (a.head_mask) zero |= a.head_mask[b * a.Hq + i] != 0;
+            if (a.head_mask) zero |= gld(a.head_mask + b * a.Hq + i) != 0;
         }
-        a.out[((int64_t)b * a.Hq + i) * D + tid] = zero ? 0.f : At / Lt;
-        if (tid == 0 && a.lse) a.lse[b * a.Hq + i] = zero ? -INFINITY : (Mt + log2f(Lt)) * kLn2;
+        gst(a.out + ((int64_t)b * a.Hq + i) * D + tid, zero ? 0.f : At / Lt);
+        if (tid == 0 && a.lse) gst(a.lse + b * a.Hq + i, zero ? -INFINITY : (Mt + log2f(Lt)) * kLn2);
     }
     if constexpr (!SPARSE) {
         if (a.lse_j) {
@@ -265,25 +279,25 @@ __device__ void route_load(const AttnArgs& a, int b, int h, int hq0, int unit, i
         r.lse = a.route_lse[b * a.Hq + hq0 + g];
         const int64_t qoff = ((int64_t)b * a.Hq + hq0 + g) * D + c * kPer;
         if constexpr (BF) {
-            r.q[0] = *(const u32x4*)((const uint16_t*)a.q + qoff);
+            r.q[0] = gld((const u32x4*)((const uint16_t*)a.q + qoff));
         } else {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) r.q[e] = *(const f32x4*)((const float*)a.q + qoff + 4 * e);
+            for (int e = 0; e < 2; ++e) r.q[e] = gld((const f32x4*)((const float*)a.q + qoff + 4 * e));
         }
     }
     if (!load_k) return;
     uint32_t row;                                      // the row of position 0
     if constexpr (PAGED)
-        row = ((uint32_t)a.block_table[(int64_t)b * a.max_blocks] * (uint32_t)a.Hkv + (uint32_t)h)
+        row = ((uint32_t)gld(a.block_table + (int64_t)b * a.max_blocks) * (uint32_t)a.Hkv + (uint32_t)h)
               << a.block_shift;
     else
         row = (uint32_t)((int64_t)unit * a.n_cap);
     if constexpr (BF) {
-        r.k[0] = *(const u32x4*)((const uint16_t*)a.k + (uint64_t)row * D + c * kPer);
+        r.k[0] = gld((const u32x4*)((const uint16_t*)a.k + (uint64_t)row * D + c * kPer));
     } else {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-            r.k[e] = *(const f32x4*)((const float*)a.k + (uint64_t)row * D + c * kPer + 4 * e);
+            r.k[e] = gld((const f32x4*)((const float*)a.k + (uint64_t)row * D + c * kPer + 4 * e));
     }
 }
 
@@ -410,14 +424,14 @@ attention_kernel(AttnArgs a_in) {
         for (int u = 0; u < kPreC; ++u) {
             const int slot = s0 + u * C::kNT + tid;
             idx_pre[u] = (u * C::kNT < a.split_len && slot < a.idx_stride)
-                ? a.idx[(int64_t)unit * a.idx_stride + slot] : 0;
+                ? gld(a.idx + (int64_t)unit * a.idx_stride + slot) : 0;
         }
     } else if constexpr (SPARSE) {
         const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
 #pragma unroll
         for (int u = 0; u < kFill; ++u) {
             const int slot = s0 + u * C::kNT + tid;
-            idx_pre[u] = (u < nfill && slot < a.idx_stride) ? irow[slot] : 0;
+            idx_pre[u] = (u < nfill && slot < a.idx_stride) ? gld(irow + slot) : 0;
         }
     }
     RoutePre<BF, D> route;
@@ -434,22 +448,22 @@ attention_kernel(AttnArgs a_in) {
 #pragma unroll
             for (int u = 0; u < kBtPer; ++u) {
                 const int e = u * C::kNT + tid;
-                bt_pre[u] = e < a.max_blocks ? a.block_table[(int64_t)b * a.max_blocks + e] : 0;
+                bt_pre[u] = e < a.max_blocks ? gld(a.block_table + (int64_t)b * a.max_blocks + e) : 0;
             }
         }
     }
-    const int len_b = a.len[b];
+    const int len_b = gld(a.len + b);
 
     // ---- slot range of this workgroup -------------------------------------------------
     int n_sel = 0, r0 = 0, n_tot = len_b;
     bool all_masked = false;
     if constexpr (SPARSE) {
-        n_sel = min(max(a.n_idx[unit], 0), a.idx_stride);
+        n_sel = min(max(gld(a.n_idx + unit), 0), a.idx_stride);
         r0 = max(0, len_b - a.n_recent);
         n_tot = len_b > 0 ? n_sel + (len_b - r0) : 0;
         if (a.head_mask) {
             all_masked = true;
-            for (int g = 0; g < G; ++g) all_masked &= a.head_mask[b * a.Hq + hq0 + g] != 0;
+            for (int g = 0; g < G; ++g) all_masked &= gld(a.head_mask + b * a.Hq + hq0 + g) != 0;
         }
         if (a.route_lse) {
             // inline group routing before any key or value row of the group is read
@@ -498,7 +512,7 @@ attention_kernel(AttnArgs a_in) {
                             pos = idx_pre[v];
                             pre = true;
                         }
-                    if (!pre) pos = irow[slot];
+                    if (!pre) pos = gld(irow + slot);
                     ok = pos >= 0 && pos < r0;
                     if (!ok) pos = len_b - 1;
                 } else {
@@ -523,7 +537,7 @@ attention_kernel(AttnArgs a_in) {
                 pos[u] = 0;
                 if (u < nfill && t < nslots) {
                     if (slot < n_sel) {
-                        pos[u] = t0 == 0 ? idx_pre[u] : irow[slot];
+                        pos[u] = t0 == 0 ? idx_pre[u] : gld(irow + slot);
                         ok[u] = pos[u] >= 0 && pos[u] < r0;
                         if (!ok[u]) pos[u] = len_b - 1;
                     } else {
@@ -539,7 +553,7 @@ attention_kernel(AttnArgs a_in) {
                     const bool crow = compact && s0 + t < n_sel;     // compact row: no lookup
                     const int blk = (u < nfill && t < nslots && !crow)
                         ? (bt_staged ? s_bt[pos[u] >> a.block_shift]
-                                     : a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)])
+                                     : gld(a.block_table + (int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)))
                         : 0;
                     row[u] = crow ? crow0 + (uint32_t)(s0 + t)
                                   : (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
@@ -563,7 +577,7 @@ attention_kernel(AttnArgs a_in) {
         const int blk0 = s0 >> a.block_shift;
         const int nblk = nslots > 0 ? ((s1 - 1) >> a.block_shift) - blk0 + 1 : 0;
         for (int t = tid; t < nblk; t += C::kNT) {
-            const int blk = a.block_table[(int64_t)b * a.max_blocks + blk0 + t];
+            const int blk = gld(a.block_table + (int64_t)b * a.max_blocks + blk0 + t);
             tab[t] = ((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift;
         }
         __syncthreads();
@@ -590,10 +604,10 @@ attention_kernel(AttnArgs a_in) {
         for (int c = 0; c < C::kNQ; ++c) {
             if constexpr (BF) {
                 const uint16_t* qp = (const uint16_t*)a.q + qoff;
-                qf[c] = has ? *(const u32x4*)(qp + 32 * c + 8 * q4) : u32x4{0u, 0u, 0u, 0u};
+                qf[c] = has ? gld((const u32x4*)(qp + 32 * c + 8 * q4)) : u32x4{0u, 0u, 0u, 0u};
             } else {
                 const float* qp = (const float*)a.q + qoff;
-                qf[c] = has ? *(const f32x4*)(qp + 16 * c + 4 * q4) : f32x4{0.f, 0.f, 0.f, 0.f};
+                qf[c] = has ? gld((const f32x4*)(qp + 16 * c + 4 * q4)) : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
     }
@@ -663,10 +677,11 @@ attention_kernel(AttnArgs a_in) {
     // loads (the K rows are read in the MFMA operand layout, 64 bytes from each of 16 rows
     // per wavefront load) slowed every step, so K loads stay ordinary.
     constexpr bool kNtV = !SPARSE;
-    auto load_k = [](const void* p) -> u32x4 { return *(const u32x4*)p; };
+    auto load_k = [](const void* p) -> u32x4 { return gld((const u32x4*)p); };
     auto load_v = [](const void* p) -> u32x4 {
-        if constexpr (kNtV) return __builtin_nontemporal_load((const u32x4*)p);
-        else return *(const u32x4*)p;
+        if constexpr (kNtV)
+            return __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)p);
+        else return gld((const u32x4*)p);
     };
     using Elem = typename std::conditional<BF, uint16_t, float>::type;
     // first element of the key (or value) row of a slot: the compact segment for index slots
@@ -691,7 +706,7 @@ attention_kernel(AttnArgs a_in) {
 #pragma unroll
             for (int c = 0; c < C::kNQ; ++c) {
                 if constexpr (BF) r.k[st][c] = load_k(kp + 32 * c + 8 * q4);
-                else r.k[st][c] = *(const f32x4*)(kp + 16 * c + 4 * q4);
+                else r.k[st][c] = gld((const f32x4*)(kp + 16 * c + 4 * q4));
             }
         }
         if constexpr (BF) {
@@ -707,7 +722,7 @@ attention_kernel(AttnArgs a_in) {
                 for (int i = 0; i < 4; ++i) {
                     const float* vp = row_ptr(pick(sb + 16 * st + 4 * q4 + i), a.v, a.cv);
 #pragma unroll
-                    for (int mb = 0; mb < D / 16; ++mb) r.v[(st * 4 + i) * (D / 16) + mb] = vp[16 * mb + n16];
+                    for (int mb = 0; mb < D / 16; ++mb) r.v[(st * 4 + i) * (D / 16) + mb] = gld(vp + 16 * mb + n16);
                 }
         }
     };
