@@ -22,6 +22,9 @@ and replayed, next to the eager value.
 cpu_baseline = the fp64 CPU oracle timed on the host on whole cycles of one layer.
 read_yardstick = a plain sequential read of 4 GiB (sfi_stream_read) on the same box; the
 rooflines also give the dense and fast rates as a fraction of it, next to the 8 TB/s peak.
+fast_roofline.floor = what the fast step's bytes cost without its arithmetic: the same rows read
+once by one launch (sfi_gather_read), a launch with almost nothing to do, and a sequential read
+of as many bytes, cold in the Infinity Cache (the fastest any one-launch read of them can be).
 """
 from __future__ import annotations
 
@@ -327,12 +330,15 @@ def routed_sink_heavy(B, torch, synth, wl, layers, descs, stride, idx_stride, L,
             "normaliser": "lse of the slow step", "routing": "all heads of a KV group"}
 
 
-def fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L, grids=(256, 1024)):
+def fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L, seq_bytes, grids=(256, 1024),
+               seq_grids=(512, 1024)):
     """Floor of the fast step's access pattern: sfi_gather_read (the same rows, read once with
     no arithmetic, one launch) over the cycle's fast steps in decode order, timed as one block at
     each workgroup count, and the GPU-side cost of one launch with almost nothing to do (a 16 KB
     read by one workgroup, replayed from a captured graph).  The fast step itself needs two launches: its split-K
-    partials and their merge."""
+    partials and their merge.  Beside them, the size floor: sfi_stream_read of seq_bytes (the
+    fast step's algorithmic bytes) from one of L buffers in turn, so that every read is as cold
+    in the Infinity Cache as a fast step's rows, the best of seq_grids workgroup counts."""
     stream = torch.cuda.current_stream()
     sink = torch.zeros(64, dtype=torch.int32, device="cuda")
     tiny = torch.zeros(4096, dtype=torch.int32, device="cuda")
@@ -362,10 +368,21 @@ def fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L, grids=(256, 1024
     launch = graph_replay(torch, lambda: [B.sfi_stream_read(tiny, 1, sink) for _ in range(n_launch)],
                           n_launch)
     best = min(gather, key=gather.get)
+    n = int(seq_bytes) // 4096 * 4096
+    bufs = [torch.zeros(n, dtype=torch.uint8, device="cuda") for _ in range(L)]
+    seq = {}
+    for g in seq_grids:
+        seq[g] = block(lambda: [B.sfi_stream_read(bufs[li], g, sink)
+                                for t in range(1, wl.cycle) for li in range(L)])
+    del bufs
+    torch.cuda.empty_cache()
+    sbest = min(seq, key=seq.get)
     return {"gather_read_us": round(gather[best], 2), "gather_read_workgroups": best,
             "gather_read_us_by_workgroups": {str(g): round(v, 2) for g, v in gather.items()},
             "one_launch_us": round(launch, 2),
-            "two_launch_floor_us": round(gather[best] + launch, 2)}
+            "two_launch_floor_us": round(gather[best] + launch, 2),
+            "sequential_read_same_bytes_us": round(seq[sbest], 2),
+            "sequential_read_workgroups": sbest}
 
 
 def graph_replay(torch, run, per_replay: int, reps: int = 3):
@@ -884,8 +901,6 @@ def main():
         print("# stack cycle replayed from a HIP graph", file=sys.stderr, flush=True)
         graph_us = graph_replay(torch, lambda: cycle("none"), wl.cycle * L)
 
-    print("# fast-step floor (gather read, one launch)", file=sys.stderr, flush=True)
-    floor = fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L)
 
     print("# fast steps on synthetic selections", file=sys.stderr, flush=True)
     synth_fast = synthetic_selection_fast_steps(B, torch, synth, wl, layers, descs, queries, out,
@@ -1001,6 +1016,11 @@ def main():
         result["two_segment"] = two_seg
     result["roofline"]["frac_of_measured_read"] = round(dense_gbps / yard["gbps"], 4)
     result["fast_roofline"]["frac_of_measured_read"] = round(fast_gbps / yard["gbps"], 4)
+    print("# fast-step floor (gather read, one launch, sequential read)", file=sys.stderr,
+          flush=True)
+    floor = fast_floor(B, torch, wl, descs, idxs, nidxs, idx_stride, L, f_bytes)
+    floor["sequential_read_frac_of_peak"] = round(
+        f_bytes / (floor["sequential_read_same_bytes_us"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
     floor["gather_read_frac_of_peak"] = round(f_bytes / (floor["gather_read_us"] * 1e-6) / 1e9
                                               / PEAK_HBM_GBS, 4)
     floor["two_launch_floor_frac_of_peak"] = round(

@@ -200,7 +200,8 @@ __device__ __forceinline__ float fused_log2(const SelArgs& a, float f, float lr)
 // start), four query heads at a time with every load of the four heads issued before any is
 // used; positions outside the chunk are masked.
 constexpr int kEvQ = kPerThread / 4 + 1;               // quads per thread (kSelChunk + 3 positions)
-__global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
+template <bool REFINE>
+__global__ void __launch_bounds__(kThreads, REFINE ? 2 : 4) evidence_kernel(SelArgs a) {
     __shared__ float s_lse[kMaxSelG];
     __shared__ uint32_t lh[kCBins0];
     __shared__ float sh[4];
@@ -231,7 +232,7 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
     load4(0);
     // the key norms of the full Selector's prior, with the first quads (clamped into the chunk)
     float nrm[kEvQ][4];
-    if (a.refine && a.key_norm) {
+    if (REFINE && a.key_norm) {
         const float* kn = a.key_norm + (int64_t)unit * a.norm_stride;
 #pragma unroll
         for (int k = 0; k < kEvQ; ++k)
@@ -244,7 +245,7 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) nrm[k][e] = 1.f;
     }
-    if (!a.refine)
+    if (!REFINE)
         for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
     if (a.lse_j) {
         // the dense step of the slow step gave the log-sum-exp over J
@@ -283,7 +284,7 @@ __global__ void __launch_bounds__(kThreads) evidence_kernel(SelArgs a) {
         }
     }
     uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
-    if (a.refine) {
+    if constexpr (REFINE) {
         // log2 of the unnormalised fused score for the refinement pass, and this chunk's share
         // of the fusion normaliser
         float* lf = a.lfused + ((int64_t)unit * a.nchunk + c) * kSelChunk;
@@ -490,6 +491,32 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
     }
 }
 
+// Over bins held kPer per thread in ascending order (thread t holds bins kPer t ... kPer t +
+// kPer - 1), finds the bin that holds the k-th largest key (0 < k <= the number of keys):
+// s_sel[0] = the bin, s_sel[1] = the number of keys in higher bins.
+template <int kPer>
+__device__ void pick_bin(const uint32_t (&bins)[kPer], uint32_t k, uint32_t* sh, uint32_t* s_sel) {
+    const int tid = threadIdx.x;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += bins[j];
+    const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
+    const uint32_t total = block_sum_u(mine, sh);
+    const uint32_t above = total - below_incl;          // keys in higher bins than this thread's
+    if (above < k && k <= above + mine) {
+        uint32_t cum = above;
+        for (int j = kPer - 1; j >= 0; --j) {
+            if (cum + bins[j] >= k) {
+                s_sel[0] = (uint32_t)(kPer * tid + j);
+                s_sel[1] = cum;
+                break;
+            }
+            cum += bins[j];
+        }
+    }
+    __syncthreads();
+}
+
 // state: [0] prefix (bits of T decided so far), [1] k_rem, [2] nJ, [3] take_all
 // A unit is active when some but not all of J is kept: !take_all, k_rem > 0 and a prefix
 // other than the keep-nothing mark 0xffffffff.
@@ -541,25 +568,7 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
     uint32_t prefix = (!take_all && k_rem == 0) ? 0xffffffffu : 0u;   // keep nothing
     const bool active = sel_active(prefix, k_rem, take_all);
     if (active) {
-        uint32_t mine = 0;
-#pragma unroll
-        for (int k = 0; k < kPer; ++k) mine += bins[k];
-        // keys in bins above this thread's bins
-        const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
-        const uint32_t total = block_sum_u(mine, sh);
-        const uint32_t above = total - below_incl;
-        if (above < (uint32_t)k_rem && (uint32_t)k_rem <= above + mine) {
-            uint32_t cum = above;
-            for (int k = kPer - 1; k >= 0; --k) {
-                if (cum + bins[k] >= (uint32_t)k_rem) {
-                    s_sel[0] = (uint32_t)(kPer * tid + k);
-                    s_sel[1] = cum;
-                    break;
-                }
-                cum += bins[k];
-            }
-        }
-        __syncthreads();
+        pick_bin<kPer>(bins, (uint32_t)k_rem, sh, s_sel);
         prefix = s_sel[0] << kCShift[0];
         k_rem -= (int32_t)s_sel[1];
     }
@@ -1135,7 +1144,8 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     const dim3 g_unit(a.Hkv, a.B);
     // with lse_j the dense step computed the log-sum-exp over J and cleared the histograms
     if (!a.lse_j) hipLaunchKernelGGL(lse_kernel, g_head, blk, 0, s, a);
-    hipLaunchKernelGGL(evidence_kernel, g_group, blk, 0, s, a);
+    if (a.refine) hipLaunchKernelGGL(evidence_kernel<true>, g_group, blk, 0, s, a);
+    else hipLaunchKernelGGL(evidence_kernel<false>, g_group, blk, 0, s, a);
     if (a.refine)
         hipLaunchKernelGGL(refine_kernel, dim3(a.nchunk * kCrossParts, a.B), dim3(kRefThreads), 0, s, a);
     hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
