@@ -201,7 +201,7 @@ __device__ __forceinline__ float fused_log2(const SelArgs& a, float f, float lr)
 // used; positions outside the chunk are masked.
 constexpr int kEvQ = kPerThread / 4 + 1;               // quads per thread (kSelChunk + 3 positions)
 template <bool REFINE>
-__global__ void __launch_bounds__(kThreads, REFINE ? 2 : 4) evidence_kernel(SelArgs a) {
+__global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
     __shared__ float s_lse[kMaxSelG];
     __shared__ uint32_t lh[kCBins0];
     __shared__ float sh[4];

@@ -189,7 +189,8 @@ def test_refined_full_size(orc):
 
 def test_refined_edges(orc):
     """Empty J, J shorter than k, k = 0, one KV head (no competition), no tail brake, no
-    key norms, G = 1, and 20 KV heads (beyond the 16 kept in registers)."""
+    key norms, G = 1, and 20 KV heads (beyond the 8 the refine pass holds in registers at a
+    time: three groups of heads, the scores computed twice)."""
     wl = synth.Workload("ref_edges", 1, 6, 6, 6, 64, "bf16", 3000, 4, 64, 100, 1)
     g = torch.Generator().manual_seed(9)
     lens = [3, 68, 150, 3000, 1, 2000]
