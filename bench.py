@@ -798,13 +798,13 @@ def main():
         for li in range(L):
             d0 = descs[li]
             e = [ev() for _ in range(3)] if rec != "none" else None
-            if e:
-                e[0].record(stream)
             # the slow step in one call: dense with logits, Selector (its normaliser over J from
-            # the dense kernels), mask; e[1] is recorded by the library after the dense kernels
+            # the dense kernels), mask; e[0] and e[1] are recorded by the library right before
+            # and after the dense kernels, so host-side checks are never inside the interval
             B.sfi_slow_step(d0[0], queries[li][0], out, lse, logits[li], stride, wl.n_sink,
                             wl.n_recent, wl.k_sel, idxs[li], idx_stride, nidxs[li],
-                            wl.mask_frac, masks[li], ws, dense_done=e[1] if e else None)
+                            wl.mask_frac, masks[li], ws, dense_done=e[1] if e else None,
+                            dense_begin=e[0] if e else None)
             if rec == "all":
                 e[2].record(stream)
             marks.append(e)

@@ -168,17 +168,18 @@ sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_
  * sfi_select's in the last bits: selections agree except at exact-tie precision.
  * logits and lse are required.  G <= 16 (the dense step's limit).  ws: at least
  * sfi_workspace_bytes(kv, SFI_OP_SLOW, 0, 0) bytes, no initialisation needed.
- * dense_done: a HIP event created by the caller, or NULL; when given it is recorded on
- * `stream` after the dense step's kernels and before the Selector's (for callers that time
- * the dense step or start other work after it, as the layer-wise schedule of SFI Sec. 4.1
- * does).  Launches: the dense step's two, the Selector's four (or one on short contexts), the
- * mask's one. */
+ * dense_begin, dense_done: HIP events created by the caller, or NULL; when given they are
+ * recorded on `stream` right before the dense step's first kernel (after every host-side
+ * check) and after its kernels, before the Selector's (for callers that time the dense step,
+ * or start other work after it as the layer-wise schedule of SFI Sec. 4.1 does).  Launches:
+ * the dense step's two, the Selector's four (or one on short contexts), the mask's one. */
 sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
                          float* logits, int64_t logit_stride,
                          int32_t n_sink, int32_t n_recent, int32_t k_sel,
                          int32_t* idx, int32_t idx_stride, int32_t* n_idx,
                          float mask_frac, uint8_t* head_mask,
-                         void* ws, size_t ws_bytes, hipEvent_t dense_done, hipStream_t stream);
+                         void* ws, size_t ws_bytes, hipEvent_t dense_begin,
+                         hipEvent_t dense_done, hipStream_t stream);
 
 /* The full Selector: sfi_select with the cache-aware prior, reverse-KL fusion and the
  * log-score refinements.  SFI Sec. 3.2 ("Cache-aware prior on allowed positions", "Position
@@ -197,8 +198,8 @@ sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float
  * With lambda = alpha_soft = alpha_cross = 0 the indices equal sfi_select's.
  * key_norm (device) fp32 [B][Hkv][norm_stride] with norm_stride >= max_len, or NULL: the norms
  * of the cached keys (statistics kept with the cache).  ws: sfi_workspace_bytes(kv,
- * SFI_OP_SELECT_REFINED, ...).  Every other argument as for sfi_select.  Seven kernel launches
- * (the chunked Selector plus two refinement passes).  SFI_E_INVALID for parameters outside the
+ * SFI_OP_SELECT_REFINED, ...).  Every other argument as for sfi_select.  Six kernel launches
+ * (the chunked Selector plus one refinement pass).  SFI_E_INVALID for parameters outside the
  * stated ranges. */
 sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
                               const float* key_norm, int64_t norm_stride,
@@ -385,10 +386,12 @@ sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
  * device buffers laid out as for the single calls (lse is required here).  dense_ws serves the
  * dense steps one after another and each sel_ws[s] holds a slot's normaliser and Selector
  * workspace: sfi_workspace_bytes(&kv[l], SFI_OP_SLOW, 0, 0) bytes suffice for both (G <= 16).
- * Measured on MI355X, pipelining only pays for mid-sized slow steps (a ragged batch of 16 at
- * 8K-32K, one 32K sequence); at 128K x 4 and at 512K, where the dense step alone keeps HBM busy,
- * a concurrent Selector competes with it and sfi_slow_step layer after layer is faster.  slot_events (n_slots), attn_event and done_event are
- * HIP events created by the caller; the library only records them and waits on them.
+ * Measured on MI355X, pipelining only pays for a ragged batch of 16 sequences of 8K-32K
+ * (294 -> 279 us per layer); at one 32K sequence, 128K x 4 and 512K, where the dense step alone
+ * keeps HBM busy or the event hand-offs cost more than the overlap saves, sfi_slow_step layer
+ * after layer is faster (57 vs 60, 408 vs 443 and 479 vs 502 us per layer), so that is the
+ * default there.  slot_events (n_slots), attn_event and done_event are HIP events created by
+ * the caller; the library only records them and waits on them.
  * stream and side_stream must differ; calls that share buffers or events must not overlap.
  * Every layer is validated before anything is queued; on an error nothing has been queued
  * (SFI_E_HIP aside, which may leave earlier layers queued). */

@@ -76,7 +76,7 @@ def lib():
         L.sfi_dense_decode.argtypes = [D, P, P, P, P, i64, P, ctypes.c_size_t, P]
         L.sfi_select.argtypes = [D, P, i64, i32, i32, i32, P, i32, P, P, ctypes.c_size_t, P]
         L.sfi_slow_step.argtypes = [D, P, P, P, P, i64, i32, i32, i32, P, i32, P, ctypes.c_float,
-                                    P, P, ctypes.c_size_t, P, P]
+                                    P, P, ctypes.c_size_t, P, P, P]
         L.sfi_sink_bypass_mask.argtypes = [D, P, i64, P, ctypes.c_float, P, P]
         L.sfi_sparse_decode.argtypes = [D, P, P, i32, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.sfi_sparse_decode_noalloc.argtypes = [D, P, P, i32, P, i32, P, P, P, P]
@@ -301,8 +301,9 @@ def sfi_dense_decode(desc: KVDesc, q, out, lse, logits, logit_stride: int, ws, s
 
 def sfi_slow_step(desc: KVDesc, q, out, lse, logits, logit_stride: int, n_sink: int,
                   n_recent: int, k_sel: int, idx, idx_stride: int, n_idx, mask_frac: float,
-                  head_mask, ws, dense_done=None, stream=None):
-    """dense_done: a torch.cuda.Event (recorded after the dense kernels) or None."""
+                  head_mask, ws, dense_done=None, stream=None, dense_begin=None):
+    """dense_begin, dense_done: torch.cuda.Events (recorded right before and after the dense
+    kernels, after the library's own checks) or None."""
     desc.need_cache("sfi_slow_step")
     _buf(q, "q", desc.cache_dtype, desc.heads * desc.c.head_dim)
     _buf(out, "out", _F32, desc.heads * desc.c.head_dim)
@@ -311,11 +312,12 @@ def sfi_slow_step(desc: KVDesc, q, out, lse, logits, logit_stride: int, n_sink: 
     _buf(head_mask, "head_mask", _U8, desc.heads, optional=True)
     st = _stream(stream)
     ev = _event_handle(dense_done, stream) if dense_done is not None else None
+    eb = _event_handle(dense_begin, stream) if dense_begin is not None else None
     _check(lib().sfi_slow_step(desc.ref, _ptr(q), _ptr(out), _ptr(lse), _ptr(logits),
                                int(logit_stride), int(n_sink), int(n_recent), int(k_sel),
                                _ptr(idx), int(idx_stride), _ptr(n_idx), float(mask_frac),
                                _ptr(head_mask), _ptr(ws), ws.numel() * ws.element_size(),
-                               ev, st), "sfi_slow_step")
+                               eb, ev, st), "sfi_slow_step")
 
 
 def _selector_bufs(desc: KVDesc, logits, logit_stride: int, idx, idx_stride: int, n_idx, ws):

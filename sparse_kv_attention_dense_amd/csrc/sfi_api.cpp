@@ -707,7 +707,8 @@ SFI_EXPORT sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float*
                                     int32_t n_recent, int32_t k_sel, int32_t* idx,
                                     int32_t idx_stride, int32_t* n_idx, float mask_frac,
                                     uint8_t* head_mask, void* ws, size_t ws_bytes,
-                                    hipEvent_t dense_done, hipStream_t stream) {
+                                    hipEvent_t dense_begin, hipEvent_t dense_done,
+                                    hipStream_t stream) {
     sfi_status st = check_desc(kv, true);
     if (st != SFI_OK) return st;
     if (!logits || !lse) return SFI_E_INVALID;
@@ -737,6 +738,7 @@ SFI_EXPORT sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float*
     da.n_recent = n_recent;
     da.sel_hist = sa.hist;
     sa.lse_j = da.lse_j;
+    if (dense_begin && hipEventRecord(dense_begin, stream) != hipSuccess) return SFI_E_HIP;
     if (launch_dense(kv, da, stream) != SFI_OK) return SFI_E_HIP;
     if (dense_done && hipEventRecord(dense_done, stream) != hipSuccess) return SFI_E_HIP;
     if (launch_select(sa, stream) != hipSuccess) return SFI_E_HIP;
