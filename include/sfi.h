@@ -386,10 +386,11 @@ sfi_status sfi_sparse_decode_compact(const sfi_kv_desc* kv, const void* q,
  * device buffers laid out as for the single calls (lse is required here).  dense_ws serves the
  * dense steps one after another and each sel_ws[s] holds a slot's normaliser and Selector
  * workspace: sfi_workspace_bytes(&kv[l], SFI_OP_SLOW, 0, 0) bytes suffice for both (G <= 16).
- * Measured on MI355X, pipelining only pays for a ragged batch of 16 sequences of 8K-32K
- * (294 -> 279 us per layer); at one 32K sequence, 128K x 4 and 512K, where the dense step alone
- * keeps HBM busy or the event hand-offs cost more than the overlap saves, sfi_slow_step layer
- * after layer is faster (57 vs 60, 408 vs 443 and 479 vs 502 us per layer), so that is the
+ * Measured on MI355X, pipelining pays for a ragged batch of 16 sequences of 8K-32K (294 -> 280
+ * us per layer) and is within the run-to-run spread for one 32K sequence (57 -> 52-60 us); at
+ * 128K x 4 and 512K, where the dense step alone keeps HBM busy, and on a 2K fp32 layer, where
+ * the event hand-offs cost more than the overlap saves, sfi_slow_step layer after layer is
+ * faster (406-408 vs 441-443, 476-479 vs 502 and 24 vs 44 us per layer), so that is the
  * default there.  slot_events (n_slots), attn_event and done_event are HIP events created by
  * the caller; the library only records them and waits on them.
  * stream and side_stream must differ; calls that share buffers or events must not overlap.
