@@ -101,13 +101,16 @@ def dense_bytes(wl, lens):
 def select_bytes(wl, lens):
     """HBM bytes the Selector of the fused slow step (sfi_slow_step) must move: the logits over J
     read once (its normaliser over J comes from the dense step), one 4-byte key written per
-    (KV head, position of J) and read back by the candidate pass and by the emit, and the index
+    (KV head, position of J) and read back by the candidate pass, and again by the emit when
+    the chunked path ends in its resolve and emit passes rather than in the one-workgroup-per-
+    unit finish (the library takes the finish when k_sel + max_len / 64 <= 8192), and the index
     rows written.  (The survey's plan counts a second logit read and the keys four times, an
-    upper bound for a Selector that computes its own normaliser.)  The candidates, well under
-    1 % of J, and the 16 KB histograms are not counted."""
+    upper bound for a Selector that computes its own normaliser.)  The candidates and kept
+    entries, about 2 % of J, and the 16 KB histograms are not counted."""
     nJ = sum(max(0, n - wl.n_recent - wl.n_sink) for n in lens)
-    return wl.Hq * nJ * 4 + 3 * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
-                                                      for _ in lens)
+    key_passes = 2 if wl.k_sel + max(lens) // 64 <= 8192 else 3
+    return wl.Hq * nJ * 4 + key_passes * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
+                                                                for _ in lens)
 
 
 def fast_bytes(wl, lens_t, n_idx_host, mask_host):

@@ -149,7 +149,7 @@ bool select_unit_path(const sfi_kv_desc& kv) {
 struct SelPlan {
     int nchunk = 0;
     size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0;
-    size_t off_cand = 0, off_cand_n = 0, bytes = 0;
+    size_t off_cand = 0, off_cand_n = 0, off_epos = 0, bytes = 0;
     size_t off_zpart = 0, off_lfused = 0, bytes_refined = 0;   // full Selector only
 };
 
@@ -165,6 +165,7 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     p->off_counts = off; off += align_up(B * Hkv * nc * 3 * sizeof(uint32_t));
     p->off_cand = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
     p->off_cand_n = off; off += align_up(B * Hkv * nc * sizeof(uint32_t));
+    p->off_epos = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(int32_t));
     p->bytes = off;
     p->off_zpart = off;  off += align_up(B * Hkv * nc * sizeof(float));
     p->off_lfused = off; off += align_up(B * Hkv * nc * kSelChunk * sizeof(float));
@@ -268,7 +269,9 @@ sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit
     a->counts = (uint32_t*)(base + plan.off_counts);
     a->cand = (uint32_t*)(base + plan.off_cand);
     a->cand_n = (uint32_t*)(base + plan.off_cand_n);
+    a->epos = (int32_t*)(base + plan.off_epos);
     a->unit_path = select_unit_path(*kv) ? 1 : 0;
+    a->finish = (int64_t)k_sel + kv->max_len / kFinishBinShare <= kFinishCap ? 1 : 0;
     a->refine = 0;
     a->key_norm = nullptr;
     a->norm_stride = 0;

@@ -81,6 +81,13 @@ hipError_t launch_attention(const AttnArgs& a, int B, int d, bool bf16, bool pag
 
 constexpr int kSelChunk = 4096;      // positions of J per workgroup
 constexpr int kRadixBins = 2048;     // LDS histogram bins of the one-launch path
+// Entries (kept keys and candidates of one unit) that finish_kernel holds in LDS.  The chunked
+// Selector ends in finish_kernel (one launch for the unit's resolve and emit) when
+// k_sel + max_len / kFinishBinShare <= kFinishCap: the kept keys and a generous bound on the
+// candidates (the digit-0 bin of the k-th largest key held 0.4-0.6 % of J on the benchmark's
+// logits) fit in LDS; otherwise in the resolve and emit passes.
+constexpr int kFinishCap = 8192;
+constexpr int64_t kFinishBinShare = 64;
 constexpr int kSelHistBins = 4096;   // digit-0 bins of the chunked path
 
 struct SelArgs {
@@ -104,6 +111,10 @@ struct SelArgs {
     const float* lse_j;              // [B][Hq] log-sum-exp over J from the dense step (natural
                                      //   log; the histograms are then already cleared), or null
     int32_t unit_path;               // 1: one workgroup per (b, KV head) does everything
+    int32_t finish;                  // 1: the chunked path ends in finish_kernel (one launch)
+                                     //   instead of the candidate, resolve and emit passes
+    int32_t* epos;                   // [B][Hkv][nchunk*kSelChunk]: positions of finish_kernel's
+                                     //   entries past its LDS (their keys go to cand)
     // full Selector (refine != 0): prior, reverse-KL fusion, Soft-NMS, cross-head exclusivity
     int32_t refine;
     const float* key_norm;           // [B][Hkv][norm_stride] or null (no key-norm factor)

@@ -13,7 +13,13 @@
 //   3. candidate_kernel   per chunk: the digit-0 bin that holds the k-th largest key (every
 //                          workgroup scans the unit's histogram), then the keys of that bin
 //                          compacted into the chunk's region, and the number of keys in
-//                          higher bins
+//                          higher bins; when finish_kernel follows, every key of that bin or
+//                          above, with its position
+//   4'. finish_kernel     (instead of 4 and 5 when a unit's kept keys and candidates fit in
+//                          its LDS: k_sel + max_len / 64 <= 8192) one workgroup per unit:
+//                          the entries of every chunk copied to LDS in position order, digits
+//                          1 and 2 of T over the entries of the digit-0 bin, then the ordered
+//                          emit over the entries
 //   4. resolve_kernel     one workgroup per unit: digits 1 and 2 (bits 18..9, 8..0) over the
 //                          candidates give the key T of the k-th largest evidence and how many
 //                          keys equal to T are kept; then the per-chunk numbers of kept keys
@@ -592,6 +598,8 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
         return;
     }
     const uint32_t d0 = prefix >> kCShift[0];
+    // candidates: the keys of bin d0, or with finish_kernel to follow, every key of bin d0 or
+    // above (with its position), so that the finish reads the kept keys from here
     uint32_t gt = 0, nc = 0;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
@@ -600,6 +608,7 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
         gt += (in && d > d0) ? 1u : 0u;
         nc += (in && d == d0) ? 1u : 0u;
     }
+    if (a.finish) nc += gt;
     // counts packed as (greater << 16) | candidates: at most kSelChunk each
     const uint32_t excl = block_exclusive_scan((gt << 16) | nc, sh);
     const uint32_t tot = block_sum_u((gt << 16) | nc, sh);
@@ -609,10 +618,18 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
         cn[1] = 0u;
         cn[2] = 0u;
     }
-    uint32_t* out = a.cand + ((int64_t)unit * a.nchunk + c) * kSelChunk + (excl & 0xffffu);
+    const int64_t region = ((int64_t)unit * a.nchunk + c) * kSelChunk + (excl & 0xffffu);
+    uint32_t* out = a.cand + region;
+    int32_t* opos = a.epos + region;
+    const int jb = a.n_sink + c * kSelChunk + tid * kPerThread;
 #pragma unroll
-    for (int k = 0; k < kPerThread; ++k)
-        if (tid * kPerThread + k < cnt && (kv[k] >> kCShift[0]) == d0) *out++ = kv[k];
+    for (int k = 0; k < kPerThread; ++k) {
+        const uint32_t d = kv[k] >> kCShift[0];
+        if (tid * kPerThread + k < cnt && (a.finish ? d >= d0 : d == d0)) {
+            *out++ = kv[k];
+            if (a.finish) *opos++ = jb + k;
+        }
+    }
 }
 
 __global__ void __launch_bounds__(kThreads) emit_kernel(SelArgs a) {
@@ -883,6 +900,178 @@ __global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
     }
 }
 
+// Over bins held kPer per thread of the 1024-thread workgroup in ascending order, finds the
+// bin that holds the k-th largest key (0 < k <= the number of keys): sm.sel[0] = the bin,
+// sm.sel[1] = the number of keys in higher bins.
+template <int kPer>
+__device__ void unit_pick_bin(const uint32_t (&bins)[kPer], uint32_t k, UnitShared& sm) {
+    const int tid = threadIdx.x;
+    uint32_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) mine += bins[j];
+    uint32_t total;
+    const uint32_t excl = unit_scan(mine, sm, &total);
+    const uint32_t above = total - excl - mine;        // keys in higher bins than this thread's
+    if (above < k && k <= above + mine) {
+        uint32_t cum = above;
+        for (int j = kPer - 1; j >= 0; --j) {
+            if (cum + bins[j] >= k) {
+                sm.sel[0] = (uint32_t)(kPer * tid + j);
+                sm.sel[1] = cum;
+                break;
+            }
+            cum += bins[j];
+        }
+    }
+    __syncthreads();
+}
+
+// Finish of the chunked Selector, one 1024-thread workgroup per (b, KV head), after the
+// candidate pass has written, per chunk and in position order, every key whose digit 0 is at or
+// above the bin of the k-th largest key, with its position: the entries of every chunk are
+// copied to LDS in chunk order (so in position order; a binary search over the scanned
+// per-chunk numbers finds each one's chunk; past kFinCap entries they are read where they lie),
+// digits 1 and 2 of T are resolved over the entries of that bin, and the ordered emit writes
+// the entries with key > T, or key == T and fewer than k_rem earlier entries equal to T, after
+// the sink positions.  It replaces the resolve and emit passes (one launch and one read of all
+// the keys fewer).
+constexpr int kFinCap = kFinishCap;                    // entries held in LDS
+constexpr int kFinChunks = kUT;                        // chunks per unit (contexts up to 4M)
+constexpr int kFinBatch = 8;                           // entry loads per thread in flight
+constexpr int kFinEmit = 8;                            // consecutive entries per thread in the emit
+static_assert((int64_t)kFinishCap * kFinishBinShare <= (int64_t)kFinChunks * kSelChunk,
+              "a context the finish takes has its chunk numbers in one scan");
+static_assert((1 << (kCShift[0] - kCShift[1])) == kUT, "one digit-1 bin per thread");
+static_assert((1 << kCShift[1]) <= kUT, "at most one digit-2 bin per thread");
+struct FinishShared {
+    UnitShared u;
+    uint32_t off[kFinChunks + 1];                      // exclusive scan of the entry numbers
+    uint32_t key[kFinCap];
+    int32_t pos[kFinCap];
+};
+
+__global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
+    __shared__ FinishShared fs;
+    UnitShared& sm = fs.u;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int unit = b * a.Hkv + h;
+    // the entry numbers, the state and the length are independent loads
+    const uint32_t n_mine = tid < a.nchunk ? a.cand_n[(int64_t)unit * a.nchunk + tid] : 0u;
+    const int32_t* st = a.state + unit * 4;
+    uint32_t T = (uint32_t)st[0];
+    int32_t k_rem = st[1];
+    const int32_t nJ = st[2], take_all = st[3];
+    const int N = a.len[b];
+    const int ns = max(0, min(a.n_sink, N));
+    int32_t* row = a.idx + (int64_t)unit * a.idx_stride;
+    for (int t = tid; t < ns; t += kUT) row[t] = t;
+    if (tid == 0) a.n_idx[unit] = ns + (take_all ? nJ : min(a.k_sel, nJ));
+    if (take_all) {
+        for (int t = tid; t < nJ; t += kUT) row[ns + t] = a.n_sink + t;
+        return;
+    }
+    if (!sel_active(T, k_rem, take_all)) return;       // keep nothing
+    uint32_t E;
+    const uint32_t ex = unit_scan(n_mine, sm, &E);
+    fs.off[tid] = ex;
+    if (tid == 0) fs.off[kFinChunks] = E;
+    __syncthreads();
+    // the chunk of entry i < E: the last c with off[c] <= i
+    auto chunk_of = [&](uint32_t i) -> int {
+        int lo = 0, hi = kFinChunks;                    // off[lo] <= i < off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (fs.off[mid] <= i) lo = mid; else hi = mid;
+        }
+        return lo;
+    };
+    const int64_t base = (int64_t)unit * a.nchunk * kSelChunk;
+    auto where = [&](uint32_t i) -> int64_t {
+        const int c = chunk_of(i);
+        return base + (int64_t)c * kSelChunk + (i - fs.off[c]);
+    };
+    const uint32_t held = min(E, (uint32_t)kFinCap);
+    for (uint32_t i0 = tid; i0 < held; i0 += kFinBatch * kUT) {
+        uint32_t kk[kFinBatch];
+        int32_t pp[kFinBatch];
+#pragma unroll
+        for (int u = 0; u < kFinBatch; ++u) {
+            const uint32_t i = i0 + u * kUT;
+            const int64_t w = i < held ? where(i) : base;
+            kk[u] = a.cand[w];
+            pp[u] = a.epos[w];
+        }
+#pragma unroll
+        for (int u = 0; u < kFinBatch; ++u) {
+            const uint32_t i = i0 + u * kUT;
+            if (i < held) {
+                fs.key[i] = kk[u];
+                fs.pos[i] = pp[u];
+            }
+        }
+    }
+    __syncthreads();
+    auto key_of = [&](uint32_t i) -> uint32_t {
+        return i < (uint32_t)kFinCap ? fs.key[i] : a.cand[where(i)];
+    };
+    // digits 1 and 2 of T over the entries of the digit-0 bin
+    for (int pass = 1; pass < 3; ++pass) {
+        sm.hist[tid] = 0u;
+        __syncthreads();
+        const uint32_t want = T >> kCShift[pass - 1];
+        for (uint32_t i = tid; i < E; i += kUT) {
+            const uint32_t key = key_of(i);
+            if ((key >> kCShift[pass - 1]) == want)
+                atomicAdd(&sm.hist[(key >> kCShift[pass]) & kCMask[pass]], 1u);
+        }
+        __syncthreads();
+        const uint32_t one[1] = {sm.hist[tid]};
+        unit_pick_bin<1>(one, (uint32_t)k_rem, sm);
+        T |= sm.sel[0] << kCShift[pass];
+        k_rem -= (int32_t)sm.sel[1];
+        __syncthreads();
+    }
+    // ordered emit: the entries are in position order; thread t takes kFinEmit consecutive
+    // entries of each round, so a round costs two scans
+    uint32_t eq_seen = 0, kept = 0;
+    for (uint32_t i0 = 0; i0 < E; i0 += kFinEmit * kUT) {
+        const uint32_t ib = i0 + kFinEmit * tid;
+        uint32_t kk[kFinEmit];
+        uint32_t n_eq_mine = 0;
+#pragma unroll
+        for (int e = 0; e < kFinEmit; ++e) {
+            kk[e] = ib + e < E ? key_of(ib + e) : 0u;
+            n_eq_mine += (ib + e < E && kk[e] == T) ? 1u : 0u;
+        }
+        uint32_t n_eq;
+        uint32_t eq_rank = eq_seen + unit_scan(n_eq_mine, sm, &n_eq);
+        uint32_t keep_mask = 0;
+#pragma unroll
+        for (int e = 0; e < kFinEmit; ++e) {
+            bool keep = false;
+            if (ib + e < E) {
+                if (kk[e] > T) {
+                    keep = true;
+                } else if (kk[e] == T) {
+                    keep = eq_rank < (uint32_t)k_rem;
+                    ++eq_rank;
+                }
+            }
+            keep_mask |= keep ? (1u << e) : 0u;
+        }
+        uint32_t n_keep;
+        uint32_t out = kept + unit_scan((uint32_t)__popc(keep_mask), sm, &n_keep);
+#pragma unroll
+        for (int e = 0; e < kFinEmit; ++e)
+            if (keep_mask & (1u << e)) {
+                const uint32_t i = ib + e;
+                row[ns + out++] = i < (uint32_t)kFinCap ? fs.pos[i] : a.epos[where(i)];
+            }
+        eq_seen += n_eq;
+        kept += n_keep;
+    }
+}
+
 __global__ void __launch_bounds__(kUT) select_unit_kernel(SelArgs a) {
     __shared__ UnitShared sm;
     const int h = blockIdx.x, b = blockIdx.y;
@@ -1149,8 +1338,12 @@ hipError_t launch_select(const SelArgs& a, hipStream_t s) {
     if (a.refine)
         hipLaunchKernelGGL(refine_kernel, dim3(a.nchunk * kCrossParts, a.B), dim3(kRefThreads), 0, s, a);
     hipLaunchKernelGGL(candidate_kernel, g_group, blk, 0, s, a);
-    hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
-    hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);
+    if (a.finish) {
+        hipLaunchKernelGGL(finish_kernel, g_unit, dim3(kUT), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(resolve_kernel, g_unit, dim3(kUT), 0, s, a);
+        hipLaunchKernelGGL(emit_kernel, g_group, blk, 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -15,6 +15,10 @@ pytestmark = pytest.mark.gpu
 # declared max_len far above the real lengths makes it choose the chunked kernels, so both
 # paths run the same cases.
 CHUNKED_MAX_LEN = 300000
+# a declared bound this long makes the chunked Selector end in its resolve and emit passes
+# instead of the one-workgroup-per-unit finish (k_sel + max_len / 64 > 8192 entries)
+PASSES_MAX_LEN = 600000
+MAX_LEN_OF = {"unit": None, "chunked": CHUNKED_MAX_LEN, "chunked_passes": PASSES_MAX_LEN}
 
 
 def _run(orc, wl, lens, z, exact, n_sink=None, n_recent=None, k_sel=None, idx_stride=None,
@@ -84,11 +88,11 @@ def test_select_random_logits_band(orc, seed, path):
     say(f"    tie-band swaps: {swaps}")
 
 
-@pytest.mark.parametrize("path", ["unit", "chunked"])
+@pytest.mark.parametrize("path", ["unit", "chunked", "chunked_passes"])
 def test_select_edges(orc, path):
     wl = synth.Workload("sel_edges", 1, 6, 8, 2, 128, "bf16", 5000, 4, 64, 100, 1)
     g = torch.Generator().manual_seed(3)
-    ml = CHUNKED_MAX_LEN if path == "chunked" else None
+    ml = MAX_LEN_OF[path]
     say(f"[select edges] {path}")
     # |J| = 0 (N - n_r <= n_s), N < n_s, |J| < k_sel (take all), |J| = k_sel, chunk edges
     lens = [60, 2, 150, 168, 4096 + 68, 8192 + 69]
@@ -106,6 +110,24 @@ def test_select_edges(orc, path):
     _run(orc, wl, lens, zq, exact=True, k_sel=1, idx_stride=5, max_len=ml)
     # every key equal: the first k_sel positions of J
     _run(orc, wl, lens, torch.zeros_like(z), exact=True, max_len=ml)
+
+
+def test_select_finish_beyond_its_lds(orc):
+    """The finish holds 8192 entries (kept keys and candidates of a unit) in LDS and reads the
+    rest where the candidate pass wrote them: all keys equal (every key of J is an entry) and
+    quantised logits with mass ties, on units of 20000 and 9000 positions, against the oracle
+    exactly, and bit for bit against the resolve and emit passes."""
+    wl = synth.Workload("sel_fin", 1, 2, 8, 2, 128, "bf16", 20068, 4, 64, 100, 1)
+    g = torch.Generator().manual_seed(11)
+    lens = [20068, 9000]
+    # a bound of 40000 positions keeps the chunked path with the finish for k_sel <= 7567
+    for z in (torch.zeros((2, 8, 20068)),
+              torch.randint(-1, 2, (2, 8, 20068), generator=g).float()):
+        for k_sel in (100, 5000):
+            say(f"[select finish overflow] k_sel={k_sel}")
+            a = _run(orc, wl, lens, z, exact=True, k_sel=k_sel, max_len=40000)
+            b = _run(orc, wl, lens, z, exact=True, k_sel=k_sel, max_len=PASSES_MAX_LEN)
+            assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("path", ["unit", "chunked"])
