@@ -150,7 +150,7 @@ struct SelPlan {
     int nchunk = 0;
     size_t off_lse = 0, off_keys = 0, off_hist = 0, off_state = 0, off_counts = 0;
     size_t off_cand = 0, off_cand_n = 0, off_epos = 0, bytes = 0;
-    size_t off_zpart = 0, off_lfused = 0, bytes_refined = 0;   // full Selector only
+    size_t off_zpart = 0, off_lfused = 0, off_epos_refined = 0, bytes_refined = 0;   // full Selector
 };
 
 void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
@@ -165,10 +165,15 @@ void plan_select(const sfi_kv_desc& kv, SelPlan* p) {
     p->off_counts = off; off += align_up(B * Hkv * nc * 3 * sizeof(uint32_t));
     p->off_cand = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(uint32_t));
     p->off_cand_n = off; off += align_up(B * Hkv * nc * sizeof(uint32_t));
-    p->off_epos = off;   off += align_up(B * Hkv * nc * kSelChunk * sizeof(int32_t));
+    const size_t common = off;
+    const size_t epos_bytes = align_up(B * Hkv * nc * kSelChunk * sizeof(int32_t));
+    p->off_epos = off;   off += epos_bytes;
     p->bytes = off;
+    // the full Selector's buffers follow the common part, then its own epos region
+    off = common;
     p->off_zpart = off;  off += align_up(B * Hkv * nc * sizeof(float));
     p->off_lfused = off; off += align_up(B * Hkv * nc * kSelChunk * sizeof(float));
+    p->off_epos_refined = off; off += epos_bytes;
     p->bytes_refined = off;
 }
 
@@ -563,6 +568,7 @@ SFI_EXPORT sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* log
     a.tail_brake = p.tail_brake;
     a.zpart = (float*)((unsigned char*)ws + plan.off_zpart);
     a.lfused = (float*)((unsigned char*)ws + plan.off_lfused);
+    a.epos = (int32_t*)((unsigned char*)ws + plan.off_epos_refined);
     return launch_select(a, stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
 }
 
