@@ -172,7 +172,8 @@ sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_
  * recorded on `stream` right before the dense step's first kernel (after every host-side
  * check) and after its kernels, before the Selector's (for callers that time the dense step,
  * or start other work after it as the layer-wise schedule of SFI Sec. 4.1 does).  Launches:
- * the dense step's two, the Selector's four (or one on short contexts), the mask's one. */
+ * the dense step's two, the Selector's three (four when k_sel + max_len / 64 > 8192; one on
+ * short contexts), the mask's one. */
 sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
                          float* logits, int64_t logit_stride,
                          int32_t n_sink, int32_t n_recent, int32_t k_sel,
@@ -198,9 +199,9 @@ sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float
  * With lambda = alpha_soft = alpha_cross = 0 the indices equal sfi_select's.
  * key_norm (device) fp32 [B][Hkv][norm_stride] with norm_stride >= max_len, or NULL: the norms
  * of the cached keys (statistics kept with the cache).  ws: sfi_workspace_bytes(kv,
- * SFI_OP_SELECT_REFINED, ...).  Every other argument as for sfi_select.  Six kernel launches
- * (the chunked Selector plus one refinement pass).  SFI_E_INVALID for parameters outside the
- * stated ranges. */
+ * SFI_OP_SELECT_REFINED, ...).  Every other argument as for sfi_select.  The chunked Selector
+ * plus one refinement pass (five or six kernel launches).  SFI_E_INVALID for parameters outside
+ * the stated ranges. */
 sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* logits, int64_t logit_stride,
                               const float* key_norm, int64_t norm_stride,
                               int32_t n_sink, int32_t n_recent, int32_t k_sel,
