@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
 DELTA = 5e-5
 CHUNKED_MAX_LEN = 300000
+PASSES_MAX_LEN = 600000           # k_sel + max_len / 64 > 8192: no finish pass
 
 
 def _gpu_refined(wl, lens, z, kn, params, n_sink, n_recent, k_sel, max_len=None):
@@ -202,6 +203,11 @@ def test_refined_edges(orc):
         n_diff, n_amb, _, _ = _compare(orc, wl, lens, z, None, params, wl.n_sink, wl.n_recent,
                                        k_sel, ig, ng)
         assert n_diff <= n_amb
+        # a bound this long ends the chunked Selector in its resolve and emit passes instead of
+        # the finish: the same keys, so the same indices
+        ip, nq = _gpu_refined(wl, lens, z, None, params, wl.n_sink, wl.n_recent, k_sel,
+                              max_len=PASSES_MAX_LEN)
+        assert np.array_equal(ip, ig) and np.array_equal(nq, ng)
     # more KV heads than the exclusivity pass holds in registers
     many = synth.Workload("ref_many", 1, 2, 40, 20, 128, "bf16", 6000, 4, 64, 200, 1)
     zm = torch.randn((2, 40, 6000), generator=g) * 2
