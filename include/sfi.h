@@ -9,10 +9,14 @@
  *     (SFI Sec. 3.2 evidence from slow-step logits, Sec. 3.3 Top-K)      -> sfi_select
  *   - a sink-bypass mask marks query heads whose token-0 attention mass is largest
  *     (SinkRouter Sec. 4.2, target regime and execution policy)          -> sfi_sink_bypass_mask
+ *   - the three in one call, the Selector's normaliser over the allowed set kept by the
+ *     dense step (SFI Sec. 3.2 and Sec. 4.2)                              -> sfi_slow_step
  *   - a fast step attends only to sink + selected + recent positions
  *     (SFI Sec. 1, the compact cache of fast steps)                       -> sfi_sparse_decode
  *   - the same with its per-step state read from a device step descriptor
  *     (SFI Sec. 4.2, the packed per-step descriptor)                     -> sfi_sparse_decode_step
+ *   - the same with its partial records in a library-held device array, for callers that
+ *     cannot allocate                                                   -> sfi_sparse_decode_noalloc
  *   - the same with SinkRouter's inline group routing (SinkRouter Sec. 4.2-4.3)
  *                                                                        -> sfi_sparse_decode_routed
  *   - the slow step over a model's layers with the Selector on a second stream
