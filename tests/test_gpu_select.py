@@ -112,6 +112,41 @@ def test_select_edges(orc, path):
     _run(orc, wl, lens, torch.zeros_like(z), exact=True, max_len=ml)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_select_chunked_random_shapes(orc, case):
+    """Seeded random shapes for the chunked Selector, planted ranks (one exact answer): batch
+    1-4, 1-8 KV heads, groups of 1-8 query heads, ragged lengths up to 40000, 0-8 sinks, a
+    recent window of 0-300 and a budget from 0 to past |J|.  Both endings of the chunked path
+    (the finish, and the resolve and emit passes) against the oracle and the planted set, and
+    against each other bit for bit."""
+    rng = np.random.default_rng(1000 + case)
+    Bn = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, 9))
+    G = int(rng.choice([1, 2, 4, 8]))
+    lens = [int(x) for x in rng.integers(1, 40001, size=Bn)]
+    n_sink = int(rng.integers(0, 9))
+    n_recent = int(rng.integers(0, 301))
+    nJ = max(0, max(lens) - n_sink - n_recent)
+    k_sel = int(rng.integers(0, max(2, min(nJ + 50, 6000))))
+    wl = synth.Workload(f"sel_rand{case}", 1, Bn, Hkv * G, Hkv, 128, "bf16", max(lens), n_sink,
+                        n_recent, k_sel, 1)
+    say(f"[select random shape {case}] B={Bn} Hkv={Hkv} G={G} lens={lens} sink={n_sink} "
+        f"recent={n_recent} k={k_sel}")
+    z, ranks = _planted(wl, lens, seed=77 + case, n_sink=n_sink, n_recent=n_recent)
+    # 40000 positions with k <= 6000: the finish; 600000: the resolve and emit passes
+    istride = max(1, n_sink + k_sel)
+    a = _run(orc, wl, lens, z, exact=True, n_sink=n_sink, n_recent=n_recent, k_sel=k_sel,
+             idx_stride=istride, max_len=40000)
+    b = _run(orc, wl, lens, z, exact=True, n_sink=n_sink, n_recent=n_recent, k_sel=k_sel,
+             idx_stride=istride, max_len=PASSES_MAX_LEN)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    ig, ng = a[0].cpu().numpy(), a[1].cpu().numpy()
+    for bi, N in enumerate(lens):
+        for h in range(Hkv):
+            keep = sorted((torch.nonzero(ranks[bi][h] < k_sel).flatten() + n_sink).tolist())
+            assert ig[bi, h, :ng[bi, h]].tolist() == list(range(min(n_sink, N))) + keep
+
+
 def test_select_finish_beyond_its_lds(orc):
     """The finish holds 8192 entries (kept keys and candidates of a unit) in LDS and reads the
     rest where the candidate pass wrote them: all keys equal (every key of J is an entry) and
