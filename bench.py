@@ -104,8 +104,8 @@ def select_bytes(wl, lens):
     (KV head, position of J) and read back by the candidate pass, and again by the emit when
     the chunked path ends in its resolve and emit passes rather than in the one-workgroup-per-
     unit finish (the library takes the finish when k_sel + max_len / 64 <= 8192), and the index
-    rows written.  (The survey's plan counts a second logit read and the keys four times, an
-    upper bound for a Selector that computes its own normaliser.)  The candidates and kept
+    rows written.  (Counting a second logit read and four passes over the keys gives an upper
+    bound, for a Selector that computes its own normaliser.)  The candidates and kept
     entries, about 2 % of J, and the 16 KB histograms are not counted."""
     nJ = sum(max(0, n - wl.n_recent - wl.n_sink) for n in lens)
     key_passes = 2 if wl.k_sel + max(lens) // 64 <= 8192 else 3
