@@ -222,7 +222,10 @@ __global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
     const float* zb = a.logits + ((int64_t)b * a.Hq + h * G) * a.logit_stride;
     const int base = lo & ~3;
     const int n4 = (hi - base + 3) >> 2;
-    // the first four heads' quads are in flight before the normalisers are known
+    // the dense step's log-sum-exp over J first (its wait then covers only itself), then the
+    // first four heads' quads, in flight before the normalisers are known
+    const float lse_j = (!REFINE && a.lse_j && tid < G) ? a.lse_j[(int64_t)b * a.Hq + h * G + tid]
+                                                        : 0.f;
     f32x4 v[4][kEvQ];
     auto load4 = [&](int g0) {
 #pragma unroll
@@ -253,11 +256,11 @@ __global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
     }
     if (!REFINE)
         for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
-    if (a.lse_j) {
-        // the dense step of the slow step gave the log-sum-exp over J
-        if (tid < G) s_lse[tid] = a.lse_j[(int64_t)b * a.Hq + h * G + tid] * kLog2e;
-    }
-    for (int g = w; !a.lse_j && g < G; g += kWaves) {
+    // the dense step of the slow step gave the log-sum-exp over J (the full Selector is always
+    // called on its own and computes it from the chunks' partial sums)
+    const bool have_lse_j = !REFINE && a.lse_j;
+    if (have_lse_j && tid < G) s_lse[tid] = lse_j * kLog2e;
+    for (int g = w; !have_lse_j && g < G; g += kWaves) {
         const float2* lp = a.lse_part + ((int64_t)b * a.Hq + h * G + g) * a.nchunk;
         float M = -INFINITY;
         for (int k = lane; k < a.nchunk; k += 64) M = fmaxf(M, lp[k].x);
@@ -311,16 +314,26 @@ __global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
         return;
     }
 #pragma unroll
-    for (int k = 0; k < kEvQ; ++k)
+    for (int k = 0; k < kEvQ; ++k) {
+        // a quad wholly inside the chunk goes out as one 16-byte store when the chunk starts on
+        // a multiple of 4
+        const int j = base + 4 * (k * kThreads + tid);
+        u32x4 kq;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int j = base + 4 * (k * kThreads + tid) + e;
-            if (j >= lo && j < hi) {
-                const uint32_t key = __float_as_uint(f[k][e]);
-                keys[j - lo] = key;
-                atomicAdd(&lh[key >> kCShift[0]], 1u);
-            }
+        for (int e = 0; e < 4; ++e) kq[e] = __float_as_uint(f[k][e]);
+        if (base == lo && j + 3 < hi) {
+            *(u32x4*)(keys + (j - lo)) = kq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&lh[kq[e] >> kCShift[0]], 1u);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j + e >= lo && j + e < hi) {
+                    keys[j + e - lo] = kq[e];
+                    atomicAdd(&lh[kq[e] >> kCShift[0]], 1u);
+                }
         }
+    }
     __syncthreads();
     uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
     // bins 2t and 2t + 1 as one 64-bit add (the low and high halves of a little-endian word;
