@@ -74,9 +74,43 @@ __device__ __forceinline__ float wave_sum(float x) {
     for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
     return x;
 }
-__device__ __forceinline__ uint32_t wave_sum_u(uint32_t x) {
-    for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+// inclusive prefix sum over the 64 lanes of a wave: DPP row shifts within each row of 16
+// lanes, then the broadcasts of lane 15 into row 1 (and row 1's into 2 and 3 via lane 31)
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0u, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
     return x;
+}
+__device__ __forceinline__ uint32_t wave_sum_u(uint32_t x) {
+    return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
+}
+
+// Exclusive prefix sum over the kW wavefronts of a workgroup in thread order, with the total,
+// in one barrier: the wave totals alternate between two rows of wt, and a wave can only reach
+// the scan after next once every wave has read this one's totals (at the next scan's barrier).
+// parity starts at 0 and is kept by the caller.
+template <int kW>
+__device__ __forceinline__ uint32_t scan_total(uint32_t x, uint32_t (&wt)[2][kW], int& parity,
+                                               uint32_t* tot) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t inc = wave_incl_scan(x);
+    uint32_t* row = wt[parity];
+    parity ^= 1;
+    if (lane == 63) row[w] = inc;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) {
+        const uint32_t t = row[ww];
+        before += ww < w ? t : 0u;
+        all += t;
+    }
+    *tot = all;
+    return before + inc - x;
 }
 
 // Block-wide reductions over the 256 threads (4 wavefronts).
@@ -108,11 +142,7 @@ __device__ uint32_t block_sum_u(uint32_t x, uint32_t* sh) {
 // Exclusive prefix sum over the 256 threads in thread order.
 __device__ uint32_t block_exclusive_scan(uint32_t x, uint32_t* sh) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t inc = x;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-    }
+    const uint32_t inc = wave_incl_scan(x);
     if (lane == 63) sh[w] = inc;
     __syncthreads();
     uint32_t before = 0;
@@ -513,14 +543,15 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
 // Over bins held kPer per thread in ascending order (thread t holds bins kPer t ... kPer t +
 // kPer - 1), finds the bin that holds the k-th largest key (0 < k <= the number of keys):
 // s_sel[0] = the bin, s_sel[1] = the number of keys in higher bins.
-template <int kPer>
-__device__ void pick_bin(const uint32_t (&bins)[kPer], uint32_t k, uint32_t* sh, uint32_t* s_sel) {
+template <int kPer, int kW>
+__device__ void pick_bin(const uint32_t (&bins)[kPer], uint32_t k, uint32_t (&wt)[2][kW],
+                         int& parity, uint32_t* s_sel) {
     const int tid = threadIdx.x;
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) mine += bins[j];
-    const uint32_t below_incl = block_exclusive_scan(mine, sh) + mine;
-    const uint32_t total = block_sum_u(mine, sh);
+    uint32_t total;
+    const uint32_t below_incl = scan_total(mine, wt, parity, &total) + mine;
     const uint32_t above = total - below_incl;          // keys in higher bins than this thread's
     if (above < k && k <= above + mine) {
         uint32_t cum = above;
@@ -570,8 +601,9 @@ __device__ __forceinline__ void load_chunk_keys(const SelArgs& a, int unit, int 
 // in the candidates' share.  Inactive units get their final counts here: everything (take_all)
 // or nothing.  The histogram, the keys and the length are loaded together at entry.
 __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
-    __shared__ uint32_t sh[4];
+    __shared__ uint32_t wt[2][kWaves];
     __shared__ uint32_t s_sel[2];
+    int parity = 0;
     constexpr int kPer = kCBins0 / kThreads;          // histogram bins per thread, ascending
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
@@ -587,7 +619,7 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
     uint32_t prefix = (!take_all && k_rem == 0) ? 0xffffffffu : 0u;   // keep nothing
     const bool active = sel_active(prefix, k_rem, take_all);
     if (active) {
-        pick_bin<kPer>(bins, (uint32_t)k_rem, sh, s_sel);
+        pick_bin<kPer>(bins, (uint32_t)k_rem, wt, parity, s_sel);
         prefix = s_sel[0] << kCShift[0];
         k_rem -= (int32_t)s_sel[1];
     }
@@ -623,8 +655,8 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
     }
     if (a.finish) nc += gt;
     // counts packed as (greater << 16) | candidates: at most kSelChunk each
-    const uint32_t excl = block_exclusive_scan((gt << 16) | nc, sh);
-    const uint32_t tot = block_sum_u((gt << 16) | nc, sh);
+    uint32_t tot;
+    const uint32_t excl = scan_total((gt << 16) | nc, wt, parity, &tot);
     if (tid == 0) {
         *cand_n = tot & 0xffffu;
         cn[0] = tot >> 16;
@@ -740,11 +772,7 @@ struct UnitShared {
 // exclusive scan over the 1024 threads (ascending thread order); total returned in *tot
 __device__ uint32_t unit_scan(uint32_t x, UnitShared& sm, uint32_t* tot) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t inc = x;
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-    }
+    const uint32_t inc = wave_incl_scan(x);
     if (lane == 63) sm.wtot[w] = inc;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -913,24 +941,57 @@ __global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
     }
 }
 
-// Over bins held kPer per thread of the 1024-thread workgroup in ascending order, finds the
-// bin that holds the k-th largest key (0 < k <= the number of keys): sm.sel[0] = the bin,
-// sm.sel[1] = the number of keys in higher bins.
+// Finish of the chunked Selector, one 1024-thread workgroup per (b, KV head), after the
+// candidate pass has written, per chunk and in position order, every key whose digit 0 is at or
+// above the bin d0 of the k-th largest key, with its position.
+//   1. The chunks' entry numbers are scanned: chunk c's entries go to [off[c], off[c + 1]).
+//   2. Each wavefront copies whole chunks to LDS (chunks w, w + 16, ..., two at a time with
+//      every load of both issued first), so no entry needs a search for its chunk; the keys of
+//      bin d0 fill the digit-1 histogram on the way.  Entries past kFinCap stay where they lie
+//      (their chunk is then found by a binary search over off).
+//   3. Digit 1 of T from that histogram; digit 2 over the entries of T's digit-1 bin.
+//   4. The ordered emit: entries above T, and those equal to T while fewer than k_rem came
+//      before, after the sink positions, with one packed (greater, equal) scan per 8192 entries.
+// It replaces the resolve and emit passes (one launch and one read of all the keys fewer).
+constexpr int kFinCap = kFinishCap;                    // entries held in LDS
+constexpr int kFinChunks = kUT;                        // chunks per unit (contexts up to 4M)
+constexpr int kFinCopy = 4;                            // entries per lane per chunk in flight
+constexpr int kFinEmit = 8;                            // consecutive entries per thread in the emit
+constexpr int kFinD1 = 1 << (kCShift[0] - kCShift[1]); // digit-1 bins
+constexpr int kFinD2 = 1 << kCShift[1];                // digit-2 bins
+static_assert((int64_t)kFinishCap * kFinishBinShare <= (int64_t)kFinChunks * kSelChunk,
+              "a context the finish takes has its chunk numbers in one scan");
+static_assert(kFinD1 == kUT && kFinD2 <= kUT, "one digit-1 bin per thread, at most one digit-2 bin");
+static_assert(kFinCap % (kFinEmit * kUT) == 0, "an emit round lies wholly in LDS or wholly past it");
+static_assert(kFinEmit * kUT < 65536, "an emit round's counts fit the halves of its packed scan");
+struct FinishShared {
+    uint32_t wt[2][kUW];
+    uint32_t sel[2];
+    uint32_t off[kFinChunks + 1];                      // exclusive scan of the entry numbers
+    uint32_t h1[kFinD1];
+    uint32_t h2[kFinD2];
+    __attribute__((aligned(16))) uint32_t key[kFinCap];
+    __attribute__((aligned(16))) int32_t pos[kFinCap];
+};
+
+// Over bins held kPer per thread of the 1024-thread workgroup in ascending order, finds the bin
+// that holds the k-th largest key (0 < k <= the number of keys): fs.sel = (the bin, the keys in
+// higher bins).
 template <int kPer>
-__device__ void unit_pick_bin(const uint32_t (&bins)[kPer], uint32_t k, UnitShared& sm) {
-    const int tid = threadIdx.x;
+__device__ void finish_pick(const uint32_t (&bins)[kPer], uint32_t k, FinishShared& fs,
+                            int& parity) {
     uint32_t mine = 0;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) mine += bins[j];
     uint32_t total;
-    const uint32_t excl = unit_scan(mine, sm, &total);
+    const uint32_t excl = scan_total(mine, fs.wt, parity, &total);
     const uint32_t above = total - excl - mine;        // keys in higher bins than this thread's
     if (above < k && k <= above + mine) {
         uint32_t cum = above;
         for (int j = kPer - 1; j >= 0; --j) {
             if (cum + bins[j] >= k) {
-                sm.sel[0] = (uint32_t)(kPer * tid + j);
-                sm.sel[1] = cum;
+                fs.sel[0] = (uint32_t)(kPer * threadIdx.x + j);
+                fs.sel[1] = cum;
                 break;
             }
             cum += bins[j];
@@ -939,34 +1000,10 @@ __device__ void unit_pick_bin(const uint32_t (&bins)[kPer], uint32_t k, UnitShar
     __syncthreads();
 }
 
-// Finish of the chunked Selector, one 1024-thread workgroup per (b, KV head), after the
-// candidate pass has written, per chunk and in position order, every key whose digit 0 is at or
-// above the bin of the k-th largest key, with its position: the entries of every chunk are
-// copied to LDS in chunk order (so in position order; a binary search over the scanned
-// per-chunk numbers finds each one's chunk; past kFinCap entries they are read where they lie),
-// digits 1 and 2 of T are resolved over the entries of that bin, and the ordered emit writes
-// the entries with key > T, or key == T and fewer than k_rem earlier entries equal to T, after
-// the sink positions.  It replaces the resolve and emit passes (one launch and one read of all
-// the keys fewer).
-constexpr int kFinCap = kFinishCap;                    // entries held in LDS
-constexpr int kFinChunks = kUT;                        // chunks per unit (contexts up to 4M)
-constexpr int kFinBatch = 8;                           // entry loads per thread in flight
-constexpr int kFinEmit = 8;                            // consecutive entries per thread in the emit
-static_assert((int64_t)kFinishCap * kFinishBinShare <= (int64_t)kFinChunks * kSelChunk,
-              "a context the finish takes has its chunk numbers in one scan");
-static_assert((1 << (kCShift[0] - kCShift[1])) == kUT, "one digit-1 bin per thread");
-static_assert((1 << kCShift[1]) <= kUT, "at most one digit-2 bin per thread");
-struct FinishShared {
-    UnitShared u;
-    uint32_t off[kFinChunks + 1];                      // exclusive scan of the entry numbers
-    uint32_t key[kFinCap];
-    int32_t pos[kFinCap];
-};
-
 __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
     __shared__ FinishShared fs;
-    UnitShared& sm = fs.u;
     const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int unit = b * a.Hkv + h;
     // the entry numbers, the state and the length are independent loads
     const uint32_t n_mine = tid < a.nchunk ? a.cand_n[(int64_t)unit * a.nchunk + tid] : 0u;
@@ -984,104 +1021,137 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
         return;
     }
     if (!sel_active(T, k_rem, take_all)) return;       // keep nothing
+    fs.h1[tid] = 0u;
+    if (tid < kFinD2) fs.h2[tid] = 0u;
+    if (tid == 0) fs.sel[0] = fs.sel[1] = 0u;
+    int parity = 0;
+    // 1. chunk c's entries go to [off[c], off[c + 1]); off[nch] = E
     uint32_t E;
-    const uint32_t ex = unit_scan(n_mine, sm, &E);
+    const uint32_t ex = scan_total(n_mine, fs.wt, parity, &E);
     fs.off[tid] = ex;
     if (tid == 0) fs.off[kFinChunks] = E;
     __syncthreads();
-    // the chunk of entry i < E: the last c with off[c] <= i
-    auto chunk_of = [&](uint32_t i) -> int {
-        int lo = 0, hi = kFinChunks;                    // off[lo] <= i < off[hi]
+    const int nch = (nJ + kSelChunk - 1) / kSelChunk;  // chunks holding positions of J
+    const int64_t base = (int64_t)unit * a.nchunk * kSelChunk;
+    // 2. copy, two chunks per wavefront at a time; loads clamped into the chunk's region
+    const uint32_t d0 = T >> kCShift[0];
+    for (int ca = w; ca < nch; ca += 2 * kUW) {
+        const int cb = ca + kUW;
+        const uint32_t oa = fs.off[ca], na = fs.off[ca + 1] - oa;
+        const uint32_t ob = cb < nch ? fs.off[cb] : 0u, nb = cb < nch ? fs.off[cb + 1] - ob : 0u;
+        const int64_t ra = base + (int64_t)ca * kSelChunk;
+        const int64_t rb = base + (int64_t)min(cb, nch - 1) * kSelChunk;
+        for (uint32_t j0 = 0; j0 < max(na, nb); j0 += 64 * kFinCopy) {
+            uint32_t ka[kFinCopy], kb[kFinCopy];
+            int32_t pa[kFinCopy], pb[kFinCopy];
+#pragma unroll
+            for (int u = 0; u < kFinCopy; ++u) {
+                const uint32_t j = min(j0 + lane + 64 * u, (uint32_t)kSelChunk - 1);
+                ka[u] = a.cand[ra + j];
+                pa[u] = a.epos[ra + j];
+                kb[u] = a.cand[rb + j];
+                pb[u] = a.epos[rb + j];
+            }
+#pragma unroll
+            for (int u = 0; u < kFinCopy; ++u) {
+                const uint32_t j = j0 + lane + 64 * u;
+                if (j < na) {
+                    if (oa + j < (uint32_t)kFinCap) {
+                        fs.key[oa + j] = ka[u];
+                        fs.pos[oa + j] = pa[u];
+                    }
+                    if ((ka[u] >> kCShift[0]) == d0)
+                        atomicAdd(&fs.h1[(ka[u] >> kCShift[1]) & kCMask[1]], 1u);
+                }
+                if (j < nb) {
+                    if (ob + j < (uint32_t)kFinCap) {
+                        fs.key[ob + j] = kb[u];
+                        fs.pos[ob + j] = pb[u];
+                    }
+                    if ((kb[u] >> kCShift[0]) == d0)
+                        atomicAdd(&fs.h1[(kb[u] >> kCShift[1]) & kCMask[1]], 1u);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // entries past kFinCap: found in their chunk's region (the last c with off[c] <= i)
+    auto where = [&](uint32_t i) -> int64_t {
+        int lo = 0, hi = nch;                           // off[lo] <= i < off[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (fs.off[mid] <= i) lo = mid; else hi = mid;
         }
-        return lo;
+        return base + (int64_t)lo * kSelChunk + (i - fs.off[lo]);
     };
-    const int64_t base = (int64_t)unit * a.nchunk * kSelChunk;
-    auto where = [&](uint32_t i) -> int64_t {
-        const int c = chunk_of(i);
-        return base + (int64_t)c * kSelChunk + (i - fs.off[c]);
-    };
-    const uint32_t held = min(E, (uint32_t)kFinCap);
-    for (uint32_t i0 = tid; i0 < held; i0 += kFinBatch * kUT) {
-        uint32_t kk[kFinBatch];
-        int32_t pp[kFinBatch];
-#pragma unroll
-        for (int u = 0; u < kFinBatch; ++u) {
-            const uint32_t i = i0 + u * kUT;
-            const int64_t w = i < held ? where(i) : base;
-            kk[u] = a.cand[w];
-            pp[u] = a.epos[w];
-        }
-#pragma unroll
-        for (int u = 0; u < kFinBatch; ++u) {
-            const uint32_t i = i0 + u * kUT;
-            if (i < held) {
-                fs.key[i] = kk[u];
-                fs.pos[i] = pp[u];
-            }
-        }
+    // 3. digits 1 and 2 of T
+    {
+        const uint32_t bins[1] = {fs.h1[tid]};
+        finish_pick<1>(bins, (uint32_t)k_rem, fs, parity);
+        T |= fs.sel[0] << kCShift[1];
+        k_rem -= (int32_t)fs.sel[1];
     }
-    __syncthreads();
-    auto key_of = [&](uint32_t i) -> uint32_t {
-        return i < (uint32_t)kFinCap ? fs.key[i] : a.cand[where(i)];
-    };
-    // digits 1 and 2 of T over the entries of the digit-0 bin
-    for (int pass = 1; pass < 3; ++pass) {
-        sm.hist[tid] = 0u;
-        __syncthreads();
-        const uint32_t want = T >> kCShift[pass - 1];
+    {
+        const uint32_t want = T >> kCShift[1];
         for (uint32_t i = tid; i < E; i += kUT) {
-            const uint32_t key = key_of(i);
-            if ((key >> kCShift[pass - 1]) == want)
-                atomicAdd(&sm.hist[(key >> kCShift[pass]) & kCMask[pass]], 1u);
+            const uint32_t key = i < (uint32_t)kFinCap ? fs.key[i] : a.cand[where(i)];
+            if ((key >> kCShift[1]) == want) atomicAdd(&fs.h2[key & kCMask[2]], 1u);
         }
         __syncthreads();
-        const uint32_t one[1] = {sm.hist[tid]};
-        unit_pick_bin<1>(one, (uint32_t)k_rem, sm);
-        T |= sm.sel[0] << kCShift[pass];
-        k_rem -= (int32_t)sm.sel[1];
-        __syncthreads();
+        const uint32_t bins[1] = {tid < kFinD2 ? fs.h2[tid] : 0u};
+        finish_pick<1>(bins, (uint32_t)k_rem, fs, parity);
+        T |= fs.sel[0];
+        k_rem -= (int32_t)fs.sel[1];
     }
-    // ordered emit: the entries are in position order; thread t takes kFinEmit consecutive
-    // entries of each round, so a round costs two scans
-    uint32_t eq_seen = 0, kept = 0;
+    // 4. ordered emit; a row never takes more than min(k_sel, nJ) positions
+    const uint32_t kr = (uint32_t)max(k_rem, 0);
+    const uint32_t n_out = (uint32_t)min(a.k_sel, nJ);
+    uint32_t gt_seen = 0, eq_seen = 0;
     for (uint32_t i0 = 0; i0 < E; i0 += kFinEmit * kUT) {
         const uint32_t ib = i0 + kFinEmit * tid;
         uint32_t kk[kFinEmit];
-        uint32_t n_eq_mine = 0;
+        int32_t pp[kFinEmit];
+        if (i0 < (uint32_t)kFinCap) {
+            const u32x4 k0 = *(const u32x4*)&fs.key[ib], k1 = *(const u32x4*)&fs.key[ib + 4];
+            const int4 p0 = *(const int4*)&fs.pos[ib], p1 = *(const int4*)&fs.pos[ib + 4];
+            kk[0] = k0[0]; kk[1] = k0[1]; kk[2] = k0[2]; kk[3] = k0[3];
+            kk[4] = k1[0]; kk[5] = k1[1]; kk[6] = k1[2]; kk[7] = k1[3];
+            pp[0] = p0.x; pp[1] = p0.y; pp[2] = p0.z; pp[3] = p0.w;
+            pp[4] = p1.x; pp[5] = p1.y; pp[6] = p1.z; pp[7] = p1.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kFinEmit; ++e) {
+                const int64_t at = ib + e < E ? where(ib + e) : base;
+                kk[e] = a.cand[at];
+                pp[e] = a.epos[at];
+            }
+        }
+        uint32_t gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < kFinEmit; ++e) {
-            kk[e] = ib + e < E ? key_of(ib + e) : 0u;
-            n_eq_mine += (ib + e < E && kk[e] == T) ? 1u : 0u;
+            const bool in = ib + e < E;
+            gt += (in && kk[e] > T) ? 1u : 0u;
+            eq += (in && kk[e] == T) ? 1u : 0u;
         }
-        uint32_t n_eq;
-        uint32_t eq_rank = eq_seen + unit_scan(n_eq_mine, sm, &n_eq);
-        uint32_t keep_mask = 0;
+        uint32_t tot;
+        const uint32_t exc = scan_total((gt << 16) | eq, fs.wt, parity, &tot);
+        uint32_t e_before = eq_seen + (exc & 0xffffu);
+        uint32_t out = gt_seen + (exc >> 16) + min(e_before, kr);
 #pragma unroll
         for (int e = 0; e < kFinEmit; ++e) {
-            bool keep = false;
-            if (ib + e < E) {
-                if (kk[e] > T) {
-                    keep = true;
-                } else if (kk[e] == T) {
-                    keep = eq_rank < (uint32_t)k_rem;
-                    ++eq_rank;
-                }
+            const bool in = ib + e < E;
+            bool keep = in && kk[e] > T;
+            if (in && kk[e] == T) {
+                keep = e_before < kr;
+                ++e_before;
             }
-            keep_mask |= keep ? (1u << e) : 0u;
+            if (keep) {
+                if (out < n_out) row[ns + out] = pp[e];
+                ++out;
+            }
         }
-        uint32_t n_keep;
-        uint32_t out = kept + unit_scan((uint32_t)__popc(keep_mask), sm, &n_keep);
-#pragma unroll
-        for (int e = 0; e < kFinEmit; ++e)
-            if (keep_mask & (1u << e)) {
-                const uint32_t i = ib + e;
-                row[ns + out++] = i < (uint32_t)kFinCap ? fs.pos[i] : a.epos[where(i)];
-            }
-        eq_seen += n_eq;
-        kept += n_keep;
+        gt_seen += tot >> 16;
+        eq_seen += tot & 0xffffu;
     }
 }
 
