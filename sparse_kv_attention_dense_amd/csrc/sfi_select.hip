@@ -603,6 +603,8 @@ __device__ __forceinline__ void load_chunk_keys(const SelArgs& a, int unit, int 
 __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
     __shared__ uint32_t wt[2][kWaves];
     __shared__ uint32_t s_sel[2];
+    __shared__ uint32_t s_key[kSelChunk];             // the chunk's candidates, staged for
+    __shared__ int32_t s_pos[kSelChunk];              //   coalesced stores
     int parity = 0;
     constexpr int kPer = kCBins0 / kThreads;          // histogram bins per thread, ascending
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
@@ -663,17 +665,23 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
         cn[1] = 0u;
         cn[2] = 0u;
     }
-    const int64_t region = ((int64_t)unit * a.nchunk + c) * kSelChunk + (excl & 0xffffu);
-    uint32_t* out = a.cand + region;
-    int32_t* opos = a.epos + region;
+    uint32_t o = excl & 0xffffu;
     const int jb = a.n_sink + c * kSelChunk + tid * kPerThread;
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
         const uint32_t d = kv[k] >> kCShift[0];
         if (tid * kPerThread + k < cnt && (a.finish ? d >= d0 : d == d0)) {
-            *out++ = kv[k];
-            if (a.finish) *opos++ = jb + k;
+            s_key[o] = kv[k];
+            s_pos[o] = jb + k;
+            ++o;
         }
+    }
+    __syncthreads();
+    const int64_t region = ((int64_t)unit * a.nchunk + c) * kSelChunk;
+    const uint32_t n = tot & 0xffffu;
+    for (uint32_t i = tid; i < n; i += kThreads) {
+        a.cand[region + i] = s_key[i];
+        if (a.finish) a.epos[region + i] = s_pos[i];
     }
 }
 
@@ -972,6 +980,7 @@ struct FinishShared {
     uint32_t h2[kFinD2];
     __attribute__((aligned(16))) uint32_t key[kFinCap];
     __attribute__((aligned(16))) int32_t pos[kFinCap];
+    int32_t out[kFinCap];                              // the kept positions, staged for the row
 };
 
 // Over bins held kPer per thread of the 1024-thread workgroup in ascending order, finds the bin
@@ -1091,11 +1100,37 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
         T |= fs.sel[0] << kCShift[1];
         k_rem -= (int32_t)fs.sel[1];
     }
+    // kFinEmit consecutive entries per thread and round (16-byte LDS reads)
+    auto entries = [&](uint32_t ib, uint32_t (&kk)[kFinEmit], int32_t (&pp)[kFinEmit], bool pos) {
+        if (ib < (uint32_t)kFinCap) {
+            const u32x4 k0 = *(const u32x4*)&fs.key[ib], k1 = *(const u32x4*)&fs.key[ib + 4];
+            kk[0] = k0[0]; kk[1] = k0[1]; kk[2] = k0[2]; kk[3] = k0[3];
+            kk[4] = k1[0]; kk[5] = k1[1]; kk[6] = k1[2]; kk[7] = k1[3];
+            if (pos) {
+                const int4 p0 = *(const int4*)&fs.pos[ib], p1 = *(const int4*)&fs.pos[ib + 4];
+                pp[0] = p0.x; pp[1] = p0.y; pp[2] = p0.z; pp[3] = p0.w;
+                pp[4] = p1.x; pp[5] = p1.y; pp[6] = p1.z; pp[7] = p1.w;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < kFinEmit; ++e) {
+                const int64_t at = ib + e < E ? where(ib + e) : base;
+                kk[e] = a.cand[at];
+                if (pos) pp[e] = a.epos[at];
+            }
+        }
+    };
     {
         const uint32_t want = T >> kCShift[1];
-        for (uint32_t i = tid; i < E; i += kUT) {
-            const uint32_t key = i < (uint32_t)kFinCap ? fs.key[i] : a.cand[where(i)];
-            if ((key >> kCShift[1]) == want) atomicAdd(&fs.h2[key & kCMask[2]], 1u);
+        for (uint32_t i0 = 0; i0 < E; i0 += kFinEmit * kUT) {
+            const uint32_t ib = i0 + kFinEmit * tid;
+            uint32_t kk[kFinEmit];
+            int32_t pp[kFinEmit];
+            entries(ib, kk, pp, false);
+#pragma unroll
+            for (int e = 0; e < kFinEmit; ++e)
+                if (ib + e < E && (kk[e] >> kCShift[1]) == want)
+                    atomicAdd(&fs.h2[kk[e] & kCMask[2]], 1u);
         }
         __syncthreads();
         const uint32_t bins[1] = {tid < kFinD2 ? fs.h2[tid] : 0u};
@@ -1103,29 +1138,15 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
         T |= fs.sel[0];
         k_rem -= (int32_t)fs.sel[1];
     }
-    // 4. ordered emit; a row never takes more than min(k_sel, nJ) positions
+    // 4. ordered emit into LDS; a row never takes more than min(k_sel, nJ) positions
     const uint32_t kr = (uint32_t)max(k_rem, 0);
-    const uint32_t n_out = (uint32_t)min(a.k_sel, nJ);
+    const uint32_t n_out = (uint32_t)min(min(a.k_sel, nJ), kFinCap);
     uint32_t gt_seen = 0, eq_seen = 0;
     for (uint32_t i0 = 0; i0 < E; i0 += kFinEmit * kUT) {
         const uint32_t ib = i0 + kFinEmit * tid;
         uint32_t kk[kFinEmit];
         int32_t pp[kFinEmit];
-        if (i0 < (uint32_t)kFinCap) {
-            const u32x4 k0 = *(const u32x4*)&fs.key[ib], k1 = *(const u32x4*)&fs.key[ib + 4];
-            const int4 p0 = *(const int4*)&fs.pos[ib], p1 = *(const int4*)&fs.pos[ib + 4];
-            kk[0] = k0[0]; kk[1] = k0[1]; kk[2] = k0[2]; kk[3] = k0[3];
-            kk[4] = k1[0]; kk[5] = k1[1]; kk[6] = k1[2]; kk[7] = k1[3];
-            pp[0] = p0.x; pp[1] = p0.y; pp[2] = p0.z; pp[3] = p0.w;
-            pp[4] = p1.x; pp[5] = p1.y; pp[6] = p1.z; pp[7] = p1.w;
-        } else {
-#pragma unroll
-            for (int e = 0; e < kFinEmit; ++e) {
-                const int64_t at = ib + e < E ? where(ib + e) : base;
-                kk[e] = a.cand[at];
-                pp[e] = a.epos[at];
-            }
-        }
+        entries(ib, kk, pp, true);
         uint32_t gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < kFinEmit; ++e) {
@@ -1146,13 +1167,17 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
                 ++e_before;
             }
             if (keep) {
-                if (out < n_out) row[ns + out] = pp[e];
+                if (out < n_out) fs.out[out] = pp[e];
                 ++out;
             }
         }
         gt_seen += tot >> 16;
         eq_seen += tot & 0xffffu;
     }
+    // the staged row, coalesced (n_out <= k_sel <= kFinCap under the finish rule)
+    __syncthreads();
+    const uint32_t n_kept = min(n_out, gt_seen + min(eq_seen, kr));
+    for (uint32_t i = tid; i < n_kept; i += kUT) row[ns + i] = fs.out[i];
 }
 
 __global__ void __launch_bounds__(kUT) select_unit_kernel(SelArgs a) {
