@@ -280,6 +280,7 @@ sfi_status prep_select(const sfi_kv_desc* kv, const float* logits, int64_t logit
     a->refine = 0;
     a->key_norm = nullptr;
     a->norm_stride = 0;
+    a->norm_vec = 0;
     a->lam = 0.f;
     a->keep_soft = a->keep_cross = 1.f;
     a->prior_decay = a->tail_frac = a->tail_brake = 0.f;
@@ -560,6 +561,7 @@ SFI_EXPORT sfi_status sfi_select_refined(const sfi_kv_desc* kv, const float* log
     a.refine = 1;
     a.key_norm = key_norm;
     a.norm_stride = norm_stride;
+    a.norm_vec = key_norm && aligned(key_norm, 16) && norm_stride % 4 == 0 ? 1 : 0;
     a.lam = p.lambda;
     a.keep_soft = 1.f - p.alpha_soft;
     a.keep_cross = 1.f - p.alpha_cross;

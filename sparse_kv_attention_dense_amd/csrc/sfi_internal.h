@@ -119,6 +119,7 @@ struct SelArgs {
     int32_t refine;
     const float* key_norm;           // [B][Hkv][norm_stride] or null (no key-norm factor)
     int64_t norm_stride;
+    int32_t norm_vec;                // 1: key_norm and norm_stride allow 16-byte loads
     float lam;                       // fusion weight of the prior, in [0, 1)
     float keep_soft, keep_cross;     // 1 - alpha_soft, 1 - alpha_cross
     float prior_decay, tail_frac, tail_brake;

@@ -88,6 +88,16 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
 __device__ __forceinline__ uint32_t wave_sum_u(uint32_t x) {
     return __builtin_amdgcn_readlane(wave_incl_scan(x), 63);
 }
+// x of the previous lane (lane 0 gets `first`) and of the next lane (lane 63 gets `last`): the
+// whole-wave DPP shifts by one lane
+__device__ __forceinline__ float lane_prev(float x, float first) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(first), __float_as_int(x),
+                                                      0x138, 0xf, 0xf, false));   // wave_shr:1
+}
+__device__ __forceinline__ float lane_next(float x, float last) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(last), __float_as_int(x),
+                                                      0x130, 0xf, 0xf, false));   // wave_shl:1
+}
 
 // Exclusive prefix sum over the kW wavefronts of a workgroup in thread order, with the total,
 // in one barrier: the wave totals alternate between two rows of wt, and a wave can only reach
@@ -269,21 +279,6 @@ __global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
         }
     };
     load4(0);
-    // the key norms of the full Selector's prior, with the first quads (clamped into the chunk)
-    float nrm[kEvQ][4];
-    if (REFINE && a.key_norm) {
-        const float* kn = a.key_norm + (int64_t)unit * a.norm_stride;
-#pragma unroll
-        for (int k = 0; k < kEvQ; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                nrm[k][e] = kn[min(max(base + 4 * (k * kThreads + tid) + e, lo), hi - 1)];
-    } else {
-#pragma unroll
-        for (int k = 0; k < kEvQ; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) nrm[k][e] = 1.f;
-    }
     if (!REFINE)
         for (int t = tid; t < kCBins0; t += kThreads) lh[t] = 0u;
     // the dense step of the slow step gave the log-sum-exp over J (the full Selector is always
@@ -325,20 +320,53 @@ __global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
     uint32_t* keys = a.keys + ((int64_t)unit * a.nchunk + c) * kSelChunk;
     if constexpr (REFINE) {
         // log2 of the unnormalised fused score for the refinement pass, and this chunk's share
-        // of the fusion normaliser
+        // of the fusion normaliser.  The key norms of the prior are loaded here, once the
+        // logits' registers are free: 16-byte loads like the logits' when the rows allow them
+        // (a.norm_vec), else each clamped into the chunk.
+        float nrm[kEvQ][4];
+        if (a.key_norm && a.norm_vec) {
+            const float* kn = a.key_norm + (int64_t)unit * a.norm_stride + base;
+#pragma unroll
+            for (int k = 0; k < kEvQ; ++k) {
+                const int f = k * kThreads + tid;
+                const f32x4 x = f < n4 ? *(const f32x4*)(kn + 4 * f) : f32x4{1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nrm[k][e] = x[e];
+            }
+        } else if (a.key_norm) {
+            const float* kn = a.key_norm + (int64_t)unit * a.norm_stride;
+#pragma unroll
+            for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    nrm[k][e] = kn[min(max(base + 4 * (k * kThreads + tid) + e, lo), hi - 1)];
+        } else {
+#pragma unroll
+            for (int k = 0; k < kEvQ; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) nrm[k][e] = 1.f;
+        }
         float* lf = a.lfused + ((int64_t)unit * a.nchunk + c) * kSelChunk;
         float zs = 0.f;
 #pragma unroll
-        for (int k = 0; k < kEvQ; ++k)
+        for (int k = 0; k < kEvQ; ++k) {
+            const int j = base + 4 * (k * kThreads + tid);
+            f32x4 lq;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = base + 4 * (k * kThreads + tid) + e;
-                if (j >= lo && j < hi) {
-                    const float l = fused_log2(a, f[k][e], prior_log2_n(a, j, r.j0, r.nJ, nrm[k][e]));
-                    lf[j - lo] = l;
-                    zs += exp2_hw(l);
-                }
+                lq[e] = fused_log2(a, f[k][e], prior_log2_n(a, j + e, r.j0, r.nJ, nrm[k][e]));
+                if (j + e >= lo && j + e < hi) zs += exp2_hw(lq[e]);
             }
+            // a quad wholly inside the chunk goes out as one 16-byte store when the chunk starts
+            // on a multiple of 4
+            if (base == lo && j + 3 < hi) {
+                *(f32x4*)(lf + (j - lo)) = lq;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j + e >= lo && j + e < hi) lf[j + e - lo] = lq[e];
+            }
+        }
         zs = block_sum(zs, sh);
         if (tid == 0) a.zpart[(int64_t)unit * a.nchunk + c] = zs;
         return;
@@ -400,7 +428,7 @@ static_assert(kRefSpan < 65536, "a 16-bit count holds every key of a workgroup")
 static_assert(kSelChunk % 4 == 0, "16-byte loads of the score buffer");
 static_assert((kRefHeads * kRefWords) % (4 * kRefThreads) == 0, "16-byte clears of the histograms");
 __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
-    __shared__ float s_z[kRefWaves][kRefHeads];
+    __shared__ float s_l2z[kRefHeads];                 // log2 of each head's fusion normaliser
     __shared__ uint32_t lh[kRefHeads][kRefWords];
     const int c = blockIdx.x / kCrossParts, part = blockIdx.x % kCrossParts;
     const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -429,7 +457,7 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
                 // the scores of pass 0 are still in registers
             } else {
                 f32x4 q[kRefHeads];
-                float ql[kRefHeads], qr[kRefHeads], zs[kRefHeads];
+                float ql[kRefHeads], qr[kRefHeads];
 #pragma unroll
                 for (int hh = 0; hh < kRefHeads; ++hh) {
                     const int unit = b * a.Hkv + h0 + min(hh, nh - 1);
@@ -437,12 +465,15 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
                     q[hh] = *(const f32x4*)(lf + jq);
                     ql[hh] = lf[jl];                   // the same address in every lane
                     qr[hh] = lf[jr];
-                    zs[hh] = 0.f;
                 }
-                for (int k = tid; k < nc; k += kRefThreads)
-#pragma unroll
-                    for (int hh = 0; hh < kRefHeads; ++hh)
-                        zs[hh] += a.zpart[(int64_t)(b * a.Hkv + h0 + min(hh, nh - 1)) * a.nchunk + k];
+                // wave w sums the chunk shares of heads w, w + kRefWaves, ...
+                for (int hh = w; hh < nh; hh += kRefWaves) {
+                    const float* zp = a.zpart + (int64_t)(b * a.Hkv + h0 + hh) * a.nchunk;
+                    float zs = 0.f;
+                    for (int k = lane; k < nc; k += 64) zs += zp[k];
+                    zs = wave_sum(zs);
+                    if (lane == 0) s_l2z[hh] = __log2f(zs);
+                }
                 if (pass == 1) {
                     // the histograms of this group start from zero; the barrier below orders the
                     // clear after the previous group's flush and before any count
@@ -450,21 +481,12 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
                     for (int t = tid; t < kRefHeads * kRefWords / 4; t += kRefThreads)
                         l4[t] = u32x4{0u, 0u, 0u, 0u};
                 }
-#pragma unroll
-                for (int hh = 0; hh < kRefHeads; ++hh) zs[hh] = wave_sum(zs[hh]);
-                if (lane == 0)
-#pragma unroll
-                    for (int hh = 0; hh < kRefHeads; ++hh) s_z[w][hh] = zs[hh];
                 __syncthreads();
 #pragma unroll
                 for (int hh = 0; hh < kRefHeads; ++hh) {
-                    float z = 0.f;
-#pragma unroll
-                    for (int v = 0; v < kRefWaves; ++v) z += s_z[v][hh];
-                    const float l2z = __log2f(z);
-                    const float up = __shfl_up(q[hh][3], 1), dn = __shfl_down(q[hh][0], 1);
-                    const float left = lane == 0 ? ql[hh] : up;
-                    const float right = lane == 63 ? qr[hh] : dn;
+                    const float l2z = s_l2z[min(hh, nh - 1)];
+                    const float left = lane_prev(q[hh][3], ql[hh]);
+                    const float right = lane_next(q[hh][0], qr[hh]);
                     const float ls[6] = {left - l2z,      q[hh][0] - l2z, q[hh][1] - l2z,
                                          q[hh][2] - l2z, q[hh][3] - l2z, right - l2z};
 #pragma unroll
@@ -476,7 +498,7 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
                                                  : -INFINITY;
                     }
                 }
-                if (a.Hkv > kRefHeads) __syncthreads();    // s_z is reused by the next group
+                if (a.Hkv > kRefHeads) __syncthreads();    // s_l2z is reused by the next group
             }
             if (pass == 0) {
 #pragma unroll

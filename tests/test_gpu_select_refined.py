@@ -24,23 +24,26 @@ CHUNKED_MAX_LEN = 300000
 PASSES_MAX_LEN = 600000           # k_sel + max_len / 64 > 8192: no finish pass
 
 
-def _gpu_refined(wl, lens, z, kn, params, n_sink, n_recent, k_sel, max_len=None):
+def _gpu_refined(wl, lens, z, kn, params, n_sink, n_recent, k_sel, max_len=None, norm_pad=0):
+    """norm_pad: extra floats per key-norm row (an odd number leaves the rows unaligned, so
+    the norms are read one by one instead of in 16-byte loads)."""
     max_len = max_len or max(lens)
     stride = round4(max(max_len, z.shape[-1]))
+    nstride = stride + norm_pad
     lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
     desc = B.KVDesc.for_logits(lens_dev, max_len, wl.Hq, wl.Hkv, wl.d)
     zd = torch.zeros((len(lens), wl.Hq, stride), device=DEV)
     zd[:, :, :z.shape[-1]] = z.to(DEV)
     knd = None
     if kn is not None:
-        knd = torch.ones((len(lens), wl.Hkv, stride), device=DEV)
+        knd = torch.ones((len(lens), wl.Hkv, nstride), device=DEV)
         knd[:, :, :kn.shape[-1]] = kn.to(DEV)
     idx_stride = n_sink + k_sel
     idx = torch.full((len(lens), wl.Hkv, idx_stride), -7, dtype=torch.int32, device=DEV)
     n_idx = torch.full((len(lens), wl.Hkv), -7, dtype=torch.int32, device=DEV)
     ws = torch.zeros(B.sfi_workspace_bytes(desc, B.SFI_OP_SELECT_REFINED), dtype=torch.uint8,
                      device=DEV)
-    B.sfi_select_refined(desc, zd, stride, knd, stride, n_sink, n_recent, k_sel, params, idx,
+    B.sfi_select_refined(desc, zd, stride, knd, nstride, n_sink, n_recent, k_sel, params, idx,
                          idx_stride, n_idx, ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy(), n_idx.cpu().numpy()
@@ -150,6 +153,24 @@ def test_refined_planted(orc, name, lens, norms):
         f"(ambiguous {n_amb})")
     assert changed > 0
     assert n_diff <= n_amb
+
+
+def test_refined_unaligned_norm_rows():
+    """Key-norm rows whose stride is not a multiple of 4 (read one by one) select exactly what
+    aligned rows (read 16 bytes at a time) select."""
+    wl = W["ragged_paged_b16"]
+    lens = [2500, 4097, 8200]
+    say(f"[refined unaligned norms] {wl.name} lens={lens}")
+    z, _ = synth.planted_logits(len(lens), wl.Hq, wl.Hkv, lens, wl.n_sink, wl.n_recent,
+                                round4(max(lens)), seed=10, noise_sink=40.0)
+    g = torch.Generator().manual_seed(11)
+    kn = torch.rand((len(lens), wl.Hkv, z.shape[-1]), generator=g) * 1.5 + 0.5
+    params = dict(B.REFINE_DEFAULTS)
+    ia, na = _gpu_refined(wl, lens, z, kn, params, wl.n_sink, wl.n_recent, wl.k_sel)
+    for pad in (1, 3):
+        ib, nb = _gpu_refined(wl, lens, z, kn, params, wl.n_sink, wl.n_recent, wl.k_sel,
+                              norm_pad=pad)
+        assert np.array_equal(ia, ib) and np.array_equal(na, nb), f"norm_pad={pad}"
 
 
 def test_refined_on_dense_logits(orc):
