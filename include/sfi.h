@@ -434,7 +434,8 @@ size_t sfi_workspace_bytes(const sfi_kv_desc* kv, int32_t op, int32_t idx_stride
  * sfi_sparse_decode reads for these arguments (index entries below the recent window, a
  * stand-in row for each skipped entry, then the recent window, through the block table when
  * paged), read once each with 16-byte loads by about n_workgroups workgroups in one launch,
- * with no arithmetic.  Timed with events it is the floor of the fast step's access pattern in
+ * with no arithmetic, in the fast step's order (row numbers built in LDS once per workgroup,
+ * then every load of a 32-slot tile issued together).  Timed with events it is the floor of the fast step's access pattern in
  * one launch (the fast step itself also computes, and merges its splits in a second launch).
  * kv, idx, idx_stride, n_idx, n_recent as for sfi_sparse_decode; sink as for sfi_stream_read.
  * SFI_E_INVALID for a null pointer, a bad size or count; asynchronous on stream. */

@@ -36,71 +36,96 @@ stream_read_kernel(const u32x4* __restrict__ p, uint64_t n16, uint64_t per_wg,
 }
 
 // Gather yardstick: the key and value rows of a fast step's slots, read with no arithmetic in
-// one launch.  Workgroup (split, h, b) takes slots [split * split_len, ...) of unit (b, h):
-// slot s < n_idx reads the row of idx[s] when 0 <= idx[s] < r0, else of position len - 1 (as
-// the fast step reads a stand-in row for a skipped entry), and the rest walk the recent
-// window [r0, len).  Each wavefront takes 32-slot tiles; lane l loads 16 bytes of row
-// l / (row_bytes / 16) of every group of rows, so each load instruction covers whole rows.  A
-// tile's index entries (and block-table entries) are loaded together, then all of its key and
-// value loads are issued before any is used.
-constexpr int kGatherRowsMax = 32 / 2;               // rows per lane per tile (rows of 512 B)
+// one launch, in the fast step's own order.  Workgroup (split, h, b) takes slots
+// [split * split_len, ...) of unit (b, h): slot s < n_idx reads the row of idx[s] when
+// 0 <= idx[s] < r0, else of position len - 1 (as the fast step reads a stand-in row for a
+// skipped entry), and the rest walk the recent window [r0, len).  As in the fast step, the
+// workgroup first builds the row numbers of its slots in LDS (every index load of a segment
+// issued together, then every block-table load), kGatherTab slots per segment; then each
+// wavefront takes the segment's 32-slot tiles w, w + 4, ...; lane l loads 16 bytes of row
+// l / (row_bytes / 16) of every group of rows, so each load instruction covers whole rows, and
+// every key and value load of a tile is issued before any is used.
+constexpr int kGatherTab = 4096;                     // row-table slots per segment (16 KB)
+constexpr int kGatherFill = kGatherTab / kStreamThreads;
+template <int ROWB>                                  // row bytes: 128, 256 or 512
 __global__ void __launch_bounds__(kStreamThreads)
 gather_read_kernel(GatherArgs a) {
+    constexpr int kLpr = ROWB / 16;                  // lanes per row
+    constexpr int kRpi = 64 / kLpr;                  // rows per load instruction
+    constexpr int kPer = 32 / kRpi;                  // rows of a tile per lane
+    __shared__ uint32_t tab[kGatherTab];
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int unit = b * a.Hkv + h;
+    const int s0 = split * a.split_len;
+    const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
+    // the first segment's index entries depend only on the slot: loaded beside the lengths
+    int pos[kGatherFill];
+#pragma unroll
+    for (int u = 0; u < kGatherFill; ++u) {
+        const int t = u * kStreamThreads + tid, slot = s0 + t;
+        pos[u] = (t < a.split_len && slot < a.idx_stride) ? irow[slot] : 0;
+    }
     const int len_b = a.len[b];
     const int n_sel = min(max(a.n_idx[unit], 0), a.idx_stride);
     const int r0 = max(0, len_b - a.n_recent);
     const int n_tot = len_b > 0 ? n_sel + (len_b - r0) : 0;
-    const int s0 = split * a.split_len;
     const int s1 = min(n_tot, s0 + a.split_len);
-    const int lpr = a.row_bytes / 16;                  // lanes per row
-    const int rpi = 64 / lpr;                          // rows per load instruction
-    const int per = 32 / rpi;                          // rows of a tile per lane (<= 16)
-    const int32_t* irow = a.idx + (int64_t)unit * a.idx_stride;
     const unsigned char* kb = (const unsigned char*)a.k;
     const unsigned char* vb = (const unsigned char*)a.v;
     const int bmask = (1 << a.block_shift) - 1;
     uint32_t acc = 0;
-    for (int t0 = s0 + 32 * w; t0 < s1; t0 += 32 * 4) {
-        int pos[kGatherRowsMax];
+    for (int g0 = s0; g0 < s1; g0 += kGatherTab) {
+        const int n = min(kGatherTab, s1 - g0);
+        if (g0 != s0) {
 #pragma unroll
-        for (int k = 0; k < kGatherRowsMax; ++k) {     // index entries of the tile, together
-            const int slot = min(t0 + lane / lpr + k * rpi, s1 - 1);
-            pos[k] = (k < per && slot < n_sel) ? irow[slot] : 0;
+            for (int u = 0; u < kGatherFill; ++u) {
+                const int slot = g0 + u * kStreamThreads + tid;
+                pos[u] = (u * kStreamThreads + tid < n && slot < n_sel) ? irow[slot] : 0;
+            }
         }
 #pragma unroll
-        for (int k = 0; k < kGatherRowsMax; ++k) {
-            const int slot = min(t0 + lane / lpr + k * rpi, s1 - 1);
+        for (int u = 0; u < kGatherFill; ++u) {
+            const int slot = g0 + u * kStreamThreads + tid;
             if (slot < n_sel) {
-                if (pos[k] < 0 || pos[k] >= r0) pos[k] = len_b - 1;
+                if (pos[u] < 0 || pos[u] >= r0) pos[u] = len_b - 1;
             } else {
-                pos[k] = r0 + (slot - n_sel);
+                pos[u] = r0 + (slot - n_sel);
             }
         }
-        uint64_t row[kGatherRowsMax];
+        uint32_t row[kGatherFill];
 #pragma unroll
-        for (int k = 0; k < kGatherRowsMax; ++k) {     // block-table entries, together
+        for (int u = 0; u < kGatherFill; ++u) {
             if (a.block_table) {
-                const uint32_t blk = k < per
-                    ? (uint32_t)a.block_table[(int64_t)b * a.max_blocks + (pos[k] >> a.block_shift)]
+                const uint32_t blk = u * kStreamThreads + tid < n
+                    ? (uint32_t)a.block_table[(int64_t)b * a.max_blocks + (pos[u] >> a.block_shift)]
                     : 0u;
-                row[k] = (((uint64_t)blk * a.Hkv + h) << a.block_shift) + (uint64_t)(pos[k] & bmask);
+                row[u] = (((uint32_t)blk * (uint32_t)a.Hkv + (uint32_t)h) << a.block_shift) |
+                         (uint32_t)(pos[u] & bmask);
             } else {
-                row[k] = (uint64_t)unit * (uint64_t)a.n_cap + (uint64_t)pos[k];
+                row[u] = (uint32_t)((int64_t)unit * a.n_cap + pos[u]);
             }
         }
-        u32x4 kv[kGatherRowsMax], vv[kGatherRowsMax];
 #pragma unroll
-        for (int k = 0; k < kGatherRowsMax; ++k) {     // every key and value load of the tile
-            const uint64_t off = row[k] * (uint64_t)a.row_bytes + (uint64_t)(lane % lpr) * 16;
-            kv[k] = k < per ? *(const u32x4*)(kb + off) : u32x4{0u, 0u, 0u, 0u};
-            vv[k] = k < per ? *(const u32x4*)(vb + off) : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < kGatherFill; ++u)
+            if (u * kStreamThreads + tid < n) tab[u * kStreamThreads + tid] = row[u];
+        __syncthreads();
+        const int ntiles = (n + 31) / 32;
+        for (int t = w; t < ntiles; t += kStreamThreads / 64) {
+            u32x4 kv[kPer], vv[kPer];
+#pragma unroll
+            for (int k = 0; k < kPer; ++k) {             // every key and value load of the tile
+                const int slot = min(t * 32 + lane / kLpr + k * kRpi, n - 1);
+                const uint64_t off = (uint64_t)tab[slot] * ROWB + (uint64_t)(lane % kLpr) * 16;
+                kv[k] = *(const u32x4*)(kb + off);
+                vv[k] = *(const u32x4*)(vb + off);
+            }
+            __builtin_amdgcn_sched_barrier(0);        // all of them issued before any is used
+#pragma unroll
+            for (int k = 0; k < kPer; ++k)
+                acc ^= kv[k].x ^ kv[k].y ^ kv[k].z ^ kv[k].w ^ vv[k].x ^ vv[k].y ^ vv[k].z ^ vv[k].w;
         }
-#pragma unroll
-        for (int k = 0; k < kGatherRowsMax; ++k)
-            acc ^= kv[k].x ^ kv[k].y ^ kv[k].z ^ kv[k].w ^ vv[k].x ^ vv[k].y ^ vv[k].z ^ vv[k].w;
+        __syncthreads();                              // the table is read before it is replaced
     }
     if (acc == 0x9e3779b9u) a.sink[(blockIdx.x + blockIdx.y) & (kStreamSinkWords - 1)] = acc;
 }
@@ -108,7 +133,11 @@ gather_read_kernel(GatherArgs a) {
 }  // namespace
 
 hipError_t launch_gather_read(const GatherArgs& a, int nsplit, int B, hipStream_t s) {
-    hipLaunchKernelGGL(gather_read_kernel, dim3(nsplit, a.Hkv, B), dim3(kStreamThreads), 0, s, a);
+    const dim3 grid(nsplit, a.Hkv, B);
+    if (a.row_bytes == 128) hipLaunchKernelGGL(gather_read_kernel<128>, grid, dim3(kStreamThreads), 0, s, a);
+    else if (a.row_bytes == 256) hipLaunchKernelGGL(gather_read_kernel<256>, grid, dim3(kStreamThreads), 0, s, a);
+    else if (a.row_bytes == 512) hipLaunchKernelGGL(gather_read_kernel<512>, grid, dim3(kStreamThreads), 0, s, a);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
