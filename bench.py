@@ -103,12 +103,12 @@ def select_bytes(wl, lens):
     read once (its normaliser over J comes from the dense step), one 4-byte key written per
     (KV head, position of J) and read back by the candidate pass, and again by the emit when
     the chunked path ends in its resolve and emit passes rather than in the one-workgroup-per-
-    unit finish (the library takes the finish when k_sel + max_len / 64 <= 8192), and the index
+    unit finish (the library takes the finish when k_sel + max_len / 64 <= 16384), and the index
     rows written.  (Counting a second logit read and four passes over the keys gives an upper
     bound, for a Selector that computes its own normaliser.)  The candidates and kept
     entries, about 2 % of J, and the 16 KB histograms are not counted."""
     nJ = sum(max(0, n - wl.n_recent - wl.n_sink) for n in lens)
-    key_passes = 2 if wl.k_sel + max(lens) // 64 <= 8192 else 3
+    key_passes = 2 if wl.k_sel + max(lens) // 64 <= 16384 else 3
     return wl.Hq * nJ * 4 + key_passes * wl.Hkv * nJ * 4 + sum(wl.Hkv * (wl.n_sink + wl.k_sel) * 4
                                                                 for _ in lens)
 

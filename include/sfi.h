@@ -176,7 +176,7 @@ sfi_status sfi_select(const sfi_kv_desc* kv, const float* logits, int64_t logit_
  * recorded on `stream` right before the dense step's first kernel (after every host-side
  * check) and after its kernels, before the Selector's (for callers that time the dense step,
  * or start other work after it as the layer-wise schedule of SFI Sec. 4.1 does).  Launches:
- * the dense step's two, the Selector's three (four when k_sel + max_len / 64 > 8192; one on
+ * the dense step's two, the Selector's three (four when k_sel + max_len / 64 > 16384; one on
  * short contexts), the mask's one. */
 sfi_status sfi_slow_step(const sfi_kv_desc* kv, const void* q, float* out, float* lse,
                          float* logits, int64_t logit_stride,

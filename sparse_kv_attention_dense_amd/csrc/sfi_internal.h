@@ -86,7 +86,7 @@ constexpr int kRadixBins = 2048;     // LDS histogram bins of the one-launch pat
 // k_sel + max_len / kFinishBinShare <= kFinishCap: the kept keys and a generous bound on the
 // candidates (the digit-0 bin of the k-th largest key held 0.4-0.6 % of J on the benchmark's
 // logits) fit in LDS; otherwise in the resolve and emit passes.
-constexpr int kFinishCap = 8192;
+constexpr int kFinishCap = 16384;
 constexpr int64_t kFinishBinShare = 64;
 constexpr int kSelHistBins = 4096;   // digit-0 bins of the chunked path
 

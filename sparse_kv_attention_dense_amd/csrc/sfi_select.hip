@@ -16,7 +16,7 @@
 //                          higher bins; when finish_kernel follows, every key of that bin or
 //                          above, with its position
 //   4'. finish_kernel     (instead of 4 and 5 when a unit's kept keys and candidates fit in
-//                          its LDS: k_sel + max_len / 64 <= 8192) one workgroup per unit:
+//                          its LDS: k_sel + max_len / 64 <= 16384) one workgroup per unit:
 //                          the entries of every chunk copied to LDS in position order, digits
 //                          1 and 2 of T over the entries of the digit-0 bin, then the ordered
 //                          emit over the entries
@@ -975,8 +975,8 @@ __global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
 // candidate pass has written, per chunk and in position order, every key whose digit 0 is at or
 // above the bin d0 of the k-th largest key, with its position.
 //   1. The chunks' entry numbers are scanned: chunk c's entries go to [off[c], off[c + 1]).
-//   2. Each wavefront copies whole chunks to LDS (chunks w, w + 16, ..., two at a time with
-//      every load of both issued first), so no entry needs a search for its chunk; the keys of
+//   2. Each wavefront copies whole chunks to LDS (chunks w, w + 16, ..., four at a time with
+//      every load of the four issued first), so no entry needs a search for its chunk; the keys of
 //      bin d0 fill the digit-1 histogram on the way.  Entries past kFinCap stay where they lie
 //      (their chunk is then found by a binary search over off).
 //   3. Digit 1 of T from that histogram; digit 2 over the entries of T's digit-1 bin.
@@ -986,6 +986,7 @@ __global__ void __launch_bounds__(kUT) resolve_kernel(SelArgs a) {
 constexpr int kFinCap = kFinishCap;                    // entries held in LDS
 constexpr int kFinChunks = kUT;                        // chunks per unit (contexts up to 4M)
 constexpr int kFinCopy = 4;                            // entries per lane per chunk in flight
+constexpr int kFinGroup = 4;                           // chunks per wavefront copied together
 constexpr int kFinEmit = 8;                            // consecutive entries per thread in the emit
 constexpr int kFinD1 = 1 << (kCShift[0] - kCShift[1]); // digit-1 bins
 constexpr int kFinD2 = 1 << kCShift[1];                // digit-2 bins
@@ -1001,8 +1002,7 @@ struct FinishShared {
     uint32_t h1[kFinD1];
     uint32_t h2[kFinD2];
     __attribute__((aligned(16))) uint32_t key[kFinCap];
-    __attribute__((aligned(16))) int32_t pos[kFinCap];
-    int32_t out[kFinCap];                              // the kept positions, staged for the row
+    __attribute__((aligned(16))) int32_t pos[kFinCap]; // also the kept positions, staged in place
 };
 
 // Over bins held kPer per thread of the 1024-thread workgroup in ascending order, finds the bin
@@ -1064,43 +1064,50 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
     __syncthreads();
     const int nch = (nJ + kSelChunk - 1) / kSelChunk;  // chunks holding positions of J
     const int64_t base = (int64_t)unit * a.nchunk * kSelChunk;
-    // 2. copy, two chunks per wavefront at a time; loads clamped into the chunk's region
+    // 2. copy, kFinGroup chunks per wavefront at a time (chunks w, w + kUW, ...), every load of
+    // the group issued before any store; loads clamped into their chunk's region, and none for
+    // a chunk past the last or a row of 64 past a chunk's entries (tests that are the same for
+    // the whole wavefront)
     const uint32_t d0 = T >> kCShift[0];
-    for (int ca = w; ca < nch; ca += 2 * kUW) {
-        const int cb = ca + kUW;
-        const uint32_t oa = fs.off[ca], na = fs.off[ca + 1] - oa;
-        const uint32_t ob = cb < nch ? fs.off[cb] : 0u, nb = cb < nch ? fs.off[cb + 1] - ob : 0u;
-        const int64_t ra = base + (int64_t)ca * kSelChunk;
-        const int64_t rb = base + (int64_t)min(cb, nch - 1) * kSelChunk;
-        for (uint32_t j0 = 0; j0 < max(na, nb); j0 += 64 * kFinCopy) {
-            uint32_t ka[kFinCopy], kb[kFinCopy];
-            int32_t pa[kFinCopy], pb[kFinCopy];
+    for (int c0 = w; c0 < nch; c0 += kFinGroup * kUW) {
+        uint32_t o[kFinGroup], nc[kFinGroup], nmax = 0;
 #pragma unroll
-            for (int u = 0; u < kFinCopy; ++u) {
-                const uint32_t j = min(j0 + lane + 64 * u, (uint32_t)kSelChunk - 1);
-                ka[u] = a.cand[ra + j];
-                pa[u] = a.epos[ra + j];
-                kb[u] = a.cand[rb + j];
-                pb[u] = a.epos[rb + j];
+        for (int q = 0; q < kFinGroup; ++q) {
+            const int c = c0 + q * kUW;
+            o[q] = c < nch ? fs.off[c] : 0u;
+            nc[q] = c < nch ? fs.off[c + 1] - o[q] : 0u;
+            nmax = max(nmax, nc[q]);
+        }
+        for (uint32_t j0 = 0; j0 < nmax; j0 += 64 * kFinCopy) {
+            uint32_t kk[kFinGroup][kFinCopy];
+            int32_t pp[kFinGroup][kFinCopy];
+#pragma unroll
+            for (int q = 0; q < kFinGroup; ++q) {
+                const int64_t r = base + (int64_t)(c0 + q * kUW) * kSelChunk;
+#pragma unroll
+                for (int u = 0; u < kFinCopy; ++u) {
+                    // rows of 64 entries that start past the chunk's entries are not loaded (one
+                    // CU pulls its unit's entries at a few tens of GB/s, so bytes matter here)
+                    if (j0 + 64 * u < nc[q]) {
+                        const uint32_t j = min(j0 + lane + 64 * u, (uint32_t)kSelChunk - 1);
+                        kk[q][u] = a.cand[r + j];
+                        pp[q][u] = a.epos[r + j];
+                    }
+                }
             }
 #pragma unroll
-            for (int u = 0; u < kFinCopy; ++u) {
-                const uint32_t j = j0 + lane + 64 * u;
-                if (j < na) {
-                    if (oa + j < (uint32_t)kFinCap) {
-                        fs.key[oa + j] = ka[u];
-                        fs.pos[oa + j] = pa[u];
+            for (int q = 0; q < kFinGroup; ++q) {
+#pragma unroll
+                for (int u = 0; u < kFinCopy; ++u) {
+                    const uint32_t j = j0 + lane + 64 * u;
+                    if (j < nc[q]) {
+                        if (o[q] + j < (uint32_t)kFinCap) {
+                            fs.key[o[q] + j] = kk[q][u];
+                            fs.pos[o[q] + j] = pp[q][u];
+                        }
+                        if ((kk[q][u] >> kCShift[0]) == d0)
+                            atomicAdd(&fs.h1[(kk[q][u] >> kCShift[1]) & kCMask[1]], 1u);
                     }
-                    if ((ka[u] >> kCShift[0]) == d0)
-                        atomicAdd(&fs.h1[(ka[u] >> kCShift[1]) & kCMask[1]], 1u);
-                }
-                if (j < nb) {
-                    if (ob + j < (uint32_t)kFinCap) {
-                        fs.key[ob + j] = kb[u];
-                        fs.pos[ob + j] = pb[u];
-                    }
-                    if ((kb[u] >> kCShift[0]) == d0)
-                        atomicAdd(&fs.h1[(kb[u] >> kCShift[1]) & kCMask[1]], 1u);
                 }
             }
         }
@@ -1160,7 +1167,10 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
         T |= fs.sel[0];
         k_rem -= (int32_t)fs.sel[1];
     }
-    // 4. ordered emit into LDS; a row never takes more than min(k_sel, nJ) positions
+    // 4. ordered emit into LDS; a row never takes more than min(k_sel, nJ) positions.  The kept
+    // positions are staged in pos itself: kept entry number `out` is at most the entry's own
+    // index, every read of a round's entries comes before the round's scan barrier and every
+    // write after it, and later rounds read only entries past this round's.
     const uint32_t kr = (uint32_t)max(k_rem, 0);
     const uint32_t n_out = (uint32_t)min(min(a.k_sel, nJ), kFinCap);
     uint32_t gt_seen = 0, eq_seen = 0;
@@ -1189,7 +1199,7 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
                 ++e_before;
             }
             if (keep) {
-                if (out < n_out) fs.out[out] = pp[e];
+                if (out < n_out) fs.pos[out] = pp[e];
                 ++out;
             }
         }
@@ -1199,7 +1209,7 @@ __global__ void __launch_bounds__(kUT) finish_kernel(SelArgs a) {
     // the staged row, coalesced (n_out <= k_sel <= kFinCap under the finish rule)
     __syncthreads();
     const uint32_t n_kept = min(n_out, gt_seen + min(eq_seen, kr));
-    for (uint32_t i = tid; i < n_kept; i += kUT) row[ns + i] = fs.out[i];
+    for (uint32_t i = tid; i < n_kept; i += kUT) row[ns + i] = fs.pos[i];
 }
 
 __global__ void __launch_bounds__(kUT) select_unit_kernel(SelArgs a) {

@@ -16,8 +16,8 @@ pytestmark = pytest.mark.gpu
 # paths run the same cases.
 CHUNKED_MAX_LEN = 300000
 # a declared bound this long makes the chunked Selector end in its resolve and emit passes
-# instead of the one-workgroup-per-unit finish (k_sel + max_len / 64 > 8192 entries)
-PASSES_MAX_LEN = 600000
+# instead of the one-workgroup-per-unit finish (k_sel + max_len / 64 > 16384 entries)
+PASSES_MAX_LEN = 1100000
 MAX_LEN_OF = {"unit": None, "chunked": CHUNKED_MAX_LEN, "chunked_passes": PASSES_MAX_LEN}
 
 
@@ -133,7 +133,7 @@ def test_select_chunked_random_shapes(orc, case):
     say(f"[select random shape {case}] B={Bn} Hkv={Hkv} G={G} lens={lens} sink={n_sink} "
         f"recent={n_recent} k={k_sel}")
     z, ranks = _planted(wl, lens, seed=77 + case, n_sink=n_sink, n_recent=n_recent)
-    # 40000 positions with k <= 6000: the finish; 600000: the resolve and emit passes
+    # 40000 positions with k <= 6000: the finish; 1100000: the resolve and emit passes
     istride = max(1, n_sink + k_sel)
     a = _run(orc, wl, lens, z, exact=True, n_sink=n_sink, n_recent=n_recent, k_sel=k_sel,
              idx_stride=istride, max_len=40000)
@@ -148,14 +148,14 @@ def test_select_chunked_random_shapes(orc, case):
 
 
 def test_select_finish_beyond_its_lds(orc):
-    """The finish holds 8192 entries (kept keys and candidates of a unit) in LDS and reads the
-    rest where the candidate pass wrote them: all keys equal (every key of J is an entry) and
-    quantised logits with mass ties, on units of 20000 and 9000 positions, against the oracle
-    exactly, and bit for bit against the resolve and emit passes."""
+    """The finish holds 16384 entries (kept keys and candidates of a unit) in LDS and reads the
+    rest where the candidate pass wrote them: all keys equal (every key of J is an entry: 20000
+    entries in the longer unit, 8932 in the shorter) and quantised logits with mass ties, against
+    the oracle exactly, and bit for bit against the resolve and emit passes."""
     wl = synth.Workload("sel_fin", 1, 2, 8, 2, 128, "bf16", 20068, 4, 64, 100, 1)
     g = torch.Generator().manual_seed(11)
     lens = [20068, 9000]
-    # a bound of 40000 positions keeps the chunked path with the finish for k_sel <= 7567
+    # a bound of 40000 positions keeps the chunked path with the finish for k_sel <= 15759
     for z in (torch.zeros((2, 8, 20068)),
               torch.randint(-1, 2, (2, 8, 20068), generator=g).float()):
         for k_sel in (100, 5000):

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
 DELTA = 5e-5
 CHUNKED_MAX_LEN = 300000
-PASSES_MAX_LEN = 600000           # k_sel + max_len / 64 > 8192: no finish pass
+PASSES_MAX_LEN = 1100000          # k_sel + max_len / 64 > 16384: no finish pass
 
 
 def _gpu_refined(wl, lens, z, kn, params, n_sink, n_recent, k_sel, max_len=None, norm_pad=0):
