@@ -395,13 +395,17 @@ __global__ void __launch_bounds__(kThreads, 4) evidence_kernel(SelArgs a) {
     __syncthreads();
     uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
     // bins 2t and 2t + 1 as one 64-bit add (the low and high halves of a little-endian word;
-    // no count reaches 2^32, so no carry crosses between them)
-    for (int t = tid; t < kCBins0 / 2; t += kThreads) {
-        const uint2 n = *(const uint2*)&lh[2 * t];
-        if (n.x | n.y)
-            atomicAdd((unsigned long long*)hg + t,
-                      (unsigned long long)n.x | ((unsigned long long)n.y << 32));
-    }
+    // no count reaches 2^32, so no carry crosses between them); every pair of this thread is
+    // read before any is tested
+    constexpr int kPairs = kCBins0 / 2 / kThreads;
+    uint2 n[kPairs];
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) n[u] = *(const uint2*)&lh[2 * (u * kThreads + tid)];
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u)
+        if (n[u].x | n[u].y)
+            atomicAdd((unsigned long long*)hg + u * kThreads + tid,
+                      (unsigned long long)n[u].x | ((unsigned long long)n[u].y << 32));
 }
 
 // Fused score, Soft-NMS and cross-head exclusivity for one quarter of a chunk of J of one
@@ -423,10 +427,12 @@ constexpr int kRefThreads = kRefSpan / 4;              // four positions per thr
 constexpr int kRefWaves = kRefThreads / 64;
 constexpr int kRefHeads = 8;                           // heads held in registers at a time
 constexpr int kRefWords = kCBins0 / 2;                 // packed histogram words per head
+constexpr int kRefFlush = 8;                           // histogram words per lane per flush batch
 static_assert(kRefThreads % 64 == 0 && kRefThreads <= 1024, "whole waves, one workgroup");
 static_assert(kRefSpan < 65536, "a 16-bit count holds every key of a workgroup");
 static_assert(kSelChunk % 4 == 0, "16-byte loads of the score buffer");
 static_assert((kRefHeads * kRefWords) % (4 * kRefThreads) == 0, "16-byte clears of the histograms");
+static_assert((kRefHeads * kRefWords) % (kRefFlush * kRefThreads) == 0, "whole flush batches");
 __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
     __shared__ float s_l2z[kRefHeads];                 // log2 of each head's fusion normaliser
     __shared__ uint32_t lh[kRefHeads][kRefWords];
@@ -547,14 +553,22 @@ __global__ void __launch_bounds__(kRefThreads) refine_kernel(SelArgs a) {
             // 2i + 1 are the low and high halves of a little-endian 64-bit word; a count stays far
             // below 2^32, so no carry crosses between them).  One word per lane keeps each wave's
             // adds on the fewest cache lines.
-            for (int t = tid; t < kRefHeads * kRefWords; t += kRefThreads) {
-                const int hh = t / kRefWords;
-                const uint32_t n = (&lh[0][0])[t];
-                if (hh < nh && n) {
-                    unsigned long long* hg = (unsigned long long*)(a.hist +
-                        (int64_t)(b * a.Hkv + h0 + hh) * kCBins0) + t % kRefWords;
-                    atomicAdd(hg, (unsigned long long)(n & 0xffffu) |
-                                  ((unsigned long long)(n >> 16) << 32));
+            // kRefFlush words per lane are read before any is tested, so the LDS latency is
+            // paid once per batch, not once per word
+            for (int t0 = 0; t0 < kRefHeads * kRefWords; t0 += kRefFlush * kRefThreads) {
+                uint32_t n[kRefFlush];
+#pragma unroll
+                for (int u = 0; u < kRefFlush; ++u) n[u] = (&lh[0][0])[t0 + u * kRefThreads + tid];
+#pragma unroll
+                for (int u = 0; u < kRefFlush; ++u) {
+                    const int t = t0 + u * kRefThreads + tid;
+                    const int hh = t / kRefWords;
+                    if (hh < nh && n[u]) {
+                        unsigned long long* hg = (unsigned long long*)(a.hist +
+                            (int64_t)(b * a.Hkv + h0 + hh) * kCBins0) + t % kRefWords;
+                        atomicAdd(hg, (unsigned long long)(n[u] & 0xffffu) |
+                                      ((unsigned long long)(n[u] >> 16) << 32));
+                    }
                 }
             }
             __syncthreads();
