@@ -645,19 +645,22 @@ __global__ void __launch_bounds__(kThreads) candidate_kernel(SelArgs a) {
     constexpr int kPer = kCBins0 / kThreads;          // histogram bins per thread, ascending
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     const int unit = b * a.Hkv + h;
-    uint32_t kv[kPerThread];
-    load_chunk_keys(a, unit, c, kv);
+    // the histogram first: loads complete in order, so the pick below (which runs whether or
+    // not the unit is active, so that these loads stay at entry) waits for the histogram only
+    // and runs while the chunk's keys are still arriving
     const uint32_t* hg = a.hist + (int64_t)unit * kCBins0;
     uint32_t bins[kPer];
 #pragma unroll
     for (int k = 0; k < kPer; ++k) bins[k] = hg[kPer * tid + k];
+    uint32_t kv[kPerThread];
+    load_chunk_keys(a, unit, c, kv);
     const int32_t nJ = j_range(a, b).nJ;
     const int32_t take_all = a.k_sel >= nJ ? 1 : 0;
     int32_t k_rem = take_all ? nJ : a.k_sel;
     uint32_t prefix = (!take_all && k_rem == 0) ? 0xffffffffu : 0u;   // keep nothing
     const bool active = sel_active(prefix, k_rem, take_all);
+    pick_bin<kPer>(bins, active ? (uint32_t)k_rem : 1u, wt, parity, s_sel);
     if (active) {
-        pick_bin<kPer>(bins, (uint32_t)k_rem, wt, parity, s_sel);
         prefix = s_sel[0] << kCShift[0];
         k_rem -= (int32_t)s_sel[1];
     }
