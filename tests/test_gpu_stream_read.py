@@ -93,3 +93,33 @@ def test_gather_read_reads_the_fast_steps_rows(paged):
         changed = bool((sink != 0).any())
         assert changed == hit, f"position {pos} of ({b},{h}): read {changed}, expected {hit}"
     say(f"    {len(cases)} planted rows: read exactly the fast step's rows")
+
+
+def test_gather_read_split_past_one_table():
+    """One workgroup per unit reading 5000 selected rows and the recent window: its slots
+    span two row tables of 4096, and a planted row in the second table, in the recent window,
+    and a row that is not selected are read, read, and not read."""
+    Bsz, Hkv, Hq, d, N, n_recent, n_sel = 1, 2, 8, 128, 12000, 64, 5000
+    g = torch.Generator().manual_seed(6)
+    sel = [sorted(torch.randperm(N - n_recent, generator=g)[:n_sel].tolist()) for _ in range(Hkv)]
+    idx = torch.tensor([sel], dtype=torch.int32).to(DEV)
+    n_idx = torch.full((Bsz, Hkv), n_sel, dtype=torch.int32, device=DEV)
+    lens = torch.full((Bsz,), N, dtype=torch.int32, device=DEV)
+    K = torch.zeros((Bsz, Hkv, N, d), dtype=torch.bfloat16, device=DEV)
+    desc = B.KVDesc(K, torch.zeros_like(K), lens, N, Hq)
+    words = K.view(torch.int32)
+    sink = torch.zeros(64, dtype=torch.int32, device=DEV)
+    for h in range(Hkv):
+        s_set = set(sel[h])
+        cases = [(sel[h][4500], True),                                       # second table
+                 (N - 3, True),                                              # recent window
+                 (next(p for p in range(N - n_recent) if p not in s_set), False)]
+        for pos, hit in cases:
+            K.zero_()
+            words[0, h, pos][5] = MAGIC
+            sink.zero_()
+            B.sfi_gather_read(desc, idx, n_sel, n_idx, n_recent, 1, sink)
+            torch.cuda.synchronize()
+            changed = bool((sink != 0).any())
+            assert changed == hit, f"position {pos} of head {h}: read {changed}, expected {hit}"
+    say("    rows past the first 4096-slot table read once each")
