@@ -34,13 +34,14 @@
 // cross-head exclusivity; the pages' formulas are lost and the library implements stated
 // readings of them): the evidence pass stores log2(f^(1-lam) r^lam) per position and sums
 // f^(1-lam) r^lam per chunk instead of building the histogram, then
-//   refine_kernel        per sequence and quarter chunk, for every KV head: s = f^(1-lam) r^lam / Z
+//   refine_kernel        per sequence and half chunk, for every KV head: s = f^(1-lam) r^lam / Z
 //                         per position (from the log2 scores the evidence pass stored, and its two
 //                         neighbours'), decayed by 1 - alpha_soft
 //                         when a neighbour in J is larger; then every KV head below the largest
 //                         at a position is decayed by 1 - alpha_cross; the results are the
 //                         keys, and the digit-0 histograms are built from them
-// before the candidate, resolve and emit passes, which are unchanged.
+// before the candidate pass and the finish (or the resolve and emit passes), which are
+// unchanged.
 // f is computed without the 1/G factor: a positive common scale does not change the order.
 //
 // Sink-bypass mask (SinkRouter Sec. 4.2): rank the query heads of each sequence by their
