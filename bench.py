@@ -25,6 +25,8 @@ rooflines also give the dense and fast rates as a fraction of it, next to the 8 
 fast_roofline.floor = what the fast step's bytes cost without its arithmetic: the same rows read
 once by one launch (sfi_gather_read), a launch with almost nothing to do, and a sequential read
 of as many bytes, cold in the Infinity Cache (the fastest any one-launch read of them can be).
+group_dot = the GQA group's dot products over a layer's key rows on the vector ALUs and on MFMA,
+beside a read of the same rows with the same access pattern (sfi_group_dot).
 """
 from __future__ import annotations
 
@@ -228,6 +230,50 @@ def read_yardstick(B, torch, gib: int = 4, grids=(1024, 2048, 4096), reps: int =
     return {"kernel": "sfi_stream_read (sequential 16-byte nontemporal loads)",
             "bytes": gib << 30, "workgroups": best, "gbps": round(per_grid[best], 1),
             "gbps_by_workgroups": {str(g): round(v, 1) for g, v in per_grid.items()}}
+
+
+def group_dot_units(B, torch, wl, layers, queries, wg: int = 1024, reps: int = 3):
+    """What the GQA group's dot products q_g . k_j cost on each arithmetic unit, next to the
+    read they ride on (sfi_group_dot over every key row of a layer, in order, the workload's G
+    heads of one query): no arithmetic, the vector ALUs, MFMA.  Each unit: two warm-up
+    launches, then `reps` passes over the rotated layers (one launch per layer, so a launch
+    does not find its rows in the Infinity Cache) timed with events; mean µs per launch.  Only
+    for bf16 rows of 128 elements and G in 1, 2, 4, 8 (None otherwise)."""
+    if wl.dtype != "bf16" or wl.d != 128 or wl.G not in (1, 2, 4, 8):
+        return None
+    stream = torch.cuda.current_stream()
+    rows = []
+    for lay in layers:
+        flat = lay.k.reshape(-1)
+        n = flat.numel() // 128 // 16 * 16
+        rows.append(flat[: n * 128].view(n, 128))
+    q = queries[0][0].reshape(-1, 128)[: wl.G].contiguous()
+    part = torch.empty(wg, device="cuda")
+    sink = torch.zeros(64, dtype=torch.int32, device="cuda")
+    us, sums = {}, {}
+    for unit in ("read", "valu", "mfma"):
+        for r in rows[:2]:
+            B.sfi_group_dot(r, q, unit, wg, part, sink)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for r in rows:
+                B.sfi_group_dot(r, q, unit, wg, part, sink)
+        e1.record(stream)
+        e1.synchronize()
+        us[unit] = e0.elapsed_time(e1) * 1e3 / (reps * len(rows))
+        if unit != "read":
+            sums[unit] = float(part.double().sum())
+    n_rows = rows[0].shape[0]
+    return {"kernel": "sfi_group_dot (16-row groups of 4 KB per wavefront, 2 in flight)",
+            "rows_per_launch": n_rows, "bytes_per_launch": n_rows * 256, "G": wl.G,
+            "workgroups": wg, "read_us": round(us["read"], 2), "valu_us": round(us["valu"], 2),
+            "mfma_us": round(us["mfma"], 2),
+            "valu_over_read": round(us["valu"] / us["read"], 3),
+            "mfma_over_read": round(us["mfma"] / us["read"], 3),
+            "read_gbps": round(n_rows * 256 / (us["read"] * 1e-6) / 1e9, 1),
+            "valu_mfma_sums_rel_diff": round(abs(sums["valu"] - sums["mfma"]) /
+                                             max(1e-30, abs(sums["mfma"])), 8)}
 
 
 def routed_fast_steps(B, torch, wl, descs, queries, logits, stride, idxs, nidxs, masks, ws,
@@ -934,6 +980,8 @@ def main():
 
     print("# streaming-read yardstick", file=sys.stderr, flush=True)
     yard = read_yardstick(B, torch)
+    print("# group dot products by arithmetic unit", file=sys.stderr, flush=True)
+    gdot = group_dot_units(B, torch, wl, layers, queries)
 
     lens0 = layers[0].len0_host
     n_idx_host = nidxs[0].cpu().tolist()
@@ -1002,6 +1050,8 @@ def main():
                           "bytes_saved_by_masked_groups": int(f_bytes_unmasked - f_bytes)},
     }
     result["read_yardstick"] = yard
+    if gdot is not None:
+        result["group_dot"] = gdot
     if graph_us is not None:
         result["graph_cycle"] = {"us_per_step": graph_us, "eager_us_per_step": round(value, 3),
                                  "what": "the same stack cycle captured once in a HIP graph "

@@ -30,6 +30,8 @@
  *                                                                        -> sfi_stream_read
  *   - a read of exactly the rows a fast step gathers, its floor (not a step of the method)
  *                                                                        -> sfi_gather_read
+ *   - the GQA group's dot products over a stream of key rows on the vector ALUs or on MFMA,
+ *     beside a read of the same rows (not a step of the method)          -> sfi_group_dot
  *
  * Conventions shared by every call
  *   - Every pointer marked "device" is HIP device memory owned by the caller.  The library
@@ -445,6 +447,31 @@ sfi_status sfi_gather_read(const sfi_kv_desc* kv, const int32_t* idx, int32_t id
 
 sfi_status sfi_stream_read(const void* buf, uint64_t bytes, int32_t n_workgroups, uint32_t* sink,
                            hipStream_t stream);
+
+/* Measurement yardstick, not a step of the method: the dot products q_g . k_j of a GQA group's
+ * G query heads with n_rows bf16 key rows of 128 elements (SinkRouter Sec. 4.3: every key row
+ * is read once for the whole group), the rows read in order by n_workgroups workgroups of 256
+ * threads, each wavefront taking 16 consecutive rows (4 KB) at a time with two such groups in
+ * flight, on one of three units:
+ *   unit 0  no arithmetic (the words folded into an XOR), a read of the same rows;
+ *   unit 1  the vector ALUs: 8 elements per lane, fp32 FMAs, the 16 lanes of a row summed with
+ *           DPP row shifts;
+ *   unit 2  MFMA (16x16x32 bf16) in the attention kernels' operand layout, heads >= G as zero
+ *           columns of Q^T.
+ * Timed with events beside each other they show what the group products cost on each unit
+ * next to the read they ride on.
+ *   rows  (device) bf16 [n_rows][128], 16-byte aligned, only read; n_rows >= 16, a multiple of 16
+ *   q     (device) bf16 [G][128], 16-byte aligned, only read
+ *   G     1, 2, 4 or 8
+ *   unit  0, 1 or 2
+ *   part  (device) float [n_workgroups], 4-byte aligned (may be null for unit 0): units 1 and 2
+ *         write workgroup w's sum of q_g . k_j over its rows and the G heads, so the sum of part
+ *         is sum_j sum_g q_g . k_j (fp32 accumulation); unit 0 leaves it untouched
+ *   sink  as for sfi_stream_read
+ * SFI_E_INVALID for a null pointer, a bad size, alignment, unit or count; SFI_E_UNSUPPORTED for
+ * another G; asynchronous on stream. */
+sfi_status sfi_group_dot(const void* rows, int64_t n_rows, const void* q, int32_t G, int32_t unit,
+                         int32_t n_workgroups, float* part, uint32_t* sink, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* sfi_status_string(sfi_status status);

@@ -25,7 +25,7 @@ EXPORTED = ("sfi_dense_decode", "sfi_select", "sfi_slow_step", "sfi_select_refin
             "sfi_sparse_decode", "sfi_sparse_decode_noalloc", "sfi_sparse_decode_step",
             "sfi_sparse_decode_routed", "sfi_reorg", "sfi_sparse_decode_compact",
             "sfi_slow_step_layers", "sfi_workspace_bytes", "sfi_stream_read", "sfi_gather_read",
-            "sfi_status_string")
+            "sfi_group_dot", "sfi_status_string")
 
 
 class SfiError(RuntimeError):
@@ -96,11 +96,13 @@ def lib():
         L.sfi_sparse_decode_compact.argtypes = [D, P, P, P, P, i32, P, i32, P, P, P, P,
                                                 ctypes.c_size_t, P]
         L.sfi_stream_read.argtypes = [P, ctypes.c_uint64, i32, P, P]
+        L.sfi_group_dot.argtypes = [P, i64, P, i32, i32, i32, P, P, P]
         L.sfi_status_string.argtypes = [ctypes.c_int]
         L.sfi_status_string.restype = ctypes.c_char_p
         for f in ("sfi_dense_decode", "sfi_select", "sfi_sink_bypass_mask", "sfi_sparse_decode",
                   "sfi_sparse_decode_routed", "sfi_slow_step_layers", "sfi_stream_read",
-                  "sfi_reorg", "sfi_sparse_decode_compact", "sfi_select_refined"):
+                  "sfi_reorg", "sfi_sparse_decode_compact", "sfi_select_refined",
+                  "sfi_group_dot"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -274,6 +276,24 @@ def sfi_stream_read(buf, n_workgroups: int, sink, stream=None):
     _buf(sink, "sink", _I32, 64)
     _check(lib().sfi_stream_read(_ptr(buf), buf.numel() * buf.element_size(), int(n_workgroups),
                                  _ptr(sink), _stream(stream)), "sfi_stream_read")
+
+
+GROUP_DOT_UNITS = {"read": 0, "valu": 1, "mfma": 2}
+
+
+def sfi_group_dot(rows, q, unit: str, n_workgroups: int, part, sink, stream=None):
+    """The GQA group's dot products with bf16 key rows of 128 elements (a measurement
+    yardstick): rows [n_rows][128] and q [G][128] bf16, unit "read", "valu" or "mfma"; part
+    float32 [n_workgroups] takes per-workgroup sums (not written by "read"); sink >= 64 int32."""
+    _buf(rows, "rows", torch.bfloat16)
+    _buf(q, "q", torch.bfloat16)
+    if rows.numel() % 128 or q.numel() % 128:
+        raise ValueError("sfi_group_dot: rows and q hold rows of 128 elements")
+    _buf(part, "part", _F32, int(n_workgroups))
+    _buf(sink, "sink", _I32, 64)
+    _check(lib().sfi_group_dot(_ptr(rows), rows.numel() // 128, _ptr(q), q.numel() // 128,
+                               GROUP_DOT_UNITS[unit], int(n_workgroups), _ptr(part), _ptr(sink),
+                               _stream(stream)), "sfi_group_dot")
 
 
 def sfi_gather_read(desc: KVDesc, idx, idx_stride: int, n_idx, n_recent: int,

@@ -795,6 +795,19 @@ SFI_EXPORT sfi_status sfi_stream_read(const void* buf, uint64_t bytes, int32_t n
                                                                                      : SFI_E_HIP;
 }
 
+SFI_EXPORT sfi_status sfi_group_dot(const void* rows, int64_t n_rows, const void* q, int32_t G,
+                                    int32_t unit, int32_t n_workgroups, float* part,
+                                    uint32_t* sink, hipStream_t stream) {
+    if (!rows || !q || !sink || n_rows < 16 || n_rows % 16 != 0 || !aligned(rows, 16) ||
+        !aligned(q, 16) || !aligned(sink, 4) || unit < 0 || unit > 2 || n_workgroups < 1 ||
+        n_workgroups > (1 << 20))
+        return SFI_E_INVALID;
+    if (unit != 0 && (!part || !aligned(part, 4))) return SFI_E_INVALID;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return SFI_E_UNSUPPORTED;
+    return launch_group_dot(rows, (uint64_t)n_rows, q, G, unit, n_workgroups, part, sink,
+                            stream) == hipSuccess ? SFI_OK : SFI_E_HIP;
+}
+
 SFI_EXPORT sfi_status sfi_gather_read(const sfi_kv_desc* kv, const int32_t* idx,
                                       int32_t idx_stride, const int32_t* n_idx, int32_t n_recent,
                                       int32_t n_workgroups, uint32_t* sink, hipStream_t stream) {

@@ -184,4 +184,10 @@ struct GatherArgs {
 };
 hipError_t launch_gather_read(const GatherArgs& a, int nsplit, int B, hipStream_t stream);
 
+// Group dot yardstick (sfi_stream.hip): the G query heads' dot products with n_rows bf16 rows of
+// 128 elements (n_rows a multiple of 16) on unit 0 (none: a read), 1 (vector ALUs) or 2 (MFMA);
+// units 1 and 2 write one partial sum per workgroup to part, unit 0 may write sink.
+hipError_t launch_group_dot(const void* rows, uint64_t n_rows, const void* q, int G, int unit,
+                            int n_wg, float* part, uint32_t* sink, hipStream_t stream);
+
 }  // namespace sfi

@@ -254,6 +254,30 @@ def test_slow_step_layers_validation(L):
     assert call(seg=(ptrs(n), ptrs(n, FAKE + 8), ptrs(n))) == B.SFI_E_INVALID   # alignment
 
 
+def test_group_dot_validation(L):
+    ok = dict(rows=FAKE, n=1 << 12, q=FAKE, G=4, unit=1, wg=64, part=FAKE, sink=FAKE)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return L.sfi_group_dot(a["rows"], a["n"], a["q"], a["G"], a["unit"], a["wg"], a["part"],
+                               a["sink"], None)
+    assert call(rows=None) == B.SFI_E_INVALID
+    assert call(q=None) == B.SFI_E_INVALID
+    assert call(sink=None) == B.SFI_E_INVALID
+    assert call(n=0) == B.SFI_E_INVALID
+    assert call(n=(1 << 12) + 8) == B.SFI_E_INVALID           # whole 16-row groups only
+    assert call(rows=FAKE + 8) == B.SFI_E_INVALID              # 16-byte loads
+    assert call(q=FAKE + 4) == B.SFI_E_INVALID
+    assert call(unit=3) == B.SFI_E_INVALID
+    assert call(unit=-1) == B.SFI_E_INVALID
+    assert call(wg=0) == B.SFI_E_INVALID
+    assert call(wg=(1 << 20) + 1) == B.SFI_E_INVALID
+    assert call(part=None) == B.SFI_E_INVALID                  # units 1 and 2 write it
+    assert call(unit=2, part=None) == B.SFI_E_INVALID
+    for G in (0, 3, 5, 16):
+        assert call(G=G) == B.SFI_E_UNSUPPORTED
+
+
 def test_stream_read_validation(L):
     assert L.sfi_stream_read(None, 1 << 20, 1024, FAKE, None) == B.SFI_E_INVALID
     assert L.sfi_stream_read(FAKE, 1 << 20, 1024, None, None) == B.SFI_E_INVALID

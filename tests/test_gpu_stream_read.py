@@ -1,4 +1,6 @@
-"""The streaming-read yardstick (sfi_stream_read) reads every 16-byte word of its buffer.
+"""The measurement yardsticks: the streaming read (sfi_stream_read) reads every 16-byte word of
+its buffer, the gather read (sfi_gather_read) the fast step's rows, and the group dot products
+(sfi_group_dot) sum q_g . k_j over every row and head on both arithmetic units.
 
 Its only visible effect is the sink word it writes when a thread's XOR of the words it read
 equals the fixed constant.  Over a zeroed buffer with the constant planted in one word, the
@@ -123,3 +125,44 @@ def test_gather_read_split_past_one_table():
             changed = bool((sink != 0).any())
             assert changed == hit, f"position {pos} of head {h}: read {changed}, expected {hit}"
     say("    rows past the first 4096-slot table read once each")
+
+
+def _dot_case(n_rows, G, positive, seed):
+    g = torch.Generator().manual_seed(seed)
+    if positive:                        # every product positive: no cancellation in the sums
+        rows = (0.5 + 1.5 * torch.rand(n_rows, 128, generator=g)).to(torch.bfloat16)
+        q = (0.5 + 1.5 * torch.rand(G, 128, generator=g)).to(torch.bfloat16)
+    else:
+        rows = torch.randn(n_rows, 128, generator=g).to(torch.bfloat16)
+        q = torch.randn(G, 128, generator=g).to(torch.bfloat16)
+    dots = rows.double() @ q.double().T                  # [n_rows][G], exact in fp64
+    return rows, q, float(dots.sum()), float(dots.abs().sum())
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("n_rows,wg", [(16 * 4099, 1024), (16 * 4099, 37), (16, 3)])
+def test_group_dot_sums_every_product(G, n_rows, wg):
+    """Units 1 (vector ALUs) and 2 (MFMA) against the fp64 sum of q_g . k_j over all rows and
+    heads.  With positive inputs one missed 16-row group or head moves the sum by more than
+    1/4100 of it, far above fp32 rounding (bound 2e-5 of the sum); with signed inputs the bound
+    is 2e-5 of the sum of magnitudes.  Unit 0 leaves part alone.  Ragged: 4099 groups over 1024
+    or 37 workgroups, and one group over 3 (two idle workgroups write zero)."""
+    for positive in (True, False):
+        say(f"[group_dot] G={G} rows={n_rows} wg={wg} positive={positive}")
+        rows, q, ref, mag = _dot_case(n_rows, G, positive, seed=G * 1000 + n_rows % 997 + wg)
+        rd, qd = rows.to(DEV), q.to(DEV)
+        sink = torch.zeros(64, dtype=torch.int32, device=DEV)
+        got = {}
+        for unit in ("valu", "mfma"):
+            part = torch.full((wg,), float("nan"), device=DEV)
+            B.sfi_group_dot(rd, qd, unit, wg, part, sink)
+            torch.cuda.synchronize()
+            assert torch.isfinite(part).all(), unit
+            got[unit] = float(part.double().sum())
+            bound = 2e-5 * (abs(ref) if positive else mag)
+            assert abs(got[unit] - ref) <= bound, (unit, got[unit], ref, bound)
+        assert abs(got["valu"] - got["mfma"]) <= 2e-5 * mag
+        part = torch.full((wg,), 7.0, device=DEV)
+        B.sfi_group_dot(rd, qd, "read", wg, part, sink)
+        torch.cuda.synchronize()
+        assert bool((part == 7.0).all())
