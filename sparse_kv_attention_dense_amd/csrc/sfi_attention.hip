@@ -104,13 +104,15 @@ __device__ bool locate_split(const AttnArgs& a, int wg, int* sh, int* loc) {
     return found;
 }
 
-// Merges the nsplit partial records of query head i of batch b into out and lse.  Thread
-// (dim, phase) folds splits phase, phase + R, ... into a running (M, L, A) with the
-// log-sum-exp rule, a batch of records at a time; the R phases then merge through LDS (s_m,
-// s_l, s_a: kThreads floats each).
-template <int D, bool SPARSE>
+constexpr int kWideCombine = 1024;                 // combine threads for many splits
+
+// Merges the nsplit partial records of query head i of batch b into out and lse with NT
+// threads.  Thread (dim, phase) folds splits phase, phase + R, ... into a running (M, L, A)
+// with the log-sum-exp rule, a batch of records at a time; the R phases then merge through
+// LDS (s_m, s_l, s_a: NT floats each).
+template <int D, bool SPARSE, int NT>
 __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s_l, float* s_a) {
-    constexpr int R = kThreads / D;
+    constexpr int R = NT / D;
     const int tid = threadIdx.x;
     const int G = a.G, h = i / G, g = i - h * G;
     const int S = SPARSE ? a.nsplit : splits_of(a, a.len[b]), rec = a.rec_floats;
@@ -119,7 +121,7 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
     // dense step of the fused slow step: the last wavefront folds the splits' (m, l) pairs over
     // J with the same rule, its first batch of loads issued before the main merge
     constexpr int kJB = 4;                           // pairs per lane per batch
-    const bool j_merge = !SPARSE && a.lse_j != nullptr && (tid >> 6) == kThreads / 64 - 1;
+    const bool j_merge = !SPARSE && a.lse_j != nullptr && (tid >> 6) == NT / 64 - 1;
     float jm[kJB], jl[kJB];
     if (j_merge) {
 #pragma unroll
@@ -206,9 +208,17 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
                 };
 #pragma unroll
                 for (int u = 0; u < kJB; ++u) fold(jm[u], jl[u]);
-                for (int sp = lane + 64 * kJB; sp < S; sp += 64) {
-                    const float* r = base + (int64_t)sp * rec + G * D + 2 * G + 2 * g;
-                    fold(r[0], r[1]);
+                // the rest kJB pairs per lane at a time, every load of a batch issued first
+                for (int sp0 = lane + 64 * kJB; sp0 < S; sp0 += 64 * kJB) {
+#pragma unroll
+                    for (int u = 0; u < kJB; ++u) {
+                        const int sp = sp0 + 64 * u;
+                        const float* r = base + (int64_t)(sp < S ? sp : 0) * rec + G * D + 2 * G + 2 * g;
+                        jm[u] = sp < S ? r[0] : -INFINITY;
+                        jl[u] = sp < S ? r[1] : 0.f;
+                    }
+#pragma unroll
+                    for (int u = 0; u < kJB; ++u) fold(jm[u], jl[u]);
                 }
                 for (int o = 32; o >= 1; o >>= 1) fold(__shfl_xor(Mj, o), __shfl_xor(Lj, o));
                 if (lane == 0) a.lse_j[b * a.Hq + i] = Lj > 0.f ? (Mj + log2f(Lj)) * kLn2 : -INFINITY;
@@ -216,7 +226,7 @@ __device__ void merge_head(const AttnArgs& a, int b, int i, float* s_m, float* s
             // the Selector's digit-0 histogram of this head's KV group starts empty
             if (g == 0 && a.sel_hist) {
                 uint32_t* hh = a.sel_hist + (int64_t)(b * a.Hkv + h) * kSelHistBins;
-                for (int t = tid; t < kSelHistBins; t += kThreads) hh[t] = 0u;
+                for (int t = tid; t < kSelHistBins; t += NT) hh[t] = 0u;
             }
         }
     }
@@ -990,15 +1000,16 @@ attention_kernel(AttnArgs a_in) {
     }
 }
 
-// One workgroup per query head (blockIdx.x) of batch blockIdx.y merges the split records.
-template <int D, bool SPARSE>
-__global__ void __launch_bounds__(kThreads) combine_kernel(AttnArgs a_in) {
-    __shared__ float s_m[kThreads], s_l[kThreads], s_a[kThreads];
+// One workgroup of NT threads per query head (blockIdx.x) of batch blockIdx.y merges the
+// split records.
+template <int D, bool SPARSE, int NT>
+__global__ void __launch_bounds__(NT) combine_kernel(AttnArgs a_in) {
+    __shared__ float s_m[NT], s_l[NT], s_a[NT];
     AttnArgs a = a_in;
     if constexpr (SPARSE) {
         if (a.step) apply_step(a);
     }
-    merge_head<D, SPARSE>(a, blockIdx.y, blockIdx.x, s_m, s_l, s_a);
+    merge_head<D, SPARSE, NT>(a, blockIdx.y, blockIdx.x, s_m, s_l, s_a);
 }
 
 template <bool BF, int D, bool PAGED, bool SPARSE>
@@ -1007,7 +1018,13 @@ hipError_t launch_one(const AttnArgs& a, int B, hipStream_t stream) {
     hipLaunchKernelGGL((attention_kernel<BF, D, PAGED, SPARSE>), grid,
                        dim3(Cfg<BF, D, PAGED, SPARSE>::kNT),
                        (size_t)a.tab_bytes, stream, a);
-    hipLaunchKernelGGL((combine_kernel<D, SPARSE>), dim3(a.Hq, B), dim3(kThreads), 0, stream, a);
+    // a head's records merge in one batch of loads per thread up to 16 * NT / D records: past
+    // 16 * kThreads / D (32 at d = 128; the dense step of one sequence at 512K has 128 per
+    // head, a single KV head's 1024) the merge takes 1024 threads
+    if (a.nsplit > 16 * (kThreads / D))
+        hipLaunchKernelGGL((combine_kernel<D, SPARSE, kWideCombine>), dim3(a.Hq, B), dim3(kWideCombine), 0, stream, a);
+    else
+        hipLaunchKernelGGL((combine_kernel<D, SPARSE, kThreads>), dim3(a.Hq, B), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -95,6 +95,10 @@ WORKLOADS = {
                  paged=True, block_size=16, len_lo=8192),
         Workload("gqa8_512k", 5000, 1, 64, 8, 128, "bf16", 524288, 4, 1024, 8192, 32,
                  sink=True, mask_frac=0.25),
+        # one GPU's share of gqa8_512k split by KV head over 8 GPUs (tensor-parallel
+        # attention): one KV group of 8 query heads at the same context and budget
+        Workload("gqa8_512k_tp8", 6000, 1, 8, 1, 128, "bf16", 524288, 4, 1024, 8192, 32,
+                 sink=True, mask_frac=0.25),
     ]
 }
 

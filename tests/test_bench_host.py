@@ -33,6 +33,8 @@ def test_more_than_one_gpu_is_refused():
     ("sink_128k_b4", 4 * 8 * 131072 * (512 + 16) + 128 * 128 * (2 + 4) + 128 * 4),
     # 1 sequence x 8 KV heads x 524288 positions x (512 B + 8 heads x 4 B), 64 query heads
     ("gqa8_512k", 8 * 524288 * (512 + 32) + 64 * 128 * (2 + 4) + 64 * 4),
+    # its share on one of 8 GPUs split by KV head: 1 KV head, 8 query heads
+    ("gqa8_512k_tp8", 1 * 524288 * (512 + 32) + 8 * 128 * (2 + 4) + 8 * 4),
     # 2048 positions, fp32 rows of 64 dims (2 x 256 B), 4 heads x 4 B of logits
     ("tiny_2k_f32", 1 * 2048 * (512 + 16) + 4 * 64 * (4 + 4) + 4 * 4),
 ])

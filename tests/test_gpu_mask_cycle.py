@@ -45,6 +45,7 @@ CYCLES = {
     "sink_128k_b4": W["sink_128k_b4"].scaled(10001, B=2),
     "ragged_paged_b16": W["ragged_paged_b16"].scaled(7000, B=3, len_lo=3000),
     "gqa8_512k": W["gqa8_512k"].scaled(14001),
+    "gqa8_512k_tp8": W["gqa8_512k_tp8"].scaled(15013),
 }
 
 
