@@ -37,6 +37,7 @@ constexpr int64_t kSmallDenseRows = int64_t(1) << 20;    // one round of workgro
 constexpr int64_t kPagedTargetWorkgroups = 2048;
 constexpr int64_t kSparseTargetWorkgroups = 256;
 constexpr int64_t kSparseQuantum = kTile;
+constexpr int64_t kSparseManySplits = 64;
 constexpr size_t kAlign = 256;
 constexpr double kUnitFixedUs = 14.7;           // Selector path estimates, see select_unit_path
 constexpr double kUnitUsPerPos = 6.0e-4;
@@ -94,6 +95,11 @@ sfi_status plan_attention(const sfi_kv_desc& kv, bool sparse, int64_t idx_stride
                                            : (small ? kSmallTargetWorkgroups : kTargetWorkgroups));
     const int64_t per_unit = ceil_div(target, units);
     int64_t split = ceil_div(ceil_div(slots, per_unit), quantum) * quantum;
+    // a fast step over few KV heads would otherwise cut each head into many splits of one or
+    // two tiles (one KV head at 512K: 145 splits of 64 slots, two of four wavefronts idle, 145
+    // records to merge); past kSparseManySplits a split holds at least one tile per wavefront
+    if (sparse && ceil_div(slots, split) > kSparseManySplits && split < kTile * kWaves)
+        split = kTile * kWaves;
     if ((sparse || paged) && split > kTabMax) split = kTabMax;
     int64_t nsplit = ceil_div(slots, split);
     if (nsplit > kMaxSplits) {
