@@ -109,6 +109,9 @@ CASES = {
     "sink_128k_b4": W["sink_128k_b4"].scaled(20001, B=2),
     "ragged_paged_b16": W["ragged_paged_b16"].scaled(9000, B=4, len_lo=3000),
     "gqa8_512k": W["gqa8_512k"].scaled(30001, k_sel=2048),
+    # one KV head over 1.2M positions: 938 dense splits per head, so the merge runs 1024
+    # threads and folds the splits' sums over J in several batches past the first 256
+    "gqa8_512k_tp8": W["gqa8_512k_tp8"].scaled(1200003, k_sel=2048),
 }
 
 
