@@ -74,6 +74,41 @@ def test_dense_paged_page_sizes(orc, dtype, d, G, block):
     assert_logits(logits, ez, lay.len0_host, tol["rel"])
 
 
+@pytest.mark.parametrize("case", range(10))
+def test_dense_random_shapes(orc, case):
+    """Seeded random dense steps against the oracle: batch 1-5 with lengths 0-20000 (a zero
+    length on every third case with more than one sequence), 1-4 KV heads, groups of 1-16 query heads, d 64 or 128, bf16
+    or fp32, a contiguous cache or pages of 1, 16 or 64 positions; out, lse and every logit
+    below each length, and no logit written past it."""
+    rng = np.random.default_rng(3000 + case)
+    Bn = int(rng.integers(1, 6))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    block = int(rng.choice([0, 1, 16, 64]))
+    lens = [int(x) for x in rng.integers(1, 20001, size=Bn)]
+    if case % 3 == 0 and Bn > 1:                 # a whole batch of empty sequences has no
+        lens[int(rng.integers(0, Bn))] = 0      # cache to point at (the ABI rejects that)
+    wl = synth.Workload(f"dense_rand{case}", 9500 + case, Bn, Hkv * G, Hkv, d, dtype,
+                        max(max(lens), 1), 4, 64, 128, 1, paged=block > 0,
+                        block_size=max(block, 1))
+    say(f"[dense random {case}] B={Bn} Hkv={Hkv} G={G} d={d} {dtype} block={block} lens={lens}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=lens)
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    out, lse, logits, _ = gpu_dense(lay, q)
+    eo, el, ez = orc.dense(oracle_cache(orc, lay, lens), q)
+    tol = tolerances(wl)
+    assert_close_out(out.cpu().numpy(), eo, tol["out"])
+    assert_close_rel(lse.cpu().numpy(), el, tol["rel"], "lse")
+    assert_logits(logits, ez, lens, tol["rel"])
+    lg = logits.cpu()
+    for b, n in enumerate(lens):
+        assert torch.isnan(lg[b, :, n:]).all(), "logits written past len"
+        if n == 0:
+            assert (out[b] == 0).all() and torch.isneginf(lse[b]).all()
+
+
 def test_dense_loose_length_bound(orc):
     """max_len is only a host-side bound for the launch plan: a bound three times the longest
     sequence (as a captured step that must serve later, longer steps would declare) gives the

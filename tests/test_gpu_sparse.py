@@ -103,6 +103,42 @@ def test_sparse_largest_split(orc):
     _check(orc, lay, q, 1, idx, n_idx)
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_sparse_random_shapes(orc, case):
+    """Seeded random fast steps against the oracle: batch 1-4, 1-4 KV heads, groups of 1-16
+    query heads, d 64 or 128, bf16 or fp32, a contiguous cache or pages of 1, 16 or 64
+    positions, lengths 1-12000, 0-8 sinks, a recent window of 0-300, a budget of 1-3000 (often
+    past the allowed set of the short sequences), span or scattered selections, a step 0-4
+    tokens into the cycle, and on every third case a random head mask."""
+    rng = np.random.default_rng(2000 + case)
+    Bn = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    block = int(rng.choice([0, 1, 16, 64]))
+    lens = [int(x) for x in rng.integers(1, 12001, size=Bn)]
+    n_sink = int(rng.integers(0, 9))
+    n_recent = int(rng.integers(0, 301))
+    k_sel = int(rng.integers(1, 3001))
+    cycle = 5
+    wl = synth.Workload(f"sp_rand{case}", 9000 + case, Bn, Hkv * G, Hkv, d, dtype, max(lens),
+                        n_sink, n_recent, k_sel, cycle, paged=block > 0,
+                        block_size=max(block, 1))
+    kind = "spans" if case % 2 else "scattered"
+    t = int(rng.integers(0, cycle))
+    say(f"[sparse random {case}] B={Bn} Hkv={Hkv} G={G} d={d} {dtype} block={block} "
+        f"lens={lens} sink={n_sink} recent={n_recent} k={k_sel} {kind} t={t}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=lens)
+    idx, n_idx = synth.synthetic_index_set(lay, kind, seed=40 + case)
+    hm = None
+    if case % 3 == 0:
+        g = torch.Generator().manual_seed(60 + case)
+        hm = (torch.rand((Bn, Hkv * G), generator=g) < 0.3).to(torch.uint8)
+    q = synth.make_query(wl, 0, t, device=DEV)
+    _check(orc, lay, q, t, idx, n_idx, head_mask=hm)
+
+
 def test_sparse_full_set_equals_dense(orc):
     """idx = every position before the recent window: the fast step is the dense step."""
     wl = W["gqa4_32k"].scaled(7001)
