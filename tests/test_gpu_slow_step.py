@@ -167,6 +167,37 @@ def test_slow_step_edges_of_the_allowed_set(orc, n_sink, n_recent, k_sel):
     _check_against_separate_calls(orc, lay, q, res, **kw)
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_slow_step_random_shapes(orc, case):
+    """Seeded random slow steps (dense step, Selector and mask in one call): batch 1-3 with
+    lengths 1-20000, 1-4 KV heads, groups of 1-8 query heads, d 64 or 128, bf16 or fp32, a
+    contiguous or 16-position paged cache, 0-8 sinks, a recent window of 0-500, a budget of
+    1-3000 and a mask over a quarter of the heads on odd cases; against the oracle chain and
+    the separate calls."""
+    import dataclasses
+    rng = np.random.default_rng(4000 + case)
+    Bn = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 5))
+    G = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    paged = bool(rng.integers(0, 2))
+    lens = [int(x) for x in rng.integers(1, 20001, size=Bn)]
+    n_sink = int(rng.integers(0, 9))
+    n_recent = int(rng.integers(0, 501))
+    k_sel = int(rng.integers(1, 3001))
+    wl = synth.Workload(f"slow_rand{case}", 9700 + case, Bn, Hkv * G, Hkv, d, dtype, max(lens),
+                        n_sink, n_recent, k_sel, 2, paged=paged, block_size=16,
+                        mask_frac=0.25 if case % 2 else 0.0)
+    say(f"[slow random {case}] B={Bn} Hkv={Hkv} G={G} d={d} {dtype} paged={paged} lens={lens} "
+        f"sink={n_sink} recent={n_recent} k={k_sel} mask={wl.mask_frac}")
+    lay = synth.make_layer(wl, 0, device=DEV, lens=lens)
+    q = synth.make_query(wl, 0, 0, device=DEV)
+    res = _slow(lay, q)
+    _check_against_oracle(orc, lay, q, res)
+    _check_against_separate_calls(orc, lay, q, res)
+
+
 def test_slow_step_full_size_128k(orc):
     """The 128K batch at full size in the benchmark's launch configuration: out, lse, logits
     identical to sfi_dense_decode; the selection against sfi_select on the same logits (near-ties
